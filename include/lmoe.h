@@ -1,0 +1,165 @@
+/*
+ * lmoe — latent mixture-of-experts block forward on AMD MI355X (gfx950).
+ *
+ * C ABI of the library liblmoe.so. The block computed by lmoe_forward is the one
+ * described for Muse Spark Open's MoE layers (LMSYS blog "SGLang and Miles Add
+ * Day-0 Support for Muse Spark Open", section "MoE with pooler, unpooler and
+ * per-expert normalization"; vLLM day-0 summary, section "Latent MoE"):
+ *
+ *   logits = x . W_router^T (+ b_router)                  [T, E]   fp32
+ *   ids, w = top-k(logits), softmax over the k selected    [T, k]
+ *   P      = x . W_pool^T                                  [T, Dp]
+ *   xp     = P / sqrt(mean(P^2) + eps_pool) * g_pool
+ *   for each selected expert e of token t (slot j):
+ *     h    = silu(xp . W_gate[e]^T) * (xp . W_up[e]^T)     [F]
+ *     y    = h . W_down[e]^T                               [Dp]
+ *     z    = y / sqrt(mean(y^2) + eps_expert) * g_expert[e]
+ *   u      = sum_j w_j * z_j    (accumulated in fp32)      [T, Dp]
+ *   out    = u . W_unpool^T                                [T, D]
+ *
+ * Precision (BF16 activations): fp32 accumulation everywhere; router logits,
+ * routing weights and the weighted sum are fp32; the pooled expert input xp, the
+ * SwiGLU output h, each expert output y (whose RMS is taken from its BF16 values,
+ * as the blog's "Fused per-expert post-norm" section describes) and the sum u
+ * (the unpooler's GEMM input) are held as bfloat16.
+ *
+ * Conventions for every function below:
+ *  - Pointers inside lmoe_weights / lmoe_aux and the x / out arguments are DEVICE
+ *    pointers on the device that was current at lmoe_create; every other pointer
+ *    is a host pointer. Device pointers must be 16-byte aligned.
+ *  - All matrices are row-major; weights use the [out][in] convention, so every
+ *    GEMM reads both operands along the contiguous inner dimension.
+ *  - Functions return an lmoe_status. On an error nothing is enqueued and
+ *    lmoe_last_error() describes it (thread-local). No C++ exception crosses
+ *    this interface.
+ */
+#ifndef LMOE_H
+#define LMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LMOE_ABI_VERSION 1
+
+typedef struct lmoe_ctx* lmoe_handle;
+
+typedef enum {
+  LMOE_OK = 0,
+  LMOE_E_INVAL = -1,        /* bad argument: null/misaligned pointer, bad size, T > max_tokens */
+  LMOE_E_UNSUPPORTED = -2,  /* valid but not implemented: shape or dtype combination */
+  LMOE_E_NOMEM = -3,        /* workspace allocation failed */
+  LMOE_E_HIP = -4           /* a HIP runtime call or kernel launch failed */
+} lmoe_status;
+
+typedef enum {
+  LMOE_F32 = 0,
+  LMOE_BF16 = 1,
+  LMOE_MXFP4 = 2,           /* reserved: expert weights as E2M1 + E8M0 per 32 */
+  LMOE_MXFP8_E4M3 = 3       /* reserved */
+} lmoe_dtype;
+
+#define LMOE_FLAG_ROUTER_BIAS 1u   /* lmoe_weights.b_router is present */
+
+/* Block configuration (host struct, copied at create).
+ * Shapes: d_model (D), d_pooled (Dp), d_ff (F) must be multiples of 64;
+ * 1 <= n_experts (E) <= 1024; 1 <= top_k (k) <= min(E, 16); max_tokens >= 1.
+ * act_dtype: LMOE_F32 or LMOE_BF16 — dtype of x, out, W_router, W_pool,
+ * W_unpool and of the expert weights (expert_wdtype must equal act_dtype).
+ * Gammas and the router bias are always fp32. */
+typedef struct {
+  int32_t abi_version;      /* LMOE_ABI_VERSION */
+  int32_t d_model;
+  int32_t d_pooled;
+  int32_t d_ff;
+  int32_t n_experts;
+  int32_t top_k;
+  float eps_pool;           /* RMSNorm eps of the pooled input */
+  float eps_expert;         /* RMSNorm eps of each expert output */
+  int32_t act_dtype;        /* lmoe_dtype */
+  int32_t expert_wdtype;    /* lmoe_dtype */
+  int32_t max_tokens;       /* the workspace is sized for this many tokens */
+  uint32_t flags;           /* LMOE_FLAG_* */
+} lmoe_config;
+
+/* Weights: device pointers, BORROWED. The caller keeps them alive and unchanged
+ * until lmoe_destroy; the library never copies or repacks them. */
+typedef struct {
+  const void* w_router;     /* [E][D]   act_dtype */
+  const float* b_router;    /* [E] fp32, required iff flags has LMOE_FLAG_ROUTER_BIAS */
+  const void* w_pool;       /* [Dp][D]  act_dtype */
+  const float* g_pool;      /* [Dp] fp32 */
+  const void* w_gate_up;    /* [E][2F][Dp]: rows [0, F) gate, rows [F, 2F) up */
+  const uint8_t* s_gate_up; /* reserved (MX scales); must be NULL */
+  const void* w_down;       /* [E][Dp][F] */
+  const uint8_t* s_down;    /* reserved (MX scales); must be NULL */
+  const float* g_expert;    /* [E][Dp] fp32 */
+  const void* w_unpool;     /* [D][Dp]  act_dtype */
+} lmoe_weights;
+
+/* Optional outputs of the routing steps (device pointers; any may be NULL).
+ * Filled by the same lmoe_forward call, asynchronously on its stream. */
+typedef struct {
+  float* logits;            /* [T][E] fp32, bias included */
+  int32_t* topk_ids;        /* [T][k], logit descending, ties to the lower expert id */
+  float* topk_w;            /* [T][k] softmax of the selected logits */
+  int32_t* expert_offsets;  /* [E+1] exclusive prefix sum of the per-expert counts */
+  int32_t* sorted_assign;   /* [T*k] assignment t*k+j at each sorted position;
+                               order (expert asc, token asc) */
+} lmoe_aux;
+
+/* Create a handle: validates cfg and the weight pointers, allocates the
+ * workspace for cfg->max_tokens on the current device. *out receives the handle
+ * (NULL on error). */
+lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, lmoe_handle* out);
+
+/* Run the block on T tokens: x [T][D] -> out [T][D] (act_dtype), enqueued on
+ * hip_stream (a hipStream_t; NULL is the null stream). Asynchronous: kernel
+ * faults surface at the caller's next synchronization. T == 0 enqueues nothing
+ * and returns LMOE_OK; T > max_tokens is LMOE_E_INVAL. out must not overlap x.
+ * The handle's workspace is shared: calls on one handle must not overlap in time
+ * (use one stream per handle). aux may be NULL. */
+lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, void* hip_stream,
+                         const lmoe_aux* aux);
+
+/* Free the workspace and the handle. NULL is allowed (LMOE_OK). The caller must
+ * make sure no enqueued forward on this handle is still running. */
+lmoe_status lmoe_destroy(lmoe_handle h);
+
+/* Device workspace bytes a handle with this configuration allocates. */
+lmoe_status lmoe_workspace_bytes(const lmoe_config* cfg, size_t* out);
+
+/* Per-stage device timing. When enabled, lmoe_forward records a HIP event pair
+ * around every stage on its stream; lmoe_get_timing waits for the recorded
+ * events and returns the accumulated milliseconds per stage and the number of
+ * forward calls timed, then resets the accumulators. */
+typedef enum {
+  LMOE_STAGE_PROJ_IN = 0,   /* router + pooler GEMM (one launch) */
+  LMOE_STAGE_TOPK = 1,      /* top-k + softmax + per-chunk expert masks */
+  LMOE_STAGE_SORT = 2,      /* counting-sort scan + scatter + tile list */
+  LMOE_STAGE_POOL_NORM = 3, /* pooled RMSNorm */
+  LMOE_STAGE_GATE_UP = 4,   /* grouped gate/up GEMM + SwiGLU */
+  LMOE_STAGE_DOWN = 5,      /* grouped down GEMM + sum-of-squares partials */
+  LMOE_STAGE_COMBINE = 6,   /* per-expert RMSNorm + weighted sum */
+  LMOE_STAGE_UNPOOL = 7,    /* unpooler GEMM */
+  LMOE_NUM_STAGES = 8
+} lmoe_stage;
+
+lmoe_status lmoe_set_timing(lmoe_handle h, int enable);
+lmoe_status lmoe_get_timing(lmoe_handle h, float* ms_per_stage /* [LMOE_NUM_STAGES] */,
+                            int32_t* n_forward);
+
+/* Static description of a status code. */
+const char* lmoe_status_str(lmoe_status s);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* lmoe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMOE_H */

@@ -1,0 +1,421 @@
+// C ABI of the latent-MoE block (include/lmoe.h): argument checks, the
+// workspace plan and the launch sequence of one forward pass on one stream.
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/lmoe.h"
+#include "kernels.h"
+
+using namespace lmoe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lmoe_status fail(lmoe_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Byte layout of the workspace for a configuration (every region 256-byte aligned).
+struct Plan {
+  size_t P, logits, ids, w, masks, chunk_base, counts, offsets, sorted_assign, inv, row_token,
+      tiles, n_tiles, xp, H, Y, ss, u;
+  size_t total;
+  int max_slots;
+};
+
+size_t grow(size_t& cur, size_t bytes) {
+  const size_t at = cur;
+  cur += (bytes + 255) & ~size_t(255);
+  return at;
+}
+
+int slots_for(int64_t T, int k, int E) {
+  const int64_t A = T * k;
+  return (int)((A + kGemmBM - 1) / kGemmBM + (A < E ? A : E));
+}
+
+Plan make_plan(const lmoe_config& c) {
+  Plan p{};
+  const int64_t Tm = c.max_tokens, k = c.top_k, E = c.n_experts, Dp = c.d_pooled, F = c.d_ff;
+  const int64_t A = Tm * k;
+  const int64_t es = c.act_dtype == LMOE_BF16 ? 2 : 4;
+  const int64_t n_chunks = (Tm + 63) / 64;
+  p.max_slots = slots_for(Tm, (int)k, (int)E);
+  size_t cur = 0;
+  p.P = grow(cur, Tm * Dp * 4);
+  p.logits = grow(cur, Tm * E * 4);
+  p.ids = grow(cur, A * 4);
+  p.w = grow(cur, A * 4);
+  p.masks = grow(cur, n_chunks * E * 8);
+  p.chunk_base = grow(cur, n_chunks * E * 4);
+  p.counts = grow(cur, E * 4);
+  p.offsets = grow(cur, (E + 1) * 4);
+  p.sorted_assign = grow(cur, A * 4);
+  p.inv = grow(cur, A * 4);
+  p.row_token = grow(cur, A * 4);
+  p.tiles = grow(cur, (size_t)p.max_slots * 8);
+  p.n_tiles = grow(cur, 4);
+  p.xp = grow(cur, Tm * Dp * es);
+  p.H = grow(cur, A * F * es);
+  p.Y = grow(cur, A * Dp * es);
+  p.ss = grow(cur, A * (Dp / 64) * 4);
+  p.u = grow(cur, Tm * Dp * es);
+  p.total = cur;
+  return p;
+}
+
+lmoe_status check_config(const lmoe_config* c) {
+  if (!c) return fail(LMOE_E_INVAL, "config is NULL");
+  if (c->abi_version != LMOE_ABI_VERSION)
+    return fail(LMOE_E_INVAL, "abi_version " + std::to_string(c->abi_version) + " != " +
+                                  std::to_string(LMOE_ABI_VERSION));
+  if (c->d_model <= 0 || c->d_pooled <= 0 || c->d_ff <= 0 || c->d_model % 64 || c->d_pooled % 64 ||
+      c->d_ff % 64)
+    return fail(LMOE_E_UNSUPPORTED, "d_model, d_pooled and d_ff must be positive multiples of 64");
+  if (c->n_experts < 1 || c->n_experts > 1024)
+    return fail(LMOE_E_UNSUPPORTED, "n_experts must be in [1, 1024]");
+  if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts)
+    return fail(LMOE_E_UNSUPPORTED, "top_k must be in [1, min(n_experts, 16)]");
+  if (!(c->eps_pool >= 0.f) || !(c->eps_expert >= 0.f) || c->eps_pool > 1e30f || c->eps_expert > 1e30f)
+    return fail(LMOE_E_INVAL, "eps_pool and eps_expert must be finite and >= 0");
+  if (c->act_dtype != LMOE_F32 && c->act_dtype != LMOE_BF16)
+    return fail(LMOE_E_UNSUPPORTED, "act_dtype must be LMOE_F32 or LMOE_BF16");
+  if (c->expert_wdtype != c->act_dtype)
+    return fail(LMOE_E_UNSUPPORTED, "expert_wdtype must equal act_dtype (MX experts not built)");
+  if (c->max_tokens < 1) return fail(LMOE_E_INVAL, "max_tokens must be >= 1");
+  if ((int64_t)c->max_tokens * c->top_k > (int64_t)INT32_MAX / 2 ||
+      (int64_t)c->max_tokens * c->top_k * c->d_ff > (int64_t)1 << 40)
+    return fail(LMOE_E_UNSUPPORTED, "max_tokens too large");
+  if (c->flags & ~LMOE_FLAG_ROUTER_BIAS) return fail(LMOE_E_INVAL, "unknown flag bits");
+  return LMOE_OK;
+}
+
+}  // namespace
+
+struct lmoe_ctx {
+  lmoe_config cfg;
+  lmoe_weights w;
+  int device;
+  Plan plan;
+  unsigned char* ws;
+  bool timing;
+  std::vector<hipEvent_t> events;   // LMOE_NUM_STAGES + 1 per timed forward
+  float acc_ms[LMOE_NUM_STAGES];
+  int n_timed;
+};
+
+extern "C" {
+
+const char* lmoe_status_str(lmoe_status s) {
+  switch (s) {
+    case LMOE_OK: return "LMOE_OK";
+    case LMOE_E_INVAL: return "LMOE_E_INVAL: invalid argument";
+    case LMOE_E_UNSUPPORTED: return "LMOE_E_UNSUPPORTED: unsupported configuration";
+    case LMOE_E_NOMEM: return "LMOE_E_NOMEM: device allocation failed";
+    case LMOE_E_HIP: return "LMOE_E_HIP: HIP runtime error";
+  }
+  return "unknown lmoe_status";
+}
+
+const char* lmoe_last_error(void) { return g_last_error.c_str(); }
+
+lmoe_status lmoe_workspace_bytes(const lmoe_config* cfg, size_t* out) {
+  if (!out) return fail(LMOE_E_INVAL, "out is NULL");
+  lmoe_status st = check_config(cfg);
+  if (st != LMOE_OK) return st;
+  *out = make_plan(*cfg).total;
+  return LMOE_OK;
+}
+
+lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, lmoe_handle* out) {
+  g_last_error.clear();
+  if (!out) return fail(LMOE_E_INVAL, "out is NULL");
+  *out = nullptr;
+  lmoe_status st = check_config(cfg);
+  if (st != LMOE_OK) return st;
+  if (!w) return fail(LMOE_E_INVAL, "weights is NULL");
+  const void* req[] = {w->w_router, w->w_pool, w->g_pool, w->w_gate_up, w->w_down, w->g_expert,
+                       w->w_unpool};
+  const char* names[] = {"w_router", "w_pool", "g_pool", "w_gate_up", "w_down", "g_expert", "w_unpool"};
+  for (int i = 0; i < 7; ++i) {
+    if (!req[i]) return fail(LMOE_E_INVAL, std::string(names[i]) + " is NULL");
+    if (!aligned16(req[i])) return fail(LMOE_E_INVAL, std::string(names[i]) + " is not 16-byte aligned");
+  }
+  const bool has_bias = (cfg->flags & LMOE_FLAG_ROUTER_BIAS) != 0;
+  if (has_bias != (w->b_router != nullptr))
+    return fail(LMOE_E_INVAL, "b_router must be given iff LMOE_FLAG_ROUTER_BIAS is set");
+  if (w->b_router && !aligned4(w->b_router)) return fail(LMOE_E_INVAL, "b_router is misaligned");
+  if (w->s_gate_up || w->s_down) return fail(LMOE_E_INVAL, "MX scale pointers must be NULL");
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(LMOE_E_HIP, "hipGetDevice failed");
+  lmoe_ctx* h = new (std::nothrow) lmoe_ctx();
+  if (!h) return fail(LMOE_E_NOMEM, "host allocation failed");
+  h->cfg = *cfg;
+  h->w = *w;
+  h->device = dev;
+  h->plan = make_plan(*cfg);
+  h->ws = nullptr;
+  if (hipMalloc(reinterpret_cast<void**>(&h->ws), h->plan.total) != hipSuccess) {
+    (void)hipGetLastError();
+    const std::string msg = "hipMalloc of " + std::to_string(h->plan.total) + " workspace bytes failed";
+    delete h;
+    return fail(LMOE_E_NOMEM, msg);
+  }
+  h->timing = false;
+  memset(h->acc_ms, 0, sizeof(h->acc_ms));
+  h->n_timed = 0;
+  *out = h;
+  return LMOE_OK;
+}
+
+lmoe_status lmoe_destroy(lmoe_handle h) {
+  if (!h) return LMOE_OK;
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  if (cur != h->device) (void)hipSetDevice(h->device);
+  for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
+  hipError_t err = h->ws ? hipFree(h->ws) : hipSuccess;
+  if (cur != h->device) (void)hipSetDevice(cur);
+  delete h;
+  if (err != hipSuccess) return fail(LMOE_E_HIP, std::string("hipFree: ") + hipGetErrorString(err));
+  return LMOE_OK;
+}
+
+lmoe_status lmoe_set_timing(lmoe_handle h, int enable) {
+  if (!h) return fail(LMOE_E_INVAL, "handle is NULL");
+  h->timing = enable != 0;
+  return LMOE_OK;
+}
+
+lmoe_status lmoe_get_timing(lmoe_handle h, float* ms_per_stage, int32_t* n_forward) {
+  if (!h || !ms_per_stage || !n_forward) return fail(LMOE_E_INVAL, "NULL argument");
+  const size_t per = LMOE_NUM_STAGES + 1;
+  for (size_t f = 0; f + per <= h->events.size(); f += per) {
+    if (hipEventSynchronize(h->events[f + per - 1]) != hipSuccess)
+      return fail(LMOE_E_HIP, "hipEventSynchronize failed");
+    for (int s = 0; s < LMOE_NUM_STAGES; ++s) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, h->events[f + s], h->events[f + s + 1]) != hipSuccess)
+        return fail(LMOE_E_HIP, "hipEventElapsedTime failed");
+      h->acc_ms[s] += ms;
+    }
+    ++h->n_timed;
+  }
+  for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
+  h->events.clear();
+  for (int s = 0; s < LMOE_NUM_STAGES; ++s) ms_per_stage[s] = h->acc_ms[s];
+  *n_forward = h->n_timed;
+  memset(h->acc_ms, 0, sizeof(h->acc_ms));
+  h->n_timed = 0;
+  return LMOE_OK;
+}
+
+lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, void* hip_stream,
+                         const lmoe_aux* aux) {
+  g_last_error.clear();
+  if (!h) return fail(LMOE_E_INVAL, "handle is NULL");
+  const lmoe_config& c = h->cfg;
+  if (T < 0 || T > c.max_tokens)
+    return fail(LMOE_E_INVAL, "T = " + std::to_string(T) + " outside [0, max_tokens = " +
+                                  std::to_string(c.max_tokens) + "]");
+  if (T == 0) return LMOE_OK;
+  if (!x || !out) return fail(LMOE_E_INVAL, "x or out is NULL");
+  if (!aligned16(x) || !aligned16(out)) return fail(LMOE_E_INVAL, "x or out is not 16-byte aligned");
+  const bool bf16 = c.act_dtype == LMOE_BF16;
+  const size_t es = bf16 ? 2 : 4;
+  const size_t io_bytes = (size_t)T * c.d_model * es;
+  const uintptr_t xb = reinterpret_cast<uintptr_t>(x), ob = reinterpret_cast<uintptr_t>(out);
+  if (xb < ob + io_bytes && ob < xb + io_bytes) return fail(LMOE_E_INVAL, "out overlaps x");
+  if (aux) {
+    const void* ap[] = {aux->logits, aux->topk_ids, aux->topk_w, aux->expert_offsets, aux->sorted_assign};
+    for (const void* q : ap)
+      if (q && !aligned4(q)) return fail(LMOE_E_INVAL, "aux pointer is not 4-byte aligned");
+  }
+
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return fail(LMOE_E_HIP, "hipGetDevice failed");
+  if (cur != h->device && hipSetDevice(h->device) != hipSuccess)
+    return fail(LMOE_E_HIP, "hipSetDevice failed");
+
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const Plan& pl = h->plan;
+  unsigned char* ws = h->ws;
+  const int E = c.n_experts, k = c.top_k, D = c.d_model, Dp = c.d_pooled, F = c.d_ff;
+  float* P = reinterpret_cast<float*>(ws + pl.P);
+  float* logits = (aux && aux->logits) ? aux->logits : reinterpret_cast<float*>(ws + pl.logits);
+  int32_t* ids = (aux && aux->topk_ids) ? aux->topk_ids : reinterpret_cast<int32_t*>(ws + pl.ids);
+  float* tw = (aux && aux->topk_w) ? aux->topk_w : reinterpret_cast<float*>(ws + pl.w);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + pl.offsets);
+  int32_t* sorted_assign = reinterpret_cast<int32_t*>(ws + pl.sorted_assign);
+  int32_t* tiles = reinterpret_cast<int32_t*>(ws + pl.tiles);
+  int32_t* n_tiles = reinterpret_cast<int32_t*>(ws + pl.n_tiles);
+  int32_t* row_token = reinterpret_cast<int32_t*>(ws + pl.row_token);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + pl.inv);
+  void* xp = ws + pl.xp;
+  void* H = ws + pl.H;
+  void* Y = ws + pl.Y;
+  float* ss = reinterpret_cast<float*>(ws + pl.ss);
+  void* u = ws + pl.u;
+  const int slots = slots_for(T, k, E);
+
+  hipEvent_t ev[LMOE_NUM_STAGES + 1] = {};
+  const bool timing = h->timing;
+  if (timing)
+    for (auto& e : ev)
+      if (hipEventCreate(&e) != hipSuccess) return fail(LMOE_E_HIP, "hipEventCreate failed");
+  int stage = 0;
+  auto mark = [&]() {
+    if (timing) (void)hipEventRecord(ev[stage], s);
+    ++stage;
+  };
+
+  hipError_t err = hipSuccess;
+  auto run = [&](hipError_t e) {
+    if (err == hipSuccess) err = e;
+  };
+
+  // 1. router + pooler: one GEMM over [W_pool; W_router]
+  mark();
+  {
+    GemmParams g{};
+    g.M = T;
+    g.N = Dp + E;
+    g.K = D;
+    g.A = x;
+    g.lda = D;
+    g.B0 = h->w.w_pool;
+    g.B1 = h->w.w_router;
+    g.n_split = Dp;
+    g.ldb = D;
+    g.out0 = P;
+    g.ldo0 = Dp;
+    g.out1 = logits;
+    g.ldo1 = E;
+    g.bias1 = h->w.b_router;
+    run(launch_gemm(g, EPI_F32, bf16, s));
+  }
+  // 2. top-k + softmax + chunk masks
+  mark();
+  uint64_t* masks = reinterpret_cast<uint64_t*>(ws + pl.masks);
+  run(launch_topk(logits, T, E, k, ids, tw, masks, s));
+  // 3. counting sort + tile list
+  mark();
+  {
+    SortParams sp{};
+    sp.ids = ids;
+    sp.topk_w = tw;
+    sp.chunk_masks = masks;
+    sp.chunk_base = reinterpret_cast<int32_t*>(ws + pl.chunk_base);
+    sp.counts = reinterpret_cast<int32_t*>(ws + pl.counts);
+    sp.offsets = offsets;
+    sp.sorted_assign = sorted_assign;
+    sp.inv = inv;
+    sp.row_token = row_token;
+    sp.tiles = tiles;
+    sp.n_tiles = n_tiles;
+    sp.T = T;
+    sp.E = E;
+    sp.k = k;
+    sp.tile_m = kGemmBM;
+    run(launch_sort(sp, s));
+  }
+  // 4. pooled RMSNorm
+  mark();
+  run(launch_pool_norm(P, h->w.g_pool, T, Dp, c.eps_pool, xp, bf16, s));
+  // 5. gate/up grouped GEMM + SwiGLU
+  mark();
+  {
+    GemmParams g{};
+    g.N = F;
+    g.K = Dp;
+    g.A = xp;
+    g.lda = Dp;
+    g.a_gather = row_token;
+    g.B0 = h->w.w_gate_up;
+    g.ldb = Dp;
+    g.b_expert_stride = (int64_t)2 * F * Dp;
+    g.tiles = tiles;
+    g.n_tiles = n_tiles;
+    g.offsets = offsets;
+    g.max_slots = slots;
+    g.out0 = H;
+    g.ldo0 = F;
+    g.F = F;
+    run(launch_gemm(g, EPI_SWIGLU, bf16, s));
+  }
+  // 6. down grouped GEMM + sum-of-squares partials
+  mark();
+  {
+    GemmParams g{};
+    g.N = Dp;
+    g.K = F;
+    g.A = H;
+    g.lda = F;
+    g.B0 = h->w.w_down;
+    g.ldb = F;
+    g.b_expert_stride = (int64_t)Dp * F;
+    g.tiles = tiles;
+    g.n_tiles = n_tiles;
+    g.offsets = offsets;
+    g.max_slots = slots;
+    g.out0 = Y;
+    g.ldo0 = Dp;
+    g.ss_out = ss;
+    g.ss_ld = Dp / 64;
+    run(launch_gemm(g, EPI_DOWN, bf16, s));
+  }
+  // 7. per-expert RMSNorm + weighted sum
+  mark();
+  {
+    CombineParams cp{};
+    cp.y = Y;
+    cp.ss = ss;
+    cp.inv = inv;
+    cp.ids = ids;
+    cp.w = tw;
+    cp.g_expert = h->w.g_expert;
+    cp.u = u;
+    cp.T = T;
+    cp.k = k;
+    cp.Dp = Dp;
+    cp.eps = c.eps_expert;
+    run(launch_combine(cp, bf16, s));
+  }
+  // 8. unpooler
+  mark();
+  {
+    GemmParams g{};
+    g.M = T;
+    g.N = D;
+    g.K = Dp;
+    g.A = u;
+    g.lda = Dp;
+    g.B0 = h->w.w_unpool;
+    g.ldb = Dp;
+    g.out0 = out;
+    g.ldo0 = D;
+    run(launch_gemm(g, EPI_ACT, bf16, s));
+  }
+  mark();
+  if (aux && aux->expert_offsets)
+    run(hipMemcpyAsync(aux->expert_offsets, offsets, sizeof(int32_t) * (E + 1), hipMemcpyDeviceToDevice, s));
+  if (aux && aux->sorted_assign)
+    run(hipMemcpyAsync(aux->sorted_assign, sorted_assign, sizeof(int32_t) * (size_t)T * k,
+                       hipMemcpyDeviceToDevice, s));
+  if (timing) h->events.insert(h->events.end(), ev, ev + LMOE_NUM_STAGES + 1);
+  if (cur != h->device) (void)hipSetDevice(cur);
+  if (err != hipSuccess) return fail(LMOE_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));
+  return LMOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,279 @@
+// MFMA GEMM engine: C = A . B^T with both operands K-contiguous ("NT"), fp32
+// accumulation, for the four GEMMs of the block:
+//   router + pooler (one launch, two B matrices)        -> EPI_F32
+//   gate/up, grouped per expert, A rows gathered          -> EPI_SWIGLU
+//   down, grouped per expert                              -> EPI_DOWN
+//   unpooler                                              -> EPI_ACT
+//
+// Block tile 128 x 128, 256 threads = 4 wave64 in a 2 x 2 grid, each wave a
+// 64 x 64 sub-tile made of 2 x 2 MFMA 32x32 tiles. A K-step stages 128 bytes of
+// every tile row (64 bf16 or 32 fp32) in LDS, double-buffered; rows are split
+// in 16-byte chunks placed at (chunk ^ (row & 7)) so that the 32 rows an MFMA
+// operand read touches spread over all banks.
+//
+// MFMA operand layout (CDNA3/CDNA4 32x32 family): lane l supplies row (or
+// column) l % 32 and its half l / 32 of the K-slice; the 32x32 result leaves
+// register v of lane l at row 8*(v/4) + 4*(l/32) + v%4, column l % 32. Each lane
+// reads one 16-byte chunk per row and K-slice; A and B pair their elements the
+// same way, so the order of K inside an instruction never matters.
+#include "common.h"
+#include "kernels.h"
+
+namespace lmoe {
+
+namespace {
+
+constexpr int BM = kGemmBM, BN = kGemmBN;
+constexpr int NT = 256;          // threads per block
+constexpr int ROWB = 128;        // bytes per tile row per K-step
+constexpr int CH = ROWB / 16;    // 16-byte chunks per tile row
+constexpr int LOADS = BM * CH / NT;  // chunks each thread loads per operand per K-step (4)
+
+struct Chunk {
+  uint4 v;
+};
+
+__device__ __forceinline__ int swz(int row, int c) { return row * ROWB + ((c ^ (row & 7)) << 4); }
+
+// One 32x32 MFMA step on a 16-byte chunk of A and of B.
+template <typename T> struct Mfma;
+template <> struct Mfma<bf16_t> {
+  __device__ static void step(const uint4& a, const uint4& b, f32x16_t& acc) {
+    bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
+    bf16x8_t bv = __builtin_bit_cast(bf16x8_t, b);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+  }
+};
+template <> struct Mfma<float> {
+  __device__ static void step(const uint4& a, const uint4& b, f32x16_t& acc) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+  }
+};
+
+template <typename T, int EPI>
+__global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * (BM + BN) * ROWB];
+  unsigned char* As = lds;
+  unsigned char* Bs = lds + 2 * BM * ROWB;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  constexpr bool kGrouped = (EPI == EPI_SWIGLU || EPI == EPI_DOWN);
+
+  // ---- tile coordinates -------------------------------------------------
+  int m0, m_end, expert = 0;
+  if (kGrouped) {
+    const int slot = blockIdx.x;
+    if (slot >= *p.n_tiles) return;
+    expert = p.tiles[2 * slot];
+    m0 = p.tiles[2 * slot + 1];
+    m_end = p.offsets[expert + 1];
+  } else {
+    m0 = blockIdx.x * BM;
+    m_end = p.M;
+  }
+  const int n0 = blockIdx.y * (EPI == EPI_SWIGLU ? BN / 2 : BN);
+
+  // ---- per-thread row pointers for the global loads ---------------------
+  const int lc = tid % CH;                 // chunk this thread loads
+  const unsigned char* a_ptr[LOADS];
+  const unsigned char* b_ptr[LOADS];
+  const T* Bbase = static_cast<const T*>(p.B0);
+  if (kGrouped) Bbase += (int64_t)expert * p.b_expert_stride;
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int r = tid / CH + i * (NT / CH);
+    int m = m0 + r;
+    if (m >= m_end) m = m_end - 1;          // rows past the end load a valid row; never stored
+    int64_t arow = (EPI == EPI_SWIGLU) ? (int64_t)p.a_gather[m] : (int64_t)m;
+    a_ptr[i] = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.A) + arow * p.lda) + lc * 16;
+    const T* brow;
+    if (EPI == EPI_SWIGLU) {
+      const int f = (r < BN / 2) ? (n0 + r) : (p.F + n0 + r - BN / 2);
+      brow = Bbase + (int64_t)f * p.ldb;
+    } else {
+      // Columns past N load row 0 of B0 (a valid row) and are never stored.
+      const int n = n0 + r;
+      if (EPI == EPI_F32 && n >= p.n_split)
+        brow = (n < p.N) ? static_cast<const T*>(p.B1) + (int64_t)(n - p.n_split) * p.ldb : Bbase;
+      else
+        brow = Bbase + (int64_t)(n < p.N ? n : 0) * p.ldb;
+    }
+    b_ptr[i] = reinterpret_cast<const unsigned char*>(brow) + lc * 16;
+  }
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+
+  uint4 ra[LOADS], rb[LOADS];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      ra[i] = *reinterpret_cast<const uint4*>(a_ptr[i] + (int64_t)kt * ROWB);
+      rb[i] = *reinterpret_cast<const uint4*>(b_ptr[i] + (int64_t)kt * ROWB);
+    }
+  };
+  auto sstore = [&](int stage) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int r = tid / CH + i * (NT / CH);
+      *reinterpret_cast<uint4*>(As + stage * BM * ROWB + swz(r, lc)) = ra[i];
+      *reinterpret_cast<uint4*>(Bs + stage * BN * ROWB + swz(r, lc)) = rb[i];
+    }
+  };
+
+  // Rows of the LDS tiles this lane reads for its MFMA operands.
+  const int l32 = lane & 31, half = lane >> 5;
+  int arow[2], brow[2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) arow[mi] = wm * 64 + mi * 32 + l32;
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni)
+    brow[ni] = (EPI == EPI_SWIGLU) ? (ni * (BN / 2) + wn * 32 + l32) : (wn * 64 + ni * 32 + l32);
+
+  const int nk = p.K * (int)sizeof(T) / ROWB;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    const unsigned char* as = As + st * BM * ROWB;
+    const unsigned char* bs = Bs + st * BN * ROWB;
+#pragma unroll
+    for (int s = 0; s < CH / 2; ++s) {
+      const int c = 2 * s + half;
+      uint4 af[2], bfr[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) af[mi] = *reinterpret_cast<const uint4*>(as + swz(arow[mi], c));
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) bfr[ni] = *reinterpret_cast<const uint4*>(bs + swz(brow[ni], c));
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) Mfma<T>::step(af[mi], bfr[ni], acc[mi][ni]);
+    }
+    if (kt + 1 < nk) sstore(st ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue ----------------------------------------------------------
+  // Register v of tile (mi, ni) holds row wm*64 + mi*32 + 8*(v/4) + 4*half + v%4.
+  if (EPI == EPI_F32 || EPI == EPI_ACT) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int n = n0 + wn * 64 + ni * 32 + l32;
+        if (n >= p.N) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = m0 + wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          if (m >= m_end) continue;
+          if (EPI == EPI_ACT) {
+            static_cast<T*>(p.out0)[(int64_t)m * p.ldo0 + n] = Elem<T>::from_f32(acc[mi][ni][v]);
+          } else if (n < p.n_split) {
+            static_cast<float*>(p.out0)[(int64_t)m * p.ldo0 + n] = acc[mi][ni][v];
+          } else {
+            const int c = n - p.n_split;
+            static_cast<float*>(p.out1)[(int64_t)m * p.ldo1 + c] =
+                acc[mi][ni][v] + (p.bias1 ? p.bias1[c] : 0.f);
+          }
+        }
+      }
+  } else if (EPI == EPI_SWIGLU) {
+    const int f = n0 + wn * 32 + l32;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        if (m >= m_end) continue;
+        const float g = acc[mi][0][v], u = acc[mi][1][v];
+        const float h = g / (1.0f + __expf(-g)) * u;
+        static_cast<T*>(p.out0)[(int64_t)m * p.ldo0 + f] = Elem<T>::from_f32(h);
+      }
+  } else {  // EPI_DOWN
+    const int nb = n0 + wn * 64;             // first column of this wave's 64-column group
+    if (nb < p.N) {
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        float ssq[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = m0 + wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          const float y0 = round_to<T>(acc[mi][0][v]);
+          const float y1 = round_to<T>(acc[mi][1][v]);
+          ssq[v] = y0 * y0 + y1 * y1;
+          if (m < m_end) {
+            T* orow = static_cast<T*>(p.out0) + (int64_t)m * p.ldo0 + nb + l32;
+            orow[0] = Elem<T>::from_f32(y0);
+            orow[32] = Elem<T>::from_f32(y1);
+          }
+        }
+        // Sum over the 32 lanes of this half (columns nb .. nb+63 of each row).
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float t = ssq[v];
+#pragma unroll
+          for (int o = 1; o < 32; o <<= 1) t += __shfl_xor(t, o, kWave);
+          ssq[v] = t;
+        }
+        if (l32 == 0) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int m = m0 + wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+            if (m < m_end) p.ss_out[(int64_t)m * p.ss_ld + nb / 64] = ssq[v];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int EPI>
+hipError_t launch_t(const GemmParams& p, hipStream_t s) {
+  dim3 grid;
+  if (EPI == EPI_SWIGLU || EPI == EPI_DOWN) {
+    grid.x = p.max_slots;
+    grid.y = (EPI == EPI_SWIGLU) ? p.F / (BN / 2) : (p.N + BN - 1) / BN;
+  } else {
+    grid.x = (p.M + BM - 1) / BM;
+    grid.y = (p.N + BN - 1) / BN;
+  }
+  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_nt_kernel<T, EPI>), grid, dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmParams& p, EpiKind epi, bool bf16, hipStream_t s) {
+  if (bf16) {
+    switch (epi) {
+      case EPI_F32: return launch_t<bf16_t, EPI_F32>(p, s);
+      case EPI_ACT: return launch_t<bf16_t, EPI_ACT>(p, s);
+      case EPI_SWIGLU: return launch_t<bf16_t, EPI_SWIGLU>(p, s);
+      case EPI_DOWN: return launch_t<bf16_t, EPI_DOWN>(p, s);
+    }
+  } else {
+    switch (epi) {
+      case EPI_F32: return launch_t<float, EPI_F32>(p, s);
+      case EPI_ACT: return launch_t<float, EPI_ACT>(p, s);
+      case EPI_SWIGLU: return launch_t<float, EPI_SWIGLU>(p, s);
+      case EPI_DOWN: return launch_t<float, EPI_DOWN>(p, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lmoe

@@ -1,0 +1,87 @@
+// Internal launch interface between the runtime (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lmoe {
+
+// Output handling of one GEMM launch (C = A . B^T, fp32 accumulation).
+enum EpiKind {
+  EPI_F32 = 0,     // cols [0, n_split) -> out0 fp32; cols [n_split, N) -> out1 fp32 (+ bias1)
+  EPI_ACT = 1,     // out0 in the element type
+  EPI_SWIGLU = 2,  // grouped: out0[p][f] = silu(gate) * up, gate/up rows of the expert's B
+  EPI_DOWN = 3     // grouped: out0[p][n] = y (element type), ss_out[p][n/64] = sum of y^2
+};
+
+struct GemmParams {
+  int M, N, K;                 // dense: M rows; N output columns; K inner
+  const void* A;
+  int64_t lda;                 // elements
+  const int32_t* a_gather;     // EPI_SWIGLU: A row of sorted position p is a_gather[p]
+  const void* B0;
+  const void* B1;              // EPI_F32: rows [n_split, N) come from B1
+  int n_split;
+  int64_t ldb;                 // elements
+  int64_t b_expert_stride;     // grouped: elements between consecutive experts' matrices
+  const int32_t* tiles;        // grouped: [slot] -> (expert, first row) pairs
+  const int32_t* n_tiles;      // grouped: number of valid slots (device)
+  const int32_t* offsets;      // grouped: [E+1] row offsets per expert
+  int max_slots;               // grouped: grid size in slots
+  void* out0;
+  int64_t ldo0;
+  void* out1;
+  int64_t ldo1;
+  const float* bias1;
+  float* ss_out;
+  int ss_ld;
+  int F;                       // EPI_SWIGLU: up rows start at F inside the expert's B
+};
+
+// GEMM tile geometry shared with the runtime's tile list.
+constexpr int kGemmBM = 128;
+constexpr int kGemmBN = 128;
+
+hipError_t launch_gemm(const GemmParams& p, EpiKind epi, bool bf16, hipStream_t s);
+
+// Router top-k + softmax; also builds, per chunk of 64 tokens, a bitmask of
+// the chunk's tokens that selected each expert.
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                       uint64_t* chunk_masks, hipStream_t s);
+
+// Counting sort of the T*k assignments by expert (stable), from the chunk masks.
+struct SortParams {
+  const int32_t* ids;
+  const float* topk_w;
+  const uint64_t* chunk_masks;  // [n_chunks][E]
+  int32_t* chunk_base;          // [n_chunks][E] scratch
+  int32_t* counts;              // [E]
+  int32_t* offsets;             // [E+1]
+  int32_t* sorted_assign;       // [T*k]
+  int32_t* inv;                 // [T*k]
+  int32_t* row_token;           // [T*k]
+  int32_t* tiles;               // [max_slots][2]
+  int32_t* n_tiles;             // [1]
+  int T, E, k, tile_m;
+};
+hipError_t launch_sort(const SortParams& p, hipStream_t s);
+
+// xp = bf16/f32( P * rsqrt(mean(P^2) + eps) * g )
+hipError_t launch_pool_norm(const float* P, const float* g, int T, int Dp, float eps, void* xp,
+                            bool bf16, hipStream_t s);
+
+// u[t] = sum_j w[t][j] * rsqrt(sum(ss[inv[t,j]]) / Dp + eps) * g_e * y[inv[t,j]]
+struct CombineParams {
+  const void* y;           // [T*k][Dp] sorted rows
+  const float* ss;         // [T*k][Dp/64]
+  const int32_t* inv;      // [T*k]
+  const int32_t* ids;      // [T][k]
+  const float* w;          // [T][k]
+  const float* g_expert;   // [E][Dp]
+  void* u;                 // [T][Dp]
+  int T, k, Dp;
+  float eps;
+};
+hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s);
+
+}  // namespace lmoe

@@ -1,0 +1,195 @@
+// Routing: top-k + softmax over the selected logits, and the token-to-expert
+// permutation as a stable counting sort.
+//
+// Top-k (LMSYS blog, "Kernel optimizations": a top-k routing kernel emits the
+// expert ids and weights in the layout the expert kernel reads): one wave64 per
+// token, each lane holding E/64 logits; k rounds of a wave arg-max on
+// (logit desc, index asc). Weights are the softmax of the k selected logits.
+//
+// Permutation (blog, "AMD support": the atomic-add expert sort became an LDS
+// kernel on MI355X). Tokens are taken in chunks of 64, one bit per token:
+//  1. while doing top-k, the chunk's workgroup ORs bit (t % 64) into an LDS
+//     mask per expert, then writes the chunk's masks out;
+//  2. a single workgroup turns the masks into per-(chunk, expert) bases
+//     (running sums of popcounts over chunks) and the per-expert offsets
+//     (exclusive prefix sum over experts with wavefront prefix sums), and lays
+//     out the grouped-GEMM tile list;
+//  3. each chunk places its assignments: the rank of token t inside expert e
+//     is the popcount of e's mask below t's bit, so equal keys keep token order.
+// Every step is integer and order-independent, hence bit-exact and
+// deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace lmoe {
+
+namespace {
+
+constexpr int kChunk = 64;
+constexpr int kMaxE = 1024;
+constexpr int kMaxPerLane = kMaxE / kWave;  // 16
+
+// (value, index) pair order: larger value first, then lower index.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                    int k, int32_t* __restrict__ ids,
+                                                    float* __restrict__ w,
+                                                    uint64_t* __restrict__ chunk_masks) {
+  __shared__ unsigned long long masks[kMaxE];
+  const int chunk = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) masks[e] = 0ull;
+  __syncthreads();
+
+  const int per = (E + kWave - 1) / kWave;
+  for (int tl = wave; tl < kChunk; tl += blockDim.x / kWave) {
+    const int t = chunk * kChunk + tl;
+    if (t >= T) break;
+    float v[kMaxPerLane];
+    unsigned taken = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxPerLane; ++q) {
+      const int e = q * kWave + lane;
+      // NaN counts as -inf, so that every round selects a valid expert index.
+      const float x = (q < per && e < E) ? logits[(int64_t)t * E + e] : -INFINITY;
+      v[q] = (x != x) ? -INFINITY : x;
+      if (!(q < per && e < E)) taken |= 1u << q;
+    }
+    float sel_v = 0.f, top = 0.f, den = 0.f;
+    int my_id = -1;  // lane j < k keeps the j-th selected expert
+    for (int j = 0; j < k; ++j) {
+      float bv = -INFINITY;
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int q = 0; q < kMaxPerLane; ++q) {
+        const int e = q * kWave + lane;
+        if (!(taken >> q & 1u) && better(v[q], e, bv, bi)) {
+          bv = v[q];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, kWave);
+        const int oi = __shfl_xor(bi, o, kWave);
+        if (better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      // Every lane now holds the winner (bv, bi).
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      if (j == 0) top = bv;
+      den += expf(bv - top);
+      if (lane == j) {
+        my_id = bi;
+        sel_v = bv;
+      }
+    }
+    if (lane < k) {
+      ids[(int64_t)t * k + lane] = my_id;
+      w[(int64_t)t * k + lane] = expf(sel_v - top) / den;
+      atomicOr(&masks[my_id], 1ull << tl);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    chunk_masks[(int64_t)chunk * E + e] = masks[e];
+}
+
+// Exclusive prefix sum over the block (blockDim.x a multiple of 64, <= 1024).
+__device__ int block_exclusive_scan(int x, int* wave_tot, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int v = lane < nw ? wave_tot[lane] : 0;
+    int vi = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(vi, o, kWave);
+      if (lane >= o) vi += y;
+    }
+    if (lane < nw) wave_tot[lane] = vi - v;        // exclusive wave bases
+    if (lane == nw - 1) *total = vi;
+  }
+  __syncthreads();
+  const int r = incl - x + wave_tot[wave];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(1024) void sort_scan_kernel(SortParams p) {
+  __shared__ int wave_tot[16];
+  __shared__ int total;
+  const int e = threadIdx.x;
+  const int n_chunks = (p.T + kChunk - 1) / kChunk;
+  int cnt = 0;
+  if (e < p.E) {
+    for (int c = 0; c < n_chunks; ++c) {
+      p.chunk_base[(int64_t)c * p.E + e] = cnt;
+      cnt += __popcll(p.chunk_masks[(int64_t)c * p.E + e]);
+    }
+    p.counts[e] = cnt;
+  }
+  const int off = block_exclusive_scan(e < p.E ? cnt : 0, wave_tot, &total);
+  if (e < p.E) p.offsets[e] = off;
+  if (e == 0) p.offsets[p.E] = total;
+  // Grouped-GEMM tiles: expert e gets ceil(count / tile_m) row tiles.
+  const int nt = (e < p.E) ? (cnt + p.tile_m - 1) / p.tile_m : 0;
+  const int tbase = block_exclusive_scan(nt, wave_tot, &total);
+  for (int q = 0; q < nt; ++q) {
+    p.tiles[2 * (tbase + q)] = e;
+    p.tiles[2 * (tbase + q) + 1] = off + q * p.tile_m;
+  }
+  if (e == 0) *p.n_tiles = total;
+}
+
+__global__ __launch_bounds__(64) void sort_scatter_kernel(SortParams p) {
+  const int chunk = blockIdx.x, lane = threadIdx.x;
+  const int t = chunk * kChunk + lane;
+  if (t >= p.T) return;
+  const uint64_t below = lanemask_lt(lane);
+  for (int j = 0; j < p.k; ++j) {
+    const int a = t * p.k + j;
+    const int e = p.ids[a];
+    const uint64_t m = p.chunk_masks[(int64_t)chunk * p.E + e];
+    const int pos = p.offsets[e] + p.chunk_base[(int64_t)chunk * p.E + e] + __popcll(m & below);
+    p.sorted_assign[pos] = a;
+    p.inv[a] = pos;
+    p.row_token[pos] = t;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                       uint64_t* chunk_masks, hipStream_t s) {
+  const int n_chunks = (T + kChunk - 1) / kChunk;
+  if (n_chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_kernel, dim3(n_chunks), dim3(256), 0, s, logits, T, E, k, ids, w,
+                     chunk_masks);
+  return hipGetLastError();
+}
+
+hipError_t launch_sort(const SortParams& p, hipStream_t s) {
+  const int n_chunks = (p.T + kChunk - 1) / kChunk;
+  if (n_chunks == 0) return hipSuccess;
+  const int threads = ((p.E + 63) / 64) * 64;
+  hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(threads), 0, s, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(sort_scatter_kernel, dim3(n_chunks), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace lmoe

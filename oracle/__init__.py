@@ -41,6 +41,7 @@ def load(path: str = LIB_PATH):
         "orc_expert": [_P, _I, _I, _P, _P, _P, _P, _I, _P, _D, _I, _I, _P, _P],
         "orc_expert_batch": [_P, _I, _I, _I, _P, _P, _P, _P, _I, _P, _D, _I, _I, _P, _P],
         "orc_combine_unpool": [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P],
+        "orc_expert_assign": [_P, _I, _P, _P, _I, _I, _P, _P, _P, _P, _I, _P, _D, _I, _I, _P, _P],
         "orc_mx_quant_e4m3": [_P, _I, _P, _P, _P],
         "orc_mx_quant_e2m1": [_P, _I, _P, _P, _P],
     }
@@ -200,24 +201,41 @@ class Oracle:
         ids, w = self.topk_softmax(logits, k)
         xp = self.pool_norm(x, wts["w_pool"], wts["g_pool"], eps_pool, mx_act, rnd)
         T, Dp = xp.shape
-        z = np.zeros((T, k, Dp), np.float64)
-        rms = np.zeros((T, k), np.float64)
-        ge = wts["g_expert"]
+        ge = self._c(wts["g_expert"], np.float32)
+        E = ge.shape[0]
+        keep = []                                   # keeps the expert arrays alive
+        ptrs = [(ctypes.c_void_p * E)() for _ in range(4)]
+        mx = "s_gate_up" in wts or (get_expert is not None and mx_act)
+        F = None
         for e in np.unique(ids):
-            tt, jj = np.nonzero(ids == e)
+            e = int(e)
             if get_expert is not None:
-                ew = get_expert(int(e))
+                ew = tuple(self._c(a) for a in get_expert(e))
             elif "s_gate_up" in wts:
                 ew = (wts["w_gate_up"][e], wts["s_gate_up"][e], wts["w_down"][e], wts["s_down"][e])
             else:
                 ew = (wts["w_gate_up"][e], wts["w_down"][e])
+            ew = tuple(self._c(a) for a in ew)
+            keep.append(ew)
             if len(ew) == 4:
-                zz, rr = self.expert(xp[tt], ew[0], ew[2], ge[e], eps_expert, mx_act,
-                                     sgu=ew[1], sd=ew[3], rnd=rnd)
+                mx = True
+                ptrs[0][e], ptrs[1][e], ptrs[2][e], ptrs[3][e] = (a.ctypes.data for a in ew)
+                F = ew[2].shape[1] * 2
+                wdt = ORC_MXFP4
             else:
-                zz, rr = self.expert(xp[tt], ew[0], ew[1], ge[e], eps_expert, mx_act, rnd=rnd)
-            z[tt, jj] = zz
-            rms[tt, jj] = rr
+                ptrs[0][e], ptrs[2][e] = ew[0].ctypes.data, ew[1].ctypes.data
+                F = ew[1].shape[1]
+                wdt = self._dt(ew[0])
+        n = T * k
+        z = np.zeros((T, k, Dp), np.float64)
+        rms = np.zeros((T, k), np.float64)
+        if n:
+            tok = np.ascontiguousarray(np.repeat(np.arange(T, dtype=np.int32), k))
+            ex = np.ascontiguousarray(ids.ravel().astype(np.int32))
+            self.lib.orc_expert_assign(xp.ctypes.data, n, tok.ctypes.data, ex.ctypes.data, Dp, F,
+                                       ptrs[0], ptrs[1] if mx else None, ptrs[2],
+                                       ptrs[3] if mx else None, wdt, ge.ctypes.data, eps_expert,
+                                       int(mx_act), int(rnd), z.ctypes.data, rms.ctypes.data)
         out = self.combine_unpool(z, w, wts["w_unpool"], rnd)
         return out, {"logits": logits, "ids": ids, "w": w, "rms_unit": rms, "xp": xp}
 

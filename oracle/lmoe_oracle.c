@@ -375,6 +375,23 @@ void orc_expert_batch(const double* xin, int n, int Dp, int F,
                z + (size_t)i * Dp, rms_unit ? rms_unit + i : NULL);
 }
 
+/* Step 5 for n (token, expert) assignments at once: assignment a runs token row
+   tok[a] of xin [*][Dp] through expert ex[a], whose weights are found in the
+   per-expert pointer arrays (sgu/sd NULL unless MXFP4). z [n][Dp], rms_unit [n]
+   or NULL. Assignments are independent, so they run in parallel. */
+void orc_expert_assign(const double* xin, int n, const int32_t* tok, const int32_t* ex, int Dp,
+                       int F, const void* const* wgu, const uint8_t* const* sgu,
+                       const void* const* wd, const uint8_t* const* sd, int wdt, const float* ge,
+                       double eps, int mx_act, int rnd, double* z, double* rms_unit) {
+#pragma omp parallel for schedule(dynamic)
+  for (int a = 0; a < n; ++a) {
+    int e = ex[a];
+    orc_expert(xin + (size_t)tok[a] * Dp, Dp, F, wgu[e], sgu ? sgu[e] : NULL, wd[e],
+               sd ? sd[e] : NULL, wdt, ge + (size_t)e * Dp, eps, mx_act, rnd, z + (size_t)a * Dp,
+               rms_unit ? rms_unit + a : NULL);
+  }
+}
+
 /* ---------------------------------------------------------------------------
  * Step 6 — weighted sum and unpooler (blog, MoE section: normalized expert
  * outputs are scaled by their routing weights and summed, then the unpooler

@@ -1,0 +1,77 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/lmoe.h declares, and its host-side checks answer without touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import latent_moe_layer_router_amd as lmoe
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "lmoe.h")
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lmoe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(lmoe.EXPORTS)
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(lmoe.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_null_destroy():
+    for s in (lmoe.LMOE_OK, lmoe.LMOE_E_INVAL, lmoe.LMOE_E_UNSUPPORTED, lmoe.LMOE_E_NOMEM, lmoe.LMOE_E_HIP):
+        assert lmoe.lmoe_status_str(s)
+    lmoe.lmoe_destroy(None)
+
+
+def test_workspace_bytes_full_size():
+    cfg = lmoe.make_config(8192, 4096, 4096, 256, 8, 16384)
+    n = lmoe.lmoe_workspace_bytes(cfg)
+    # intermediates: P fp32, xp, H, Y, u, sum-of-squares partials, logits, routing arrays
+    assert 2.4 * 2 ** 30 < n < 2.7 * 2 ** 30
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("abi_version", 2, lmoe.LMOE_E_INVAL),
+    ("d_model", 100, lmoe.LMOE_E_UNSUPPORTED),
+    ("d_pooled", 0, lmoe.LMOE_E_UNSUPPORTED),
+    ("n_experts", 1025, lmoe.LMOE_E_UNSUPPORTED),
+    ("top_k", 0, lmoe.LMOE_E_UNSUPPORTED),
+    ("top_k", 17, lmoe.LMOE_E_UNSUPPORTED),
+    ("act_dtype", lmoe.LMOE_MXFP4, lmoe.LMOE_E_UNSUPPORTED),
+    ("expert_wdtype", lmoe.LMOE_MXFP4, lmoe.LMOE_E_UNSUPPORTED),
+    ("max_tokens", 0, lmoe.LMOE_E_INVAL),
+    ("eps_pool", -1.0, lmoe.LMOE_E_INVAL),
+    ("eps_expert", float("nan"), lmoe.LMOE_E_INVAL),
+    ("flags", 2, lmoe.LMOE_E_INVAL),
+])
+def test_config_validation(field, value, status):
+    cfg = lmoe.make_config(8192, 4096, 4096, 256, 8, 128)
+    setattr(cfg, field, value)
+    with pytest.raises(lmoe.LmoeError) as e:
+        lmoe.lmoe_workspace_bytes(cfg)
+    assert e.value.status == status
+    assert lmoe.lmoe_last_error()
+
+
+def test_create_rejects_null_weights_before_touching_a_device():
+    cfg = lmoe.make_config(256, 128, 128, 8, 2, 64)
+    with pytest.raises(lmoe.LmoeError) as e:
+        lmoe.lmoe_create(cfg, lmoe.lmoe_weights())
+    assert e.value.status == lmoe.LMOE_E_INVAL
+
+
+def test_forward_rejects_null_handle():
+    with pytest.raises(lmoe.LmoeError) as e:
+        lmoe.lmoe_forward(None, 0, 0, 1, 0)
+    assert e.value.status == lmoe.LMOE_E_INVAL
