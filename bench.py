@@ -1,0 +1,187 @@
+"""Benchmark of the latent-MoE block forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_bf16]
+                    [--also prefill_bf16] [--no-cpu-baseline]
+
+A step is one lmoe_forward over one batch of synthetic tokens already resident
+in HBM: routing, permutation, pooler, experts, combine, unpooler. The headline
+workload is decode-sized (T=128 tokens; D=8192, Dp=4096, F=4096, E=256, k=8,
+bf16), which streams the touched experts' weights and is bound by HBM; the
+prefill chunk (T=16384) is reported beside it against the bf16 MFMA peak.
+Prints one JSON line. Weights are random-initialized (seed 0) with the model's
+shapes; inputs are synthetic (see synth/).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "latent-MoE layer tokens/sec + % bf16 MFMA peak (T=16K) / % HBM BW (T=128)"
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+
+def algorithmic(w, n_active: int, kernel: str):
+    """Algorithmic bytes and flops of one launch of a kernel (every touched weight
+    read once, every activation it consumes read once and its output written once)."""
+    es = 2
+    T, D, Dp, F, E, k = w.T, w.D, w.Dp, w.F, w.E, w.k
+    A = T * k
+    if kernel == "gate_up":
+        return (n_active * 2 * F * Dp * es + T * Dp * es + A * F * es), 2.0 * A * Dp * 2 * F
+    if kernel == "down":
+        return (n_active * Dp * F * es + A * F * es + A * Dp * es), 2.0 * A * F * Dp
+    raise ValueError(kernel)
+
+
+def step_work(w, n_active: int):
+    """Algorithmic bytes and flops of one whole step."""
+    es = 2
+    T, D, Dp, F, E, k = w.T, w.D, w.Dp, w.F, w.E, w.k
+    byts = (n_active * 3 * F * Dp * es + (E + 2 * Dp) * D * es + T * D * es + T * D * 4
+            + (Dp + E * Dp) * 4)
+    flops = 2.0 * T * (E * D + Dp * D + k * 3 * Dp * F + D * Dp)
+    return byts, flops
+
+
+def run_workload(lmoe, torch, synth, sdev, block, w, steps, warmup, dev):
+    x = sdev.upload_x(w, dev)
+    out = torch.empty((w.T, w.D), dtype=torch.float32, device=dev)
+    _, aux = block.forward(x, out=out, aux=True)
+    torch.cuda.synchronize()
+    counts = (aux["expert_offsets"][1:] - aux["expert_offsets"][:-1]).cpu()
+    n_active = int((counts > 0).sum())
+    for _ in range(warmup):
+        block.forward(x, out=out)
+    torch.cuda.synchronize()
+    block.set_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        block.forward(x, out=out)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    block.set_timing(False)
+    stage_ms, n = block.get_timing()
+    stage_ms = {s: v / n for s, v in stage_ms.items()}
+    ms = (t1 - t0) * 1e3 / steps
+    return ms, stage_ms, n_active, counts
+
+
+def roofline(w, stage_ms, n_active, bound):
+    byts, flops = algorithmic(w, n_active, "gate_up")
+    t = stage_ms["gate_up"] * 1e-3
+    if bound == "hbm":
+        ach = byts / t / 1e9
+        return {"kernel": "gate_up grouped GEMM + SwiGLU", "bound": "hbm", "achieved": round(ach, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                "traffic": None, "algorithmic_bytes": byts, "avg_ms": round(stage_ms["gate_up"], 4)}
+    ach = flops / t / 1e12
+    return {"kernel": "gate_up grouped GEMM + SwiGLU", "bound": "mfma", "achieved": round(ach, 1),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "traffic": None, "algorithmic_flops": flops, "avg_ms": round(stage_ms["gate_up"], 4)}
+
+
+def cpu_baseline(synth, w):
+    """The CPU oracle on the whole decode batch (its T tokens), timed on this
+    host's cores; expert weights are generated before the clock starts."""
+    import numpy as np
+
+    import oracle
+    x = synth.x(w)
+    wts = {"w_router": synth.w_router(w), "b_router": synth.router_bias(w),
+           "w_pool": synth.w_pool(w), "g_pool": synth.g_pool(w), "g_expert": synth.g_expert(w),
+           "w_unpool": synth.w_unpool(w)}
+    O = oracle.default()
+    ids, _ = O.topk_softmax(O.router(x, wts["w_router"], wts["b_router"]), w.k)
+    experts = {int(e): (synth.w_gate_up(w, int(e)), synth.w_down(w, int(e))) for e in np.unique(ids)}
+    t0 = time.perf_counter()
+    O.forward(x, wts, w.k, w.eps_pool, w.eps_expert, get_expert=experts.__getitem__,
+              rnd=w.act == synth.BF16)
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
+    return {"value": round(w.T / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"all {w.T} tokens of the {w.name} batch (one full step), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_bf16")
+    ap.add_argument("--also", default="prefill_bf16", help="comma-separated extra workloads, or ''")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB (a kernel of "
+                         "known traffic, to calibrate hardware byte counters against)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the block is built and "
+              "measured on a single MI355X", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import latent_moe_layer_router_amd as lmoe
+    import synth
+    from synth import device as sdev
+
+    dev = torch.device("cuda:0")
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    w = synth.WORKLOADS[args.workload]
+    extra = [synth.WORKLOADS[n] for n in args.also.split(",") if n]
+    max_tokens = max([w.T] + [e.T for e in extra])
+    t0 = time.perf_counter()
+    tw = sdev.upload_weights(w, dev)
+    print(f"[bench] weights uploaded in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    block = lmoe.LatentMoE(tw, w.k, max_tokens, w.eps_pool, w.eps_expert, out_dtype=torch.float32)
+
+    ms, stage_ms, n_active, _ = run_workload(lmoe, torch, synth, sdev, block, w, args.steps,
+                                             args.warmup, dev)
+    print(f"[bench] {w.name}: {ms:.3f} ms/step, stages {stage_ms}", file=sys.stderr, flush=True)
+    byts, flops = step_work(w, n_active)
+    res = {
+        "metric": METRIC, "value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) random-init weights)",
+        "config": {"workload": w.name, "T": w.T, "D": w.D, "Dp": w.Dp, "F": w.F, "E": w.E, "k": w.k,
+                   "out_dtype": "f32", "active_experts": n_active},
+        "step_hbm_frac": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "roofline": roofline(w, stage_ms, n_active, "hbm"),
+        "stages_ms": {s: round(v, 4) for s, v in stage_ms.items()},
+    }
+    also = []
+    for e in extra:
+        ems, est, ena, _ = run_workload(lmoe, torch, synth, sdev, block, e, args.steps, args.warmup, dev)
+        print(f"[bench] {e.name}: {ems:.3f} ms/step, stages {est}", file=sys.stderr, flush=True)
+        eb, ef = step_work(e, ena)
+        also.append({"workload": e.name, "T": e.T, "value": round(e.T / (ems * 1e-3), 1),
+                     "unit": "tokens/s", "ms_per_step": round(ems, 4),
+                     "step_tflops": round(ef / (ems * 1e-3) / 1e12, 1),
+                     "step_mfma_frac": round(ef / (ems * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "roofline": roofline(e, est, ena, "mfma"),
+                     "stages_ms": {s: round(v, 4) for s, v in est.items()}})
+    res["also"] = also
+    block.close()
+    del tw
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(synth, w)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -67,8 +67,10 @@ typedef enum {
 /* Block configuration (host struct, copied at create).
  * Shapes: d_model (D), d_pooled (Dp), d_ff (F) must be multiples of 64;
  * 1 <= n_experts (E) <= 1024; 1 <= top_k (k) <= min(E, 16); max_tokens >= 1.
- * act_dtype: LMOE_F32 or LMOE_BF16 — dtype of x, out, W_router, W_pool,
- * W_unpool and of the expert weights (expert_wdtype must equal act_dtype).
+ * act_dtype: LMOE_F32 or LMOE_BF16 — dtype of x, W_router, W_pool, W_unpool
+ * and of the expert weights (expert_wdtype must equal act_dtype).
+ * out_dtype: LMOE_F32 (the unpooler's fp32 accumulators as they are) or
+ * act_dtype (those accumulators rounded to nearest even).
  * Gammas and the router bias are always fp32. */
 typedef struct {
   int32_t abi_version;      /* LMOE_ABI_VERSION */
@@ -81,6 +83,7 @@ typedef struct {
   float eps_expert;         /* RMSNorm eps of each expert output */
   int32_t act_dtype;        /* lmoe_dtype */
   int32_t expert_wdtype;    /* lmoe_dtype */
+  int32_t out_dtype;        /* lmoe_dtype: LMOE_F32 or act_dtype */
   int32_t max_tokens;       /* the workspace is sized for this many tokens */
   uint32_t flags;           /* LMOE_FLAG_* */
 } lmoe_config;
@@ -116,7 +119,7 @@ typedef struct {
  * (NULL on error). */
 lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, lmoe_handle* out);
 
-/* Run the block on T tokens: x [T][D] -> out [T][D] (act_dtype), enqueued on
+/* Run the block on T tokens: x [T][D] -> out [T][D] (out_dtype), enqueued on
  * hip_stream (a hipStream_t; NULL is the null stream). Asynchronous: kernel
  * faults surface at the caller's next synchronization. T == 0 enqueues nothing
  * and returns LMOE_OK; T > max_tokens is LMOE_E_INVAL. out must not overlap x.

@@ -33,7 +33,8 @@ class lmoe_config(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("eps_pool", ctypes.c_float), ("eps_expert", ctypes.c_float),
                 ("act_dtype", ctypes.c_int32), ("expert_wdtype", ctypes.c_int32),
-                ("max_tokens", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("out_dtype", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
 
 
 class lmoe_weights(ctypes.Structure):
@@ -130,10 +131,12 @@ def lmoe_get_timing(h: int):
 
 
 def make_config(D, Dp, F, E, k, max_tokens, act="bf16", eps_pool=1e-6, eps_expert=1e-6,
-                router_bias=False) -> lmoe_config:
-    dt = {"bf16": LMOE_BF16, "f32": LMOE_F32}[act]
-    return lmoe_config(LMOE_ABI_VERSION, D, Dp, F, E, k, eps_pool, eps_expert, dt, dt, max_tokens,
-                       LMOE_FLAG_ROUTER_BIAS if router_bias else 0)
+                router_bias=False, out=None) -> lmoe_config:
+    """act / out: "bf16" or "f32" (out defaults to act)."""
+    dts = {"bf16": LMOE_BF16, "f32": LMOE_F32}
+    dt = dts[act]
+    return lmoe_config(LMOE_ABI_VERSION, D, Dp, F, E, k, eps_pool, eps_expert, dt, dt,
+                       dts[out or act], max_tokens, LMOE_FLAG_ROUTER_BIAS if router_bias else 0)
 
 
 class LatentMoE:
@@ -141,9 +144,11 @@ class LatentMoE:
     library borrows them). weights: w_router [E, D], b_router [E] or None,
     w_pool [Dp, D], g_pool [Dp], w_gate_up [E, 2F, Dp], w_down [E, Dp, F],
     g_expert [E, Dp], w_unpool [D, Dp]; activations and weights in one dtype
-    (torch.bfloat16 or torch.float32), gammas and bias float32."""
+    (torch.bfloat16 or torch.float32), gammas and bias float32. out_dtype:
+    torch.float32 or the activation dtype (the default)."""
 
-    def __init__(self, weights: dict, top_k: int, max_tokens: int, eps_pool=1e-6, eps_expert=1e-6):
+    def __init__(self, weights: dict, top_k: int, max_tokens: int, eps_pool=1e-6, eps_expert=1e-6,
+                 out_dtype=None):
         import torch
         wp = weights["w_pool"]
         act = {torch.bfloat16: "bf16", torch.float32: "f32"}[wp.dtype]
@@ -152,10 +157,12 @@ class LatentMoE:
         F = weights["w_down"].shape[2]
         self.weights = weights
         self.dtype = wp.dtype
+        self.out_dtype = out_dtype or wp.dtype
+        out = {torch.bfloat16: "bf16", torch.float32: "f32"}[self.out_dtype]
         self.D, self.Dp, self.F, self.E, self.k = D, Dp, F, E, top_k
         self.max_tokens = max_tokens
         self.cfg = make_config(D, Dp, F, E, top_k, max_tokens, act, eps_pool, eps_expert,
-                               weights.get("b_router") is not None)
+                               weights.get("b_router") is not None, out)
         ptr = lambda name: weights[name].data_ptr() if weights.get(name) is not None else None
         self.cw = lmoe_weights(ptr("w_router"), ptr("b_router"), ptr("w_pool"), ptr("g_pool"),
                                ptr("w_gate_up"), None, ptr("w_down"), None, ptr("g_expert"),
@@ -167,7 +174,8 @@ class LatentMoE:
         T = x.shape[0]
         assert x.dtype == self.dtype and x.is_contiguous() and x.shape[1] == self.D
         if out is None:
-            out = torch.empty_like(x)
+            out = torch.empty(x.shape, dtype=self.out_dtype, device=x.device)
+        assert out.dtype == self.out_dtype and out.is_contiguous() and out.shape == x.shape
         a = None
         res = {}
         if aux:

@@ -91,6 +91,8 @@ lmoe_status check_config(const lmoe_config* c) {
     return fail(LMOE_E_UNSUPPORTED, "act_dtype must be LMOE_F32 or LMOE_BF16");
   if (c->expert_wdtype != c->act_dtype)
     return fail(LMOE_E_UNSUPPORTED, "expert_wdtype must equal act_dtype (MX experts not built)");
+  if (c->out_dtype != LMOE_F32 && c->out_dtype != c->act_dtype)
+    return fail(LMOE_E_UNSUPPORTED, "out_dtype must be LMOE_F32 or act_dtype");
   if (c->max_tokens < 1) return fail(LMOE_E_INVAL, "max_tokens must be >= 1");
   if ((int64_t)c->max_tokens * c->top_k > (int64_t)INT32_MAX / 2 ||
       (int64_t)c->max_tokens * c->top_k * c->d_ff > (int64_t)1 << 40)
@@ -232,10 +234,11 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   if (!x || !out) return fail(LMOE_E_INVAL, "x or out is NULL");
   if (!aligned16(x) || !aligned16(out)) return fail(LMOE_E_INVAL, "x or out is not 16-byte aligned");
   const bool bf16 = c.act_dtype == LMOE_BF16;
-  const size_t es = bf16 ? 2 : 4;
-  const size_t io_bytes = (size_t)T * c.d_model * es;
+  const bool out_f32 = c.out_dtype == LMOE_F32;
+  const size_t x_bytes = (size_t)T * c.d_model * (bf16 ? 2 : 4);
+  const size_t o_bytes = (size_t)T * c.d_model * (out_f32 ? 4 : 2);
   const uintptr_t xb = reinterpret_cast<uintptr_t>(x), ob = reinterpret_cast<uintptr_t>(out);
-  if (xb < ob + io_bytes && ob < xb + io_bytes) return fail(LMOE_E_INVAL, "out overlaps x");
+  if (xb < ob + o_bytes && ob < xb + x_bytes) return fail(LMOE_E_INVAL, "out overlaps x");
   if (aux) {
     const void* ap[] = {aux->logits, aux->topk_ids, aux->topk_w, aux->expert_offsets, aux->sorted_assign};
     for (const void* q : ap)
@@ -404,7 +407,8 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     g.ldb = Dp;
     g.out0 = out;
     g.ldo0 = D;
-    run(launch_gemm(g, EPI_ACT, bf16, s));
+    g.n_split = D;                       // EPI_F32: every column goes to out0 as fp32
+    run(launch_gemm(g, out_f32 ? EPI_F32 : EPI_ACT, bf16, s));
   }
   mark();
   if (aux && aux->expert_offsets)

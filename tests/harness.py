@@ -54,16 +54,32 @@ def out_error(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.abs(got - ref).max() / np.sqrt((ref ** 2).mean()))
 
 
-def check_routing(ids_gpu, w_gpu, logits_ref, ids_ref, w_ref, k):
-    """Selection bit-exact (same ids in the same order) and weights within 1e-6
-    wherever the oracle's gap exceeds GAP; elsewhere the GPU's selection must
-    still be a valid top-k of the oracle's logits. Returns the mask of near-tie rows."""
+def check_routing(ids_gpu, w_gpu, logits_gpu, logits_ref, ids_ref, w_ref, k):
+    """Routing checks. Logits: within 1e-4 + 4 ulp(|l|) of the oracle's (both
+    are fp32 roundings of the same dot product plus bias; the GPU sums in fp32,
+    and a large bias makes the final add round at a coarse ulp). Selection:
+    bit-exact (same ids, same order) wherever the oracle's k-th/(k+1)-th gap
+    exceeds GAP; elsewhere the GPU's choice must still be a valid top-k.
+    Weights: the softmax of the GPU's own selected logits within 1e-6, and the
+    oracle's weights within the first-order bound |dw_j| <= 2 w_j max_i|dl_i|
+    that the logit difference implies (plus 1e-6). Returns the near-tie mask."""
+    logits_gpu = np.asarray(logits_gpu, np.float64)
+    logits_ref = np.asarray(logits_ref, np.float64)
+    diff = np.abs(logits_gpu - logits_ref)
+    lim = 1e-4 + 4 * 2.0 ** -24 * np.abs(logits_ref)
+    assert np.all(diff <= lim), f"router logits differ by {(diff - lim).max() + 1e-4:.3e}"
     gap = oracle.topk_gap(logits_ref, k)
     near = gap <= GAP
     ok = ~near
     assert np.array_equal(ids_gpu[ok], ids_ref[ok]), \
         f"selection differs on {int((ids_gpu[ok] != ids_ref[ok]).any(1).sum())} tokens"
-    assert np.abs(w_gpu[ok] - w_ref[ok]).max(initial=0.0) <= 1e-6
+    sel = np.take_along_axis(logits_gpu, ids_gpu.astype(np.int64), 1)
+    dl = np.take_along_axis(diff, ids_gpu.astype(np.int64), 1).max(axis=1)   # selected logits only
+    own = np.exp(sel - sel.max(1, keepdims=True))
+    own /= own.sum(1, keepdims=True)
+    assert np.abs(w_gpu - own).max(initial=0.0) <= 1e-6
+    bound = 2 * w_ref[ok] * dl[ok][:, None] + 1e-6
+    assert np.all(np.abs(w_gpu[ok] - w_ref[ok]) <= bound)
     for t in np.nonzero(near)[0]:
         kth = np.sort(logits_ref[t])[::-1][k - 1]
         assert np.all(logits_ref[t][ids_gpu[t]] >= kth - GAP)

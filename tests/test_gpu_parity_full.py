@@ -28,7 +28,7 @@ def full():
     H.say("[gpu] full-size: uploading weights (seed 0, 25.8 GB of experts)")
     tw = sdev.upload_weights(w, DEV)
     hw = H.host_weights(w, with_experts=False)
-    block = lmoe.LatentMoE(tw, w.k, MAX_TOKENS, w.eps_pool, w.eps_expert)
+    block = lmoe.LatentMoE(tw, w.k, MAX_TOKENS, w.eps_pool, w.eps_expert, out_dtype=torch.float32)
     yield tw, hw, block
     block.close()
 
@@ -46,7 +46,7 @@ def check(w, x, got, a, hw, rows):
     O = oracle.default()
     logits = O.router(x, hw["w_router"], hw.get("b_router"))
     ids, wts = O.topk_softmax(logits, w.k)
-    near = H.check_routing(a["topk_ids"], a["topk_w"], logits, ids, wts, w.k)
+    near = H.check_routing(a["topk_ids"], a["topk_w"], a["logits"], logits, ids, wts, w.k)
     H.check_permutation(a["topk_ids"], a["expert_offsets"], a["sorted_assign"], w.E)
     ref, _ = H.oracle_ref(w, x[rows], hw)
     keep = ~near[rows]
@@ -66,6 +66,19 @@ def test_decode_T128_all_tokens(full):
     check(w, x, got, a, hw, np.arange(w.T))
 
 
+def test_decode_bf16_output_is_rounded_fp32_output(full):
+    tw, hw, block = full
+    w = synth.WORKLOADS["decode_bf16"]
+    H.say("[gpu] full-size decode: bf16 output vs rounded fp32 output")
+    b16 = lmoe.LatentMoE(tw, w.k, MAX_TOKENS, w.eps_pool, w.eps_expert)
+    x = sdev.to_device(synth.x(w), DEV)
+    o32 = block.forward(x)
+    o16 = b16.forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(o16.view(torch.int16), o32.to(torch.bfloat16).view(torch.int16))
+    b16.close()
+
+
 def test_prefill_T16384_subset(full):
     tw, hw, block = full
     w = synth.WORKLOADS["prefill_bf16"]
@@ -79,7 +92,8 @@ def test_prefill_T16384_subset(full):
     O = oracle.default()
     logits = O.router(x[sel], hw["w_router"])
     ids, wts = O.topk_softmax(logits, w.k)
-    near = H.check_routing(a["topk_ids"][sel], a["topk_w"][sel], logits, ids, wts, w.k)
+    near = H.check_routing(a["topk_ids"][sel], a["topk_w"][sel], a["logits"][sel], logits, ids,
+                           wts, w.k)
     H.check_permutation(a["topk_ids"], a["expert_offsets"], a["sorted_assign"], w.E)
     ref, _ = H.oracle_ref(w, x[rows], hw)
     keep = ~near[np.searchsorted(sel, rows)]
@@ -97,7 +111,7 @@ def test_skewed_T4096(full):
     tws["b_router"] = sdev.to_device(b, DEV)
     hws = dict(hw)
     hws["b_router"] = b
-    block = lmoe.LatentMoE(tws, w.k, MAX_TOKENS, w.eps_pool, w.eps_expert)
+    block = lmoe.LatentMoE(tws, w.k, MAX_TOKENS, w.eps_pool, w.eps_expert, out_dtype=torch.float32)
     x = synth.x(w)
     got, a = forward(block, x)
     check(w, x, got, a, hws, synth.subset(w))
