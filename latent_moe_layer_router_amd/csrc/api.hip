@@ -27,7 +27,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 // Byte layout of the workspace for a configuration (every region 256-byte aligned).
 struct Plan {
   size_t P, logits, ids, w, masks, chunk_base, counts, offsets, sorted_assign, inv, row_token,
-      tiles, n_tiles, xp, H, Y, ss, u;
+      tiles, n_tiles, xp, H, Y, ss, u, part;
   size_t total;
   int max_slots;
 };
@@ -69,6 +69,15 @@ Plan make_plan(const lmoe_config& c) {
   p.Y = grow(cur, A * Dp * es);
   p.ss = grow(cur, A * (Dp / 64) * 4);
   p.u = grow(cur, Tm * Dp * es);
+  // split-K partials of the small-batch dense projections (bf16, T <= 128)
+  int64_t part = 0;
+  if (c.act_dtype == LMOE_BF16) {
+    const int64_t Ts = Tm < dense_stream_max_tokens() ? Tm : dense_stream_max_tokens();
+    const int64_t a = Ts * (Dp + E) * dense_stream_slices(c.d_model);
+    const int64_t b = Ts * (int64_t)c.d_model * dense_stream_slices(c.d_pooled);
+    part = (a > b ? a : b) * 4;
+  }
+  p.part = grow(cur, part);
   p.total = cur;
   return p;
 }
@@ -270,6 +279,9 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   float* ss = reinterpret_cast<float*>(ws + pl.ss);
   void* u = ws + pl.u;
   const int slots = slots_for(T, k, E);
+  // Experts with few rows go to the weight-streaming kernels (bf16, K multiple of 128).
+  const bool stream_ok = bf16 && Dp % 128 == 0 && F % 128 == 0;
+  const int small_max = stream_ok ? stream_max_rows() : 0;
 
   hipEvent_t ev[LMOE_NUM_STAGES + 1] = {};
   const bool timing = h->timing;
@@ -287,9 +299,33 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     if (err == hipSuccess) err = e;
   };
 
+  // Small batches: the dense projections stream their weights with split-K.
+  const bool dense_stream = bf16 && T <= dense_stream_max_tokens();
+  float* part = reinterpret_cast<float*>(ws + pl.part);
+  const int slices_in = dense_stream_slices(D), slices_un = dense_stream_slices(Dp);
+
   // 1. router + pooler: one GEMM over [W_pool; W_router]
   mark();
-  {
+  if (dense_stream && slices_in > 0) {
+    DenseStreamParams d{};
+    d.A = x;
+    d.lda = D;
+    d.B0 = h->w.w_pool;
+    d.B1 = h->w.w_router;
+    d.n_split = Dp;
+    d.ldb = D;
+    d.T = T;
+    d.N = Dp + E;
+    d.K = D;
+    d.slices = slices_in;
+    d.part = part;
+    d.out0 = P;
+    d.ldo0 = Dp;
+    d.out1 = logits;
+    d.ldo1 = E;
+    d.bias1 = h->w.b_router;
+    run(launch_dense_stream(d, s));
+  } else {
     GemmParams g{};
     g.M = T;
     g.N = Dp + E;
@@ -330,6 +366,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     sp.E = E;
     sp.k = k;
     sp.tile_m = kGemmBM;
+    sp.small_max = small_max;
     run(launch_sort(sp, s));
   }
   // 4. pooled RMSNorm
@@ -337,6 +374,24 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   run(launch_pool_norm(P, h->w.g_pool, T, Dp, c.eps_pool, xp, bf16, s));
   // 5. gate/up grouped GEMM + SwiGLU
   mark();
+  if (stream_ok) {
+    StreamParams sp{};
+    sp.A = xp;
+    sp.lda = Dp;
+    sp.a_gather = row_token;
+    sp.B = h->w.w_gate_up;
+    sp.ldb = Dp;
+    sp.b_expert_stride = (int64_t)2 * F * Dp;
+    sp.offsets = offsets;
+    sp.n_experts = E;
+    sp.groups = F / 32;
+    sp.max_rows = small_max;
+    sp.K = Dp;
+    sp.F = F;
+    sp.out = H;
+    sp.ldo = F;
+    run(launch_stream(sp, EPI_SWIGLU, s));
+  }
   {
     GemmParams g{};
     g.N = F;
@@ -358,6 +413,25 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   }
   // 6. down grouped GEMM + sum-of-squares partials
   mark();
+  if (stream_ok) {
+    StreamParams sp{};
+    sp.A = H;
+    sp.lda = F;
+    sp.B = h->w.w_down;
+    sp.ldb = F;
+    sp.b_expert_stride = (int64_t)Dp * F;
+    sp.offsets = offsets;
+    sp.n_experts = E;
+    sp.groups = Dp / 64;
+    sp.max_rows = small_max;
+    sp.K = F;
+    sp.F = F;
+    sp.out = Y;
+    sp.ldo = Dp;
+    sp.ss_out = ss;
+    sp.ss_ld = Dp / 64;
+    run(launch_stream(sp, EPI_DOWN, s));
+  }
   {
     GemmParams g{};
     g.N = Dp;
@@ -396,7 +470,24 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   }
   // 8. unpooler
   mark();
-  {
+  if (dense_stream && slices_un > 0) {
+    DenseStreamParams d{};
+    d.A = u;
+    d.lda = Dp;
+    d.B0 = h->w.w_unpool;
+    d.B1 = h->w.w_unpool;
+    d.n_split = D;
+    d.ldb = Dp;
+    d.T = T;
+    d.N = D;
+    d.K = Dp;
+    d.slices = slices_un;
+    d.part = part;
+    d.out0 = out;
+    d.ldo0 = D;
+    d.out0_bf16 = !out_f32;
+    run(launch_dense_stream(d, s));
+  } else {
     GemmParams g{};
     g.M = T;
     g.N = D;

@@ -16,6 +16,8 @@
 // register v of lane l at row 8*(v/4) + 4*(l/32) + v%4, column l % 32. Each lane
 // reads one 16-byte chunk per row and K-slice; A and B pair their elements the
 // same way, so the order of K inside an instruction never matters.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -167,75 +169,72 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmParams p) {
   }
 
   // ---- epilogue ----------------------------------------------------------
+  // The output tile is staged in LDS (free after the last K-step) as row-major
+  // [BM][OBN] of the output type, then written with 16-byte stores per lane, so
+  // every store instruction covers whole contiguous row segments.
   // Register v of tile (mi, ni) holds row wm*64 + mi*32 + 8*(v/4) + 4*half + v%4.
-  if (EPI == EPI_F32 || EPI == EPI_ACT) {
+  using OT = typename std::conditional<EPI == EPI_F32, float, T>::type;
+  constexpr int OBN = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  OT* stile = reinterpret_cast<OT*>(lds);
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int n = n0 + wn * 64 + ni * 32 + l32;
-        if (n >= p.N) continue;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = m0 + wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          if (m >= m_end) continue;
-          if (EPI == EPI_ACT) {
-            static_cast<T*>(p.out0)[(int64_t)m * p.ldo0 + n] = Elem<T>::from_f32(acc[mi][ni][v]);
-          } else if (n < p.n_split) {
-            static_cast<float*>(p.out0)[(int64_t)m * p.ldo0 + n] = acc[mi][ni][v];
-          } else {
-            const int c = n - p.n_split;
-            static_cast<float*>(p.out1)[(int64_t)m * p.ldo1 + c] =
-                acc[mi][ni][v] + (p.bias1 ? p.bias1[c] : 0.f);
-          }
-        }
-      }
-  } else if (EPI == EPI_SWIGLU) {
-    const int f = n0 + wn * 32 + l32;
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-        if (m >= m_end) continue;
+    for (int v = 0; v < 16; ++v) {
+      const int r = wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+      if (EPI == EPI_SWIGLU) {
         const float g = acc[mi][0][v], u = acc[mi][1][v];
-        const float h = g / (1.0f + __expf(-g)) * u;
-        static_cast<T*>(p.out0)[(int64_t)m * p.ldo0 + f] = Elem<T>::from_f32(h);
-      }
-  } else {  // EPI_DOWN
-    const int nb = n0 + wn * 64;             // first column of this wave's 64-column group
-    if (nb < p.N) {
+        stile[r * OBN + wn * 32 + l32] = Elem<T>::from_f32(g / (1.0f + __expf(-g)) * u);
+      } else {
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        float ssq[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = m0 + wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          const float y0 = round_to<T>(acc[mi][0][v]);
-          const float y1 = round_to<T>(acc[mi][1][v]);
-          ssq[v] = y0 * y0 + y1 * y1;
-          if (m < m_end) {
-            T* orow = static_cast<T*>(p.out0) + (int64_t)m * p.ldo0 + nb + l32;
-            orow[0] = Elem<T>::from_f32(y0);
-            orow[32] = Elem<T>::from_f32(y1);
-          }
-        }
-        // Sum over the 32 lanes of this half (columns nb .. nb+63 of each row).
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float t = ssq[v];
-#pragma unroll
-          for (int o = 1; o < 32; o <<= 1) t += __shfl_xor(t, o, kWave);
-          ssq[v] = t;
-        }
-        if (l32 == 0) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int m = m0 + wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-            if (m < m_end) p.ss_out[(int64_t)m * p.ss_ld + nb / 64] = ssq[v];
+        for (int ni = 0; ni < 2; ++ni) {
+          const int c = wn * 64 + ni * 32 + l32;
+          float val = acc[mi][ni][v];
+          if (EPI == EPI_F32) {
+            const int n = n0 + c;
+            if (p.bias1 && n >= p.n_split && n < p.N) val += p.bias1[n - p.n_split];
+            stile[r * OBN + c] = val;
+          } else {
+            stile[r * OBN + c] = Elem<T>::from_f32(val);   // EPI_DOWN: y rounded once, here
           }
         }
       }
+    }
+  __syncthreads();
+
+  constexpr int EPC = 16 / (int)sizeof(OT);   // elements per 16-byte chunk
+  constexpr int CPR = OBN / EPC;              // chunks per tile row
+  for (int i = tid; i < BM * CPR; i += NT) {
+    const int r = i / CPR, c = (i % CPR) * EPC;
+    const int m = m0 + r;
+    const int n = n0 + c;
+    if (m >= m_end) continue;
+    const uint4 val = *reinterpret_cast<const uint4*>(stile + r * OBN + c);
+    if (EPI == EPI_F32) {
+      if (n < p.n_split) {
+        *reinterpret_cast<uint4*>(static_cast<float*>(p.out0) + (int64_t)m * p.ldo0 + n) = val;
+      } else {
+        // second output (router logits): any width, so element stores
+        const float* f = reinterpret_cast<const float*>(&val);
+#pragma unroll
+        for (int q = 0; q < EPC; ++q)
+          if (n + q < p.N) static_cast<float*>(p.out1)[(int64_t)m * p.ldo1 + n + q - p.n_split] = f[q];
+      }
+    } else if (n < p.N || EPI == EPI_SWIGLU) {
+      *reinterpret_cast<uint4*>(static_cast<T*>(p.out0) + (int64_t)m * p.ldo0 + n) = val;
+    }
+  }
+  if (EPI == EPI_DOWN) {
+    // Sum of squares of the stored (rounded) values per row and 64-column group.
+    const int r = tid >> 1, grp = tid & 1;
+    const int m = m0 + r, nb = n0 + grp * 64;
+    if (m < m_end && nb < p.N) {
+      const OT* row = stile + r * OBN + grp * 64;
+      float ssq = 0.f;
+      for (int j = 0; j < 64; ++j) {
+        const float y = Elem<T>::to_f32(row[j]);
+        ssq += y * y;
+      }
+      p.ss_out[(int64_t)m * p.ss_ld + nb / 64] = ssq;
     }
   }
 }

@@ -44,6 +44,52 @@ constexpr int kGemmBN = 128;
 
 hipError_t launch_gemm(const GemmParams& p, EpiKind epi, bool bf16, hipStream_t s);
 
+// Weight-streaming grouped GEMM (bf16) for experts with 1..max_rows rows; one
+// wave per (expert, group of 64 weight rows). EPI_SWIGLU or EPI_DOWN.
+struct StreamParams {
+  const void* A;
+  int64_t lda;
+  const int32_t* a_gather;     // EPI_SWIGLU: token row of each sorted position
+  const void* B;
+  int64_t ldb;
+  int64_t b_expert_stride;
+  const int32_t* offsets;      // [E+1]
+  int n_experts;
+  int groups;                  // weight-row groups per expert (F/32 for SwiGLU, Dp/64 for down)
+  int max_rows;                // experts with more rows are left to the tiled GEMM
+  int K;                       // multiple of 128
+  int F;
+  void* out;
+  int64_t ldo;
+  float* ss_out;
+  int ss_ld;
+};
+int stream_max_rows();
+hipError_t launch_stream(const StreamParams& p, EpiKind epi, hipStream_t s);
+
+// Dense C = A . B^T for T <= dense_stream_max_tokens() rows (bf16), split over
+// K-slices into fp32 partials, then reduced in slice order.
+struct DenseStreamParams {
+  const void* A;
+  int64_t lda;
+  const void* B0;
+  const void* B1;              // rows [n_split, N) come from B1
+  int n_split;
+  int64_t ldb;
+  int T, N, K;
+  int slices;                  // from dense_stream_slices(K)
+  float* part;                 // [slices][T][N] scratch
+  void* out0;                  // [T][ldo0] fp32, or bf16 if out0_bf16
+  int64_t ldo0;
+  int out0_bf16;
+  float* out1;                 // [T][ldo1] fp32
+  int64_t ldo1;
+  const float* bias1;
+};
+int dense_stream_max_tokens();
+int dense_stream_slices(int K);   // 0 if K does not split evenly
+hipError_t launch_dense_stream(const DenseStreamParams& p, hipStream_t s);
+
 // Router top-k + softmax; also builds, per chunk of 64 tokens, a bitmask of
 // the chunk's tokens that selected each expert.
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
@@ -63,6 +109,7 @@ struct SortParams {
   int32_t* tiles;               // [max_slots][2]
   int32_t* n_tiles;             // [1]
   int T, E, k, tile_m;
+  int small_max;                // experts with 1..small_max rows get no tiles (streamed instead)
 };
 hipError_t launch_sort(const SortParams& p, hipStream_t s);
 

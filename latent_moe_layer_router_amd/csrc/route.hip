@@ -29,15 +29,27 @@ constexpr int kChunk = 64;
 constexpr int kMaxE = 1024;
 constexpr int kMaxPerLane = kMaxE / kWave;  // 16
 
-// (value, index) pair order: larger value first, then lower index.
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
+// Wave-wide maximum with DPP moves (no LDS round trip): butterflies inside
+// quads, half-rows and rows of 16 lanes, then row broadcasts carry each row's
+// maximum upward; lane 63 ends with the wave's maximum.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x142, 0xA, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x143, 0xC, 0xF, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
-                                                    int k, int32_t* __restrict__ ids,
-                                                    float* __restrict__ w,
-                                                    uint64_t* __restrict__ chunk_masks) {
+// One workgroup (16 waves) per chunk of 64 tokens; each wave selects for 4
+// tokens. Per round: every lane keeps its best untaken logit (lowest index on
+// ties), the wave maximum comes from wave_max, and the winner is the lowest
+// index among the lanes holding that maximum (usually a single lane).
+__global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                     int k, int32_t* __restrict__ ids,
+                                                     float* __restrict__ w,
+                                                     uint64_t* __restrict__ chunk_masks) {
   __shared__ unsigned long long masks[kMaxE];
   const int chunk = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -64,29 +76,30 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
       float bv = -INFINITY;
       int bi = 0x7FFFFFFF;
 #pragma unroll
-      for (int q = 0; q < kMaxPerLane; ++q) {
-        const int e = q * kWave + lane;
-        if (!(taken >> q & 1u) && better(v[q], e, bv, bi)) {
+      for (int q = 0; q < kMaxPerLane; ++q)
+        if (!(taken >> q & 1u) && v[q] > bv) {   // ascending q: ties keep the lower index
           bv = v[q];
-          bi = e;
+          bi = q * kWave + lane;
+        }
+      const float vmax = wave_max(bv);
+      const uint64_t tie = __ballot(bi != 0x7FFFFFFF && bv == vmax);
+      int win;
+      if (__popcll(tie) == 1) {
+        win = __builtin_amdgcn_readlane(bi, __ffsll((unsigned long long)tie) - 1);
+      } else {                                   // several lanes hold the maximum
+        win = 0x7FFFFFFF;
+        for (uint64_t m = tie; m; m &= m - 1) {
+          const int l = __ffsll((unsigned long long)m) - 1;
+          const int c = __builtin_amdgcn_readlane(bi, l);
+          win = c < win ? c : win;
         }
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, kWave);
-        const int oi = __shfl_xor(bi, o, kWave);
-        if (better(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      // Every lane now holds the winner (bv, bi).
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (j == 0) top = bv;
-      den += expf(bv - top);
+      if ((win & 63) == lane) taken |= 1u << (win >> 6);
+      if (j == 0) top = vmax;
+      den += expf(vmax - top);
       if (lane == j) {
-        my_id = bi;
-        sel_v = bv;
+        my_id = win;
+        sel_v = vmax;
       }
     }
     if (lane < k) {
@@ -144,8 +157,9 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(SortParams p) {
   const int off = block_exclusive_scan(e < p.E ? cnt : 0, wave_tot, &total);
   if (e < p.E) p.offsets[e] = off;
   if (e == 0) p.offsets[p.E] = total;
-  // Grouped-GEMM tiles: expert e gets ceil(count / tile_m) row tiles.
-  const int nt = (e < p.E) ? (cnt + p.tile_m - 1) / p.tile_m : 0;
+  // Grouped-GEMM tiles: expert e gets ceil(count / tile_m) row tiles, unless its
+  // rows are few enough for the weight-streaming kernel.
+  const int nt = (e < p.E && cnt > p.small_max) ? (cnt + p.tile_m - 1) / p.tile_m : 0;
   const int tbase = block_exclusive_scan(nt, wave_tot, &total);
   for (int q = 0; q < nt; ++q) {
     p.tiles[2 * (tbase + q)] = e;
@@ -176,7 +190,7 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
                        uint64_t* chunk_masks, hipStream_t s) {
   const int n_chunks = (T + kChunk - 1) / kChunk;
   if (n_chunks == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(n_chunks), dim3(256), 0, s, logits, T, E, k, ids, w,
+  hipLaunchKernelGGL(topk_kernel, dim3(n_chunks), dim3(1024), 0, s, logits, T, E, k, ids, w,
                      chunk_masks);
   return hipGetLastError();
 }

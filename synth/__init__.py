@@ -85,6 +85,8 @@ def _lib():
     lib.synth_mxfp4_normal.argtypes = [u64, u64, ctypes.c_size_t, ctypes.c_float,
                                        ctypes.c_void_p, ctypes.c_void_p]
     lib.synth_mxfp4_normal.restype = None
+    lib.synth_f32_to_bf16.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.synth_f32_to_bf16.restype = None
     return lib
 
 
@@ -129,6 +131,14 @@ def bf16_to_f32(a: np.ndarray) -> np.ndarray:
 
 def as_f32(a: np.ndarray) -> np.ndarray:
     return bf16_to_f32(a) if a.dtype == np.uint16 else a
+
+
+def lib_round_bf16(a: np.ndarray) -> np.ndarray:
+    """float32 array -> bfloat16 bits (uint16), nearest even (for hand-made inputs)."""
+    a = np.ascontiguousarray(a, np.float32)
+    out = np.empty(a.shape, np.uint16)
+    lib().synth_f32_to_bf16(a.ctypes.data, a.size, out.ctypes.data)
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -93,6 +93,61 @@ def test_experts_with_zero_and_one_rows():
     assert (counts == 0).any() and (counts == 1).any()
 
 
+def crafted_routing(w, assign, margin=8.0):
+    """Weights and tokens of workload w where token t is routed to expert
+    assign[t] (k = 1): router rows are the first E unit vectors and token t gets
+    `margin` added at coordinate assign[t], so its logit leads by about margin."""
+    wts = synth.dense_weights(w)
+    wr = np.zeros((w.E, w.D), np.float32)
+    wr[np.arange(w.E), np.arange(w.E)] = 1.0
+    x = synth.as_f32(synth.x(w)).copy()
+    x[np.arange(w.T), assign] += margin
+    if w.act == synth.BF16:
+        wr = synth.lib_round_bf16(wr)
+        x = synth.lib_round_bf16(x)
+    wts["w_router"] = wr
+    return wts, x
+
+
+def run_crafted(w, assign):
+    wts, x = crafted_routing(w, assign)
+    H.say(f"[gpu] crafted routing T={w.T} E={w.E} counts={np.bincount(assign, minlength=w.E).tolist()}")
+    block = lmoe.LatentMoE(upload(wts), w.k, w.T, out_dtype=torch.float32)
+    out, aux = block.forward(sdev.to_device(x, DEV), aux=True)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    a = {n: t.cpu().numpy() for n, t in aux.items()}
+    ref, raux = H.oracle_ref(w, x, wts)
+    H.check_routing(a["topk_ids"], a["topk_w"], a["logits"], raux["logits"], raux["ids"], raux["w"], w.k)
+    H.check_permutation(a["topk_ids"], a["expert_offsets"], a["sorted_assign"], w.E)
+    err = H.out_error(got, ref)
+    H.say(f"[gpu]   max|err|/rms = {err:.3e}")
+    assert err <= H.TOL[w.act]
+    block.close()
+    return a
+
+
+def test_stream_path_row_boundaries():
+    """Experts with 64 rows (the weight-streaming kernel's limit), 65 rows (the
+    tiled GEMM), 1 row and 0 rows in one call."""
+    assign = np.array([0] * 64 + [1] * 65 + [2], np.int64)
+    w = tiny(T=len(assign), D=256, Dp=128, F_=256, E=4, k=1, seed=110, act=synth.BF16)
+    a = run_crafted(w, assign)
+    assert np.diff(a["expert_offsets"]).tolist() == [64, 65, 1, 0]
+
+
+def test_stream_and_tiled_mixed():
+    """Uneven routing over 16 experts: some experts above 64 rows (tiled GEMM),
+    the rest streamed, several token tiles per streamed expert."""
+    rng = np.random.default_rng(11)
+    p = np.array([10, 8, 6, 1, 1, 1, 1, 1, 0.5, 0.5, 0.5, 0.5, 0.3, 0.3, 0.2, 0.2])
+    assign = rng.choice(16, size=700, p=p / p.sum())
+    w = tiny(T=700, D=512, Dp=256, F_=384, E=16, k=1, seed=111, act=synth.BF16)
+    a = run_crafted(w, assign)
+    counts = np.diff(a["expert_offsets"])
+    assert (counts > 64).any() and ((counts > 16) & (counts <= 64)).any()
+
+
 def test_deterministic_and_token_permutation_invariant():
     """Two runs give identical bits; permuting the tokens permutes the output
     rows bit-exactly (every row's arithmetic is independent of the batch)."""
