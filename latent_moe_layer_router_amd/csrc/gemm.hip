@@ -29,11 +29,6 @@ constexpr int BM = kGemmBM, BN = kGemmBN;
 constexpr int NT = 256;          // threads per block
 constexpr int ROWB = 128;        // bytes per tile row per K-step
 constexpr int CH = ROWB / 16;    // 16-byte chunks per tile row
-constexpr int LOADS = BM * CH / NT;  // chunks each thread loads per operand per K-step (4)
-
-struct Chunk {
-  uint4 v;
-};
 
 __device__ __forceinline__ int swz(int row, int c) { return row * ROWB + ((c ^ (row & 7)) << 4); }
 
@@ -81,18 +76,18 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmParams p) {
   const int n0 = blockIdx.y * (EPI == EPI_SWIGLU ? BN / 2 : BN);
 
   // ---- per-thread row pointers for the global loads ---------------------
+  // Thread t loads chunk t % 8 of tile rows t / 8 + 32 * i, i = 0..3, of both
+  // operands. Four named pointers (not an array) keep everything in registers.
   const int lc = tid % CH;                 // chunk this thread loads
-  const unsigned char* a_ptr[LOADS];
-  const unsigned char* b_ptr[LOADS];
   const T* Bbase = static_cast<const T*>(p.B0);
   if (kGrouped) Bbase += (int64_t)expert * p.b_expert_stride;
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int r = tid / CH + i * (NT / CH);
+  auto a_row = [&](int r) -> const unsigned char* {
     int m = m0 + r;
     if (m >= m_end) m = m_end - 1;          // rows past the end load a valid row; never stored
-    int64_t arow = (EPI == EPI_SWIGLU) ? (int64_t)p.a_gather[m] : (int64_t)m;
-    a_ptr[i] = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.A) + arow * p.lda) + lc * 16;
+    const int64_t arow = (EPI == EPI_SWIGLU) ? (int64_t)p.a_gather[m] : (int64_t)m;
+    return reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.A) + arow * p.lda) + lc * 16;
+  };
+  auto b_row = [&](int r) -> const unsigned char* {
     const T* brow;
     if (EPI == EPI_SWIGLU) {
       const int f = (r < BN / 2) ? (n0 + r) : (p.F + n0 + r - BN / 2);
@@ -105,8 +100,18 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmParams p) {
       else
         brow = Bbase + (int64_t)(n < p.N ? n : 0) * p.ldb;
     }
-    b_ptr[i] = reinterpret_cast<const unsigned char*>(brow) + lc * 16;
-  }
+    return reinterpret_cast<const unsigned char*>(brow) + lc * 16;
+  };
+  const int r0 = tid / CH;
+  const unsigned char* pa0 = a_row(r0);
+  const unsigned char* pa1 = a_row(r0 + 32);
+  const unsigned char* pa2 = a_row(r0 + 64);
+  const unsigned char* pa3 = a_row(r0 + 96);
+  const unsigned char* pb0 = b_row(r0);
+  const unsigned char* pb1 = b_row(r0 + 32);
+  const unsigned char* pb2 = b_row(r0 + 64);
+  const unsigned char* pb3 = b_row(r0 + 96);
+  const int so0 = swz(r0, lc), so1 = swz(r0 + 32, lc), so2 = swz(r0 + 64, lc), so3 = swz(r0 + 96, lc);
 
   f32x16_t acc[2][2];
 #pragma unroll
@@ -116,57 +121,66 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
-  uint4 ra[LOADS], rb[LOADS];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      ra[i] = *reinterpret_cast<const uint4*>(a_ptr[i] + (int64_t)kt * ROWB);
-      rb[i] = *reinterpret_cast<const uint4*>(b_ptr[i] + (int64_t)kt * ROWB);
-    }
-  };
-  auto sstore = [&](int stage) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int r = tid / CH + i * (NT / CH);
-      *reinterpret_cast<uint4*>(As + stage * BM * ROWB + swz(r, lc)) = ra[i];
-      *reinterpret_cast<uint4*>(Bs + stage * BN * ROWB + swz(r, lc)) = rb[i];
-    }
-  };
-
-  // Rows of the LDS tiles this lane reads for its MFMA operands.
+  // Rows of the LDS tiles this lane reads for its MFMA operands (byte offsets of
+  // the row starts; the chunk swizzle is applied per read).
   const int l32 = lane & 31, half = lane >> 5;
-  int arow[2], brow[2];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) arow[mi] = wm * 64 + mi * 32 + l32;
-#pragma unroll
-  for (int ni = 0; ni < 2; ++ni)
-    brow[ni] = (EPI == EPI_SWIGLU) ? (ni * (BN / 2) + wn * 32 + l32) : (wn * 64 + ni * 32 + l32);
+  const int arow0 = wm * 64 + l32, arow1 = wm * 64 + 32 + l32;
+  const int brow0 = (EPI == EPI_SWIGLU) ? (wn * 32 + l32) : (wn * 64 + l32);
+  const int brow1 = (EPI == EPI_SWIGLU) ? (BN / 2 + wn * 32 + l32) : (wn * 64 + 32 + l32);
 
   const int nk = p.K * (int)sizeof(T) / ROWB;
-  gload(0);
-  sstore(0);
+  uint4 xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3;
+#define LMOE_GLOAD(off)                                              \
+  xa0 = *reinterpret_cast<const uint4*>(pa0 + (off));                \
+  xa1 = *reinterpret_cast<const uint4*>(pa1 + (off));                \
+  xa2 = *reinterpret_cast<const uint4*>(pa2 + (off));                \
+  xa3 = *reinterpret_cast<const uint4*>(pa3 + (off));                \
+  xb0 = *reinterpret_cast<const uint4*>(pb0 + (off));                \
+  xb1 = *reinterpret_cast<const uint4*>(pb1 + (off));                \
+  xb2 = *reinterpret_cast<const uint4*>(pb2 + (off));                \
+  xb3 = *reinterpret_cast<const uint4*>(pb3 + (off));
+#define LMOE_SSTORE(ab, bb)                                          \
+  *reinterpret_cast<uint4*>((ab) + so0) = xa0;                       \
+  *reinterpret_cast<uint4*>((ab) + so1) = xa1;                       \
+  *reinterpret_cast<uint4*>((ab) + so2) = xa2;                       \
+  *reinterpret_cast<uint4*>((ab) + so3) = xa3;                       \
+  *reinterpret_cast<uint4*>((bb) + so0) = xb0;                       \
+  *reinterpret_cast<uint4*>((bb) + so1) = xb1;                       \
+  *reinterpret_cast<uint4*>((bb) + so2) = xb2;                       \
+  *reinterpret_cast<uint4*>((bb) + so3) = xb3;
+  LMOE_GLOAD(0)
+  LMOE_SSTORE(As, Bs)
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+    const bool more = kt + 1 < nk;
+    if (more) {
+      const int64_t off = (int64_t)(kt + 1) * ROWB;
+      LMOE_GLOAD(off)
+    }
     const unsigned char* as = As + st * BM * ROWB;
     const unsigned char* bs = Bs + st * BN * ROWB;
 #pragma unroll
     for (int s = 0; s < CH / 2; ++s) {
       const int c = 2 * s + half;
-      uint4 af[2], bfr[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi) af[mi] = *reinterpret_cast<const uint4*>(as + swz(arow[mi], c));
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) bfr[ni] = *reinterpret_cast<const uint4*>(bs + swz(brow[ni], c));
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) Mfma<T>::step(af[mi], bfr[ni], acc[mi][ni]);
+      const uint4 a0 = *reinterpret_cast<const uint4*>(as + swz(arow0, c));
+      const uint4 a1 = *reinterpret_cast<const uint4*>(as + swz(arow1, c));
+      const uint4 b0 = *reinterpret_cast<const uint4*>(bs + swz(brow0, c));
+      const uint4 b1 = *reinterpret_cast<const uint4*>(bs + swz(brow1, c));
+      Mfma<T>::step(a0, b0, acc[0][0]);
+      Mfma<T>::step(a0, b1, acc[0][1]);
+      Mfma<T>::step(a1, b0, acc[1][0]);
+      Mfma<T>::step(a1, b1, acc[1][1]);
     }
-    if (kt + 1 < nk) sstore(st ^ 1);
+    if (more) {
+      unsigned char* an = As + (st ^ 1) * BM * ROWB;
+      unsigned char* bn = Bs + (st ^ 1) * BN * ROWB;
+      LMOE_SSTORE(an, bn)
+    }
     __syncthreads();
   }
+#undef LMOE_GLOAD
+#undef LMOE_SSTORE
 
   // ---- epilogue ----------------------------------------------------------
   // The output tile is staged in LDS (free after the last K-step) as row-major
@@ -214,7 +228,7 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmParams p) {
         *reinterpret_cast<uint4*>(static_cast<float*>(p.out0) + (int64_t)m * p.ldo0 + n) = val;
       } else {
         // second output (router logits): any width, so element stores
-        const float* f = reinterpret_cast<const float*>(&val);
+        const float* f = reinterpret_cast<const float*>(stile + r * OBN + c);
 #pragma unroll
         for (int q = 0; q < EPC; ++q)
           if (n + q < p.N) static_cast<float*>(p.out1)[(int64_t)m * p.ldo1 + n + q - p.n_split] = f[q];
