@@ -27,7 +27,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 // Byte layout of the workspace for a configuration (every region 256-byte aligned).
 struct Plan {
   size_t P, logits, ids, w, masks, chunk_base, counts, offsets, sorted_assign, inv, row_token,
-      tiles, n_tiles, xp, H, Y, ss, u, part;
+      tiles, n_tiles, mt_off, xp, H, Y, ss, u, part;
   size_t total;
   int max_slots;
 };
@@ -64,6 +64,7 @@ Plan make_plan(const lmoe_config& c) {
   p.row_token = grow(cur, A * 4);
   p.tiles = grow(cur, (size_t)p.max_slots * 8);
   p.n_tiles = grow(cur, 4);
+  p.mt_off = grow(cur, (E + 1) * 4);
   p.xp = grow(cur, Tm * Dp * es);
   p.H = grow(cur, A * F * es);
   p.Y = grow(cur, A * Dp * es);
@@ -282,6 +283,11 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   // Experts with few rows go to the weight-streaming kernels (bf16, K multiple of 128).
   const bool stream_ok = bf16 && Dp % 128 == 0 && F % 128 == 0;
   const int small_max = stream_ok ? stream_max_rows() : 0;
+  // Experts with many rows: the 256 x 256 tile GEMM (bf16, Dp % 256 == 0, F % 128 == 0).
+  const bool big_ok = bf16 && Dp % 256 == 0 && F % 128 == 0;
+  int32_t* mt_off = reinterpret_cast<int32_t*>(ws + pl.mt_off);
+  const int64_t A_ = (int64_t)T * k;
+  const int mtiles_bound = (int)((A_ + 255) / 256 + (A_ < E ? A_ : E));
 
   hipEvent_t ev[LMOE_NUM_STAGES + 1] = {};
   const bool timing = h->timing;
@@ -367,6 +373,8 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     sp.k = k;
     sp.tile_m = kGemmBM;
     sp.small_max = small_max;
+    sp.mt_off = mt_off;
+    sp.tile_m2 = gemm256_tile_m();
     run(launch_sort(sp, s));
   }
   // 4. pooled RMSNorm
@@ -392,7 +400,25 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     sp.ldo = F;
     run(launch_stream(sp, EPI_SWIGLU, s));
   }
-  {
+  if (big_ok) {
+    Gemm256Params g{};
+    g.A = xp;
+    g.lda = Dp;
+    g.a_gather = row_token;
+    g.B = h->w.w_gate_up;
+    g.ldb = Dp;
+    g.b_expert_stride = (int64_t)2 * F * Dp;
+    g.offsets = offsets;
+    g.mt_off = mt_off;
+    g.E = E;
+    g.ntiles_n = F / 128;
+    g.max_tiles = g.ntiles_n * mtiles_bound;
+    g.K = Dp;
+    g.F = F;
+    g.out = H;
+    g.ldo = F;
+    run(launch_gemm256(g, EPI_SWIGLU, s));
+  } else {
     GemmParams g{};
     g.N = F;
     g.K = Dp;
@@ -432,7 +458,26 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     sp.ss_ld = Dp / 64;
     run(launch_stream(sp, EPI_DOWN, s));
   }
-  {
+  if (big_ok) {
+    Gemm256Params g{};
+    g.A = H;
+    g.lda = F;
+    g.B = h->w.w_down;
+    g.ldb = F;
+    g.b_expert_stride = (int64_t)Dp * F;
+    g.offsets = offsets;
+    g.mt_off = mt_off;
+    g.E = E;
+    g.ntiles_n = Dp / 256;
+    g.max_tiles = g.ntiles_n * mtiles_bound;
+    g.K = F;
+    g.F = F;
+    g.out = Y;
+    g.ldo = Dp;
+    g.ss_out = ss;
+    g.ss_ld = Dp / 64;
+    run(launch_gemm256(g, EPI_DOWN, s));
+  } else {
     GemmParams g{};
     g.N = Dp;
     g.K = F;

@@ -90,6 +90,31 @@ int dense_stream_max_tokens();
 int dense_stream_slices(int K);   // 0 if K does not split evenly
 hipError_t launch_dense_stream(const DenseStreamParams& p, hipStream_t s);
 
+// Large-tile (256 x 256) grouped GEMM for experts with many rows (bf16).
+// Tiles of expert e: mt_off[e+1] - mt_off[e] row tiles of 256 (in sorted row
+// order from offsets[e]) times ntiles_n column tiles.
+struct Gemm256Params {
+  const void* A;
+  int64_t lda;
+  const int32_t* a_gather;     // EPI_SWIGLU: token row of each sorted position
+  const void* B;
+  int64_t ldb;
+  int64_t b_expert_stride;
+  const int32_t* offsets;      // [E+1] rows per expert (sorted order)
+  const int32_t* mt_off;       // [E+1] exclusive prefix of 256-row tiles per expert
+  int E;
+  int ntiles_n;                // F/128 (SwiGLU: 128 gate + 128 up rows per tile) or Dp/256
+  int max_tiles;               // grid bound: ntiles_n * (ceil(T*k/256) + min(E, T*k))
+  int K;                       // multiple of 64
+  int F;
+  void* out;
+  int64_t ldo;
+  float* ss_out;
+  int ss_ld;
+};
+int gemm256_tile_m();
+hipError_t launch_gemm256(const Gemm256Params& p, EpiKind epi, hipStream_t s);
+
 // Router top-k + softmax; also builds, per chunk of 64 tokens, a bitmask of
 // the chunk's tokens that selected each expert.
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
@@ -110,6 +135,8 @@ struct SortParams {
   int32_t* n_tiles;             // [1]
   int T, E, k, tile_m;
   int small_max;                // experts with 1..small_max rows get no tiles (streamed instead)
+  int32_t* mt_off;              // [E+1] 256-row tile prefix for the large-tile GEMM
+  int tile_m2;                  // 256
 };
 hipError_t launch_sort(const SortParams& p, hipStream_t s);
 

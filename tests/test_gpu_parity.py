@@ -72,10 +72,13 @@ def test_multi_tile_fp32():
     run_case(tiny(T=300, D=512, Dp=256, F_=384, E=12, k=3, seed=104, act=synth.F32))
 
 
-def test_all_tokens_same_experts():
+@pytest.mark.parametrize("Dp,F", [(128, 128), (256, 256)])
+def test_all_tokens_same_experts(Dp, F):
     """A router bias forces every token onto the same k experts: three full
-    experts of 300 rows (3 tiles each, ragged) and every other expert empty."""
-    w = tiny(T=300, D=256, Dp=128, F_=128, E=16, k=3, seed=105, act=synth.BF16)
+    experts of 300 rows and every other expert empty. With Dp = F = 128 they
+    run as three 128-row tiles each; with Dp = F = 256 on the 256-row tiles,
+    one full tile plus a 44-row tail each."""
+    w = tiny(T=300, D=256, Dp=Dp, F_=F, E=16, k=3, seed=105, act=synth.BF16)
     wts = synth.dense_weights(w)
     b = np.zeros(w.E, np.float32)
     b[[3, 5, 7]] = [60.0, 50.0, 40.0]
