@@ -2,11 +2,15 @@
 // GEMMs of the block (gate/up with the SwiGLU epilogue, down with the bf16
 // output and per-64-column sums of squares).
 //
-// Tile 256 x 256 (A rows x B rows), K-step 64 bf16 (128 bytes per row), LDS
-// double-buffered (2 x 64 KiB), 256 threads = 4 wave64 in a 2 x 2 grid, each
-// wave a 128 x 128 sub-tile of 4 x 4 MFMA 32x32x16 bf16 (the accumulators live
-// in AGPRs). Per K-step a wave reads 8 operand chunks from LDS for 16 MFMAs,
-// which keeps LDS traffic well under its bandwidth.
+// Tile 256 x 256 (A rows x B rows), 256 threads = 4 wave64 in a 2 x 2 grid,
+// each wave a 128 x 128 sub-tile of 4 x 4 MFMA 32x32x16 bf16 (accumulators in
+// AGPRs). Per 16-wide K-slice a wave reads 8 operand chunks from LDS for 16
+// MFMAs, which keeps LDS traffic well under its bandwidth.
+//
+// Operands reach LDS through gfx950's direct global-to-LDS loads (no register
+// staging) in a four-stage pipeline of 32-wide K-steps (4 x 32 KiB): the loads
+// for step k + 3 are issued while step k computes, so three steps of latency
+// (about 3000 cycles at full MFMA rate) are covered.
 //
 // Scheduling for the 8 XCDs: the tiles of all experts form one index space
 // ordered (expert, n-tile, m-tile); it is cut into 8 contiguous chunks and
@@ -24,20 +28,46 @@ namespace {
 
 constexpr int BM = 256, BNB = 256;   // A rows, B rows per tile
 constexpr int NT = 256;
-constexpr int ROWB = 128;
-constexpr int CH = 8;
-constexpr int STAGE_A = BM * ROWB, STAGE_B = BNB * ROWB;
+constexpr int RB = 64;                // bytes of each tile row per pipeline stage (32 bf16)
+constexpr int SB = BM * RB;           // bytes per operand per stage (16 KiB)
 
-__device__ __forceinline__ int swz(int row, int c) { return row * ROWB + ((c ^ (row & 7)) << 4); }
+#define LMOE_AS3 __attribute__((address_space(3)))
+
+// Four pipeline stages for A and B, each a separate LDS object so that the
+// compiler can tell the stages apart when it orders reads against the
+// asynchronous global-to-LDS loads still in flight for other stages.
+__shared__ __attribute__((aligned(16))) unsigned char sA0[SB], sB0[SB], sA1[SB], sB1[SB],
+    sA2[SB], sB2[SB], sA3[SB], sB3[SB];
+
+// Byte offset of logical 16-byte chunk c (0..3) of tile row r. The chunk is
+// stored at position c ^ ((r >> 2) & 3): the eight rows a 128-bit LDS read
+// phase touches then cover distinct banks.
+__device__ __forceinline__ int swz(int r, int c) { return r * RB + ((c ^ ((r >> 2) & 3)) << 4); }
 
 __device__ __forceinline__ void mfma32(const uint4& a, const uint4& b, f32x16_t& acc) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                 __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
 }
 
+// Wait until this wave has at most 16 global loads in flight (two later
+// stages of 8), without waiting on LDS or export counters.
+__device__ __forceinline__ void wait_vm(int) { __builtin_amdgcn_s_waitcnt(0x4F70); }
+
+// Stage hand-off barrier. __syncthreads would fence global memory and so wait
+// for every load in flight (the later pipeline stages), and even an LDS-scoped
+// release fence waits for them, since direct-to-LDS loads count as LDS writes.
+// So: each wave first waits explicitly for its own loads of the stage (wait_vm),
+// then the barrier, then an LDS-scoped acquire fence that keeps the compiler
+// from hoisting the stage's LDS reads above the barrier. Reads of the buffer a
+// new load is about to overwrite all fed MFMAs before the barrier, so they have
+// completed.
+__device__ __forceinline__ void bar() {
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int EPI>
 __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * (STAGE_A + STAGE_B)];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
@@ -56,32 +86,45 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
   const int mt_e = p.mt_off[e + 1] - p.mt_off[e];
   const int tl = t - p.ntiles_n * p.mt_off[e];
   const int ntile = tl / mt_e, mtile = tl % mt_e;
-  const int row0 = p.offsets[e];
-  const int m0 = row0 + mtile * BM;
+  const int m0 = p.offsets[e] + mtile * BM;
   const int m_end = p.offsets[e + 1];
   const int n0 = ntile * (EPI == EPI_SWIGLU ? BNB / 2 : BNB);   // output column start
 
-  // ---- global load addresses: thread loads chunk tid % 8 of rows tid/8 + 32 i
-  const int lc = tid % CH, r0 = tid / CH;
+  // ---- global-to-LDS loads ------------------------------------------------
+  // Per stage each wave moves 4 x 16 rows of A and of B, one 1 KiB load each:
+  // lane i carries row (4 w + j) * 16 + i / 4 and lands at LDS chunk position
+  // i % 4 of that row, so it fetches the logical chunk stored there.
   const bf16_t* Be = static_cast<const bf16_t*>(p.B) + (int64_t)e * p.b_expert_stride;
-  auto a_row = [&](int r) -> const unsigned char* {
+  const int pos = lane & 3;
+  auto a_src = [&](int r) -> const unsigned char* {
     int m = m0 + r;
-    if (m >= m_end) m = m_end - 1;
+    if (m >= m_end) m = m_end - 1;           // rows past the end load a valid row; never stored
     const int64_t src = (EPI == EPI_SWIGLU) ? (int64_t)p.a_gather[m] : (int64_t)m;
-    return reinterpret_cast<const unsigned char*>(static_cast<const bf16_t*>(p.A) + src * p.lda) + lc * 16;
+    const int c = pos ^ ((r >> 2) & 3);
+    return reinterpret_cast<const unsigned char*>(static_cast<const bf16_t*>(p.A) + src * p.lda) + c * 16;
   };
-  auto b_row = [&](int r) -> const unsigned char* {
+  auto b_src = [&](int r) -> const unsigned char* {
     const int n = (EPI == EPI_SWIGLU) ? ((r < BNB / 2) ? (n0 + r) : (p.F + n0 + r - BNB / 2)) : (n0 + r);
-    return reinterpret_cast<const unsigned char*>(Be + (int64_t)n * p.ldb) + lc * 16;
+    const int c = pos ^ ((r >> 2) & 3);
+    return reinterpret_cast<const unsigned char*>(Be + (int64_t)n * p.ldb) + c * 16;
   };
-#define LMOE_PTRS(X, f)                                                               \
-  const unsigned char *X##0 = f(r0), *X##1 = f(r0 + 32), *X##2 = f(r0 + 64), *X##3 = f(r0 + 96), \
-                      *X##4 = f(r0 + 128), *X##5 = f(r0 + 160), *X##6 = f(r0 + 192),              \
-                      *X##7 = f(r0 + 224);
-  LMOE_PTRS(pa, a_row)
-  LMOE_PTRS(pb, b_row)
-#undef LMOE_PTRS
-  const int so = swz(r0, lc);                 // rows r0 + 32 i keep the same swizzle (32 % 8 == 0)
+  const int rr = wave * 64 + (lane >> 2);    // row of load j is rr + 16 j
+  const unsigned char *ga0 = a_src(rr), *ga1 = a_src(rr + 16), *ga2 = a_src(rr + 32), *ga3 = a_src(rr + 48);
+  const unsigned char *gb0 = b_src(rr), *gb1 = b_src(rr + 16), *gb2 = b_src(rr + 32), *gb3 = b_src(rr + 48);
+  const int dbase = wave * 64 * RB;          // this wave's 4 KiB region of each operand stage
+
+#define LMOE_ISSUE(kt, SA, SBB)                                                                         \
+  {                                                                                                    \
+    const int64_t o = (int64_t)(kt) * RB;                                                              \
+    __builtin_amdgcn_global_load_lds(ga0 + o, (LMOE_AS3 void*)((SA) + dbase), 16, 0, 0);                \
+    __builtin_amdgcn_global_load_lds(ga1 + o, (LMOE_AS3 void*)((SA) + dbase + 16 * RB), 16, 0, 0);      \
+    __builtin_amdgcn_global_load_lds(ga2 + o, (LMOE_AS3 void*)((SA) + dbase + 32 * RB), 16, 0, 0);      \
+    __builtin_amdgcn_global_load_lds(ga3 + o, (LMOE_AS3 void*)((SA) + dbase + 48 * RB), 16, 0, 0);      \
+    __builtin_amdgcn_global_load_lds(gb0 + o, (LMOE_AS3 void*)((SBB) + dbase), 16, 0, 0);               \
+    __builtin_amdgcn_global_load_lds(gb1 + o, (LMOE_AS3 void*)((SBB) + dbase + 16 * RB), 16, 0, 0);     \
+    __builtin_amdgcn_global_load_lds(gb2 + o, (LMOE_AS3 void*)((SBB) + dbase + 32 * RB), 16, 0, 0);     \
+    __builtin_amdgcn_global_load_lds(gb3 + o, (LMOE_AS3 void*)((SBB) + dbase + 48 * RB), 16, 0, 0);     \
+  }
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -91,104 +134,118 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
-  uint4 xa0, xa1, xa2, xa3, xa4, xa5, xa6, xa7, xb0, xb1, xb2, xb3, xb4, xb5, xb6, xb7;
-#define LMOE_LD(off)                                                                       \
-  xa0 = *reinterpret_cast<const uint4*>(pa0 + (off)); xa1 = *reinterpret_cast<const uint4*>(pa1 + (off)); \
-  xa2 = *reinterpret_cast<const uint4*>(pa2 + (off)); xa3 = *reinterpret_cast<const uint4*>(pa3 + (off)); \
-  xa4 = *reinterpret_cast<const uint4*>(pa4 + (off)); xa5 = *reinterpret_cast<const uint4*>(pa5 + (off)); \
-  xa6 = *reinterpret_cast<const uint4*>(pa6 + (off)); xa7 = *reinterpret_cast<const uint4*>(pa7 + (off)); \
-  xb0 = *reinterpret_cast<const uint4*>(pb0 + (off)); xb1 = *reinterpret_cast<const uint4*>(pb1 + (off)); \
-  xb2 = *reinterpret_cast<const uint4*>(pb2 + (off)); xb3 = *reinterpret_cast<const uint4*>(pb3 + (off)); \
-  xb4 = *reinterpret_cast<const uint4*>(pb4 + (off)); xb5 = *reinterpret_cast<const uint4*>(pb5 + (off)); \
-  xb6 = *reinterpret_cast<const uint4*>(pb6 + (off)); xb7 = *reinterpret_cast<const uint4*>(pb7 + (off));
-#define LMOE_ST(as, bs)                                                                    \
-  *reinterpret_cast<uint4*>((as) + so) = xa0;                                              \
-  *reinterpret_cast<uint4*>((as) + so + 32 * ROWB) = xa1;                                  \
-  *reinterpret_cast<uint4*>((as) + so + 64 * ROWB) = xa2;                                  \
-  *reinterpret_cast<uint4*>((as) + so + 96 * ROWB) = xa3;                                  \
-  *reinterpret_cast<uint4*>((as) + so + 128 * ROWB) = xa4;                                 \
-  *reinterpret_cast<uint4*>((as) + so + 160 * ROWB) = xa5;                                 \
-  *reinterpret_cast<uint4*>((as) + so + 192 * ROWB) = xa6;                                 \
-  *reinterpret_cast<uint4*>((as) + so + 224 * ROWB) = xa7;                                 \
-  *reinterpret_cast<uint4*>((bs) + so) = xb0;                                              \
-  *reinterpret_cast<uint4*>((bs) + so + 32 * ROWB) = xb1;                                  \
-  *reinterpret_cast<uint4*>((bs) + so + 64 * ROWB) = xb2;                                  \
-  *reinterpret_cast<uint4*>((bs) + so + 96 * ROWB) = xb3;                                  \
-  *reinterpret_cast<uint4*>((bs) + so + 128 * ROWB) = xb4;                                 \
-  *reinterpret_cast<uint4*>((bs) + so + 160 * ROWB) = xb5;                                 \
-  *reinterpret_cast<uint4*>((bs) + so + 192 * ROWB) = xb6;                                 \
-  *reinterpret_cast<uint4*>((bs) + so + 224 * ROWB) = xb7;
-
   // LDS rows of this lane's MFMA operands: A rows wm*128 + 32 mi + l32; B rows:
   // SwiGLU pairs gate (ni = 0, 1) and up (ni = 2, 3) of the same 64 columns.
   const int l32 = lane & 31, half = lane >> 5;
-  const int abase = wm * 128 + l32;
+  const int aoff0 = swz(wm * 128 + l32, half), aoff1 = swz(wm * 128 + l32, 2 + half);
   auto brow_of = [&](int ni) {
     return (EPI == EPI_SWIGLU) ? ((ni >> 1) * (BNB / 2) + wn * 64 + (ni & 1) * 32 + l32)
                                : (wn * 128 + ni * 32 + l32);
   };
-  const int bb0 = brow_of(0), bb1 = brow_of(1), bb2 = brow_of(2), bb3 = brow_of(3);
+  const int b00 = swz(brow_of(0), half), b01 = swz(brow_of(0), 2 + half);
+  const int b10 = swz(brow_of(1), half), b11 = swz(brow_of(1), 2 + half);
+  const int b20 = swz(brow_of(2), half), b21 = swz(brow_of(2), 2 + half);
+  const int b30 = swz(brow_of(3), half), b31 = swz(brow_of(3), 2 + half);
   // rows of this wave that hold real tokens (tail tiles skip empty 32-row groups)
   const int mrows = m_end - (m0 + wm * 128);
-  const int nmi = mrows <= 0 ? 0 : (mrows >= 128 ? 4 : (mrows + 31) / 32);
+  const int nmi = __builtin_amdgcn_readfirstlane(mrows <= 0 ? 0 : (mrows >= 128 ? 4 : (mrows + 31) / 32));
 
-  const int nk = p.K * 2 / ROWB;
-  LMOE_LD(0)
-  LMOE_ST(lds, lds + STAGE_A)
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int64_t off = (int64_t)(kt + 1) * ROWB;
-      LMOE_LD(off)
-    }
-    const unsigned char* as = lds + st * (STAGE_A + STAGE_B);
-    const unsigned char* bs = as + STAGE_A;
-#pragma unroll
-    for (int s = 0; s < CH / 2; ++s) {
-      const int c = 2 * s + half;
-      const uint4 b0 = *reinterpret_cast<const uint4*>(bs + swz(bb0, c));
-      const uint4 b1 = *reinterpret_cast<const uint4*>(bs + swz(bb1, c));
-      const uint4 b2 = *reinterpret_cast<const uint4*>(bs + swz(bb2, c));
-      const uint4 b3 = *reinterpret_cast<const uint4*>(bs + swz(bb3, c));
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        if (mi < nmi) {
-          const uint4 a = *reinterpret_cast<const uint4*>(as + swz(abase + mi * 32, c));
-          mfma32(a, b0, acc[mi][0]);
-          mfma32(a, b1, acc[mi][1]);
-          mfma32(a, b2, acc[mi][2]);
-          mfma32(a, b3, acc[mi][3]);
-        }
-      }
-    }
-    if (more) {
-      unsigned char* an = lds + (st ^ 1) * (STAGE_A + STAGE_B);
-      LMOE_ST(an, an + STAGE_A)
-    }
-    __syncthreads();
+#define LMOE_SUB(FULL, SA, SBB, AO, B0, B1, B2, B3)                                              \
+  {                                                                                            \
+    const uint4 b0 = *reinterpret_cast<const uint4*>((SBB) + (B0));                            \
+    const uint4 b1 = *reinterpret_cast<const uint4*>((SBB) + (B1));                            \
+    const uint4 b2 = *reinterpret_cast<const uint4*>((SBB) + (B2));                            \
+    const uint4 b3 = *reinterpret_cast<const uint4*>((SBB) + (B3));                            \
+    const uint4 a0 = *reinterpret_cast<const uint4*>((SA) + (AO));                             \
+    const uint4 a1 = *reinterpret_cast<const uint4*>((SA) + (AO) + 32 * RB);                   \
+    const uint4 a2 = *reinterpret_cast<const uint4*>((SA) + (AO) + 64 * RB);                   \
+    const uint4 a3 = *reinterpret_cast<const uint4*>((SA) + (AO) + 96 * RB);                   \
+    if (FULL || nmi > 0) {                                                                     \
+      mfma32(a0, b0, acc[0][0]); mfma32(a0, b1, acc[0][1]);                                    \
+      mfma32(a0, b2, acc[0][2]); mfma32(a0, b3, acc[0][3]);                                    \
+    }                                                                                          \
+    if (FULL || nmi > 1) {                                                                     \
+      mfma32(a1, b0, acc[1][0]); mfma32(a1, b1, acc[1][1]);                                    \
+      mfma32(a1, b2, acc[1][2]); mfma32(a1, b3, acc[1][3]);                                    \
+    }                                                                                          \
+    if (FULL || nmi > 2) {                                                                     \
+      mfma32(a2, b0, acc[2][0]); mfma32(a2, b1, acc[2][1]);                                    \
+      mfma32(a2, b2, acc[2][2]); mfma32(a2, b3, acc[2][3]);                                    \
+    }                                                                                          \
+    if (FULL || nmi > 3) {                                                                     \
+      mfma32(a3, b0, acc[3][0]); mfma32(a3, b1, acc[3][1]);                                    \
+      mfma32(a3, b2, acc[3][2]); mfma32(a3, b3, acc[3][3]);                                    \
+    }                                                                                          \
   }
-#undef LMOE_LD
-#undef LMOE_ST
+  // One K-step: wait for this stage (this wave's loads, then everyone's), start
+  // the load three stages ahead into the buffer freed by the previous step,
+  // then run its 32 MFMAs per wave. The load is issued unconditionally (near
+  // the end it re-reads the last stage into a buffer no later step reads), so
+  // every step has exactly three stages in flight and a branch-free body.
+#define LMOE_STEP(FULL, k, SA, SBB, NA, NB)                                                      \
+  {                                                                                            \
+    wait_vm(16);                                                                               \
+    bar();                                                                                     \
+    LMOE_ISSUE(((k) + 3 < nk ? (k) + 3 : nk - 1), NA, NB)                                       \
+    LMOE_SUB(FULL, SA, SBB, aoff0, b00, b10, b20, b30)                                         \
+    LMOE_SUB(FULL, SA, SBB, aoff1, b01, b11, b21, b31)                                         \
+  }
+#define LMOE_KLOOP(FULL)                                                                         \
+  for (int k = 0; k < nk; k += 4) {                                                            \
+    LMOE_STEP(FULL, k, sA0, sB0, sA3, sB3)                                                     \
+    LMOE_STEP(FULL, k + 1, sA1, sB1, sA0, sB0)                                                 \
+    LMOE_STEP(FULL, k + 2, sA2, sB2, sA1, sB1)                                                 \
+    LMOE_STEP(FULL, k + 3, sA3, sB3, sA2, sB2)                                                 \
+  }
+
+  const int nk = p.K / 32;                   // a multiple of 4 (K % 128 == 0)
+  LMOE_ISSUE(0, sA0, sB0)
+  LMOE_ISSUE(1, sA1, sB1)
+  LMOE_ISSUE(2, sA2, sB2)
+  if (nmi == 4) {
+    LMOE_KLOOP(true)
+  } else {
+    LMOE_KLOOP(false)
+  }
+#undef LMOE_KLOOP
+#undef LMOE_STEP
+#undef LMOE_SUB
+#undef LMOE_ISSUE
+  __syncthreads();   // every load has landed and every wave has finished reading
 
   // ---- epilogue: stage [256][OBN] bf16 in LDS, 16-byte stores ----------------
+  // The staging tile spans the stage buffers: rows [32 q, 32 q + 32) live in
+  // buffer q (A0, B0, A1, ..., B3 in declaration order), 16 KiB each.
   constexpr int OBN = (EPI == EPI_SWIGLU) ? BNB / 2 : BNB;
-  bf16_t* stile = reinterpret_cast<bf16_t*>(lds);
+  auto srow = [&](int r) -> bf16_t* {
+    unsigned char* b;
+    switch (r >> 5) {
+      case 0: b = sA0; break;
+      case 1: b = sB0; break;
+      case 2: b = sA1; break;
+      case 3: b = sB1; break;
+      case 4: b = sA2; break;
+      case 5: b = sB2; break;
+      case 6: b = sA3; break;
+      default: b = sB3; break;
+    }
+    return reinterpret_cast<bf16_t*>(b) + (r & 31) * OBN;
+  };
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int r = wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+      bf16_t* row = srow(r);
       if (EPI == EPI_SWIGLU) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const float g = acc[mi][h][v], u = acc[mi][2 + h][v];
-          stile[r * OBN + wn * 64 + h * 32 + l32] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+          row[wn * 64 + h * 32 + l32] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
         }
       } else {
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) stile[r * OBN + wn * 128 + ni * 32 + l32] = f32_to_bf16(acc[mi][ni][v]);
+        for (int ni = 0; ni < 4; ++ni) row[wn * 128 + ni * 32 + l32] = f32_to_bf16(acc[mi][ni][v]);
       }
     }
   __syncthreads();
@@ -198,7 +255,7 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
     const int m = m0 + r;
     if (m >= m_end) continue;
     *reinterpret_cast<uint4*>(static_cast<bf16_t*>(p.out) + (int64_t)m * p.ldo + n0 + c) =
-        *reinterpret_cast<const uint4*>(stile + r * OBN + c);
+        *reinterpret_cast<const uint4*>(srow(r) + c);
   }
   if (EPI == EPI_DOWN) {
     // sums of squares of the stored bf16 values, per row and 64-column group
@@ -206,7 +263,7 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
       const int r = i / (BNB / 64), grp = i % (BNB / 64);
       const int m = m0 + r;
       if (m >= m_end) continue;
-      const bf16_t* row = stile + r * OBN + grp * 64;
+      const bf16_t* row = srow(r) + grp * 64;
       float ssq = 0.f;
       for (int j = 0; j < 64; ++j) {
         const float y = bf16_to_f32(row[j]);
