@@ -12,6 +12,7 @@ Prints one JSON line. Weights are random-initialized (seed 0) with the model's
 shapes; inputs are synthetic (see synth/).
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -72,23 +73,61 @@ def run_workload(lmoe, torch, synth, sdev, block, w, steps, warmup, dev):
     return ms, stage_ms, n_active, counts
 
 
+# The gate/up kernel of each regime and the sources that define it: the
+# weight-streaming kernel for decode-sized batches, the 256 x 256 tile GEMM for
+# prefill-sized ones.
+CSRC = os.path.join(ROOT, "latent_moe_layer_router_amd", "csrc")
+GATE_UP_KERNEL = {"hbm": ("stream_kernel<EPI_SWIGLU>", ("stream.hip", "common.h")),
+                  "mfma": ("gemm256_kernel<EPI_SWIGLU>", ("gemm256.hip", "common.h"))}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.txt")
+
+
+def kernel_digest(bound):
+    h = hashlib.sha256()
+    for f in GATE_UP_KERNEL[bound][1]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, bound):
+    """HBM bytes per launch of the gate/up kernel, as read by the FETCH_SIZE and
+    WRITE_SIZE counters (each scaled by its plain-copy calibration factor) on
+    this workload. None unless they were taken on the kernel source as it is now."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            lines = fh.read().splitlines()
+    except OSError:
+        return None
+    digest = kernel_digest(bound)
+    for ln in lines:
+        f = ln.split()
+        if len(f) == 4 and not ln.startswith("#") and f[0] == workload and f[1] == digest:
+            return int(f[2]) + int(f[3])
+    return None
+
+
 def roofline(w, stage_ms, n_active, bound):
     byts, flops = algorithmic(w, n_active, "gate_up")
     t = stage_ms["gate_up"] * 1e-3
+    traffic = measured_traffic(w.name, bound)
+    common = {"kernel": GATE_UP_KERNEL[bound][0] + " (gate/up grouped GEMM + SwiGLU)",
+              "traffic": traffic, "algorithmic_bytes": byts,
+              "traffic_over_algorithmic": None if traffic is None else round(traffic / byts, 3),
+              "avg_ms": round(stage_ms["gate_up"], 4)}
     if bound == "hbm":
         ach = byts / t / 1e9
-        return {"kernel": "gate_up grouped GEMM + SwiGLU", "bound": "hbm", "achieved": round(ach, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                "traffic": None, "algorithmic_bytes": byts, "avg_ms": round(stage_ms["gate_up"], 4)}
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), **common}
     ach = flops / t / 1e12
-    return {"kernel": "gate_up grouped GEMM + SwiGLU", "bound": "mfma", "achieved": round(ach, 1),
-            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-            "traffic": None, "algorithmic_flops": flops, "avg_ms": round(stage_ms["gate_up"], 4)}
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4), "algorithmic_flops": flops, **common}
 
 
 def cpu_baseline(synth, w):
-    """The CPU oracle on the whole decode batch (its T tokens), timed on this
-    host's cores; expert weights are generated before the clock starts."""
+    """The CPU oracle on the whole decode batch (its T tokens, four times over),
+    timed on this host's cores; expert weights are generated before the clock
+    starts."""
     import numpy as np
 
     import oracle
@@ -99,13 +138,16 @@ def cpu_baseline(synth, w):
     O = oracle.default()
     ids, _ = O.topk_softmax(O.router(x, wts["w_router"], wts["b_router"]), w.k)
     experts = {int(e): (synth.w_gate_up(w, int(e)), synth.w_down(w, int(e))) for e in np.unique(ids)}
+    reps = 4
     t0 = time.perf_counter()
-    O.forward(x, wts, w.k, w.eps_pool, w.eps_expert, get_expert=experts.__getitem__,
-              rnd=w.act == synth.BF16)
+    for _ in range(reps):
+        O.forward(x, wts, w.k, w.eps_pool, w.eps_expert, get_expert=experts.__getitem__,
+                  rnd=w.act == synth.BF16)
     dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
-    return {"value": round(w.T / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"all {w.T} tokens of the {w.name} batch (one full step), {dt:.1f} s"}
+    return {"value": round(reps * w.T / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"all {w.T} tokens of the {w.name} batch (one full step) run {reps} times, "
+                      f"{dt:.1f} s in total"}
 
 
 def main():

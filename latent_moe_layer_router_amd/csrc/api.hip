@@ -287,7 +287,12 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   const bool big_ok = bf16 && Dp % 256 == 0 && F % 128 == 0;
   int32_t* mt_off = reinterpret_cast<int32_t*>(ws + pl.mt_off);
   const int64_t A_ = (int64_t)T * k;
-  const int mtiles_bound = (int)((A_ + 255) / 256 + (A_ < E ? A_ : E));
+  // Row tiles of 256 over the experts with more than small_max rows: at most
+  // floor(A / 256) full ones plus one partial per such expert, and there are at
+  // most floor(A / (small_max + 1)) such experts. The bound sizes the grid, so a
+  // tight one keeps the launch cheap when few or no experts are large (decode).
+  const int64_t n_big = A_ / (small_max + 1) < E ? A_ / (small_max + 1) : E;
+  const int mtiles_bound = (int)(A_ / 256 + n_big);
 
   hipEvent_t ev[LMOE_NUM_STAGES + 1] = {};
   const bool timing = h->timing;

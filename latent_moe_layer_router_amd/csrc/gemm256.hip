@@ -49,18 +49,19 @@ __device__ __forceinline__ void mfma32(const uint4& a, const uint4& b, f32x16_t&
                                                 __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
 }
 
-// Wait until this wave has at most 16 global loads in flight (two later
-// stages of 8), without waiting on LDS or export counters.
-__device__ __forceinline__ void wait_vm(int) { __builtin_amdgcn_s_waitcnt(0x4F70); }
+// Before the stage barrier: wait until this wave has at most 16 global loads
+// in flight (its two later stages of 8) and none of its LDS reads outstanding.
+// The second part matters because the scheduler may move the previous step's
+// MFMAs (not their LDS reads) past the barrier, after which another wave's
+// load may overwrite the buffer those reads come from.
+__device__ __forceinline__ void wait_vm(int) { __builtin_amdgcn_s_waitcnt(0x4070); }
 
 // Stage hand-off barrier. __syncthreads would fence global memory and so wait
 // for every load in flight (the later pipeline stages), and even an LDS-scoped
 // release fence waits for them, since direct-to-LDS loads count as LDS writes.
-// So: each wave first waits explicitly for its own loads of the stage (wait_vm),
-// then the barrier, then an LDS-scoped acquire fence that keeps the compiler
-// from hoisting the stage's LDS reads above the barrier. Reads of the buffer a
-// new load is about to overwrite all fed MFMAs before the barrier, so they have
-// completed.
+// So: each wave first waits explicitly for its own loads of the stage and its
+// own LDS reads (wait_vm), then the barrier, then an LDS-scoped acquire fence
+// that keeps the compiler from hoisting the stage's LDS reads above it.
 __device__ __forceinline__ void bar() {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");

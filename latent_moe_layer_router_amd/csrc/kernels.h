@@ -104,7 +104,7 @@ struct Gemm256Params {
   const int32_t* mt_off;       // [E+1] exclusive prefix of 256-row tiles per expert
   int E;
   int ntiles_n;                // F/128 (SwiGLU: 128 gate + 128 up rows per tile) or Dp/256
-  int max_tiles;               // grid bound: ntiles_n * (ceil(T*k/256) + min(E, T*k))
+  int max_tiles;               // grid size, a bound on the tile count
   int K;                       // multiple of 64
   int F;
   void* out;

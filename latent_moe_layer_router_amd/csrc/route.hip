@@ -166,7 +166,7 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(SortParams p) {
     p.tiles[2 * (tbase + q) + 1] = off + q * p.tile_m;
   }
   if (e == 0) *p.n_tiles = total;
-  // the same for the large-tile GEMM's 256-row tiles
+  // the large-tile GEMM: ceil(count / 256) row tiles
   const int nt2 = (e < p.E && cnt > p.small_max) ? (cnt + p.tile_m2 - 1) / p.tile_m2 : 0;
   const int mbase = block_exclusive_scan(nt2, wave_tot, &total);
   if (e < p.E) p.mt_off[e] = mbase;
