@@ -284,7 +284,11 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   const bool stream_ok = bf16 && Dp % 128 == 0 && F % 128 == 0;
   const int small_max = stream_ok ? stream_max_rows() : 0;
   // Experts with many rows: the 256 x 256 tile GEMM (bf16, Dp % 256 == 0, F % 128 == 0).
-  const bool big_ok = bf16 && Dp % 256 == 0 && F % 128 == 0;
+  // Its buffer loads take 32-bit byte offsets: the activations (xp, H) and one
+  // expert's weights must each stay below 2 GiB.
+  const bool big_ok = bf16 && Dp % 256 == 0 && F % 128 == 0 &&
+                      (int64_t)T * k * F * 2 < ((int64_t)1 << 31) && (int64_t)T * Dp * 2 < ((int64_t)1 << 31) &&
+                      (int64_t)2 * F * Dp * 2 < ((int64_t)1 << 31);
   int32_t* mt_off = reinterpret_cast<int32_t*>(ws + pl.mt_off);
   const int64_t A_ = (int64_t)T * k;
   // Row tiles of 256 over the experts with more than small_max rows: at most
@@ -418,6 +422,8 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     g.E = E;
     g.ntiles_n = F / 128;
     g.max_tiles = g.ntiles_n * mtiles_bound;
+    g.a_bytes = (uint32_t)((int64_t)T * Dp * 2);
+    g.b_bytes = (uint32_t)((int64_t)2 * F * Dp * 2);
     g.K = Dp;
     g.F = F;
     g.out = H;
@@ -475,6 +481,8 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     g.E = E;
     g.ntiles_n = Dp / 256;
     g.max_tiles = g.ntiles_n * mtiles_bound;
+    g.a_bytes = (uint32_t)(A_ * F * 2);
+    g.b_bytes = (uint32_t)((int64_t)Dp * F * 2);
     g.K = F;
     g.F = F;
     g.out = Y;

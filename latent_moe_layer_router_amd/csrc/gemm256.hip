@@ -33,16 +33,26 @@ constexpr int SB = BM * RB;           // bytes per operand per stage (16 KiB)
 
 #define LMOE_AS3 __attribute__((address_space(3)))
 
+// Fourth word of a raw buffer descriptor on CDNA (no swizzle, no stride,
+// 32-bit data format field set so that offsets are bytes).
+constexpr int kBufWord3 = 0x00020000;
+
 // Four pipeline stages for A and B, each a separate LDS object so that the
 // compiler can tell the stages apart when it orders reads against the
 // asynchronous global-to-LDS loads still in flight for other stages.
 __shared__ __attribute__((aligned(16))) unsigned char sA0[SB], sB0[SB], sA1[SB], sB1[SB],
     sA2[SB], sB2[SB], sA3[SB], sB3[SB];
 
-// Byte offset of logical 16-byte chunk c (0..3) of tile row r. The chunk is
-// stored at position c ^ ((r >> 2) & 3): the eight rows a 128-bit LDS read
-// phase touches then cover distinct banks.
-__device__ __forceinline__ int swz(int r, int c) { return r * RB + ((c ^ ((r >> 2) & 3)) << 4); }
+// Byte offset of logical 16-byte chunk c (0..3) of tile row r (64-byte rows).
+// The chunk is stored at position c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3.
+// A 128-bit fragment read has 32 lanes on 32 consecutive rows at one logical
+// chunk; with this f any 8 consecutive rows (from a multiple of 8) land on 8
+// distinct 16-byte slots of a 128-byte bank line, and any 16 (from a multiple
+// of 16) on 16 distinct slots of 256 bytes, so the read is conflict-free
+// whether the LDS serves 8 or 16 lanes of a 128-bit read per clock.
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * RB + ((c ^ (((r >> 1) ^ (r >> 3)) & 3)) << 4);
+}
 
 __device__ __forceinline__ void mfma32(const uint4& a, const uint4& b, f32x16_t& acc) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -69,7 +79,8 @@ __device__ __forceinline__ void bar() {
 
 template <int EPI>
 __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets in SGPRs
   const int wm = wave >> 1, wn = wave & 1;
 
   // ---- tile of this workgroup (XCD-chunked order) --------------------------
@@ -95,36 +106,48 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
   // Per stage each wave moves 4 x 16 rows of A and of B, one 1 KiB load each:
   // lane i carries row (4 w + j) * 16 + i / 4 and lands at LDS chunk position
   // i % 4 of that row, so it fetches the logical chunk stored there.
-  const bf16_t* Be = static_cast<const bf16_t*>(p.B) + (int64_t)e * p.b_expert_stride;
+  // The loads are buffer loads: the base addresses and extents sit in two
+  // buffer descriptors (SGPRs), each lane keeps a 32-bit byte offset per row,
+  // and the K-step's offset is a scalar. Reads past an extent return zero.
+  // (Buffer loads, unlike global ones, are known to the compiler to touch only
+  // global memory and LDS through the DMA path, so it keeps exact LDS-read
+  // wait counts around them.)
+  const __amdgpu_buffer_rsrc_t rsA =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.A), (short)0, (int)p.a_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(static_cast<const bf16_t*>(p.B) + (int64_t)e * p.b_expert_stride), (short)0,
+      (int)p.b_bytes, kBufWord3);
   const int pos = lane & 3;
-  auto a_src = [&](int r) -> const unsigned char* {
+  auto a_off = [&](int r) -> uint32_t {
     int m = m0 + r;
     if (m >= m_end) m = m_end - 1;           // rows past the end load a valid row; never stored
-    const int64_t src = (EPI == EPI_SWIGLU) ? (int64_t)p.a_gather[m] : (int64_t)m;
-    const int c = pos ^ ((r >> 2) & 3);
-    return reinterpret_cast<const unsigned char*>(static_cast<const bf16_t*>(p.A) + src * p.lda) + c * 16;
+    const uint32_t src = (EPI == EPI_SWIGLU) ? (uint32_t)p.a_gather[m] : (uint32_t)m;
+    const uint32_t c = pos ^ (((r >> 1) ^ (r >> 3)) & 3);
+    return src * (uint32_t)(p.lda * 2) + c * 16;
   };
-  auto b_src = [&](int r) -> const unsigned char* {
+  auto b_off = [&](int r) -> uint32_t {
     const int n = (EPI == EPI_SWIGLU) ? ((r < BNB / 2) ? (n0 + r) : (p.F + n0 + r - BNB / 2)) : (n0 + r);
-    const int c = pos ^ ((r >> 2) & 3);
-    return reinterpret_cast<const unsigned char*>(Be + (int64_t)n * p.ldb) + c * 16;
+    const uint32_t c = pos ^ (((r >> 1) ^ (r >> 3)) & 3);
+    return (uint32_t)n * (uint32_t)(p.ldb * 2) + c * 16;
   };
   const int rr = wave * 64 + (lane >> 2);    // row of load j is rr + 16 j
-  const unsigned char *ga0 = a_src(rr), *ga1 = a_src(rr + 16), *ga2 = a_src(rr + 32), *ga3 = a_src(rr + 48);
-  const unsigned char *gb0 = b_src(rr), *gb1 = b_src(rr + 16), *gb2 = b_src(rr + 32), *gb3 = b_src(rr + 48);
+  const uint32_t ga0 = a_off(rr), ga1 = a_off(rr + 16), ga2 = a_off(rr + 32), ga3 = a_off(rr + 48);
+  const uint32_t gb0 = b_off(rr), gb1 = b_off(rr + 16), gb2 = b_off(rr + 32), gb3 = b_off(rr + 48);
   const int dbase = wave * 64 * RB;          // this wave's 4 KiB region of each operand stage
 
+#define LMOE_LD(RS, OFF, DST, KO) \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds((RS), (LMOE_AS3 void*)(DST), 16, (int)(OFF), (KO), 0, 0);
 #define LMOE_ISSUE(kt, SA, SBB)                                                                         \
   {                                                                                                    \
-    const int64_t o = (int64_t)(kt) * RB;                                                              \
-    __builtin_amdgcn_global_load_lds(ga0 + o, (LMOE_AS3 void*)((SA) + dbase), 16, 0, 0);                \
-    __builtin_amdgcn_global_load_lds(ga1 + o, (LMOE_AS3 void*)((SA) + dbase + 16 * RB), 16, 0, 0);      \
-    __builtin_amdgcn_global_load_lds(ga2 + o, (LMOE_AS3 void*)((SA) + dbase + 32 * RB), 16, 0, 0);      \
-    __builtin_amdgcn_global_load_lds(ga3 + o, (LMOE_AS3 void*)((SA) + dbase + 48 * RB), 16, 0, 0);      \
-    __builtin_amdgcn_global_load_lds(gb0 + o, (LMOE_AS3 void*)((SBB) + dbase), 16, 0, 0);               \
-    __builtin_amdgcn_global_load_lds(gb1 + o, (LMOE_AS3 void*)((SBB) + dbase + 16 * RB), 16, 0, 0);     \
-    __builtin_amdgcn_global_load_lds(gb2 + o, (LMOE_AS3 void*)((SBB) + dbase + 32 * RB), 16, 0, 0);     \
-    __builtin_amdgcn_global_load_lds(gb3 + o, (LMOE_AS3 void*)((SBB) + dbase + 48 * RB), 16, 0, 0);     \
+    const int ko = (kt) * RB;                                                                          \
+    LMOE_LD(rsA, ga0, (SA) + dbase, ko)                                                                \
+    LMOE_LD(rsA, ga1, (SA) + dbase + 16 * RB, ko)                                                      \
+    LMOE_LD(rsA, ga2, (SA) + dbase + 32 * RB, ko)                                                      \
+    LMOE_LD(rsA, ga3, (SA) + dbase + 48 * RB, ko)                                                      \
+    LMOE_LD(rsB, gb0, (SBB) + dbase, ko)                                                               \
+    LMOE_LD(rsB, gb1, (SBB) + dbase + 16 * RB, ko)                                                     \
+    LMOE_LD(rsB, gb2, (SBB) + dbase + 32 * RB, ko)                                                     \
+    LMOE_LD(rsB, gb3, (SBB) + dbase + 48 * RB, ko)                                                     \
   }
 
   f32x16_t acc[4][4];
@@ -151,67 +174,101 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
   const int mrows = m_end - (m0 + wm * 128);
   const int nmi = __builtin_amdgcn_readfirstlane(mrows <= 0 ? 0 : (mrows >= 128 ? 4 : (mrows + 31) / 32));
 
-#define LMOE_SUB(FULL, SA, SBB, AO, B0, B1, B2, B3)                                              \
-  {                                                                                            \
-    const uint4 b0 = *reinterpret_cast<const uint4*>((SBB) + (B0));                            \
-    const uint4 b1 = *reinterpret_cast<const uint4*>((SBB) + (B1));                            \
-    const uint4 b2 = *reinterpret_cast<const uint4*>((SBB) + (B2));                            \
-    const uint4 b3 = *reinterpret_cast<const uint4*>((SBB) + (B3));                            \
-    const uint4 a0 = *reinterpret_cast<const uint4*>((SA) + (AO));                             \
-    const uint4 a1 = *reinterpret_cast<const uint4*>((SA) + (AO) + 32 * RB);                   \
-    const uint4 a2 = *reinterpret_cast<const uint4*>((SA) + (AO) + 64 * RB);                   \
-    const uint4 a3 = *reinterpret_cast<const uint4*>((SA) + (AO) + 96 * RB);                   \
-    if (FULL || nmi > 0) {                                                                     \
-      mfma32(a0, b0, acc[0][0]); mfma32(a0, b1, acc[0][1]);                                    \
-      mfma32(a0, b2, acc[0][2]); mfma32(a0, b3, acc[0][3]);                                    \
-    }                                                                                          \
-    if (FULL || nmi > 1) {                                                                     \
-      mfma32(a1, b0, acc[1][0]); mfma32(a1, b1, acc[1][1]);                                    \
-      mfma32(a1, b2, acc[1][2]); mfma32(a1, b3, acc[1][3]);                                    \
-    }                                                                                          \
-    if (FULL || nmi > 2) {                                                                     \
-      mfma32(a2, b0, acc[2][0]); mfma32(a2, b1, acc[2][1]);                                    \
-      mfma32(a2, b2, acc[2][2]); mfma32(a2, b3, acc[2][3]);                                    \
-    }                                                                                          \
-    if (FULL || nmi > 3) {                                                                     \
-      mfma32(a3, b0, acc[3][0]); mfma32(a3, b1, acc[3][1]);                                    \
-      mfma32(a3, b2, acc[3][2]); mfma32(a3, b3, acc[3][3]);                                    \
-    }                                                                                          \
+  // Operand fragments: two register sets, so that the LDS reads of the next
+  // 16-wide K-slice are in flight while the MFMAs of the current one run.
+  uint4 xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3;
+  uint4 ya0, ya1, ya2, ya3, yb0, yb1, yb2, yb3;
+
+  // Reads of one K-slice's fragments (only the A rows of the NMI live 32-row
+  // groups; none at all if NMI == 0).
+#define LMOE_READ(NMI, SA, SBB, AO, B0, B1, B2, B3, PA, PB)                                      \
+  if ((NMI) > 0) {                                                                              \
+    PB##0 = *reinterpret_cast<const uint4*>((SBB) + (B0));                                      \
+    PB##1 = *reinterpret_cast<const uint4*>((SBB) + (B1));                                      \
+    PB##2 = *reinterpret_cast<const uint4*>((SBB) + (B2));                                      \
+    PB##3 = *reinterpret_cast<const uint4*>((SBB) + (B3));                                      \
+    PA##0 = *reinterpret_cast<const uint4*>((SA) + (AO));                                       \
+  }                                                                                             \
+  if ((NMI) > 1) PA##1 = *reinterpret_cast<const uint4*>((SA) + (AO) + 32 * RB);                \
+  if ((NMI) > 2) PA##2 = *reinterpret_cast<const uint4*>((SA) + (AO) + 64 * RB);                \
+  if ((NMI) > 3) PA##3 = *reinterpret_cast<const uint4*>((SA) + (AO) + 96 * RB);
+#define LMOE_MFMA(NMI, PA, PB)                                                                   \
+  if ((NMI) > 0) {                                                                              \
+    mfma32(PA##0, PB##0, acc[0][0]); mfma32(PA##0, PB##1, acc[0][1]);                           \
+    mfma32(PA##0, PB##2, acc[0][2]); mfma32(PA##0, PB##3, acc[0][3]);                           \
+  }                                                                                             \
+  if ((NMI) > 1) {                                                                              \
+    mfma32(PA##1, PB##0, acc[1][0]); mfma32(PA##1, PB##1, acc[1][1]);                           \
+    mfma32(PA##1, PB##2, acc[1][2]); mfma32(PA##1, PB##3, acc[1][3]);                           \
+  }                                                                                             \
+  if ((NMI) > 2) {                                                                              \
+    mfma32(PA##2, PB##0, acc[2][0]); mfma32(PA##2, PB##1, acc[2][1]);                           \
+    mfma32(PA##2, PB##2, acc[2][2]); mfma32(PA##2, PB##3, acc[2][3]);                           \
+  }                                                                                             \
+  if ((NMI) > 3) {                                                                              \
+    mfma32(PA##3, PB##0, acc[3][0]); mfma32(PA##3, PB##1, acc[3][1]);                           \
+    mfma32(PA##3, PB##2, acc[3][2]); mfma32(PA##3, PB##3, acc[3][3]);                           \
   }
-  // One K-step: wait for this stage (this wave's loads, then everyone's), start
-  // the load three stages ahead into the buffer freed by the previous step,
-  // then run its 32 MFMAs per wave. The load is issued unconditionally (near
-  // the end it re-reads the last stage into a buffer no later step reads), so
-  // every step has exactly three stages in flight and a branch-free body.
-#define LMOE_STEP(FULL, k, SA, SBB, NA, NB)                                                      \
-  {                                                                                            \
-    wait_vm(16);                                                                               \
-    bar();                                                                                     \
-    LMOE_ISSUE(((k) + 3 < nk ? (k) + 3 : nk - 1), NA, NB)                                       \
-    LMOE_SUB(FULL, SA, SBB, aoff0, b00, b10, b20, b30)                                         \
-    LMOE_SUB(FULL, SA, SBB, aoff1, b01, b11, b21, b31)                                         \
+  // K-step k (stage k in buffers SA/SBB, stage k + 1 in NA/NB). On entry stage k
+  // is visible to all waves, the loads of stages k + 1 .. k + 3 are in flight and
+  // the x registers hold the fragments of the step's first K-slice. The step
+  //   reads the second slice (y) and runs the first slice's MFMAs (x);
+  //   waits for stage k + 1 and for its own LDS reads, then the barrier: after
+  //   it no wave reads stage k any more, so the loads of stage k + 4 go into
+  //   its buffer (clamped to the last stage: a harmless re-read into a buffer
+  //   no later step reads, so every step has the same loads in flight);
+  //   reads the next step's first slice (x) and runs the second slice's MFMAs (y).
+  // The scheduling barriers keep each group of LDS reads ahead of the MFMAs
+  // that follow it, so their latency hides behind those MFMAs.
+#define LMOE_STEP(NMI, k, SA, SBB, NA, NB)                                                       \
+  {                                                                                             \
+    LMOE_READ(NMI, SA, SBB, aoff1, b01, b11, b21, b31, ya, yb)                                  \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
+    LMOE_MFMA(NMI, xa, xb)                                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
+    wait_vm(16);                                                                                \
+    bar();                                                                                      \
+    LMOE_ISSUE(((k) + 4 < nk ? (k) + 4 : nk - 1), SA, SBB)                                      \
+    LMOE_READ(NMI, NA, NB, aoff0, b00, b10, b20, b30, xa, xb)                                   \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
+    LMOE_MFMA(NMI, ya, yb)                                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
   }
-#define LMOE_KLOOP(FULL)                                                                         \
-  for (int k = 0; k < nk; k += 4) {                                                            \
-    LMOE_STEP(FULL, k, sA0, sB0, sA3, sB3)                                                     \
-    LMOE_STEP(FULL, k + 1, sA1, sB1, sA0, sB0)                                                 \
-    LMOE_STEP(FULL, k + 2, sA2, sB2, sA1, sB1)                                                 \
-    LMOE_STEP(FULL, k + 3, sA3, sB3, sA2, sB2)                                                 \
+#define LMOE_KLOOP(NMI)                                                                          \
+  {                                                                                             \
+    LMOE_READ(NMI, sA0, sB0, aoff0, b00, b10, b20, b30, xa, xb)                                 \
+    for (int k = 0; k < nk; k += 4) {                                                           \
+      LMOE_STEP(NMI, k, sA0, sB0, sA1, sB1)                                                     \
+      LMOE_STEP(NMI, k + 1, sA1, sB1, sA2, sB2)                                                 \
+      LMOE_STEP(NMI, k + 2, sA2, sB2, sA3, sB3)                                                 \
+      LMOE_STEP(NMI, k + 3, sA3, sB3, sA0, sB0)                                                 \
+    }                                                                                           \
   }
 
+  // Prologue: stages 0..2 in flight; wait for stage 0, then start stage 3.
   const int nk = p.K / 32;                   // a multiple of 4 (K % 128 == 0)
   LMOE_ISSUE(0, sA0, sB0)
   LMOE_ISSUE(1, sA1, sB1)
   LMOE_ISSUE(2, sA2, sB2)
-  if (nmi == 4) {
-    LMOE_KLOOP(true)
+  wait_vm(16);
+  bar();
+  LMOE_ISSUE(3, sA3, sB3)
+  // One K loop per number of live 32-row groups (uniform per wave; waves of a
+  // tile may differ, and all run the same barriers): full, half (1-2 groups,
+  // computing 2) and none (3 groups run the full loop).
+  if (nmi > 2) {
+    LMOE_KLOOP(4)
+  } else if (nmi > 0) {
+    LMOE_KLOOP(2)
   } else {
-    LMOE_KLOOP(false)
+    LMOE_KLOOP(0)
   }
 #undef LMOE_KLOOP
 #undef LMOE_STEP
-#undef LMOE_SUB
+#undef LMOE_MFMA
+#undef LMOE_READ
 #undef LMOE_ISSUE
+#undef LMOE_LD
   __syncthreads();   // every load has landed and every wave has finished reading
 
   // ---- epilogue: stage [256][OBN] bf16 in LDS, 16-byte stores ----------------

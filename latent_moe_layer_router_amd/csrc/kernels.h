@@ -105,6 +105,8 @@ struct Gemm256Params {
   int E;
   int ntiles_n;                // F/128 (SwiGLU: 128 gate + 128 up rows per tile) or Dp/256
   int max_tiles;               // grid size, a bound on the tile count
+  uint32_t a_bytes;            // extent of A in bytes (below 2^31)
+  uint32_t b_bytes;            // extent of one expert's B in bytes (below 2^31)
   int K;                       // multiple of 64
   int F;
   void* out;
