@@ -281,14 +281,15 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   void* u = ws + pl.u;
   const int slots = slots_for(T, k, E);
   // Experts with few rows go to the weight-streaming kernels (bf16, K multiple of 128).
-  const bool stream_ok = bf16 && Dp % 128 == 0 && F % 128 == 0;
+  // The grouped kernels' buffer loads take 32-bit byte offsets: the activations
+  // (xp, H) and one expert's weights must each stay below 2 GiB.
+  const bool off32_ok = (int64_t)T * k * F * 2 < ((int64_t)1 << 31) &&
+                        (int64_t)T * Dp * 2 < ((int64_t)1 << 31) &&
+                        (int64_t)2 * F * Dp * 2 < ((int64_t)1 << 31);
+  const bool stream_ok = bf16 && Dp % 128 == 0 && F % 128 == 0 && off32_ok;
   const int small_max = stream_ok ? stream_max_rows() : 0;
   // Experts with many rows: the 256 x 256 tile GEMM (bf16, Dp % 256 == 0, F % 128 == 0).
-  // Its buffer loads take 32-bit byte offsets: the activations (xp, H) and one
-  // expert's weights must each stay below 2 GiB.
-  const bool big_ok = bf16 && Dp % 256 == 0 && F % 128 == 0 &&
-                      (int64_t)T * k * F * 2 < ((int64_t)1 << 31) && (int64_t)T * Dp * 2 < ((int64_t)1 << 31) &&
-                      (int64_t)2 * F * Dp * 2 < ((int64_t)1 << 31);
+  const bool big_ok = bf16 && Dp % 256 == 0 && F % 128 == 0 && off32_ok;
   int32_t* mt_off = reinterpret_cast<int32_t*>(ws + pl.mt_off);
   const int64_t A_ = (int64_t)T * k;
   // Row tiles of 256 over the experts with more than small_max rows: at most
@@ -405,6 +406,8 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     sp.max_rows = small_max;
     sp.K = Dp;
     sp.F = F;
+    sp.a_bytes = (uint32_t)((int64_t)T * Dp * 2);
+    sp.b_bytes = (uint32_t)((int64_t)2 * F * Dp * 2);
     sp.out = H;
     sp.ldo = F;
     run(launch_stream(sp, EPI_SWIGLU, s));
@@ -463,6 +466,8 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     sp.max_rows = small_max;
     sp.K = F;
     sp.F = F;
+    sp.a_bytes = (uint32_t)(A_ * F * 2);
+    sp.b_bytes = (uint32_t)((int64_t)Dp * F * 2);
     sp.out = Y;
     sp.ldo = Dp;
     sp.ss_out = ss;

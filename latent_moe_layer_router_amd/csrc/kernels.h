@@ -59,6 +59,8 @@ struct StreamParams {
   int max_rows;                // experts with more rows are left to the tiled GEMM
   int K;                       // multiple of 128
   int F;
+  uint32_t a_bytes;            // extent of A in bytes (below 2^31)
+  uint32_t b_bytes;            // extent of one expert's B in bytes (below 2^31)
   void* out;
   int64_t ldo;
   float* ss_out;

@@ -1,12 +1,23 @@
 // Weight-streaming grouped GEMM for experts that received few rows (decode).
 //
 // With a handful of tokens per expert the expert GEMMs are bound by reading
-// the weights from HBM, so the kernel is shaped for bytes in flight rather than
-// for MFMA reuse: one wave64 per (expert, group of 64 weight rows) streams those
-// rows over the whole K with 16-byte loads straight into registers (no LDS in
-// the main loop, no block barrier), and multiplies them with the expert's
-// token rows (up to 4 tiles of 16) on MFMA 16x16x32. Every weight byte is read
-// exactly once; the token rows come from L2.
+// the weights from HBM, so the kernel is shaped for the memory system rather
+// than for MFMA reuse: one wave64 per (expert, group of 64 weight rows) streams
+// those rows over the whole K, and multiplies them with the expert's token rows
+// (up to 4 tiles of 16) on MFMA 16x16x32. Every weight byte is read once.
+//
+// The weights go through LDS so that each load instruction covers whole
+// 128-byte lines: a direct global-to-LDS load moves 8 rows x 128 bytes (lane i:
+// row i / 8, 16-byte chunk i % 8), marked non-temporal. In the MFMA layout a
+// lane needs 16 different rows, which would make every load cover half lines;
+// on MI355X half-line loads stream at about 5.8 TB/s, whole-line non-temporal
+// ones at about 6.8 TB/s. The token rows take the same path (from L2), so one
+// wait count covers a whole stage. Two stages of 64 K-columns: the loads of
+// the next stage are in flight while the current one is multiplied.
+//
+// LDS layout of a stage: rows of 128 bytes (64 bf16), the 16-byte chunk c of
+// row r stored at position c ^ f(r), f(r) = ((r >> 1) ^ (r << 2)) & 7, which
+// makes the 16-row fragment reads conflict-free for 8- and 16-lane phases.
 //
 // MFMA 16x16x32 layout (CDNA4): lane l supplies row l % 16 and the 8-element
 // K-chunk l / 16 of the 32-wide K-slice, for both operands; the 16x16 result
@@ -25,8 +36,16 @@ namespace lmoe {
 
 namespace {
 
-constexpr int MT = 4;   // token tiles of 16 per wave: experts with up to 64 rows
-constexpr int U = 4;    // K-slices of 32 per loop iteration (256 bytes of each weight row)
+constexpr int MT = 4;            // token tiles of 16 per wave: experts with up to 64 rows
+constexpr int KC = 64;           // K-columns per stage (128 bytes of each row)
+constexpr int kBufWord3 = 0x00020000;   // raw buffer descriptor, fourth word (CDNA)
+
+#define LMOE_AS3 __attribute__((address_space(3)))
+
+// Two stages of 64 weight rows and up to 64 token rows, 128 bytes each; separate
+// objects so that the compiler can tell the stages apart.
+__shared__ __attribute__((aligned(16))) unsigned char sw0[64 * 128], sw1[64 * 128];
+__shared__ __attribute__((aligned(16))) unsigned char sa0[64 * 128], sa1[64 * 128];
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
@@ -35,65 +54,105 @@ __device__ __forceinline__ void mfma16(const uint4& a, const uint4& b, f32x4& ac
                                                 __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
 }
 
-template <int EPI>
-__global__ __launch_bounds__(64) void stream_kernel(StreamParams p) {
-  __shared__ __attribute__((aligned(16))) bf16_t stile[MT * 16 * 64];
-  const int e = blockIdx.x / p.groups, grp = blockIdx.x % p.groups;
-  const int lo = p.offsets[e];
-  const int m_e = p.offsets[e + 1] - lo;
-  if (m_e == 0 || m_e > p.max_rows) return;
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) ^ (r << 2)) & 7; }
+
+// s_waitcnt immediate: at most n vector-memory operations outstanding (no
+// condition on the other counters).
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// s_waitcnt immediate: no LDS (or scalar memory) operation outstanding.
+constexpr int kLdsIdle = 15 | (3 << 14) | (7 << 4);
+
+template <int EPI, int NMT>
+__device__ __forceinline__ void stream_body(const StreamParams& p, int e, int grp, int lo, int m_e) {
   const int lane = threadIdx.x, r16 = lane & 15, kq = lane >> 4;
-  const int n_mt = (m_e + 15) >> 4;        // token tiles in use (wave-uniform)
+  const int lrow = lane >> 3, lc = lane & 7;
 
-  const bf16_t* Be = static_cast<const bf16_t*>(p.B) + (int64_t)e * p.b_expert_stride;
-  const bf16_t* brow[4];
+  // Weights: load j moves local rows 8j .. 8j+7 (lane: row 8j + lrow).
+  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(static_cast<const bf16_t*>(p.B) + (int64_t)e * p.b_expert_stride), (short)0,
+      (int)p.b_bytes, kBufWord3);
+  uint32_t wo[8];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    int row;
-    if (EPI == EPI_SWIGLU) row = (t < 2 ? 0 : p.F) + grp * 32 + (t & 1) * 16 + r16;
-    else row = grp * 64 + t * 16 + r16;
-    brow[t] = Be + (int64_t)row * p.ldb + kq * 8;
+  for (int j = 0; j < 8; ++j) {
+    const int lr = 8 * j + lrow;
+    const int row = (EPI == EPI_SWIGLU) ? ((lr < 32 ? 0 : p.F - 32) + grp * 32 + lr) : (grp * 64 + lr);
+    wo[j] = (uint32_t)row * (uint32_t)(p.ldb * 2) + (uint32_t)((lc ^ swz8(lr)) << 4);
   }
-  const bf16_t* arow[MT];
+  // Tokens: load i moves token rows 8i .. 8i+7 of the expert (rows past its end
+  // load its last row; never stored).
+  const __amdgpu_buffer_rsrc_t rsA =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.A), (short)0, (int)p.a_bytes, kBufWord3);
+  uint32_t ao[2 * NMT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    int i = mt * 16 + r16;
-    if (i >= m_e) i = m_e - 1;               // rows past the end load a valid row; never stored
-    const int64_t src = (EPI == EPI_SWIGLU) ? (int64_t)p.a_gather[lo + i] : (int64_t)(lo + i);
-    arow[mt] = static_cast<const bf16_t*>(p.A) + src * p.lda + kq * 8;
+  for (int i = 0; i < 2 * NMT; ++i) {
+    const int tr = 8 * i + lrow;
+    const int pos = lo + (tr < m_e ? tr : m_e - 1);
+    const uint32_t src = (EPI == EPI_SWIGLU) ? (uint32_t)p.a_gather[pos] : (uint32_t)pos;
+    ao[i] = src * (uint32_t)(p.lda * 2) + (uint32_t)((lc ^ swz8(tr)) << 4);
+  }
+#define LMOE_ISSUE(c, SW, SA)                                                                   \
+  {                                                                                            \
+    const int ko_ = (c) * KC * 2;                                                              \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                              \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (LMOE_AS3 void*)((SW) + 1024 * j), 16,     \
+                                               (int)wo[j], ko_, 0, 2);                         \
+    _Pragma("unroll") for (int i = 0; i < 2 * NMT; ++i)                                        \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (LMOE_AS3 void*)((SA) + 1024 * i), 16,     \
+                                               (int)ao[i], ko_, 0, 0);                         \
   }
 
-  f32x4 acc[MT][4];
+  f32x4 acc[NMT][4];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k = 0; k < p.K; k += 32 * U) {
-    uint4 b[U][4], a[U][MT];
+  // LDS byte offsets of this lane's fragments: row t*16 + r16 (weights) or
+  // mt*16 + r16 (tokens), logical chunk 4u + kq of the stage.
+  int fo[2];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) b[u][t] = *reinterpret_cast<const uint4*>(brow[t] + k + 32 * u);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        if (mt < n_mt) a[u][mt] = *reinterpret_cast<const uint4*>(arow[mt] + k + 32 * u);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        if (mt < n_mt)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) mfma16(a[u][mt], b[u][t], acc[mt][t]);
+  for (int u = 0; u < 2; ++u) fo[u] = r16 * 128 + (((4 * u + kq) ^ swz8(r16)) << 4);
+  // (swz8 depends on the row's low 4 bits only, so rows 16 t + r16 share fo[u].)
+
+#define LMOE_COMPUTE(SW, SA)                                                                    \
+  _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                              \
+    uint4 b[4], a[NMT];                                                                        \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t)                                              \
+      b[t] = *reinterpret_cast<const uint4*>((SW) + t * 2048 + fo[u]);                         \
+    _Pragma("unroll") for (int mt = 0; mt < NMT; ++mt)                                         \
+      a[mt] = *reinterpret_cast<const uint4*>((SA) + mt * 2048 + fo[u]);                       \
+    _Pragma("unroll") for (int mt = 0; mt < NMT; ++mt)                                         \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t) mfma16(a[mt], b[t], acc[mt][t]);           \
   }
+  // One stage: the previous reads of the buffer about to be refilled are done
+  // (all LDS reads complete), start the next stage's loads (at the end a
+  // harmless repeat of the last stage into the buffer no later stage reads),
+  // wait until only those are outstanding, then an LDS acquire fence keeps the
+  // stage's reads below the wait, and multiply.
+#define LMOE_STAGE(c, SW, SA, NW, NA)                                                           \
+  {                                                                                            \
+    __builtin_amdgcn_s_waitcnt(kLdsIdle);                                                      \
+    LMOE_ISSUE(((c) + 1 < nc ? (c) + 1 : nc - 1), NW, NA)                                       \
+    __builtin_amdgcn_s_waitcnt(vm_wait(8 + 2 * NMT));                                          \
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");                           \
+    LMOE_COMPUTE(SW, SA)                                                                       \
+  }
+  const int nc = p.K / KC;                   // even (K % 128 == 0)
+  LMOE_ISSUE(0, sw0, sa0)
+  for (int c = 0; c < nc; c += 2) {
+    LMOE_STAGE(c, sw0, sa0, sw1, sa1)
+    LMOE_STAGE(c + 1, sw1, sa1, sw0, sa0)
+  }
+#undef LMOE_STAGE
+#undef LMOE_COMPUTE
+#undef LMOE_ISSUE
+  __builtin_amdgcn_s_waitcnt(0);             // the last (repeated) loads have landed; reads done
 
   // ---- epilogue: stage the [rows][cols] tile in LDS, store 16-byte chunks ----
   constexpr int OC = (EPI == EPI_SWIGLU) ? 32 : 64;   // output columns of the wave
+  bf16_t* stile = reinterpret_cast<bf16_t*>(sw0);    // up to 64 x 64 bf16 = 8 KiB
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    if (mt >= n_mt) break;
+  for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int i = mt * 16 + 4 * kq + v;
@@ -126,6 +185,20 @@ __global__ __launch_bounds__(64) void stream_kernel(StreamParams p) {
     const int i = c / CPR, q = c % CPR;
     *reinterpret_cast<uint4*>(static_cast<bf16_t*>(p.out) + (int64_t)(lo + i) * p.ldo + col0 + q * 8) =
         *reinterpret_cast<const uint4*>(stile + i * OC + q * 8);
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(64) void stream_kernel(StreamParams p) {
+  const int e = blockIdx.x / p.groups, grp = blockIdx.x % p.groups;
+  const int lo = p.offsets[e];
+  const int m_e = p.offsets[e + 1] - lo;
+  if (m_e == 0 || m_e > p.max_rows) return;
+  switch ((m_e + 15) >> 4) {                 // token tiles in use (uniform)
+    case 1: stream_body<EPI, 1>(p, e, grp, lo, m_e); break;
+    case 2: stream_body<EPI, 2>(p, e, grp, lo, m_e); break;
+    case 3: stream_body<EPI, 3>(p, e, grp, lo, m_e); break;
+    default: stream_body<EPI, 4>(p, e, grp, lo, m_e); break;
   }
 }
 
@@ -169,7 +242,7 @@ __global__ __launch_bounds__(64) void dense_stream_kernel(DenseStreamParams p) {
 #pragma unroll
     for (int u = 0; u < UD; ++u)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) b[u][t] = *reinterpret_cast<const uint4*>(brow[t] + k + 32 * u);
+      for (int t = 0; t < 4; ++t) b[u][t] = load_stream16(brow[t] + k + 32 * u);
 #pragma unroll
     for (int u = 0; u < UD; ++u)
 #pragma unroll
