@@ -58,8 +58,9 @@ typedef enum {
 typedef enum {
   LMOE_F32 = 0,
   LMOE_BF16 = 1,
-  LMOE_MXFP4 = 2,           /* reserved: expert weights as E2M1 + E8M0 per 32 */
-  LMOE_MXFP8_E4M3 = 3       /* reserved */
+  LMOE_MXFP4 = 2,           /* expert weights: E2M1 codes + one E8M0 scale per 32 along K */
+  LMOE_MXFP8_E4M3 = 3       /* not a configuration value: the format the MXFP4 path gives its
+                               expert inputs (see lmoe_mx_quantize_e4m3) */
 } lmoe_dtype;
 
 #define LMOE_FLAG_ROUTER_BIAS 1u   /* lmoe_weights.b_router is present */
@@ -67,8 +68,15 @@ typedef enum {
 /* Block configuration (host struct, copied at create).
  * Shapes: d_model (D), d_pooled (Dp), d_ff (F) must be multiples of 64;
  * 1 <= n_experts (E) <= 1024; 1 <= top_k (k) <= min(E, 16); max_tokens >= 1.
- * act_dtype: LMOE_F32 or LMOE_BF16 — dtype of x, W_router, W_pool, W_unpool
- * and of the expert weights (expert_wdtype must equal act_dtype).
+ * act_dtype: LMOE_F32 or LMOE_BF16 — dtype of x, W_router, W_pool, W_unpool.
+ * expert_wdtype: act_dtype, or LMOE_MXFP4 (with act_dtype LMOE_BF16, d_pooled
+ * and d_ff multiples of 1024): MXFP4 expert weights as the LMSYS blog's "NVFP4
+ * as a third MMA type" section describes the format (E2M1 values, one UE8M0
+ * scale per 32 along K; encodings of OCP Microscaling v1.0). The experts'
+ * inputs — the normalized pooled row xp and the SwiGLU output h — are then
+ * quantized on the fly to MXFP8 E4M3 blocks of 32 (lmoe_mx_quantize_e4m3's
+ * rule), multiplied on the block-scaled MFMA with fp32 accumulation, and each
+ * expert output is held as bfloat16 as in the BF16 configuration.
  * out_dtype: LMOE_F32 (the unpooler's fp32 accumulators as they are) or
  * act_dtype (those accumulators rounded to nearest even).
  * Gammas and the router bias are always fp32. */
@@ -95,10 +103,11 @@ typedef struct {
   const float* b_router;    /* [E] fp32, required iff flags has LMOE_FLAG_ROUTER_BIAS */
   const void* w_pool;       /* [Dp][D]  act_dtype */
   const float* g_pool;      /* [Dp] fp32 */
-  const void* w_gate_up;    /* [E][2F][Dp]: rows [0, F) gate, rows [F, 2F) up */
-  const uint8_t* s_gate_up; /* reserved (MX scales); must be NULL */
-  const void* w_down;       /* [E][Dp][F] */
-  const uint8_t* s_down;    /* reserved (MX scales); must be NULL */
+  const void* w_gate_up;    /* [E][2F][Dp]: rows [0, F) gate, rows [F, 2F) up.
+                               MXFP4: [E][2F][Dp/2] bytes, element 2i in the low nibble */
+  const uint8_t* s_gate_up; /* MXFP4: [E][2F][Dp/32] E8M0 scales; otherwise NULL */
+  const void* w_down;       /* [E][Dp][F]. MXFP4: [E][Dp][F/2] bytes */
+  const uint8_t* s_down;    /* MXFP4: [E][Dp][F/32] E8M0 scales; otherwise NULL */
   const float* g_expert;    /* [E][Dp] fp32 */
   const void* w_unpool;     /* [D][Dp]  act_dtype */
 } lmoe_weights;
@@ -131,6 +140,17 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
 /* Free the workspace and the handle. NULL is allowed (LMOE_OK). The caller must
  * make sure no enqueued forward on this handle is still running. */
 lmoe_status lmoe_destroy(lmoe_handle h);
+
+/* Quantize n fp32 values (device pointer x, n a multiple of 32) to MXFP8 E4M3
+ * (OCP Microscaling v1.0): each block of 32 consecutive values shares one E8M0
+ * scale 2^X with X = floor(log2(max |v|)) - 8, clamped to [-127, 127] (an
+ * all-zero block takes -127); each value becomes the E4M3 code of v / 2^X,
+ * rounded to nearest with ties to even and saturated at 448. codes: n bytes,
+ * scales: n/32 bytes (device). x and codes 16-byte aligned; values finite.
+ * This is the rule the MXFP4-expert path applies to its expert inputs.
+ * Asynchronous on hip_stream; LMOE_E_INVAL on bad arguments (nothing enqueued). */
+lmoe_status lmoe_mx_quantize_e4m3(const float* x, int64_t n, uint8_t* codes, uint8_t* scales,
+                                  void* hip_stream);
 
 /* Device workspace bytes a handle with this configuration allocates. */
 lmoe_status lmoe_workspace_bytes(const lmoe_config* cfg, size_t* out);

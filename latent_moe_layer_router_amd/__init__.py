@@ -3,7 +3,8 @@
 Argument marshalling only: every step of the block runs in the library's HIP
 kernels. The functions mirror the C ABI in include/lmoe.h one to one
 (lmoe_create, lmoe_forward, lmoe_destroy, lmoe_workspace_bytes,
-lmoe_set_timing, lmoe_get_timing, lmoe_status_str, lmoe_last_error) and take raw
+lmoe_set_timing, lmoe_get_timing, lmoe_status_str, lmoe_last_error,
+lmoe_mx_quantize_e4m3) and take raw
 device pointers; LatentMoE wraps them for torch tensors, which serve only as
 device memory and streams. Importing works without a GPU; loading the library
 raises if it has not been built (there is no fallback path).
@@ -24,7 +25,8 @@ STAGES = ["proj_in", "topk", "sort", "pool_norm", "gate_up", "down", "combine", 
 LMOE_NUM_STAGES = len(STAGES)
 
 EXPORTS = ["lmoe_create", "lmoe_forward", "lmoe_destroy", "lmoe_workspace_bytes",
-           "lmoe_set_timing", "lmoe_get_timing", "lmoe_status_str", "lmoe_last_error"]
+           "lmoe_set_timing", "lmoe_get_timing", "lmoe_status_str", "lmoe_last_error",
+           "lmoe_mx_quantize_e4m3"]
 
 
 class lmoe_config(ctypes.Structure):
@@ -73,8 +75,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lmoe_workspace_bytes.argtypes = [ctypes.POINTER(lmoe_config), ctypes.POINTER(ctypes.c_size_t)]
     lib.lmoe_set_timing.argtypes = [P, ctypes.c_int]
     lib.lmoe_get_timing.argtypes = [P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(I32)]
+    lib.lmoe_mx_quantize_e4m3.argtypes = [P, ctypes.c_int64, P, P, P]
     for f in ("lmoe_create", "lmoe_forward", "lmoe_destroy", "lmoe_workspace_bytes",
-              "lmoe_set_timing", "lmoe_get_timing"):
+              "lmoe_set_timing", "lmoe_get_timing", "lmoe_mx_quantize_e4m3"):
         getattr(lib, f).restype = ctypes.c_int
     lib.lmoe_status_str.argtypes = [ctypes.c_int]
     lib.lmoe_status_str.restype = ctypes.c_char_p
@@ -130,13 +133,19 @@ def lmoe_get_timing(h: int):
     return dict(zip(STAGES, list(ms))), n.value
 
 
+def lmoe_mx_quantize_e4m3(x: int, n: int, codes: int, scales: int, stream: int = 0):
+    _check(load().lmoe_mx_quantize_e4m3(x, n, codes, scales, stream), "lmoe_mx_quantize_e4m3")
+
+
 def make_config(D, Dp, F, E, k, max_tokens, act="bf16", eps_pool=1e-6, eps_expert=1e-6,
-                router_bias=False, out=None) -> lmoe_config:
-    """act / out: "bf16" or "f32" (out defaults to act)."""
-    dts = {"bf16": LMOE_BF16, "f32": LMOE_F32}
+                router_bias=False, out=None, experts=None) -> lmoe_config:
+    """act / out: "bf16" or "f32" (out defaults to act); experts: the expert
+    weight format, act (default) or "mxfp4"."""
+    dts = {"bf16": LMOE_BF16, "f32": LMOE_F32, "mxfp4": LMOE_MXFP4}
     dt = dts[act]
-    return lmoe_config(LMOE_ABI_VERSION, D, Dp, F, E, k, eps_pool, eps_expert, dt, dt,
-                       dts[out or act], max_tokens, LMOE_FLAG_ROUTER_BIAS if router_bias else 0)
+    return lmoe_config(LMOE_ABI_VERSION, D, Dp, F, E, k, eps_pool, eps_expert, dt,
+                       dts[experts or act], dts[out or act], max_tokens,
+                       LMOE_FLAG_ROUTER_BIAS if router_bias else 0)
 
 
 class LatentMoE:
@@ -144,8 +153,10 @@ class LatentMoE:
     library borrows them). weights: w_router [E, D], b_router [E] or None,
     w_pool [Dp, D], g_pool [Dp], w_gate_up [E, 2F, Dp], w_down [E, Dp, F],
     g_expert [E, Dp], w_unpool [D, Dp]; activations and weights in one dtype
-    (torch.bfloat16 or torch.float32), gammas and bias float32. out_dtype:
-    torch.float32 or the activation dtype (the default)."""
+    (torch.bfloat16 or torch.float32), gammas and bias float32. MXFP4 experts:
+    w_gate_up [E, 2F, Dp/2] and w_down [E, Dp, F/2] as uint8 E2M1 pairs plus
+    s_gate_up [E, 2F, Dp/32] and s_down [E, Dp, F/32] uint8 E8M0 scales.
+    out_dtype: torch.float32 or the activation dtype (the default)."""
 
     def __init__(self, weights: dict, top_k: int, max_tokens: int, eps_pool=1e-6, eps_expert=1e-6,
                  out_dtype=None):
@@ -154,7 +165,8 @@ class LatentMoE:
         act = {torch.bfloat16: "bf16", torch.float32: "f32"}[wp.dtype]
         E, D = weights["w_router"].shape
         Dp = wp.shape[0]
-        F = weights["w_down"].shape[2]
+        mx = weights.get("s_down") is not None
+        F = weights["w_down"].shape[2] * (2 if mx else 1)
         self.weights = weights
         self.dtype = wp.dtype
         self.out_dtype = out_dtype or wp.dtype
@@ -162,10 +174,12 @@ class LatentMoE:
         self.D, self.Dp, self.F, self.E, self.k = D, Dp, F, E, top_k
         self.max_tokens = max_tokens
         self.cfg = make_config(D, Dp, F, E, top_k, max_tokens, act, eps_pool, eps_expert,
-                               weights.get("b_router") is not None, out)
+                               weights.get("b_router") is not None, out,
+                               "mxfp4" if mx else None)
         ptr = lambda name: weights[name].data_ptr() if weights.get(name) is not None else None
         self.cw = lmoe_weights(ptr("w_router"), ptr("b_router"), ptr("w_pool"), ptr("g_pool"),
-                               ptr("w_gate_up"), None, ptr("w_down"), None, ptr("g_expert"),
+                               ptr("w_gate_up"), ptr("s_gate_up"), ptr("w_down"), ptr("s_down"),
+                               ptr("g_expert"),
                                ptr("w_unpool"))
         self.handle = lmoe_create(self.cfg, self.cw)
 

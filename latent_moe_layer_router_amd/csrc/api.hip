@@ -27,7 +27,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 // Byte layout of the workspace for a configuration (every region 256-byte aligned).
 struct Plan {
   size_t P, logits, ids, w, masks, chunk_base, counts, offsets, sorted_assign, inv, row_token,
-      tiles, n_tiles, mt_off, xp, H, Y, ss, u, part;
+      tiles, n_tiles, mt_off, xp, H, xq, xs, hq, hs, Y, ss, u, part;
   size_t total;
   int max_slots;
 };
@@ -65,8 +65,15 @@ Plan make_plan(const lmoe_config& c) {
   p.tiles = grow(cur, (size_t)p.max_slots * 8);
   p.n_tiles = grow(cur, 4);
   p.mt_off = grow(cur, (E + 1) * 4);
-  p.xp = grow(cur, Tm * Dp * es);
-  p.H = grow(cur, A * F * es);
+  // Expert inputs: bf16/fp32 xp and H, or (MXFP4 experts) their MXFP8 codes
+  // and scales.
+  const bool mx = c.expert_wdtype == LMOE_MXFP4;
+  p.xp = grow(cur, mx ? 0 : Tm * Dp * es);
+  p.H = grow(cur, mx ? 0 : A * F * es);
+  p.xq = grow(cur, mx ? Tm * Dp : 0);
+  p.xs = grow(cur, mx ? Tm * Dp / 32 : 0);
+  p.hq = grow(cur, mx ? A * F : 0);
+  p.hs = grow(cur, mx ? A * F / 32 : 0);
   p.Y = grow(cur, A * Dp * es);
   p.ss = grow(cur, A * (Dp / 64) * 4);
   p.u = grow(cur, Tm * Dp * es);
@@ -99,8 +106,20 @@ lmoe_status check_config(const lmoe_config* c) {
     return fail(LMOE_E_INVAL, "eps_pool and eps_expert must be finite and >= 0");
   if (c->act_dtype != LMOE_F32 && c->act_dtype != LMOE_BF16)
     return fail(LMOE_E_UNSUPPORTED, "act_dtype must be LMOE_F32 or LMOE_BF16");
-  if (c->expert_wdtype != c->act_dtype)
-    return fail(LMOE_E_UNSUPPORTED, "expert_wdtype must equal act_dtype (MX experts not built)");
+  if (c->expert_wdtype == LMOE_MXFP4) {
+    // MXFP4 experts: bf16 activations elsewhere, MXFP8 expert inputs, the
+    // block-scaled 256-tile GEMM (K a multiple of 1024, 32-bit byte offsets).
+    if (c->act_dtype != LMOE_BF16)
+      return fail(LMOE_E_UNSUPPORTED, "MXFP4 experts need act_dtype LMOE_BF16");
+    if (c->d_pooled % 1024 || c->d_ff % 1024)
+      return fail(LMOE_E_UNSUPPORTED, "MXFP4 experts need d_pooled and d_ff multiples of 1024");
+    const int64_t A = (int64_t)c->max_tokens * c->top_k;
+    if (A * c->d_ff >= ((int64_t)1 << 31) || (int64_t)c->max_tokens * c->d_pooled >= ((int64_t)1 << 31) ||
+        (int64_t)c->d_ff * c->d_pooled >= ((int64_t)1 << 31))
+      return fail(LMOE_E_UNSUPPORTED, "MXFP4 experts: max_tokens too large for 32-bit offsets");
+  } else if (c->expert_wdtype != c->act_dtype) {
+    return fail(LMOE_E_UNSUPPORTED, "expert_wdtype must be act_dtype or LMOE_MXFP4");
+  }
   if (c->out_dtype != LMOE_F32 && c->out_dtype != c->act_dtype)
     return fail(LMOE_E_UNSUPPORTED, "out_dtype must be LMOE_F32 or act_dtype");
   if (c->max_tokens < 1) return fail(LMOE_E_INVAL, "max_tokens must be >= 1");
@@ -148,6 +167,19 @@ lmoe_status lmoe_workspace_bytes(const lmoe_config* cfg, size_t* out) {
   return LMOE_OK;
 }
 
+lmoe_status lmoe_mx_quantize_e4m3(const float* x, int64_t n, uint8_t* codes, uint8_t* scales,
+                                  void* hip_stream) {
+  g_last_error.clear();
+  if (n < 0 || n % 32) return fail(LMOE_E_INVAL, "n must be a non-negative multiple of 32");
+  if (n == 0) return LMOE_OK;
+  if (!x || !codes || !scales) return fail(LMOE_E_INVAL, "x, codes and scales must not be NULL");
+  if (!aligned16(x) || !aligned16(codes)) return fail(LMOE_E_INVAL, "x and codes must be 16-byte aligned");
+  if (n / 32 > (int64_t)INT32_MAX) return fail(LMOE_E_UNSUPPORTED, "n too large");
+  const hipError_t e = launch_mx_quant(x, n, codes, scales, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(LMOE_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+  return LMOE_OK;
+}
+
 lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, lmoe_handle* out) {
   g_last_error.clear();
   if (!out) return fail(LMOE_E_INVAL, "out is NULL");
@@ -166,7 +198,13 @@ lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, lmoe_hand
   if (has_bias != (w->b_router != nullptr))
     return fail(LMOE_E_INVAL, "b_router must be given iff LMOE_FLAG_ROUTER_BIAS is set");
   if (w->b_router && !aligned4(w->b_router)) return fail(LMOE_E_INVAL, "b_router is misaligned");
-  if (w->s_gate_up || w->s_down) return fail(LMOE_E_INVAL, "MX scale pointers must be NULL");
+  if (cfg->expert_wdtype == LMOE_MXFP4) {
+    if (!w->s_gate_up || !w->s_down) return fail(LMOE_E_INVAL, "MXFP4 experts need s_gate_up and s_down");
+    if (!aligned16(w->s_gate_up) || !aligned16(w->s_down))
+      return fail(LMOE_E_INVAL, "s_gate_up / s_down are not 16-byte aligned");
+  } else if (w->s_gate_up || w->s_down) {
+    return fail(LMOE_E_INVAL, "MX scale pointers must be NULL unless expert_wdtype is LMOE_MXFP4");
+  }
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(LMOE_E_HIP, "hipGetDevice failed");
@@ -276,6 +314,11 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   int32_t* inv = reinterpret_cast<int32_t*>(ws + pl.inv);
   void* xp = ws + pl.xp;
   void* H = ws + pl.H;
+  uint8_t* xq = ws + pl.xq;
+  uint8_t* xs = ws + pl.xs;
+  uint8_t* hq = ws + pl.hq;
+  uint8_t* hs = ws + pl.hs;
+  const bool mx = c.expert_wdtype == LMOE_MXFP4;
   void* Y = ws + pl.Y;
   float* ss = reinterpret_cast<float*>(ws + pl.ss);
   void* u = ws + pl.u;
@@ -286,10 +329,10 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   const bool off32_ok = (int64_t)T * k * F * 2 < ((int64_t)1 << 31) &&
                         (int64_t)T * Dp * 2 < ((int64_t)1 << 31) &&
                         (int64_t)2 * F * Dp * 2 < ((int64_t)1 << 31);
-  const bool stream_ok = bf16 && Dp % 128 == 0 && F % 128 == 0 && off32_ok;
+  const bool stream_ok = bf16 && !mx && Dp % 128 == 0 && F % 128 == 0 && off32_ok;
   const int small_max = stream_ok ? stream_max_rows() : 0;
   // Experts with many rows: the 256 x 256 tile GEMM (bf16, Dp % 256 == 0, F % 128 == 0).
-  const bool big_ok = bf16 && Dp % 256 == 0 && F % 128 == 0 && off32_ok;
+  const bool big_ok = bf16 && !mx && Dp % 256 == 0 && F % 128 == 0 && off32_ok;
   int32_t* mt_off = reinterpret_cast<int32_t*>(ws + pl.mt_off);
   const int64_t A_ = (int64_t)T * k;
   // Row tiles of 256 over the experts with more than small_max rows: at most
@@ -389,7 +432,10 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   }
   // 4. pooled RMSNorm
   mark();
-  run(launch_pool_norm(P, h->w.g_pool, T, Dp, c.eps_pool, xp, bf16, s));
+  if (mx)
+    run(launch_pool_norm_mx(P, h->w.g_pool, T, Dp, c.eps_pool, xq, xs, s));
+  else
+    run(launch_pool_norm(P, h->w.g_pool, T, Dp, c.eps_pool, xp, bf16, s));
   // 5. gate/up grouped GEMM + SwiGLU
   mark();
   if (stream_ok) {
@@ -412,7 +458,29 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     sp.ldo = F;
     run(launch_stream(sp, EPI_SWIGLU, s));
   }
-  if (big_ok) {
+  if (mx) {
+    Gemm256MxParams g{};
+    g.A = xq;
+    g.As = xs;
+    g.a_gather = row_token;
+    g.B = static_cast<const uint8_t*>(h->w.w_gate_up);
+    g.Bs = h->w.s_gate_up;
+    g.N = 2 * F;
+    g.offsets = offsets;
+    g.mt_off = mt_off;
+    g.E = E;
+    g.ntiles_n = F / 128;
+    g.max_tiles = g.ntiles_n * mtiles_bound;
+    g.a_bytes = (uint32_t)((int64_t)T * Dp);
+    g.as_bytes = (uint32_t)((int64_t)T * Dp / 32);
+    g.K = Dp;
+    g.F = F;
+    g.out = hq;
+    g.ldo = F;
+    g.out_scales = hs;
+    g.ldos = F / 32;
+    run(launch_gemm256_mx(g, EPI_SWIGLU, s));
+  } else if (big_ok) {
     Gemm256Params g{};
     g.A = xp;
     g.lda = Dp;
@@ -474,7 +542,28 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     sp.ss_ld = Dp / 64;
     run(launch_stream(sp, EPI_DOWN, s));
   }
-  if (big_ok) {
+  if (mx) {
+    Gemm256MxParams g{};
+    g.A = hq;
+    g.As = hs;
+    g.B = static_cast<const uint8_t*>(h->w.w_down);
+    g.Bs = h->w.s_down;
+    g.N = Dp;
+    g.offsets = offsets;
+    g.mt_off = mt_off;
+    g.E = E;
+    g.ntiles_n = Dp / 256;
+    g.max_tiles = g.ntiles_n * mtiles_bound;
+    g.a_bytes = (uint32_t)(A_ * F);
+    g.as_bytes = (uint32_t)(A_ * F / 32);
+    g.K = F;
+    g.F = F;
+    g.out = Y;
+    g.ldo = Dp;
+    g.ss_out = ss;
+    g.ss_ld = Dp / 64;
+    run(launch_gemm256_mx(g, EPI_DOWN, s));
+  } else if (big_ok) {
     Gemm256Params g{};
     g.A = H;
     g.lda = F;

@@ -1,0 +1,402 @@
+// Large-tile grouped GEMM of the MXFP4-expert path: MXFP8 E4M3 activations
+// times MXFP4 (E2M1) expert weights, both with one E8M0 scale per 32 values
+// along K, on gfx950's block-scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4),
+// fp32 accumulation. The two expert GEMMs of the block:
+//   gate/up: H = silu(xq . Wg^T) * (xq . Wu^T), quantized again to MXFP8 E4M3
+//            blocks of 32 (codes + scales) as the down GEMM's input;
+//   down:    y = H . Wd^T in bf16 plus per-64-column sums of squares of the
+//            stored values (for the per-expert RMSNorm in the combine).
+// MXFP4 as the expert weight format with per-32 UE8M0 scales: LMSYS Muse Spark
+// Open blog, "NVFP4 as a third MMA type"; encodings: OCP Microscaling v1.0.
+//
+// Scaled-MFMA operand layout (gfx950, 32x32x64; lane l: row r = l % 32 of the
+// operand, group q = l / 32):
+//   fp8 operand, 32 bytes: bytes 0..15 hold K [16q, 16q + 16), bytes 16..31 hold
+//     K [32 + 16q, 32 + 16q + 16);
+//   fp4 operand, 16 bytes: two E2M1 values per byte, low nibble first, holding
+//     K [32q, 32q + 32);
+//   scale: one E8M0 byte per lane, for K [32q, 32q + 32) of its row;
+//   result: as the other 32x32 MFMAs (register v of lane l: row 8 (v / 4) +
+//     4q + v % 4, column l % 32).
+//
+// Tile 256 x 256 (A rows x B rows), 4 waves of 128 x 128 = 4 x 4 MFMAs per
+// K-step of 64. A stage holds one K-step: A 256 rows x 64 bytes (fp8), B 256
+// rows x 32 bytes (fp4), moved by direct global-to-LDS buffer loads; four
+// stages, three in flight. The scales come in groups of 8 K-steps (512
+// columns = 16 bytes per row of A and of B) into one of two scale buffers;
+// a group travels with the data of the step four ahead of the group's start.
+// LDS: 4 x 24 KiB + 2 x 8 KiB = 112 KiB.
+//
+// Tile order over the 8 XCDs as in the bf16 256-tile GEMM: one index space
+// (expert, n-tile, m-tile) cut into 8 contiguous chunks.
+#include "common.h"
+#include "kernels.h"
+#include "mx.h"
+
+namespace lmoe {
+
+namespace {
+
+constexpr int BM = 256, BNB = 256;
+constexpr int NT = 256;
+constexpr int RA = 64;                // bytes per A row per stage (64 fp8)
+constexpr int RBB = 32;               // bytes per B row per stage (64 fp4)
+constexpr int kBufWord3 = 0x00020000;   // raw buffer descriptor, fourth word (CDNA)
+
+#define LMOE_AS3 __attribute__((address_space(3)))
+
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+
+__shared__ __attribute__((aligned(16))) unsigned char mA0[BM * RA], mA1[BM * RA], mA2[BM * RA], mA3[BM * RA];
+__shared__ __attribute__((aligned(16))) unsigned char mB0[BNB * RBB], mB1[BNB * RBB], mB2[BNB * RBB],
+    mB3[BNB * RBB];
+// scale buffers: A scales [256 rows][16 B] then B scales [256 rows][16 B]
+__shared__ __attribute__((aligned(16))) unsigned char mS0[2 * 256 * 16], mS1[2 * 256 * 16];
+
+// A rows: 16-byte chunk c of row r at position c ^ fa(r) (as the bf16 tile GEMM).
+__device__ __forceinline__ int fa(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// B rows (two chunks): chunk c of row r at position c ^ fb(r); 8 consecutive
+// rows (from a multiple of 8) then cover distinct 16-byte bank slots of 128
+// bytes, 16 (from a multiple of 16) those of 256 bytes.
+__device__ __forceinline__ int fb(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+
+__device__ __forceinline__ void mfma_mx(const uint4& a0, const uint4& a1, const uint4& b, int sa, int sb,
+                                        f32x16_t& acc) {
+  const i32x8_t av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  const i32x8_t bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  // A format 0 = fp8 E4M3, B format 4 = fp4 E2M1; scales in byte 0 of sa / sb.
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 4, 0, sa, 0, sb);
+}
+
+// s_waitcnt immediates: at most n vector-memory operations outstanding and no
+// LDS operation outstanding.
+constexpr int vm_lds_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+__device__ __forceinline__ void bar() {
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int EPI>
+__global__ __launch_bounds__(NT, 1) void gemm256_mx_kernel(Gemm256MxParams p) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- tile of this workgroup (XCD-chunked order) --------------------------
+  const int total = p.ntiles_n * p.mt_off[p.E];
+  const int chunk = (total + 7) / 8;
+  const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+  const int t = xcd * chunk + local;
+  if (local >= chunk || t >= total) return;
+  int lo = 0, hi = p.E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.ntiles_n * p.mt_off[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int mt_e = p.mt_off[e + 1] - p.mt_off[e];
+  const int tl = t - p.ntiles_n * p.mt_off[e];
+  const int ntile = tl / mt_e, mtile = tl % mt_e;
+  const int m0 = p.offsets[e] + mtile * BM;
+  const int m_end = p.offsets[e + 1];
+  const int n0 = ntile * (EPI == EPI_SWIGLU ? BNB / 2 : BNB);   // output column start
+  const int K = p.K;
+
+  // ---- buffer descriptors and per-lane load offsets ------------------------
+  const __amdgpu_buffer_rsrc_t rA =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.A), (short)0, (int)p.a_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rAs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.As), (short)0, (int)p.as_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.B + (int64_t)e * p.N * (K / 2)), (short)0, p.N * (K / 2), kBufWord3);
+  const __amdgpu_buffer_rsrc_t rBs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.Bs + (int64_t)e * p.N * (K / 32)), (short)0, p.N * (K / 32), kBufWord3);
+  auto a_src = [&](int r) -> uint32_t {     // source row (token or sorted position) of tile row r
+    int m = m0 + r;
+    if (m >= m_end) m = m_end - 1;           // rows past the end load a valid row; never stored
+    return (EPI == EPI_SWIGLU) ? (uint32_t)p.a_gather[m] : (uint32_t)m;
+  };
+  auto b_row = [&](int r) -> uint32_t {     // B row of tile row r
+    return (EPI == EPI_SWIGLU) ? (uint32_t)((r < BNB / 2) ? (n0 + r) : (p.F + n0 + r - BNB / 2))
+                               : (uint32_t)(n0 + r);
+  };
+  // A: load j moves rows wave*64 + 16 j + lane/4, lane position lane % 4.
+  uint32_t ga[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = wave * 64 + 16 * j + (lane >> 2);
+    ga[j] = a_src(r) * (uint32_t)K + (uint32_t)(((lane & 3) ^ fa(r)) << 4);
+  }
+  // B: load j moves rows wave*64 + 32 j + lane/2, lane position lane % 2.
+  uint32_t gb[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = wave * 64 + 32 * j + (lane >> 1);
+    gb[j] = b_row(r) * (uint32_t)(K / 2) + (uint32_t)(((lane & 1) ^ fb(r)) << 4);
+  }
+  // Scales: one load each for A and B, row wave*64 + lane, 16 bytes per group.
+  const uint32_t gsa = a_src(wave * 64 + lane) * (uint32_t)(K / 32);
+  const uint32_t gsb = b_row(wave * 64 + lane) * (uint32_t)(K / 32);
+
+#define LMOE_DATA(kt, SA, SB)                                                                    \
+  {                                                                                             \
+    const int koa = (kt) * RA, kob = (kt) * RBB;                                                \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                               \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (LMOE_AS3 void*)((SA) + wave * 4096 + 1024 * j), \
+                                               16, (int)ga[j], koa, 0, 0);                      \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j)                                               \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (LMOE_AS3 void*)((SB) + wave * 2048 + 1024 * j), \
+                                               16, (int)gb[j], kob, 0, 0);                      \
+  }
+#define LMOE_SCALES(g, SS)                                                                       \
+  {                                                                                             \
+    const int kos = (g) * 16;                                                                   \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, (LMOE_AS3 void*)((SS) + wave * 1024), 16,      \
+                                             (int)gsa, kos, 0, 0);                              \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, (LMOE_AS3 void*)((SS) + 4096 + wave * 1024), 16, \
+                                             (int)gsb, kos, 0, 0);                              \
+  }
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+
+  // ---- fragment addresses ---------------------------------------------------
+  const int l32 = lane & 31, q = lane >> 5;
+  // aoff / boff: operand chunks in a stage buffer; asc / bsc: the row's scale
+  // bytes (plus q) in a scale buffer.
+  int aoff[4][2], boff[4], asc[4], bsc[4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    const int r = wm * 128 + mi * 32 + l32;
+    asc[mi] = r * 16 + q;
+    aoff[mi][0] = r * RA + ((q ^ fa(r)) << 4);
+    aoff[mi][1] = r * RA + (((2 + q) ^ fa(r)) << 4);
+  }
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    // SwiGLU: gate (ni = 0, 1) and up (ni = 2, 3) of the same 64 output columns
+    const int r = (EPI == EPI_SWIGLU) ? ((ni >> 1) * (BNB / 2) + wn * 64 + (ni & 1) * 32 + l32)
+                                      : (wn * 128 + ni * 32 + l32);
+    bsc[ni] = 4096 + r * 16 + q;
+    boff[ni] = r * RBB + ((q ^ fb(r)) << 4);
+  }
+  const int mrows = m_end - (m0 + wm * 128);
+  const int nmi = __builtin_amdgcn_readfirstlane(mrows <= 0 ? 0 : (mrows >= 128 ? 4 : (mrows + 31) / 32));
+
+  // Fragment registers of one K-step (x: the step being multiplied, y: the next).
+  uint4 xa[4][2], xb[4], ya[4][2], yb[4];
+  int xsa[4], xsb[4], ysa[4], ysb[4];
+
+  // Reads of one step's fragments and scales: the step is step J (0..7) of its
+  // scale group (buffer SS), its scales at bytes 2 J + q of each row's 16.
+  // NMI live 32-row groups.
+#define LMOE_READ(NMI, SA, SB, SS, J, PA, PB, PSA, PSB)                                           \
+  if ((NMI) > 0) {                                                                              \
+    _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) {                                          \
+      PB[ni] = *reinterpret_cast<const uint4*>((SB) + boff[ni]);                                \
+      PSB[ni] = (int)(SS)[bsc[ni] + 2 * (J)];                                                    \
+    }                                                                                           \
+    _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) if (mi < (NMI)) {                          \
+      PA[mi][0] = *reinterpret_cast<const uint4*>((SA) + aoff[mi][0]);                          \
+      PA[mi][1] = *reinterpret_cast<const uint4*>((SA) + aoff[mi][1]);                          \
+      PSA[mi] = (int)(SS)[asc[mi] + 2 * (J)];                                                    \
+    }                                                                                           \
+  }
+#define LMOE_MFMA(NMI, PA, PB, PSA, PSB)                                                          \
+  _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) if (mi < (NMI)) {                            \
+    _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                            \
+      mfma_mx(PA[mi][0], PA[mi][1], PB[ni], PSA[mi], PSB[ni], acc[mi][ni]);                     \
+  }
+  // K-step k (data of step k in SA/SB, scales of its group in SS; step k + 1 in
+  // NA/NB with scales NS). On entry step k's fragments are in the x registers
+  // and steps k + 1 .. k + 3 are in flight. The step waits for step k + 1 and
+  // its own LDS reads, passes the barrier (after which no wave reads step k's
+  // buffers), starts the loads of step k + 4 into them — with the next scale
+  // group when k + 4 starts a group's second half — reads step k + 1's
+  // fragments (y) and runs step k's MFMAs (x). Loads past the last step repeat
+  // it (harmless re-reads into buffers no later step reads), so the number of
+  // loads in flight, and with it every wait count, is the same on every pass.
+#define LMOE_STEP(NMI, k, j, SA, SB, SS, NA, NB, NS, XA, XB, XSA, XSB, YA, YB, YSA, YSB)           \
+  {                                                                                             \
+    __builtin_amdgcn_s_waitcnt(vm_lds_wait(((j) == 1 || (j) == 2) ? 14 : 12));                  \
+    bar();                                                                                      \
+    LMOE_DATA(((k) + 4 < nk ? (k) + 4 : nk - 1), SA, SB)                                        \
+    if ((j) == 0) {                                                                             \
+      const int g_ = (k) / 8 + 1;                                                               \
+      LMOE_SCALES((g_ < ng ? g_ : ng - 1), (((k) / 8) & 1) ? mS0 : mS1)                          \
+    }                                                                                           \
+    LMOE_READ(NMI, NA, NB, NS, ((j) + 1) & 7, YA, YB, YSA, YSB)                                  \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
+    LMOE_MFMA(NMI, XA, XB, XSA, XSB)                                                            \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
+  }
+  // Eight steps = one scale group (g = k / 8, buffer mS[g % 2]); the stage
+  // buffers rotate with period 4. The group's first step reads the group's
+  // scales (buffer SG), its last step also those of the next group (SN).
+#define LMOE_GROUP(NMI, SG, SN)                                                                   \
+  {                                                                                             \
+    LMOE_STEP(NMI, k + 0, 0, mA0, mB0, SG, mA1, mB1, SG, xa, xb, xsa, xsb, ya, yb, ysa, ysb)     \
+    LMOE_STEP(NMI, k + 1, 1, mA1, mB1, SG, mA2, mB2, SG, ya, yb, ysa, ysb, xa, xb, xsa, xsb)     \
+    LMOE_STEP(NMI, k + 2, 2, mA2, mB2, SG, mA3, mB3, SG, xa, xb, xsa, xsb, ya, yb, ysa, ysb)     \
+    LMOE_STEP(NMI, k + 3, 3, mA3, mB3, SG, mA0, mB0, SG, ya, yb, ysa, ysb, xa, xb, xsa, xsb)     \
+    LMOE_STEP(NMI, k + 4, 4, mA0, mB0, SG, mA1, mB1, SG, xa, xb, xsa, xsb, ya, yb, ysa, ysb)     \
+    LMOE_STEP(NMI, k + 5, 5, mA1, mB1, SG, mA2, mB2, SG, ya, yb, ysa, ysb, xa, xb, xsa, xsb)     \
+    LMOE_STEP(NMI, k + 6, 6, mA2, mB2, SG, mA3, mB3, SG, xa, xb, xsa, xsb, ya, yb, ysa, ysb)     \
+    LMOE_STEP(NMI, k + 7, 7, mA3, mB3, SG, mA0, mB0, SN, ya, yb, ysa, ysb, xa, xb, xsa, xsb)     \
+  }
+#define LMOE_KLOOP(NMI)                                                                          \
+  {                                                                                             \
+    LMOE_READ(NMI, mA0, mB0, mS0, 0, xa, xb, xsa, xsb)                                          \
+    for (int k0_ = 0; k0_ < nk; k0_ += 16) {                                                    \
+      { const int k = k0_; LMOE_GROUP(NMI, mS0, mS1) }                                          \
+      { const int k = k0_ + 8; LMOE_GROUP(NMI, mS1, mS0) }                                      \
+    }                                                                                           \
+  }
+
+  // Prologue: scale group 0, steps 0..2 in flight; wait for step 0 (steps 1, 2
+  // may remain: 12 loads), then start step 3.
+  const int nk = K / 64;                     // a multiple of 16 (K % 1024 == 0)
+  const int ng = nk / 8;
+  LMOE_SCALES(0, mS0)
+  LMOE_DATA(0, mA0, mB0)
+  LMOE_DATA(1, mA1, mB1)
+  LMOE_DATA(2, mA2, mB2)
+  __builtin_amdgcn_s_waitcnt(vm_lds_wait(12));
+  bar();
+  LMOE_DATA(3, mA3, mB3)
+  if (nmi > 2) {
+    LMOE_KLOOP(4)
+  } else if (nmi > 0) {
+    LMOE_KLOOP(2)
+  } else {
+    LMOE_KLOOP(0)
+  }
+#undef LMOE_KLOOP
+#undef LMOE_GROUP
+#undef LMOE_STEP
+#undef LMOE_MFMA
+#undef LMOE_READ
+#undef LMOE_SCALES
+#undef LMOE_DATA
+  __syncthreads();   // every load has landed and every wave has finished reading
+
+  // ---- epilogue, in two halves of 128 rows (waves wm = 0, then wm = 1) ------
+  // The staging area spans the four A stage buffers: rows [32 b, 32 b + 32) of
+  // the half live in buffer b, 512 bytes per row.
+  auto srow = [&](int r) -> unsigned char* {
+    unsigned char* b;
+    switch (r >> 5) {
+      case 0: b = mA0; break;
+      case 1: b = mA1; break;
+      case 2: b = mA2; break;
+      default: b = mA3; break;
+    }
+    return b + (r & 31) * 512;
+  };
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = mi * 32 + 8 * (v >> 2) + 4 * q + (v & 3);
+          unsigned char* row = srow(r);
+          if (EPI == EPI_SWIGLU) {
+            // fp32 h at column c (0..127), 16-byte chunk c / 4 stored at
+            // position (c / 4) ^ (r & 7) of the row
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const float g = acc[mi][h][v], u = acc[mi][2 + h][v];
+              const int c = wn * 64 + h * 32 + l32;
+              *reinterpret_cast<float*>(row + ((((c >> 2) ^ (r & 7)) << 4) | ((c & 3) << 2))) =
+                  g / (1.0f + __expf(-g)) * u;
+            }
+          } else {
+            // bf16 y at column c (0..255)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+              reinterpret_cast<bf16_t*>(row)[wn * 128 + ni * 32 + l32] = f32_to_bf16(acc[mi][ni][v]);
+          }
+        }
+    }
+    __syncthreads();
+    if (EPI == EPI_SWIGLU) {
+      // one thread per (row, block of 32 columns): quantize to MXFP8 E4M3
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int item = it * NT + tid;
+        const int r = item & 127, blk = item >> 7;
+        const int m = m0 + half * 128 + r;
+        if (m < m_end) {
+          const unsigned char* row = srow(r);
+          float v[32];
+#pragma unroll
+          for (int c4 = 0; c4 < 8; ++c4) {
+            const float4 f = *reinterpret_cast<const float4*>(row + (((blk * 8 + c4) ^ (r & 7)) << 4));
+            v[4 * c4] = f.x; v[4 * c4 + 1] = f.y; v[4 * c4 + 2] = f.z; v[4 * c4 + 3] = f.w;
+          }
+          float amax = 0.f;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+          const int X = mx_e4m3_exponent(amax);
+          uint32_t w[8];
+#pragma unroll
+          for (int d = 0; d < 8; ++d)
+            w[d] = (uint32_t)mx_e4m3_code(v[4 * d], X) | ((uint32_t)mx_e4m3_code(v[4 * d + 1], X) << 8) |
+                   ((uint32_t)mx_e4m3_code(v[4 * d + 2], X) << 16) |
+                   ((uint32_t)mx_e4m3_code(v[4 * d + 3], X) << 24);
+          uint8_t* dst = static_cast<uint8_t*>(p.out) + (int64_t)m * p.ldo + n0 + 32 * blk;
+          reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+          reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+          p.out_scales[(int64_t)m * p.ldos + n0 / 32 + blk] = mx_scale_code(X);
+        }
+      }
+    } else {
+      // 16-byte stores of the bf16 rows, then the sums of squares of the stored
+      // values per row and 64-column group
+      for (int i = tid; i < 128 * (BNB / 8); i += NT) {
+        const int r = i / (BNB / 8), c = (i % (BNB / 8)) * 8;
+        const int m = m0 + half * 128 + r;
+        if (m >= m_end) continue;
+        *reinterpret_cast<uint4*>(static_cast<bf16_t*>(p.out) + (int64_t)m * p.ldo + n0 + c) =
+            *reinterpret_cast<const uint4*>(srow(r) + 2 * c);
+      }
+      for (int i = tid; i < 128 * (BNB / 64); i += NT) {
+        const int r = i / (BNB / 64), grp = i % (BNB / 64);
+        const int m = m0 + half * 128 + r;
+        if (m >= m_end) continue;
+        const bf16_t* row = reinterpret_cast<const bf16_t*>(srow(r)) + grp * 64;
+        float ssq = 0.f;
+        for (int j = 0; j < 64; ++j) {
+          const float y = bf16_to_f32(row[j]);
+          ssq += y * y;
+        }
+        p.ss_out[(int64_t)m * p.ss_ld + (n0 + grp * 64) / 64] = ssq;
+      }
+    }
+    __syncthreads();   // the half is read out before the next one is staged
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm256_mx(const Gemm256MxParams& p, EpiKind epi, hipStream_t s) {
+  if (p.max_tiles <= 0) return hipSuccess;
+  const int grid = ((p.max_tiles + 7) / 8) * 8;
+  if (epi == EPI_SWIGLU)
+    hipLaunchKernelGGL(gemm256_mx_kernel<EPI_SWIGLU>, dim3(grid), dim3(NT), 0, s, p);
+  else if (epi == EPI_DOWN)
+    hipLaunchKernelGGL(gemm256_mx_kernel<EPI_DOWN>, dim3(grid), dim3(NT), 0, s, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace lmoe

@@ -119,6 +119,34 @@ struct Gemm256Params {
 int gemm256_tile_m();
 hipError_t launch_gemm256(const Gemm256Params& p, EpiKind epi, hipStream_t s);
 
+// The same tiling for the MXFP4-expert path: MXFP8 E4M3 activations x MXFP4
+// weights on the block-scaled MFMA. EPI_SWIGLU writes H as MXFP8 (codes to out,
+// scales to out_scales); EPI_DOWN writes y as bf16 and the sums of squares.
+struct Gemm256MxParams {
+  const uint8_t* A;            // [rows][K] E4M3 codes (gathered through a_gather for EPI_SWIGLU)
+  const uint8_t* As;           // [rows][K/32] E8M0 scales
+  const int32_t* a_gather;
+  const uint8_t* B;            // [E][N][K/2] E2M1 codes, two per byte (low nibble first)
+  const uint8_t* Bs;           // [E][N][K/32] E8M0 scales
+  int N;                       // B rows per expert (2F for gate/up, Dp for down)
+  const int32_t* offsets;      // [E+1]
+  const int32_t* mt_off;       // [E+1]
+  int E;
+  int ntiles_n;
+  int max_tiles;
+  uint32_t a_bytes;            // extents of A and As in bytes (below 2^31)
+  uint32_t as_bytes;
+  int K;                       // multiple of 512
+  int F;
+  void* out;                   // EPI_SWIGLU: [rows][F] E4M3 codes; EPI_DOWN: [rows][ldo] bf16
+  int64_t ldo;
+  uint8_t* out_scales;         // EPI_SWIGLU: [rows][ldos] E8M0
+  int64_t ldos;
+  float* ss_out;               // EPI_DOWN
+  int ss_ld;
+};
+hipError_t launch_gemm256_mx(const Gemm256MxParams& p, EpiKind epi, hipStream_t s);
+
 // Router top-k + softmax; also builds, per chunk of 64 tokens, a bitmask of
 // the chunk's tokens that selected each expert.
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
@@ -147,6 +175,13 @@ hipError_t launch_sort(const SortParams& p, hipStream_t s);
 // xp = bf16/f32( P * rsqrt(mean(P^2) + eps) * g )
 hipError_t launch_pool_norm(const float* P, const float* g, int T, int Dp, float eps, void* xp,
                             bool bf16, hipStream_t s);
+
+// MXFP4-expert path: xp quantized to MXFP8 E4M3 blocks of 32 (codes [T][Dp],
+// scales [T][Dp/32]) instead of stored as bf16.
+hipError_t launch_pool_norm_mx(const float* P, const float* g, int T, int Dp, float eps, uint8_t* codes,
+                               uint8_t* scales, hipStream_t s);
+// n fp32 values (n a multiple of 32) -> MXFP8 E4M3 codes [n] and scales [n/32].
+hipError_t launch_mx_quant(const float* x, int64_t n, uint8_t* codes, uint8_t* scales, hipStream_t s);
 
 // u[t] = sum_j w[t][j] * rsqrt(sum(ss[inv[t,j]]) / Dp + eps) * g_e * y[inv[t,j]]
 struct CombineParams {

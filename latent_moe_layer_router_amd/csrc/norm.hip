@@ -14,6 +14,7 @@
 // RL backend: FP32 weighted sum).
 #include "common.h"
 #include "kernels.h"
+#include "mx.h"
 
 namespace lmoe {
 
@@ -56,6 +57,70 @@ __global__ __launch_bounds__(kThreads) void pool_norm_kernel(const float* __rest
     out[c + 2] = Elem<T>::from_f32(v.z * r * gg.z);
     out[c + 3] = Elem<T>::from_f32(v.w * r * gg.w);
   }
+}
+
+// Quantize 32 values held by one thread to an MXFP8 E4M3 block: 32 code bytes
+// (two 16-byte stores) and one E8M0 scale byte.
+__device__ __forceinline__ void mx_store_block(const float (&v)[32], uint8_t* codes, uint8_t* scale) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int X = mx_e4m3_exponent(amax);
+  uint32_t w[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d)
+    w[d] = (uint32_t)mx_e4m3_code(v[4 * d], X) | ((uint32_t)mx_e4m3_code(v[4 * d + 1], X) << 8) |
+           ((uint32_t)mx_e4m3_code(v[4 * d + 2], X) << 16) | ((uint32_t)mx_e4m3_code(v[4 * d + 3], X) << 24);
+  reinterpret_cast<uint4*>(codes)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  reinterpret_cast<uint4*>(codes)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  *scale = mx_scale_code(X);
+}
+
+// MX variant of pool_norm (MXFP4-expert path): the normalized row is quantized
+// to MXFP8 E4M3 blocks of 32 (codes [T][Dp], scales [T][Dp/32]) as the experts'
+// input. One thread per block after the row's sum of squares.
+__global__ __launch_bounds__(kThreads) void pool_norm_mx_kernel(const float* __restrict__ P,
+                                                                const float* __restrict__ g, int Dp,
+                                                                float eps, uint8_t* __restrict__ codes,
+                                                                uint8_t* __restrict__ scales) {
+  __shared__ float red[kThreads / kWave];
+  const int t = blockIdx.x;
+  const float* row = P + (int64_t)t * Dp;
+  float ss = 0.f;
+  for (int c = threadIdx.x * 4; c < Dp; c += kThreads * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(row + c);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = block_sum(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)Dp + eps);
+  for (int b = threadIdx.x; b < Dp / 32; b += kThreads) {
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; i += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(row + 32 * b + i);
+      const float4 gg = *reinterpret_cast<const float4*>(g + 32 * b + i);
+      v[i] = x.x * r * gg.x;
+      v[i + 1] = x.y * r * gg.y;
+      v[i + 2] = x.z * r * gg.z;
+      v[i + 3] = x.w * r * gg.w;
+    }
+    mx_store_block(v, codes + (int64_t)t * Dp + 32 * b, scales + (int64_t)t * (Dp / 32) + b);
+  }
+}
+
+// Stand-alone MXFP8 E4M3 quantization of n fp32 values (n a multiple of 32).
+__global__ __launch_bounds__(kThreads) void mx_quant_kernel(const float* __restrict__ x, int64_t nb,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (b >= nb) return;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; i += 4) {
+    const float4 q = *reinterpret_cast<const float4*>(x + 32 * b + i);
+    v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z; v[i + 3] = q.w;
+  }
+  mx_store_block(v, codes + 32 * b, scales + b);
 }
 
 template <typename T>
@@ -106,6 +171,21 @@ hipError_t launch_pool_norm(const float* P, const float* g, int T, int Dp, float
   else
     hipLaunchKernelGGL(pool_norm_kernel<float>, dim3(T), dim3(kThreads), 0, s, P, g, Dp, eps,
                        static_cast<float*>(xp));
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_norm_mx(const float* P, const float* g, int T, int Dp, float eps, uint8_t* codes,
+                               uint8_t* scales, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(pool_norm_mx_kernel, dim3(T), dim3(kThreads), 0, s, P, g, Dp, eps, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant(const float* x, int64_t n, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  const int64_t nb = n / 32;
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)((nb + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+                     x, nb, codes, scales);
   return hipGetLastError();
 }
 

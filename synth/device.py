@@ -25,8 +25,8 @@ def to_device(a: np.ndarray, device) -> torch.Tensor:
 
 
 def upload_weights(w: synth.Workload, device, experts=None) -> dict:
-    """Every weight of workload w on `device` (expert tensors stacked [E, ...])."""
-    dt = _tdtype(w.expert_w)
+    """Every weight of workload w on `device` (expert tensors stacked [E, ...];
+    MXFP4 experts as uint8 codes and scales)."""
     out = {
         "w_router": to_device(synth.w_router(w), device),
         "w_pool": to_device(synth.w_pool(w), device),
@@ -36,6 +36,17 @@ def upload_weights(w: synth.Workload, device, experts=None) -> dict:
     }
     b = synth.router_bias(w)
     out["b_router"] = to_device(b, device) if b is not None else None
+    if w.expert_w == synth.MXFP4:
+        shapes = {"w_gate_up": (2 * w.F, w.Dp // 2), "s_gate_up": (2 * w.F, w.Dp // 32),
+                  "w_down": (w.Dp, w.F // 2), "s_down": (w.Dp, w.F // 32)}
+        for n, sh in shapes.items():
+            out[n] = torch.empty((w.E,) + sh, dtype=torch.uint8, device=device)
+        for e in range(w.E):
+            (cg, sg), (cd, sd) = synth.w_gate_up(w, e), synth.w_down(w, e)
+            for n, a in (("w_gate_up", cg), ("s_gate_up", sg), ("w_down", cd), ("s_down", sd)):
+                out[n][e].copy_(torch.from_numpy(a))
+        return out
+    dt = _tdtype(w.expert_w)
     gu = torch.empty((w.E, 2 * w.F, w.Dp), dtype=dt, device=device)
     dn = torch.empty((w.E, w.Dp, w.F), dtype=dt, device=device)
     npdt = np.float32 if w.expert_w == synth.F32 else np.uint16

@@ -16,6 +16,11 @@ GAP = 1e-5          # tokens whose k-th/(k+1)-th logit gap is at most this have 
 TOL = {synth.F32: 1e-4, synth.BF16: 2e-2, synth.MXFP4: 6e-2}
 
 
+def tol(w: synth.Workload) -> float:
+    """Output tolerance of a workload: its activation dtype's, or MXFP4's."""
+    return TOL[synth.MXFP4] if w.mx_act else TOL[w.act]
+
+
 def say(msg: str):
     print(msg, flush=True)
     sys.stdout.flush()

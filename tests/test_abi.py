@@ -15,7 +15,7 @@ def declared_functions():
     with open(HEADER) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lmoe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(lmoe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_and_binding_agree():
@@ -49,14 +49,15 @@ def test_workspace_bytes_full_size():
     ("top_k", 0, lmoe.LMOE_E_UNSUPPORTED),
     ("top_k", 17, lmoe.LMOE_E_UNSUPPORTED),
     ("act_dtype", lmoe.LMOE_MXFP4, lmoe.LMOE_E_UNSUPPORTED),
-    ("expert_wdtype", lmoe.LMOE_MXFP4, lmoe.LMOE_E_UNSUPPORTED),
+    ("expert_wdtype", lmoe.LMOE_MXFP8_E4M3, lmoe.LMOE_E_UNSUPPORTED),
+    ("d_ff", 4096 + 512, lmoe.LMOE_E_UNSUPPORTED),     # with MXFP4 experts: K % 1024
     ("max_tokens", 0, lmoe.LMOE_E_INVAL),
     ("eps_pool", -1.0, lmoe.LMOE_E_INVAL),
     ("eps_expert", float("nan"), lmoe.LMOE_E_INVAL),
     ("flags", 2, lmoe.LMOE_E_INVAL),
 ])
 def test_config_validation(field, value, status):
-    cfg = lmoe.make_config(8192, 4096, 4096, 256, 8, 128)
+    cfg = lmoe.make_config(8192, 4096, 4096, 256, 8, 128, experts="mxfp4" if field == "d_ff" else None)
     setattr(cfg, field, value)
     with pytest.raises(lmoe.LmoeError) as e:
         lmoe.lmoe_workspace_bytes(cfg)
@@ -75,3 +76,24 @@ def test_forward_rejects_null_handle():
     with pytest.raises(lmoe.LmoeError) as e:
         lmoe.lmoe_forward(None, 0, 0, 1, 0)
     assert e.value.status == lmoe.LMOE_E_INVAL
+
+
+def test_mxfp4_config():
+    """MXFP4 experts: bf16 activations only; the expert inputs are held as MXFP8
+    codes + scales (1 + 1/32 bytes per value instead of 2)."""
+    bf = lmoe.lmoe_workspace_bytes(lmoe.make_config(8192, 4096, 4096, 256, 8, 16384))
+    mx = lmoe.lmoe_workspace_bytes(lmoe.make_config(8192, 4096, 4096, 256, 8, 16384, experts="mxfp4"))
+    A = 16384 * 8
+    assert bf - mx == pytest.approx((16384 * 4096 + A * 4096) * (2 - 1 - 1 / 32), abs=2 ** 20)
+    cfg = lmoe.make_config(8192, 4096, 4096, 256, 8, 128, act="f32", experts="mxfp4")
+    with pytest.raises(lmoe.LmoeError) as e:
+        lmoe.lmoe_workspace_bytes(cfg)
+    assert e.value.status == lmoe.LMOE_E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("n,ptr", [(33, 16), (-32, 16), (64, 0)])
+def test_mx_quantize_rejects_bad_arguments(n, ptr):
+    with pytest.raises(lmoe.LmoeError) as e:
+        lmoe.lmoe_mx_quantize_e4m3(ptr, n, ptr, ptr)
+    assert e.value.status == lmoe.LMOE_E_INVAL
+    lmoe.lmoe_mx_quantize_e4m3(0, 0, 0, 0)     # empty: nothing to do

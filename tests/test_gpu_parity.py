@@ -43,7 +43,7 @@ def run_case(w, T=None, wts=None, max_tokens=None, check_out=True):
     H.check_permutation(a["topk_ids"], a["expert_offsets"], a["sorted_assign"], w.E)
     err = H.out_error(got[~near], ref[~near]) if check_out else 0.0
     H.say(f"[gpu]   max|err|/rms = {err:.3e}, near-ties = {int(near.sum())}")
-    assert err <= H.TOL[w.act], err
+    assert err <= H.tol(w), err
     block.close()
     return got, a
 

@@ -53,7 +53,7 @@ def check(w, x, got, a, hw, rows):
     err = H.out_error(got[rows][keep], ref[keep])
     H.say(f"[gpu]   {w.name}: max|err|/rms = {err:.3e} on {int(keep.sum())} tokens, "
           f"near-ties = {int(near.sum())} of {len(near)}")
-    assert err <= H.TOL[w.act], err
+    assert err <= H.tol(w), err
     return near
 
 
@@ -99,7 +99,7 @@ def test_prefill_T16384_subset(full):
     keep = ~near[np.searchsorted(sel, rows)]
     err = H.out_error(got[rows][keep], ref[keep])
     H.say(f"[gpu]   prefill: max|err|/rms = {err:.3e} on {int(keep.sum())} tokens")
-    assert err <= H.TOL[w.act], err
+    assert err <= H.tol(w), err
 
 
 def test_skewed_T4096(full):
