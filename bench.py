@@ -1,13 +1,14 @@
 """Benchmark of the latent-MoE block forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_bf16]
-                    [--also prefill_bf16] [--no-cpu-baseline]
+                    [--also prefill_bf16,mxfp4] [--no-cpu-baseline]
 
 A step is one lmoe_forward over one batch of synthetic tokens already resident
 in HBM: routing, permutation, pooler, experts, combine, unpooler. The headline
 workload is decode-sized (T=128 tokens; D=8192, Dp=4096, F=4096, E=256, k=8,
 bf16), which streams the touched experts' weights and is bound by HBM; the
-prefill chunk (T=16384) is reported beside it against the bf16 MFMA peak.
+prefill chunk (T=16384) is reported beside it against the bf16 MFMA peak, and
+the same chunk with MXFP4 experts (MXFP8 expert inputs) against the fp8 peak.
 Prints one JSON line. Weights are random-initialized (seed 0) with the model's
 shapes; inputs are synthetic (see synth/).
 """
@@ -24,18 +25,29 @@ sys.path.insert(0, ROOT)
 METRIC = "latent-MoE layer tokens/sec + % bf16 MFMA peak (T=16K) / % HBM BW (T=128)"
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA (the MXFP4 experts' fp8 x fp4 products)
+
+
+def expert_bytes_per_weight(w):
+    """Bytes per expert weight element: bf16, or MXFP4 (half a byte + 1/32 scale)."""
+    return 0.5 + 1 / 32 if w.mx_act else 2
+
+
+def act_bytes(w):
+    """Bytes per expert-input activation element: bf16, or MXFP8 (1 + 1/32)."""
+    return 1 + 1 / 32 if w.mx_act else 2
 
 
 def algorithmic(w, n_active: int, kernel: str):
     """Algorithmic bytes and flops of one launch of a kernel (every touched weight
     read once, every activation it consumes read once and its output written once)."""
-    es = 2
+    wb, ab = expert_bytes_per_weight(w), act_bytes(w)
     T, D, Dp, F, E, k = w.T, w.D, w.Dp, w.F, w.E, w.k
     A = T * k
     if kernel == "gate_up":
-        return (n_active * 2 * F * Dp * es + T * Dp * es + A * F * es), 2.0 * A * Dp * 2 * F
+        return int(n_active * 2 * F * Dp * wb + T * Dp * ab + A * F * ab), 2.0 * A * Dp * 2 * F
     if kernel == "down":
-        return (n_active * Dp * F * es + A * F * es + A * Dp * es), 2.0 * A * F * Dp
+        return int(n_active * Dp * F * wb + A * F * ab + A * Dp * 2), 2.0 * A * F * Dp
     raise ValueError(kernel)
 
 
@@ -43,8 +55,8 @@ def step_work(w, n_active: int):
     """Algorithmic bytes and flops of one whole step."""
     es = 2
     T, D, Dp, F, E, k = w.T, w.D, w.Dp, w.F, w.E, w.k
-    byts = (n_active * 3 * F * Dp * es + (E + 2 * Dp) * D * es + T * D * es + T * D * 4
-            + (Dp + E * Dp) * 4)
+    byts = int(n_active * 3 * F * Dp * expert_bytes_per_weight(w) + (E + 2 * Dp) * D * es
+               + T * D * es + T * D * 4 + (Dp + E * Dp) * 4)
     flops = 2.0 * T * (E * D + Dp * D + k * 3 * Dp * F + D * Dp)
     return byts, flops
 
@@ -78,7 +90,8 @@ def run_workload(lmoe, torch, synth, sdev, block, w, steps, warmup, dev):
 # prefill-sized ones.
 CSRC = os.path.join(ROOT, "latent_moe_layer_router_amd", "csrc")
 GATE_UP_KERNEL = {"hbm": ("stream_kernel<EPI_SWIGLU>", ("stream.hip", "common.h")),
-                  "mfma": ("gemm256_kernel<EPI_SWIGLU>", ("gemm256.hip", "common.h"))}
+                  "mfma": ("gemm256_kernel<EPI_SWIGLU>", ("gemm256.hip", "common.h")),
+                  "mfma_mx": ("gemm256_mx_kernel<EPI_SWIGLU>", ("gemm256_mx.hip", "mx.h", "common.h"))}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.txt")
 
 
@@ -120,8 +133,9 @@ def roofline(w, stage_ms, n_active, bound):
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), **common}
     ach = flops / t / 1e12
-    return {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(ach / PEAK_BF16_TFLOPS, 4), "algorithmic_flops": flops, **common}
+    peak = PEAK_FP8_TFLOPS if bound == "mfma_mx" else PEAK_BF16_TFLOPS
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(ach / peak, 4), "algorithmic_flops": flops, **common}
 
 
 def cpu_baseline(synth, w):
@@ -156,7 +170,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_bf16")
-    ap.add_argument("--also", default="prefill_bf16", help="comma-separated extra workloads, or ''")
+    ap.add_argument("--also", default="prefill_bf16,mxfp4",
+                    help="comma-separated extra workloads, or ''")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a kernel of "
@@ -206,19 +221,35 @@ def main():
     }
     also = []
     for e in extra:
+        if e.expert_w != w.expert_w:
+            # another expert format (MXFP4): its own weights and handle, after
+            # the bf16 ones are released
+            block.close()
+            del tw
+            torch.cuda.empty_cache()
+            t0 = time.perf_counter()
+            tw = sdev.upload_weights(e, dev)
+            print(f"[bench] {e.name} weights uploaded in {time.perf_counter() - t0:.1f} s",
+                  file=sys.stderr, flush=True)
+            w = e
+            block = lmoe.LatentMoE(tw, e.k, max_tokens, e.eps_pool, e.eps_expert,
+                                   out_dtype=torch.float32)
         ems, est, ena, _ = run_workload(lmoe, torch, synth, sdev, block, e, args.steps, args.warmup, dev)
         print(f"[bench] {e.name}: {ems:.3f} ms/step, stages {est}", file=sys.stderr, flush=True)
         eb, ef = step_work(e, ena)
-        also.append({"workload": e.name, "T": e.T, "value": round(e.T / (ems * 1e-3), 1),
-                     "unit": "tokens/s", "ms_per_step": round(ems, 4),
-                     "step_tflops": round(ef / (ems * 1e-3) / 1e12, 1),
-                     "step_mfma_frac": round(ef / (ems * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "roofline": roofline(e, est, ena, "mfma"),
-                     "stages_ms": {s: round(v, 4) for s, v in est.items()}})
+        entry = {"workload": e.name, "T": e.T, "expert_weights": e.expert_w,
+                 "value": round(e.T / (ems * 1e-3), 1), "unit": "tokens/s",
+                 "ms_per_step": round(ems, 4), "step_tflops": round(ef / (ems * 1e-3) / 1e12, 1),
+                 "roofline": roofline(e, est, ena, "mfma_mx" if e.mx_act else "mfma"),
+                 "stages_ms": {s: round(v, 4) for s, v in est.items()}}
+        if not e.mx_act:
+            entry["step_mfma_frac"] = round(ef / (ems * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        also.append(entry)
     res["also"] = also
     block.close()
     del tw
     torch.cuda.empty_cache()
+    w = synth.WORKLOADS[args.workload]
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(synth, w)
