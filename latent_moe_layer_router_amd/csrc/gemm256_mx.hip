@@ -20,12 +20,14 @@
 //     4q + v % 4, column l % 32).
 //
 // Tile 256 x 256 (A rows x B rows), 4 waves of 128 x 128 = 4 x 4 MFMAs per
-// K-step of 64. A stage holds one K-step: A 256 rows x 64 bytes (fp8), B 256
-// rows x 32 bytes (fp4), moved by direct global-to-LDS buffer loads; four
-// stages, three in flight. The scales come in groups of 8 K-steps (512
-// columns = 16 bytes per row of A and of B) into one of two scale buffers;
-// a group travels with the data of the step four ahead of the group's start.
-// LDS: 4 x 24 KiB + 2 x 8 KiB = 112 KiB.
+// MFMA K-step of 64. A stage holds two K-steps (128 columns): A 256 rows x 128
+// bytes (fp8), B 256 rows x 64 bytes (fp4), moved by direct global-to-LDS
+// buffer loads that cover 128 and 64 contiguous bytes of a row (narrower
+// segments cost a full 64-byte request each, which halves the load rate). Two
+// stage buffers: the next stage loads while the current one is multiplied,
+// with one barrier per stage. The scales come in groups of 4 stages (512
+// columns = 16 bytes per row of A and of B) into one of two scale buffers.
+// LDS: 2 x 48 KiB + 2 x 8 KiB = 112 KiB.
 //
 // Tile order over the 8 XCDs as in the bf16 256-tile GEMM: one index space
 // (expert, n-tile, m-tile) cut into 8 contiguous chunks.
@@ -39,26 +41,27 @@ namespace {
 
 constexpr int BM = 256, BNB = 256;
 constexpr int NT = 256;
-constexpr int RA = 64;                // bytes per A row per stage (64 fp8)
-constexpr int RBB = 32;               // bytes per B row per stage (64 fp4)
+constexpr int RA = 128;               // bytes per A row per stage (128 fp8)
+constexpr int RBB = 64;               // bytes per B row per stage (128 fp4)
 constexpr int kBufWord3 = 0x00020000;   // raw buffer descriptor, fourth word (CDNA)
 
 #define LMOE_AS3 __attribute__((address_space(3)))
 
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 
-__shared__ __attribute__((aligned(16))) unsigned char mA0[BM * RA], mA1[BM * RA], mA2[BM * RA], mA3[BM * RA];
-__shared__ __attribute__((aligned(16))) unsigned char mB0[BNB * RBB], mB1[BNB * RBB], mB2[BNB * RBB],
-    mB3[BNB * RBB];
+__shared__ __attribute__((aligned(16))) unsigned char mA0[BM * RA], mA1[BM * RA];
+__shared__ __attribute__((aligned(16))) unsigned char mB0[BNB * RBB], mB1[BNB * RBB];
 // scale buffers: A scales [256 rows][16 B] then B scales [256 rows][16 B]
 __shared__ __attribute__((aligned(16))) unsigned char mS0[2 * 256 * 16], mS1[2 * 256 * 16];
 
-// A rows: 16-byte chunk c of row r at position c ^ fa(r) (as the bf16 tile GEMM).
-__device__ __forceinline__ int fa(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-// B rows (two chunks): chunk c of row r at position c ^ fb(r); 8 consecutive
-// rows (from a multiple of 8) then cover distinct 16-byte bank slots of 128
-// bytes, 16 (from a multiple of 16) those of 256 bytes.
-__device__ __forceinline__ int fb(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+// A rows (eight 16-byte chunks): chunk c of row r at position c ^ fa(r). Any 8
+// consecutive rows (from a multiple of 8) then put one chunk index on 8
+// distinct 16-byte bank slots of a 128-byte bank line, and any 16 (from a
+// multiple of 16) on 16 distinct slots of 256 bytes.
+__device__ __forceinline__ int fa(int r) { return ((r >> 1) ^ (r << 2)) & 7; }
+// B rows (four chunks): chunk c of row r at position c ^ fb(r), the same
+// property for 64-byte rows.
+__device__ __forceinline__ int fb(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 __device__ __forceinline__ void mfma_mx(const uint4& a0, const uint4& a1, const uint4& b, int sa, int sb,
                                         f32x16_t& acc) {
@@ -68,9 +71,8 @@ __device__ __forceinline__ void mfma_mx(const uint4& a0, const uint4& a1, const 
   acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 4, 0, sa, 0, sb);
 }
 
-// s_waitcnt immediates: at most n vector-memory operations outstanding and no
-// LDS operation outstanding.
-constexpr int vm_lds_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+// s_waitcnt immediate: no vector-memory and no LDS operation outstanding.
+constexpr int kAllIdle = 7 << 4;
 
 __device__ __forceinline__ void bar() {
   __builtin_amdgcn_s_barrier();
@@ -121,32 +123,32 @@ __global__ __launch_bounds__(NT, 1) void gemm256_mx_kernel(Gemm256MxParams p) {
     return (EPI == EPI_SWIGLU) ? (uint32_t)((r < BNB / 2) ? (n0 + r) : (p.F + n0 + r - BNB / 2))
                                : (uint32_t)(n0 + r);
   };
-  // A: load j moves rows wave*64 + 16 j + lane/4, lane position lane % 4.
-  uint32_t ga[4];
+  // A: load j moves rows wave*64 + 8 j + lane/8, lane position lane % 8.
+  uint32_t ga[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = wave * 64 + 8 * j + (lane >> 3);
+    ga[j] = a_src(r) * (uint32_t)K + (uint32_t)(((lane & 7) ^ fa(r)) << 4);
+  }
+  // B: load j moves rows wave*64 + 16 j + lane/4, lane position lane % 4.
+  uint32_t gb[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = wave * 64 + 16 * j + (lane >> 2);
-    ga[j] = a_src(r) * (uint32_t)K + (uint32_t)(((lane & 3) ^ fa(r)) << 4);
-  }
-  // B: load j moves rows wave*64 + 32 j + lane/2, lane position lane % 2.
-  uint32_t gb[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = wave * 64 + 32 * j + (lane >> 1);
-    gb[j] = b_row(r) * (uint32_t)(K / 2) + (uint32_t)(((lane & 1) ^ fb(r)) << 4);
+    gb[j] = b_row(r) * (uint32_t)(K / 2) + (uint32_t)(((lane & 3) ^ fb(r)) << 4);
   }
   // Scales: one load each for A and B, row wave*64 + lane, 16 bytes per group.
   const uint32_t gsa = a_src(wave * 64 + lane) * (uint32_t)(K / 32);
   const uint32_t gsb = b_row(wave * 64 + lane) * (uint32_t)(K / 32);
 
-#define LMOE_DATA(kt, SA, SB)                                                                    \
+#define LMOE_DATA(st, SA, SB)                                                                    \
   {                                                                                             \
-    const int koa = (kt) * RA, kob = (kt) * RBB;                                                \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                               \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (LMOE_AS3 void*)((SA) + wave * 4096 + 1024 * j), \
+    const int koa = (st) * RA, kob = (st) * RBB;                                                \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                               \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (LMOE_AS3 void*)((SA) + wave * 8192 + 1024 * j), \
                                                16, (int)ga[j], koa, 0, 0);                      \
-    _Pragma("unroll") for (int j = 0; j < 2; ++j)                                               \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (LMOE_AS3 void*)((SB) + wave * 2048 + 1024 * j), \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                               \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (LMOE_AS3 void*)((SB) + wave * 4096 + 1024 * j), \
                                                16, (int)gb[j], kob, 0, 0);                      \
   }
 #define LMOE_SCALES(g, SS)                                                                       \
@@ -167,16 +169,19 @@ __global__ __launch_bounds__(NT, 1) void gemm256_mx_kernel(Gemm256MxParams p) {
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
   // ---- fragment addresses ---------------------------------------------------
+  // Row r of the A fragment mi, row of the B fragment ni; for MFMA step s of a
+  // stage, lane group q reads A chunks 4s + q and 4s + 2 + q, B chunk 2s + q.
   const int l32 = lane & 31, q = lane >> 5;
-  // aoff / boff: operand chunks in a stage buffer; asc / bsc: the row's scale
-  // bytes (plus q) in a scale buffer.
-  int aoff[4][2], boff[4], asc[4], bsc[4];
+  int aoff[2][4][2], boff[2][4], asc[4], bsc[4];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     const int r = wm * 128 + mi * 32 + l32;
     asc[mi] = r * 16 + q;
-    aoff[mi][0] = r * RA + ((q ^ fa(r)) << 4);
-    aoff[mi][1] = r * RA + (((2 + q) ^ fa(r)) << 4);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      aoff[s2][mi][0] = r * RA + (((4 * s2 + q) ^ fa(r)) << 4);
+      aoff[s2][mi][1] = r * RA + (((4 * s2 + 2 + q) ^ fa(r)) << 4);
+    }
   }
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) {
@@ -184,27 +189,28 @@ __global__ __launch_bounds__(NT, 1) void gemm256_mx_kernel(Gemm256MxParams p) {
     const int r = (EPI == EPI_SWIGLU) ? ((ni >> 1) * (BNB / 2) + wn * 64 + (ni & 1) * 32 + l32)
                                       : (wn * 128 + ni * 32 + l32);
     bsc[ni] = 4096 + r * 16 + q;
-    boff[ni] = r * RBB + ((q ^ fb(r)) << 4);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) boff[s2][ni] = r * RBB + (((2 * s2 + q) ^ fb(r)) << 4);
   }
   const int mrows = m_end - (m0 + wm * 128);
   const int nmi = __builtin_amdgcn_readfirstlane(mrows <= 0 ? 0 : (mrows >= 128 ? 4 : (mrows + 31) / 32));
 
-  // Fragment registers of one K-step (x: the step being multiplied, y: the next).
+  // Fragment registers: x for the first MFMA step of a stage, y for the second.
   uint4 xa[4][2], xb[4], ya[4][2], yb[4];
   int xsa[4], xsb[4], ysa[4], ysb[4];
 
-  // Reads of one step's fragments and scales: the step is step J (0..7) of its
-  // scale group (buffer SS), its scales at bytes 2 J + q of each row's 16.
-  // NMI live 32-row groups.
-#define LMOE_READ(NMI, SA, SB, SS, J, PA, PB, PSA, PSB)                                           \
+  // Reads of MFMA step S2 (0, 1) of a stage in SA/SB whose scales are step J
+  // (0..7) of its scale group in SS (bytes 2 J + q of each row's 16). NMI live
+  // 32-row groups.
+#define LMOE_READ(NMI, SA, SB, SS, S2, J, PA, PB, PSA, PSB)                                       \
   if ((NMI) > 0) {                                                                              \
     _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) {                                          \
-      PB[ni] = *reinterpret_cast<const uint4*>((SB) + boff[ni]);                                \
+      PB[ni] = *reinterpret_cast<const uint4*>((SB) + boff[S2][ni]);                            \
       PSB[ni] = (int)(SS)[bsc[ni] + 2 * (J)];                                                    \
     }                                                                                           \
     _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) if (mi < (NMI)) {                          \
-      PA[mi][0] = *reinterpret_cast<const uint4*>((SA) + aoff[mi][0]);                          \
-      PA[mi][1] = *reinterpret_cast<const uint4*>((SA) + aoff[mi][1]);                          \
+      PA[mi][0] = *reinterpret_cast<const uint4*>((SA) + aoff[S2][mi][0]);                      \
+      PA[mi][1] = *reinterpret_cast<const uint4*>((SA) + aoff[S2][mi][1]);                      \
       PSA[mi] = (int)(SS)[asc[mi] + 2 * (J)];                                                    \
     }                                                                                           \
   }
@@ -213,63 +219,60 @@ __global__ __launch_bounds__(NT, 1) void gemm256_mx_kernel(Gemm256MxParams p) {
     _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                            \
       mfma_mx(PA[mi][0], PA[mi][1], PB[ni], PSA[mi], PSB[ni], acc[mi][ni]);                     \
   }
-  // K-step k (data of step k in SA/SB, scales of its group in SS; step k + 1 in
-  // NA/NB with scales NS). On entry step k's fragments are in the x registers
-  // and steps k + 1 .. k + 3 are in flight. The step waits for step k + 1 and
-  // its own LDS reads, passes the barrier (after which no wave reads step k's
-  // buffers), starts the loads of step k + 4 into them — with the next scale
-  // group when k + 4 starts a group's second half — reads step k + 1's
-  // fragments (y) and runs step k's MFMAs (x). Loads past the last step repeat
-  // it (harmless re-reads into buffers no later step reads), so the number of
-  // loads in flight, and with it every wait count, is the same on every pass.
-#define LMOE_STEP(NMI, k, j, SA, SB, SS, NA, NB, NS, XA, XB, XSA, XSB, YA, YB, YSA, YSB)           \
+  // Stage k (buffers SA/SB, the k-th of its scale group: position P = k % 4 in
+  // buffer SS; stage k + 1 in NA/NB with scales NS). On entry the x registers
+  // hold stage k's first step and every wave has passed the barrier after
+  // which stage k is visible. The stage reads its second step (y), runs the
+  // first step's MFMAs, waits for its own loads (stage k + 1) and LDS reads and
+  // passes the barrier; then no wave reads stage k's buffers any more, so the
+  // loads of stage k + 2 go into them (past the last stage: a harmless repeat
+  // of the last one), and at the last stage of a scale group the scales of the
+  // group after next go into the buffer of the group that just ended. Then it
+  // reads stage k + 1's first step (x) and runs its own second step's MFMAs (y).
+#define LMOE_STAGE(NMI, k, P, SA, SB, SS, NA, NB, NS, SFREE)                                      \
   {                                                                                             \
-    __builtin_amdgcn_s_waitcnt(vm_lds_wait(((j) == 1 || (j) == 2) ? 14 : 12));                  \
+    LMOE_READ(NMI, SA, SB, SS, 1, 2 * (P) + 1, ya, yb, ysa, ysb)                                \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
+    LMOE_MFMA(NMI, xa, xb, xsa, xsb)                                                            \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
+    __builtin_amdgcn_s_waitcnt(kAllIdle);                                                       \
     bar();                                                                                      \
-    LMOE_DATA(((k) + 4 < nk ? (k) + 4 : nk - 1), SA, SB)                                        \
-    if ((j) == 0) {                                                                             \
-      const int g_ = (k) / 8 + 1;                                                               \
-      LMOE_SCALES((g_ < ng ? g_ : ng - 1), (((k) / 8) & 1) ? mS0 : mS1)                          \
+    LMOE_DATA(((k) + 2 < nst ? (k) + 2 : nst - 1), SA, SB)                                      \
+    if ((P) == 3) {                                                                             \
+      const int g_ = ((k) + 1) / 4 + 1;                                                         \
+      LMOE_SCALES((g_ < ng ? g_ : ng - 1), SFREE)                                               \
     }                                                                                           \
-    LMOE_READ(NMI, NA, NB, NS, ((j) + 1) & 7, YA, YB, YSA, YSB)                                  \
+    LMOE_READ(NMI, NA, NB, NS, 0, (2 * ((P) + 1)) & 7, xa, xb, xsa, xsb)                        \
     __builtin_amdgcn_sched_barrier(0);                                                          \
-    LMOE_MFMA(NMI, XA, XB, XSA, XSB)                                                            \
+    LMOE_MFMA(NMI, ya, yb, ysa, ysb)                                                            \
     __builtin_amdgcn_sched_barrier(0);                                                          \
   }
-  // Eight steps = one scale group (g = k / 8, buffer mS[g % 2]); the stage
-  // buffers rotate with period 4. The group's first step reads the group's
-  // scales (buffer SG), its last step also those of the next group (SN).
-#define LMOE_GROUP(NMI, SG, SN)                                                                   \
-  {                                                                                             \
-    LMOE_STEP(NMI, k + 0, 0, mA0, mB0, SG, mA1, mB1, SG, xa, xb, xsa, xsb, ya, yb, ysa, ysb)     \
-    LMOE_STEP(NMI, k + 1, 1, mA1, mB1, SG, mA2, mB2, SG, ya, yb, ysa, ysb, xa, xb, xsa, xsb)     \
-    LMOE_STEP(NMI, k + 2, 2, mA2, mB2, SG, mA3, mB3, SG, xa, xb, xsa, xsb, ya, yb, ysa, ysb)     \
-    LMOE_STEP(NMI, k + 3, 3, mA3, mB3, SG, mA0, mB0, SG, ya, yb, ysa, ysb, xa, xb, xsa, xsb)     \
-    LMOE_STEP(NMI, k + 4, 4, mA0, mB0, SG, mA1, mB1, SG, xa, xb, xsa, xsb, ya, yb, ysa, ysb)     \
-    LMOE_STEP(NMI, k + 5, 5, mA1, mB1, SG, mA2, mB2, SG, ya, yb, ysa, ysb, xa, xb, xsa, xsb)     \
-    LMOE_STEP(NMI, k + 6, 6, mA2, mB2, SG, mA3, mB3, SG, xa, xb, xsa, xsb, ya, yb, ysa, ysb)     \
-    LMOE_STEP(NMI, k + 7, 7, mA3, mB3, SG, mA0, mB0, SN, ya, yb, ysa, ysb, xa, xb, xsa, xsb)     \
-  }
+  // Eight stages: two scale groups (buffers mS0, mS1), the stage buffers
+  // alternating.
 #define LMOE_KLOOP(NMI)                                                                          \
   {                                                                                             \
-    LMOE_READ(NMI, mA0, mB0, mS0, 0, xa, xb, xsa, xsb)                                          \
-    for (int k0_ = 0; k0_ < nk; k0_ += 16) {                                                    \
-      { const int k = k0_; LMOE_GROUP(NMI, mS0, mS1) }                                          \
-      { const int k = k0_ + 8; LMOE_GROUP(NMI, mS1, mS0) }                                      \
+    LMOE_READ(NMI, mA0, mB0, mS0, 0, 0, xa, xb, xsa, xsb)                                       \
+    for (int k0_ = 0; k0_ < nst; k0_ += 8) {                                                    \
+      LMOE_STAGE(NMI, k0_ + 0, 0, mA0, mB0, mS0, mA1, mB1, mS0, mS1)                            \
+      LMOE_STAGE(NMI, k0_ + 1, 1, mA1, mB1, mS0, mA0, mB0, mS0, mS1)                            \
+      LMOE_STAGE(NMI, k0_ + 2, 2, mA0, mB0, mS0, mA1, mB1, mS0, mS1)                            \
+      LMOE_STAGE(NMI, k0_ + 3, 3, mA1, mB1, mS0, mA0, mB0, mS1, mS0)                            \
+      LMOE_STAGE(NMI, k0_ + 4, 0, mA0, mB0, mS1, mA1, mB1, mS1, mS0)                            \
+      LMOE_STAGE(NMI, k0_ + 5, 1, mA1, mB1, mS1, mA0, mB0, mS1, mS0)                            \
+      LMOE_STAGE(NMI, k0_ + 6, 2, mA0, mB0, mS1, mA1, mB1, mS1, mS0)                            \
+      LMOE_STAGE(NMI, k0_ + 7, 3, mA1, mB1, mS1, mA0, mB0, mS0, mS1)                            \
     }                                                                                           \
   }
 
-  // Prologue: scale group 0, steps 0..2 in flight; wait for step 0 (steps 1, 2
-  // may remain: 12 loads), then start step 3.
-  const int nk = K / 64;                     // a multiple of 16 (K % 1024 == 0)
-  const int ng = nk / 8;
+  // Prologue: scale groups 0 and 1, stage 0; wait for them; start stage 1.
+  const int nst = K / 128;                   // a multiple of 8 (K % 1024 == 0)
+  const int ng = nst / 4;
   LMOE_SCALES(0, mS0)
+  LMOE_SCALES((ng > 1 ? 1 : 0), mS1)
   LMOE_DATA(0, mA0, mB0)
-  LMOE_DATA(1, mA1, mB1)
-  LMOE_DATA(2, mA2, mB2)
-  __builtin_amdgcn_s_waitcnt(vm_lds_wait(12));
+  __builtin_amdgcn_s_waitcnt(kAllIdle);
   bar();
-  LMOE_DATA(3, mA3, mB3)
+  LMOE_DATA((nst > 1 ? 1 : 0), mA1, mB1)
   if (nmi > 2) {
     LMOE_KLOOP(4)
   } else if (nmi > 0) {
@@ -278,8 +281,7 @@ __global__ __launch_bounds__(NT, 1) void gemm256_mx_kernel(Gemm256MxParams p) {
     LMOE_KLOOP(0)
   }
 #undef LMOE_KLOOP
-#undef LMOE_GROUP
-#undef LMOE_STEP
+#undef LMOE_STAGE
 #undef LMOE_MFMA
 #undef LMOE_READ
 #undef LMOE_SCALES
@@ -287,18 +289,9 @@ __global__ __launch_bounds__(NT, 1) void gemm256_mx_kernel(Gemm256MxParams p) {
   __syncthreads();   // every load has landed and every wave has finished reading
 
   // ---- epilogue, in two halves of 128 rows (waves wm = 0, then wm = 1) ------
-  // The staging area spans the four A stage buffers: rows [32 b, 32 b + 32) of
+  // The staging area spans the two A stage buffers: rows [64 b, 64 b + 64) of
   // the half live in buffer b, 512 bytes per row.
-  auto srow = [&](int r) -> unsigned char* {
-    unsigned char* b;
-    switch (r >> 5) {
-      case 0: b = mA0; break;
-      case 1: b = mA1; break;
-      case 2: b = mA2; break;
-      default: b = mA3; break;
-    }
-    return b + (r & 31) * 512;
-  };
+  auto srow = [&](int r) -> unsigned char* { return ((r >> 6) ? mA1 : mA0) + (r & 63) * 512; };
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     if (wm == half) {
