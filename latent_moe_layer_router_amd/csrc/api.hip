@@ -26,7 +26,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 // Byte layout of the workspace for a configuration (every region 256-byte aligned).
 struct Plan {
-  size_t P, logits, ids, w, masks, chunk_base, counts, offsets, sorted_assign, inv, row_token,
+  size_t P, logits, ids, w, masks, chunk_base, counts, offsets, sorted_assign, inv,
       tiles, n_tiles, mt_off, xp, H, xq, xs, hq, hs, Y, ss, u, part;
   size_t total;
   int max_slots;
@@ -61,17 +61,17 @@ Plan make_plan(const lmoe_config& c) {
   p.offsets = grow(cur, (E + 1) * 4);
   p.sorted_assign = grow(cur, A * 4);
   p.inv = grow(cur, A * 4);
-  p.row_token = grow(cur, A * 4);
   p.tiles = grow(cur, (size_t)p.max_slots * 8);
   p.n_tiles = grow(cur, 4);
   p.mt_off = grow(cur, (E + 1) * 4);
-  // Expert inputs: bf16/fp32 xp and H, or (MXFP4 experts) their MXFP8 codes
-  // and scales.
+  // Expert inputs, rows in sorted (expert-major) order: bf16/fp32 xp (each
+  // token's row once per selected expert) and H, or (MXFP4 experts) their
+  // MXFP8 codes and scales.
   const bool mx = c.expert_wdtype == LMOE_MXFP4;
-  p.xp = grow(cur, mx ? 0 : Tm * Dp * es);
+  p.xp = grow(cur, mx ? 0 : A * Dp * es);
   p.H = grow(cur, mx ? 0 : A * F * es);
-  p.xq = grow(cur, mx ? Tm * Dp : 0);
-  p.xs = grow(cur, mx ? Tm * Dp / 32 : 0);
+  p.xq = grow(cur, mx ? A * Dp : 0);
+  p.xs = grow(cur, mx ? A * Dp / 32 : 0);
   p.hq = grow(cur, mx ? A * F : 0);
   p.hs = grow(cur, mx ? A * F / 32 : 0);
   p.Y = grow(cur, A * Dp * es);
@@ -114,7 +114,7 @@ lmoe_status check_config(const lmoe_config* c) {
     if (c->d_pooled % 1024 || c->d_ff % 1024)
       return fail(LMOE_E_UNSUPPORTED, "MXFP4 experts need d_pooled and d_ff multiples of 1024");
     const int64_t A = (int64_t)c->max_tokens * c->top_k;
-    if (A * c->d_ff >= ((int64_t)1 << 31) || (int64_t)c->max_tokens * c->d_pooled >= ((int64_t)1 << 31) ||
+    if (A * c->d_ff >= ((int64_t)1 << 31) || A * c->d_pooled >= ((int64_t)1 << 31) ||
         (int64_t)c->d_ff * c->d_pooled >= ((int64_t)1 << 31))
       return fail(LMOE_E_UNSUPPORTED, "MXFP4 experts: max_tokens too large for 32-bit offsets");
   } else if (c->expert_wdtype != c->act_dtype) {
@@ -310,7 +310,6 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   int32_t* sorted_assign = reinterpret_cast<int32_t*>(ws + pl.sorted_assign);
   int32_t* tiles = reinterpret_cast<int32_t*>(ws + pl.tiles);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(ws + pl.n_tiles);
-  int32_t* row_token = reinterpret_cast<int32_t*>(ws + pl.row_token);
   int32_t* inv = reinterpret_cast<int32_t*>(ws + pl.inv);
   void* xp = ws + pl.xp;
   void* H = ws + pl.H;
@@ -327,7 +326,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   // The grouped kernels' buffer loads take 32-bit byte offsets: the activations
   // (xp, H) and one expert's weights must each stay below 2 GiB.
   const bool off32_ok = (int64_t)T * k * F * 2 < ((int64_t)1 << 31) &&
-                        (int64_t)T * Dp * 2 < ((int64_t)1 << 31) &&
+                        (int64_t)T * k * Dp * 2 < ((int64_t)1 << 31) &&
                         (int64_t)2 * F * Dp * 2 < ((int64_t)1 << 31);
   const bool stream_ok = bf16 && !mx && Dp % 128 == 0 && F % 128 == 0 && off32_ok;
   const int small_max = stream_ok ? stream_max_rows() : 0;
@@ -363,9 +362,39 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   float* part = reinterpret_cast<float*>(ws + pl.part);
   const int slices_in = dense_stream_slices(D), slices_un = dense_stream_slices(Dp);
 
+  // Larger batches: the dense projections on 256 x 256 tiles (bf16; K a
+  // multiple of 128, the pooler's rows a multiple of 256, 32-bit offsets).
+  const bool dense256 = bf16 && !dense_stream && D % 128 == 0 && Dp % 256 == 0 &&
+                        (int64_t)T * D * 2 < ((int64_t)1 << 31) && (int64_t)T * Dp * 2 < ((int64_t)1 << 31) &&
+                        (int64_t)256 * D * 2 < ((int64_t)1 << 31);
+  auto dense_params = [&](const void* A, int K, int N) {
+    Gemm256Params g{};
+    g.A = A;
+    g.lda = K;
+    g.ldb = K;
+    g.K = K;
+    g.M = T;
+    g.N = N;
+    g.ntiles_n = (N + 255) / 256;
+    g.max_tiles = g.ntiles_n * ((T + 255) / 256);
+    g.a_bytes = (uint32_t)((int64_t)T * K * 2);
+    return g;
+  };
+
   // 1. router + pooler: one GEMM over [W_pool; W_router]
   mark();
-  if (dense_stream && slices_in > 0) {
+  if (dense256) {
+    Gemm256Params g = dense_params(x, D, Dp + E);
+    g.B = h->w.w_pool;
+    g.B1 = h->w.w_router;
+    g.n_split = Dp;
+    g.out = P;
+    g.ldo = Dp;
+    g.out1 = logits;
+    g.ldo1 = E;
+    g.bias1 = h->w.b_router;
+    run(launch_gemm256(g, EPI_F32, s));
+  } else if (dense_stream && slices_in > 0) {
     DenseStreamParams d{};
     d.A = x;
     d.lda = D;
@@ -418,7 +447,6 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     sp.offsets = offsets;
     sp.sorted_assign = sorted_assign;
     sp.inv = inv;
-    sp.row_token = row_token;
     sp.tiles = tiles;
     sp.n_tiles = n_tiles;
     sp.T = T;
@@ -433,16 +461,15 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   // 4. pooled RMSNorm
   mark();
   if (mx)
-    run(launch_pool_norm_mx(P, h->w.g_pool, T, Dp, c.eps_pool, xq, xs, s));
+    run(launch_pool_norm_mx(P, h->w.g_pool, T, Dp, c.eps_pool, inv, k, xq, xs, s));
   else
-    run(launch_pool_norm(P, h->w.g_pool, T, Dp, c.eps_pool, xp, bf16, s));
+    run(launch_pool_norm(P, h->w.g_pool, T, Dp, c.eps_pool, inv, k, xp, bf16, s));
   // 5. gate/up grouped GEMM + SwiGLU
   mark();
   if (stream_ok) {
     StreamParams sp{};
     sp.A = xp;
     sp.lda = Dp;
-    sp.a_gather = row_token;
     sp.B = h->w.w_gate_up;
     sp.ldb = Dp;
     sp.b_expert_stride = (int64_t)2 * F * Dp;
@@ -452,7 +479,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     sp.max_rows = small_max;
     sp.K = Dp;
     sp.F = F;
-    sp.a_bytes = (uint32_t)((int64_t)T * Dp * 2);
+    sp.a_bytes = (uint32_t)(A_ * Dp * 2);
     sp.b_bytes = (uint32_t)((int64_t)2 * F * Dp * 2);
     sp.out = H;
     sp.ldo = F;
@@ -462,7 +489,6 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     Gemm256MxParams g{};
     g.A = xq;
     g.As = xs;
-    g.a_gather = row_token;
     g.B = static_cast<const uint8_t*>(h->w.w_gate_up);
     g.Bs = h->w.s_gate_up;
     g.N = 2 * F;
@@ -471,8 +497,8 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     g.E = E;
     g.ntiles_n = F / 128;
     g.max_tiles = g.ntiles_n * mtiles_bound;
-    g.a_bytes = (uint32_t)((int64_t)T * Dp);
-    g.as_bytes = (uint32_t)((int64_t)T * Dp / 32);
+    g.a_bytes = (uint32_t)(A_ * Dp);
+    g.as_bytes = (uint32_t)(A_ * Dp / 32);
     g.K = Dp;
     g.F = F;
     g.out = hq;
@@ -484,7 +510,6 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     Gemm256Params g{};
     g.A = xp;
     g.lda = Dp;
-    g.a_gather = row_token;
     g.B = h->w.w_gate_up;
     g.ldb = Dp;
     g.b_expert_stride = (int64_t)2 * F * Dp;
@@ -493,7 +518,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     g.E = E;
     g.ntiles_n = F / 128;
     g.max_tiles = g.ntiles_n * mtiles_bound;
-    g.a_bytes = (uint32_t)((int64_t)T * Dp * 2);
+    g.a_bytes = (uint32_t)(A_ * Dp * 2);
     g.b_bytes = (uint32_t)((int64_t)2 * F * Dp * 2);
     g.K = Dp;
     g.F = F;
@@ -506,7 +531,6 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     g.K = Dp;
     g.A = xp;
     g.lda = Dp;
-    g.a_gather = row_token;
     g.B0 = h->w.w_gate_up;
     g.ldb = Dp;
     g.b_expert_stride = (int64_t)2 * F * Dp;
@@ -622,7 +646,15 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   }
   // 8. unpooler
   mark();
-  if (dense_stream && slices_un > 0) {
+  if (dense256) {
+    Gemm256Params g = dense_params(u, Dp, D);
+    g.B = h->w.w_unpool;
+    g.B1 = h->w.w_unpool;
+    g.n_split = D;
+    g.out = out;
+    g.ldo = D;
+    run(launch_gemm256(g, out_f32 ? EPI_F32 : EPI_ACT, s));
+  } else if (dense_stream && slices_un > 0) {
     DenseStreamParams d{};
     d.A = u;
     d.lda = Dp;

@@ -84,8 +84,7 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmParams p) {
   auto a_row = [&](int r) -> const unsigned char* {
     int m = m0 + r;
     if (m >= m_end) m = m_end - 1;          // rows past the end load a valid row; never stored
-    const int64_t arow = (EPI == EPI_SWIGLU) ? (int64_t)p.a_gather[m] : (int64_t)m;
-    return reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.A) + arow * p.lda) + lc * 16;
+    return reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.A) + (int64_t)m * p.lda) + lc * 16;
   };
   auto b_row = [&](int r) -> const unsigned char* {
     const T* brow;

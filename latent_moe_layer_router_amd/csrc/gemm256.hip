@@ -84,22 +84,33 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
   const int wm = wave >> 1, wn = wave & 1;
 
   // ---- tile of this workgroup (XCD-chunked order) --------------------------
-  const int total = p.ntiles_n * p.mt_off[p.E];
+  // Grouped (p.M == 0): tiles (expert, n-tile, m-tile) of the experts' sorted
+  // rows. Dense (p.M > 0): tiles (m-tile, n-tile) of an M x N product.
+  const bool dense = p.M > 0;
+  const int ntm = dense ? (p.M + BM - 1) / BM : 0;
+  const int total = dense ? ntm * p.ntiles_n : p.ntiles_n * p.mt_off[p.E];
   const int chunk = (total + 7) / 8;
   const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
   const int t = xcd * chunk + local;
   if (local >= chunk || t >= total) return;
-  int lo = 0, hi = p.E;                      // expert e: ntiles_n*mt_off[e] <= t < ntiles_n*mt_off[e+1]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.ntiles_n * p.mt_off[mid] <= t) lo = mid; else hi = mid;
+  int e = 0, ntile, m0, m_end;
+  if (dense) {
+    ntile = t % p.ntiles_n;
+    m0 = (t / p.ntiles_n) * BM;
+    m_end = p.M;
+  } else {
+    int lo = 0, hi = p.E;                    // expert e: ntiles_n*mt_off[e] <= t < ntiles_n*mt_off[e+1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.ntiles_n * p.mt_off[mid] <= t) lo = mid; else hi = mid;
+    }
+    e = lo;
+    const int mt_e = p.mt_off[e + 1] - p.mt_off[e];
+    const int tl = t - p.ntiles_n * p.mt_off[e];
+    ntile = tl / mt_e;
+    m0 = p.offsets[e] + (tl % mt_e) * BM;
+    m_end = p.offsets[e + 1];
   }
-  const int e = lo;
-  const int mt_e = p.mt_off[e + 1] - p.mt_off[e];
-  const int tl = t - p.ntiles_n * p.mt_off[e];
-  const int ntile = tl / mt_e, mtile = tl % mt_e;
-  const int m0 = p.offsets[e] + mtile * BM;
-  const int m_end = p.offsets[e + 1];
   const int n0 = ntile * (EPI == EPI_SWIGLU ? BNB / 2 : BNB);   // output column start
 
   // ---- global-to-LDS loads ------------------------------------------------
@@ -114,19 +125,32 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
   // wait counts around them.)
   const __amdgpu_buffer_rsrc_t rsA =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.A), (short)0, (int)p.a_bytes, kBufWord3);
-  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(static_cast<const bf16_t*>(p.B) + (int64_t)e * p.b_expert_stride), (short)0,
-      (int)p.b_bytes, kBufWord3);
+  // B rows of the tile: grouped, the expert's matrix (rows n0 + r, or the
+  // gate/up pairs); dense, the tile's own 256 rows from B (columns below
+  // n_split) or B1, the extent ending at row N (rows past it read as zero).
+  const bf16_t* Bt;
+  int b_ext;
+  if (dense) {
+    Bt = (n0 < p.n_split) ? static_cast<const bf16_t*>(p.B) + (int64_t)n0 * p.ldb
+                          : static_cast<const bf16_t*>(p.B1) + (int64_t)(n0 - p.n_split) * p.ldb;
+    const int rows = min(BNB, p.N - n0);
+    b_ext = rows * (int)p.ldb * 2;
+  } else {
+    Bt = static_cast<const bf16_t*>(p.B) + (int64_t)e * p.b_expert_stride;
+    b_ext = (int)p.b_bytes;
+  }
+  const __amdgpu_buffer_rsrc_t rsB =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(Bt), (short)0, b_ext, kBufWord3);
   const int pos = lane & 3;
   auto a_off = [&](int r) -> uint32_t {
     int m = m0 + r;
     if (m >= m_end) m = m_end - 1;           // rows past the end load a valid row; never stored
-    const uint32_t src = (EPI == EPI_SWIGLU) ? (uint32_t)p.a_gather[m] : (uint32_t)m;
+    const uint32_t src = (uint32_t)m;
     const uint32_t c = pos ^ (((r >> 1) ^ (r >> 3)) & 3);
     return src * (uint32_t)(p.lda * 2) + c * 16;
   };
   auto b_off = [&](int r) -> uint32_t {
-    const int n = (EPI == EPI_SWIGLU) ? ((r < BNB / 2) ? (n0 + r) : (p.F + n0 + r - BNB / 2)) : (n0 + r);
+    const int n = dense ? r : (EPI == EPI_SWIGLU) ? ((r < BNB / 2) ? (n0 + r) : (p.F + n0 + r - BNB / 2)) : (n0 + r);
     const uint32_t c = pos ^ (((r >> 1) ^ (r >> 3)) & 3);
     return (uint32_t)n * (uint32_t)(p.ldb * 2) + c * 16;
   };
@@ -271,6 +295,30 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
 #undef LMOE_LD
   __syncthreads();   // every load has landed and every wave has finished reading
 
+  if (EPI == EPI_F32) {
+    // fp32 out, straight from the accumulators: the 32 lanes of a half-wave
+    // store 32 consecutive columns of a row (128 bytes). Columns below n_split
+    // go to out, the rest to out1 plus bias1 (router logits).
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        if (m >= m_end) continue;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const int n = n0 + wn * 128 + ni * 32 + l32;
+          if (n >= p.N) continue;
+          if (n < p.n_split)
+            static_cast<float*>(p.out)[(int64_t)m * p.ldo + n] = acc[mi][ni][v];
+          else
+            p.out1[(int64_t)m * p.ldo1 + (n - p.n_split)] =
+                acc[mi][ni][v] + (p.bias1 ? p.bias1[n - p.n_split] : 0.f);
+        }
+      }
+    return;
+  }
+
   // ---- epilogue: stage [256][OBN] bf16 in LDS, 16-byte stores ----------------
   // The staging tile spans the stage buffers: rows [32 q, 32 q + 32) live in
   // buffer q (A0, B0, A1, ..., B3 in declaration order), 16 KiB each.
@@ -311,7 +359,7 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
   for (int i = tid; i < BM * CPR; i += NT) {
     const int r = i / CPR, c = (i % CPR) * 8;
     const int m = m0 + r;
-    if (m >= m_end) continue;
+    if (m >= m_end || (dense && n0 + c >= p.N)) continue;
     *reinterpret_cast<uint4*>(static_cast<bf16_t*>(p.out) + (int64_t)m * p.ldo + n0 + c) =
         *reinterpret_cast<const uint4*>(srow(r) + c);
   }
@@ -343,6 +391,10 @@ hipError_t launch_gemm256(const Gemm256Params& p, EpiKind epi, hipStream_t s) {
     hipLaunchKernelGGL(gemm256_kernel<EPI_SWIGLU>, dim3(grid), dim3(NT), 0, s, p);
   else if (epi == EPI_DOWN)
     hipLaunchKernelGGL(gemm256_kernel<EPI_DOWN>, dim3(grid), dim3(NT), 0, s, p);
+  else if (epi == EPI_F32 && p.M > 0)
+    hipLaunchKernelGGL(gemm256_kernel<EPI_F32>, dim3(grid), dim3(NT), 0, s, p);
+  else if (epi == EPI_ACT && p.M > 0)
+    hipLaunchKernelGGL(gemm256_kernel<EPI_ACT>, dim3(grid), dim3(NT), 0, s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -114,10 +114,10 @@ __global__ __launch_bounds__(NT, 1) void gemm256_mx_kernel(Gemm256MxParams p) {
       const_cast<uint8_t*>(p.B + (int64_t)e * p.N * (K / 2)), (short)0, p.N * (K / 2), kBufWord3);
   const __amdgpu_buffer_rsrc_t rBs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.Bs + (int64_t)e * p.N * (K / 32)), (short)0, p.N * (K / 32), kBufWord3);
-  auto a_src = [&](int r) -> uint32_t {     // source row (token or sorted position) of tile row r
+  auto a_src = [&](int r) -> uint32_t {     // A row (sorted position) of tile row r
     int m = m0 + r;
     if (m >= m_end) m = m_end - 1;           // rows past the end load a valid row; never stored
-    return (EPI == EPI_SWIGLU) ? (uint32_t)p.a_gather[m] : (uint32_t)m;
+    return (uint32_t)m;
   };
   auto b_row = [&](int r) -> uint32_t {     // B row of tile row r
     return (EPI == EPI_SWIGLU) ? (uint32_t)((r < BNB / 2) ? (n0 + r) : (p.F + n0 + r - BNB / 2))

@@ -18,7 +18,6 @@ struct GemmParams {
   int M, N, K;                 // dense: M rows; N output columns; K inner
   const void* A;
   int64_t lda;                 // elements
-  const int32_t* a_gather;     // EPI_SWIGLU: A row of sorted position p is a_gather[p]
   const void* B0;
   const void* B1;              // EPI_F32: rows [n_split, N) come from B1
   int n_split;
@@ -49,7 +48,6 @@ hipError_t launch_gemm(const GemmParams& p, EpiKind epi, bool bf16, hipStream_t 
 struct StreamParams {
   const void* A;
   int64_t lda;
-  const int32_t* a_gather;     // EPI_SWIGLU: token row of each sorted position
   const void* B;
   int64_t ldb;
   int64_t b_expert_stride;
@@ -92,13 +90,15 @@ int dense_stream_max_tokens();
 int dense_stream_slices(int K);   // 0 if K does not split evenly
 hipError_t launch_dense_stream(const DenseStreamParams& p, hipStream_t s);
 
-// Large-tile (256 x 256) grouped GEMM for experts with many rows (bf16).
-// Tiles of expert e: mt_off[e+1] - mt_off[e] row tiles of 256 (in sorted row
-// order from offsets[e]) times ntiles_n column tiles.
+// Large-tile (256 x 256) GEMM (bf16). Grouped (M == 0), for experts with many
+// rows: expert e has mt_off[e+1] - mt_off[e] row tiles of 256 (in sorted row
+// order from offsets[e]; the last may be partial), each times ntiles_n column
+// tiles; EPI_SWIGLU or EPI_DOWN. Dense (M > 0): out = A . B^T over M rows and
+// N columns (ntiles_n tiles of 256, the last may be partial), rows [n_split, N)
+// of B^T taken from B1; EPI_F32 (fp32 out, out1 + bias1) or EPI_ACT (bf16 out).
 struct Gemm256Params {
   const void* A;
   int64_t lda;
-  const int32_t* a_gather;     // EPI_SWIGLU: token row of each sorted position
   const void* B;
   int64_t ldb;
   int64_t b_expert_stride;
@@ -109,12 +109,20 @@ struct Gemm256Params {
   int max_tiles;               // grid size, a bound on the tile count
   uint32_t a_bytes;            // extent of A in bytes (below 2^31)
   uint32_t b_bytes;            // extent of one expert's B in bytes (below 2^31)
-  int K;                       // multiple of 64
+  int K;                       // multiple of 128
   int F;
   void* out;
   int64_t ldo;
   float* ss_out;
   int ss_ld;
+  // dense mode
+  int M;                       // rows (0: grouped)
+  int N;                       // columns
+  const void* B1;              // rows of B^T at n_split and above
+  int n_split;                 // multiple of 256
+  float* out1;
+  int64_t ldo1;
+  const float* bias1;
 };
 int gemm256_tile_m();
 hipError_t launch_gemm256(const Gemm256Params& p, EpiKind epi, hipStream_t s);
@@ -123,9 +131,8 @@ hipError_t launch_gemm256(const Gemm256Params& p, EpiKind epi, hipStream_t s);
 // weights on the block-scaled MFMA. EPI_SWIGLU writes H as MXFP8 (codes to out,
 // scales to out_scales); EPI_DOWN writes y as bf16 and the sums of squares.
 struct Gemm256MxParams {
-  const uint8_t* A;            // [rows][K] E4M3 codes (gathered through a_gather for EPI_SWIGLU)
+  const uint8_t* A;            // [rows][K] E4M3 codes, rows in sorted order
   const uint8_t* As;           // [rows][K/32] E8M0 scales
-  const int32_t* a_gather;
   const uint8_t* B;            // [E][N][K/2] E2M1 codes, two per byte (low nibble first)
   const uint8_t* Bs;           // [E][N][K/32] E8M0 scales
   int N;                       // B rows per expert (2F for gate/up, Dp for down)
@@ -162,7 +169,6 @@ struct SortParams {
   int32_t* offsets;             // [E+1]
   int32_t* sorted_assign;       // [T*k]
   int32_t* inv;                 // [T*k]
-  int32_t* row_token;           // [T*k]
   int32_t* tiles;               // [max_slots][2]
   int32_t* n_tiles;             // [1]
   int T, E, k, tile_m;
@@ -172,14 +178,15 @@ struct SortParams {
 };
 hipError_t launch_sort(const SortParams& p, hipStream_t s);
 
-// xp = bf16/f32( P * rsqrt(mean(P^2) + eps) * g )
-hipError_t launch_pool_norm(const float* P, const float* g, int T, int Dp, float eps, void* xp,
-                            bool bf16, hipStream_t s);
+// xp = bf16/f32( P * rsqrt(mean(P^2) + eps) * g ), written to the token's k rows
+// of the sorted order: row inv[t*k + j] for j < k (the experts' input rows).
+hipError_t launch_pool_norm(const float* P, const float* g, int T, int Dp, float eps, const int32_t* inv,
+                            int k, void* xp, bool bf16, hipStream_t s);
 
 // MXFP4-expert path: xp quantized to MXFP8 E4M3 blocks of 32 (codes [T][Dp],
 // scales [T][Dp/32]) instead of stored as bf16.
-hipError_t launch_pool_norm_mx(const float* P, const float* g, int T, int Dp, float eps, uint8_t* codes,
-                               uint8_t* scales, hipStream_t s);
+hipError_t launch_pool_norm_mx(const float* P, const float* g, int T, int Dp, float eps, const int32_t* inv,
+                               int k, uint8_t* codes, uint8_t* scales, hipStream_t s);
 // n fp32 values (n a multiple of 32) -> MXFP8 E4M3 codes [n] and scales [n/32].
 hipError_t launch_mx_quant(const float* x, int64_t n, uint8_t* codes, uint8_t* scales, hipStream_t s);
 

@@ -3,7 +3,8 @@
 // pool_norm — the pooled input is RMS-normalized before the experts run (LMSYS
 // blog, "MoE with pooler, unpooler and per-expert normalization"): one workgroup
 // per token reads the fp32 pooler output row, reduces its sum of squares and
-// writes xp = P / sqrt(mean(P^2) + eps) * g_pool in the expert GEMM's input type.
+// writes xp = P / sqrt(mean(P^2) + eps) * g_pool in the expert GEMM's input type
+// to each of the token's k rows in the experts' sorted order.
 //
 // combine — the finalize step of the blog's "AMD support" section (unpermute +
 // per-expert RMSNorm + weighted sum in one kernel). One workgroup per token
@@ -34,10 +35,25 @@ __device__ float block_sum(float v, float* red) {
   return s;
 }
 
+// Store 8 consecutive values as bf16 (one 16-byte store) or fp32 (two).
+__device__ __forceinline__ void store8(bf16_t* dst, const float (&v)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+  *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+__device__ __forceinline__ void store8(float* dst, const float (&v)[8]) {
+  reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// The normalized row goes to the token's k rows of the sorted (expert-major)
+// order, inv[t*k + j], so that the expert GEMMs read their rows contiguously.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void pool_norm_kernel(const float* __restrict__ P,
                                                              const float* __restrict__ g, int Dp,
-                                                             float eps, T* __restrict__ xp) {
+                                                             float eps, const int32_t* __restrict__ inv,
+                                                             int k, T* __restrict__ xp) {
   __shared__ float red[kThreads / kWave];
   const int t = blockIdx.x;
   const float* row = P + (int64_t)t * Dp;
@@ -48,14 +64,18 @@ __global__ __launch_bounds__(kThreads) void pool_norm_kernel(const float* __rest
   }
   ss = block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)Dp + eps);
-  T* out = xp + (int64_t)t * Dp;
-  for (int c = threadIdx.x * 4; c < Dp; c += kThreads * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(row + c);
-    const float4 gg = *reinterpret_cast<const float4*>(g + c);
-    out[c + 0] = Elem<T>::from_f32(v.x * r * gg.x);
-    out[c + 1] = Elem<T>::from_f32(v.y * r * gg.y);
-    out[c + 2] = Elem<T>::from_f32(v.z * r * gg.z);
-    out[c + 3] = Elem<T>::from_f32(v.w * r * gg.w);
+  for (int c = threadIdx.x * 8; c < Dp; c += kThreads * 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; i += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(row + c + i);
+      const float4 gg = *reinterpret_cast<const float4*>(g + c + i);
+      v[i] = x.x * r * gg.x;
+      v[i + 1] = x.y * r * gg.y;
+      v[i + 2] = x.z * r * gg.z;
+      v[i + 3] = x.w * r * gg.w;
+    }
+    for (int j = 0; j < k; ++j) store8(xp + (int64_t)inv[t * k + j] * Dp + c, v);
   }
 }
 
@@ -81,7 +101,8 @@ __device__ __forceinline__ void mx_store_block(const float (&v)[32], uint8_t* co
 // input. One thread per block after the row's sum of squares.
 __global__ __launch_bounds__(kThreads) void pool_norm_mx_kernel(const float* __restrict__ P,
                                                                 const float* __restrict__ g, int Dp,
-                                                                float eps, uint8_t* __restrict__ codes,
+                                                                float eps, const int32_t* __restrict__ inv,
+                                                                int k, uint8_t* __restrict__ codes,
                                                                 uint8_t* __restrict__ scales) {
   __shared__ float red[kThreads / kWave];
   const int t = blockIdx.x;
@@ -104,7 +125,16 @@ __global__ __launch_bounds__(kThreads) void pool_norm_mx_kernel(const float* __r
       v[i + 2] = x.z * r * gg.z;
       v[i + 3] = x.w * r * gg.w;
     }
-    mx_store_block(v, codes + (int64_t)t * Dp + 32 * b, scales + (int64_t)t * (Dp / 32) + b);
+    // one quantization, stored to the token's k sorted rows
+    uint8_t* c0 = codes + (int64_t)inv[t * k] * Dp + 32 * b;
+    uint8_t* s0 = scales + (int64_t)inv[t * k] * (Dp / 32) + b;
+    mx_store_block(v, c0, s0);
+    for (int j = 1; j < k; ++j) {
+      const int64_t pos = inv[t * k + j];
+      reinterpret_cast<uint4*>(codes + pos * Dp + 32 * b)[0] = reinterpret_cast<const uint4*>(c0)[0];
+      reinterpret_cast<uint4*>(codes + pos * Dp + 32 * b)[1] = reinterpret_cast<const uint4*>(c0)[1];
+      scales[pos * (Dp / 32) + b] = *s0;
+    }
   }
 }
 
@@ -162,22 +192,23 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
 
 }  // namespace
 
-hipError_t launch_pool_norm(const float* P, const float* g, int T, int Dp, float eps, void* xp,
-                            bool bf16, hipStream_t s) {
+hipError_t launch_pool_norm(const float* P, const float* g, int T, int Dp, float eps, const int32_t* inv,
+                            int k, void* xp, bool bf16, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (bf16)
-    hipLaunchKernelGGL(pool_norm_kernel<bf16_t>, dim3(T), dim3(kThreads), 0, s, P, g, Dp, eps,
+    hipLaunchKernelGGL(pool_norm_kernel<bf16_t>, dim3(T), dim3(kThreads), 0, s, P, g, Dp, eps, inv, k,
                        static_cast<bf16_t*>(xp));
   else
-    hipLaunchKernelGGL(pool_norm_kernel<float>, dim3(T), dim3(kThreads), 0, s, P, g, Dp, eps,
+    hipLaunchKernelGGL(pool_norm_kernel<float>, dim3(T), dim3(kThreads), 0, s, P, g, Dp, eps, inv, k,
                        static_cast<float*>(xp));
   return hipGetLastError();
 }
 
-hipError_t launch_pool_norm_mx(const float* P, const float* g, int T, int Dp, float eps, uint8_t* codes,
-                               uint8_t* scales, hipStream_t s) {
+hipError_t launch_pool_norm_mx(const float* P, const float* g, int T, int Dp, float eps, const int32_t* inv,
+                               int k, uint8_t* codes, uint8_t* scales, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(pool_norm_mx_kernel, dim3(T), dim3(kThreads), 0, s, P, g, Dp, eps, codes, scales);
+  hipLaunchKernelGGL(pool_norm_mx_kernel, dim3(T), dim3(kThreads), 0, s, P, g, Dp, eps, inv, k, codes,
+                     scales);
   return hipGetLastError();
 }
 

@@ -185,7 +185,6 @@ __global__ __launch_bounds__(64) void sort_scatter_kernel(SortParams p) {
     const int pos = p.offsets[e] + p.chunk_base[(int64_t)chunk * p.E + e] + __popcll(m & below);
     p.sorted_assign[pos] = a;
     p.inv[a] = pos;
-    p.row_token[pos] = t;
   }
 }
 

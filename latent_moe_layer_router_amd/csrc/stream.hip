@@ -87,8 +87,7 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int e, int gr
   for (int i = 0; i < 2 * NMT; ++i) {
     const int tr = 8 * i + lrow;
     const int pos = lo + (tr < m_e ? tr : m_e - 1);
-    const uint32_t src = (EPI == EPI_SWIGLU) ? (uint32_t)p.a_gather[pos] : (uint32_t)pos;
-    ao[i] = src * (uint32_t)(p.lda * 2) + (uint32_t)((lc ^ swz8(tr)) << 4);
+    ao[i] = (uint32_t)pos * (uint32_t)(p.lda * 2) + (uint32_t)((lc ^ swz8(tr)) << 4);
   }
 #define LMOE_ISSUE(c, SW, SA)                                                                   \
   {                                                                                            \
