@@ -36,6 +36,8 @@ constexpr int SB = BM * RB;           // bytes per operand per stage (16 KiB)
 // Fourth word of a raw buffer descriptor on CDNA (no swizzle, no stride,
 // 32-bit data format field set so that offsets are bytes).
 constexpr int kBufWord3 = 0x00020000;
+// A buffer offset past every extent used here (all below 2^31).
+constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // Four pipeline stages for A and B, each a separate LDS object so that the
 // compiler can tell the stages apart when it orders reads against the
@@ -142,12 +144,15 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
   const __amdgpu_buffer_rsrc_t rsB =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(Bt), (short)0, b_ext, kBufWord3);
   const int pos = lane & 3;
+  // Rows past the end (tail tiles) get an offset beyond every extent: the
+  // buffer load then reads nothing from memory (its lanes return zero), so a
+  // tile with few rows costs little more than its B slice. Those rows are
+  // never stored.
   auto a_off = [&](int r) -> uint32_t {
-    int m = m0 + r;
-    if (m >= m_end) m = m_end - 1;           // rows past the end load a valid row; never stored
-    const uint32_t src = (uint32_t)m;
+    const int m = m0 + r;
+    if (m >= m_end) return kOutOfRange;
     const uint32_t c = pos ^ (((r >> 1) ^ (r >> 3)) & 3);
-    return src * (uint32_t)(p.lda * 2) + c * 16;
+    return (uint32_t)m * (uint32_t)(p.lda * 2) + c * 16;
   };
   auto b_off = [&](int r) -> uint32_t {
     const int n = dense ? r : (EPI == EPI_SWIGLU) ? ((r < BNB / 2) ? (n0 + r) : (p.F + n0 + r - BNB / 2)) : (n0 + r);

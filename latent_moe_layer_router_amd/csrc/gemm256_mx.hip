@@ -44,6 +44,8 @@ constexpr int NT = 256;
 constexpr int RA = 128;               // bytes per A row per stage (128 fp8)
 constexpr int RBB = 64;               // bytes per B row per stage (128 fp4)
 constexpr int kBufWord3 = 0x00020000;   // raw buffer descriptor, fourth word (CDNA)
+// A buffer offset past every extent used here (all below 2^31).
+constexpr uint32_t kOutOfRange = 0x80000000u;
 
 #define LMOE_AS3 __attribute__((address_space(3)))
 
@@ -114,11 +116,10 @@ __global__ __launch_bounds__(NT, 1) void gemm256_mx_kernel(Gemm256MxParams p) {
       const_cast<uint8_t*>(p.B + (int64_t)e * p.N * (K / 2)), (short)0, p.N * (K / 2), kBufWord3);
   const __amdgpu_buffer_rsrc_t rBs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.Bs + (int64_t)e * p.N * (K / 32)), (short)0, p.N * (K / 32), kBufWord3);
-  auto a_src = [&](int r) -> uint32_t {     // A row (sorted position) of tile row r
-    int m = m0 + r;
-    if (m >= m_end) m = m_end - 1;           // rows past the end load a valid row; never stored
-    return (uint32_t)m;
-  };
+  // A row (sorted position) of tile row r. Rows past the end (tail tiles) get
+  // offsets beyond every extent: their loads read nothing from memory; they are
+  // never stored.
+  auto a_live = [&](int r) { return m0 + r < m_end; };
   auto b_row = [&](int r) -> uint32_t {     // B row of tile row r
     return (EPI == EPI_SWIGLU) ? (uint32_t)((r < BNB / 2) ? (n0 + r) : (p.F + n0 + r - BNB / 2))
                                : (uint32_t)(n0 + r);
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(NT, 1) void gemm256_mx_kernel(Gemm256MxParams p) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = wave * 64 + 8 * j + (lane >> 3);
-    ga[j] = a_src(r) * (uint32_t)K + (uint32_t)(((lane & 7) ^ fa(r)) << 4);
+    ga[j] = a_live(r) ? (uint32_t)(m0 + r) * (uint32_t)K + (uint32_t)(((lane & 7) ^ fa(r)) << 4) : kOutOfRange;
   }
   // B: load j moves rows wave*64 + 16 j + lane/4, lane position lane % 4.
   uint32_t gb[4];
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(NT, 1) void gemm256_mx_kernel(Gemm256MxParams p) {
     gb[j] = b_row(r) * (uint32_t)(K / 2) + (uint32_t)(((lane & 3) ^ fb(r)) << 4);
   }
   // Scales: one load each for A and B, row wave*64 + lane, 16 bytes per group.
-  const uint32_t gsa = a_src(wave * 64 + lane) * (uint32_t)(K / 32);
+  const uint32_t gsa = a_live(wave * 64 + lane) ? (uint32_t)(m0 + wave * 64 + lane) * (uint32_t)(K / 32) : kOutOfRange;
   const uint32_t gsb = b_row(wave * 64 + lane) * (uint32_t)(K / 32);
 
 #define LMOE_DATA(st, SA, SB)                                                                    \
