@@ -221,6 +221,15 @@ lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, lmoe_hand
     delete h;
     return fail(LMOE_E_NOMEM, msg);
   }
+  // The top-k kernel ORs into the chunk masks; the sort clears them after use,
+  // so they start at zero once here.
+  if (hipMemset(h->ws + h->plan.masks, 0, h->plan.chunk_base - h->plan.masks) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(h->ws);
+    delete h;
+    return fail(LMOE_E_HIP, "clearing the workspace failed");
+  }
   h->timing = false;
   memset(h->acc_ms, 0, sizeof(h->acc_ms));
   h->n_timed = 0;

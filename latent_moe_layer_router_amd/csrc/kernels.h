@@ -155,7 +155,8 @@ struct Gemm256MxParams {
 hipError_t launch_gemm256_mx(const Gemm256MxParams& p, EpiKind epi, hipStream_t s);
 
 // Router top-k + softmax; also builds, per chunk of 64 tokens, a bitmask of
-// the chunk's tokens that selected each expert.
+// the chunk's tokens that selected each expert (ORed into chunk_masks, which
+// must be zero on entry; launch_sort leaves them zero again).
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                        uint64_t* chunk_masks, hipStream_t s);
 
@@ -163,7 +164,7 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 struct SortParams {
   const int32_t* ids;
   const float* topk_w;
-  const uint64_t* chunk_masks;  // [n_chunks][E]
+  uint64_t* chunk_masks;        // [n_chunks][E]; cleared again by the sort
   int32_t* chunk_base;          // [n_chunks][E] scratch
   int32_t* counts;              // [E]
   int32_t* offsets;             // [E+1]

@@ -46,6 +46,20 @@ __device__ __forceinline__ void store8(float* dst, const float (&v)[8]) {
   reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
   reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
+// Load 8 consecutive values (one 16-byte bf16 load, or two fp32).
+__device__ __forceinline__ void load8(const bf16_t* src, float (&v)[8]) {
+  const uint4 q = *reinterpret_cast<const uint4*>(src);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* src, float (&v)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(src)[0], b = reinterpret_cast<const float4*>(src)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
 
 // The normalized row goes to the token's k rows of the sorted (expert-major)
 // order, inv[t*k + j], so that the expert GEMMs read their rows contiguously.
@@ -174,19 +188,22 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   __syncthreads();
   const T* y = static_cast<const T*>(p.y);
   T* u = static_cast<T*>(p.u) + (int64_t)t * p.Dp;
-  for (int c = threadIdx.x * 4; c < p.Dp; c += kThreads * 4) {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  // 8 consecutive columns per thread (16-byte bf16 loads and stores); the k
+  // terms of each column are added in slot order.
+  for (int c = threadIdx.x * 8; c < p.Dp; c += kThreads * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < p.k; ++j) {
-      const T* yr = y + (int64_t)pos[j] * p.Dp + c;
-      const float4 gg = *reinterpret_cast<const float4*>(p.g_expert + (int64_t)eid[j] * p.Dp + c);
+      float yv[8];
+      load8(y + (int64_t)pos[j] * p.Dp + c, yv);
+      const float* gr = p.g_expert + (int64_t)eid[j] * p.Dp + c;
+      const float4 g0 = *reinterpret_cast<const float4*>(gr);
+      const float4 g1 = *reinterpret_cast<const float4*>(gr + 4);
+      const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
       const float s = scale[j];
-      acc[0] += s * gg.x * Elem<T>::to_f32(yr[0]);
-      acc[1] += s * gg.y * Elem<T>::to_f32(yr[1]);
-      acc[2] += s * gg.z * Elem<T>::to_f32(yr[2]);
-      acc[3] += s * gg.w * Elem<T>::to_f32(yr[3]);
-    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) u[c + i] = Elem<T>::from_f32(acc[i]);
+      for (int i = 0; i < 8; ++i) acc[i] += s * gg[i] * yv[i];
+    }
+    store8(u + c, acc);
   }
 }
 

@@ -8,8 +8,9 @@
 //
 // Permutation (blog, "AMD support": the atomic-add expert sort became an LDS
 // kernel on MI355X). Tokens are taken in chunks of 64, one bit per token:
-//  1. while doing top-k, the chunk's workgroup ORs bit (t % 64) into an LDS
-//     mask per expert, then writes the chunk's masks out;
+//  1. while doing top-k, each token ORs bit (t % 64) into its chunk's mask of
+//     every expert it selected (global atomic OR; the masks start at zero and
+//     step 3 clears them again after use);
 //  2. a single workgroup turns the masks into per-(chunk, expert) bases
 //     (running sums of popcounts over chunks) and the per-expert offsets
 //     (exclusive prefix sum over experts with wavefront prefix sums), and lays
@@ -42,75 +43,72 @@ __device__ __forceinline__ float wave_max(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// One workgroup (16 waves) per chunk of 64 tokens; each wave selects for 4
-// tokens. Per round: every lane keeps its best untaken logit (lowest index on
-// ties), the wave maximum comes from wave_max, and the winner is the lowest
-// index among the lanes holding that maximum (usually a single lane).
-__global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ logits, int T, int E,
-                                                     int k, int32_t* __restrict__ ids,
-                                                     float* __restrict__ w,
-                                                     uint64_t* __restrict__ chunk_masks) {
-  __shared__ unsigned long long masks[kMaxE];
-  const int chunk = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) masks[e] = 0ull;
-  __syncthreads();
+// One wave per token (4 per workgroup), so that even a decode-sized batch
+// spreads over the GPU: k rounds of a wave arg-max, each on the lanes' best
+// untaken logits (lowest index on ties) with the wave maximum from wave_max and
+// the winner the lowest index among the lanes holding it (usually one lane).
+// The token's bit goes into its chunk's mask of each selected expert with a
+// global atomic OR, which gives the same masks in any order.
+constexpr int kTopkWaves = 4;
 
+__global__ __launch_bounds__(kTopkWaves * 64) void topk_kernel(const float* __restrict__ logits, int T,
+                                                               int E, int k, int32_t* __restrict__ ids,
+                                                               float* __restrict__ w,
+                                                               uint64_t* __restrict__ chunk_masks) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kTopkWaves + (threadIdx.x >> 6);
+  if (t >= T) return;                        // whole waves
   const int per = (E + kWave - 1) / kWave;
-  for (int tl = wave; tl < kChunk; tl += blockDim.x / kWave) {
-    const int t = chunk * kChunk + tl;
-    if (t >= T) break;
-    float v[kMaxPerLane];
-    unsigned taken = 0;
+  float v[kMaxPerLane];
+  unsigned taken = 0;
 #pragma unroll
-    for (int q = 0; q < kMaxPerLane; ++q) {
-      const int e = q * kWave + lane;
-      // NaN counts as -inf, so that every round selects a valid expert index.
-      const float x = (q < per && e < E) ? logits[(int64_t)t * E + e] : -INFINITY;
-      v[q] = (x != x) ? -INFINITY : x;
-      if (!(q < per && e < E)) taken |= 1u << q;
-    }
-    float sel_v = 0.f, top = 0.f, den = 0.f;
-    int my_id = -1;  // lane j < k keeps the j-th selected expert
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int bi = 0x7FFFFFFF;
+  for (int q = 0; q < kMaxPerLane; ++q) {
+    const int e = q * kWave + lane;
+    const bool ok = q < per && e < E;
+    // unconditional load from a clamped (valid) address, masked afterwards
+    const float x = logits[(int64_t)t * E + (e < E ? e : E - 1)];
+    // NaN counts as -inf, so that every round selects a valid expert index.
+    v[q] = (!ok || x != x) ? -INFINITY : x;
+    if (!ok) taken |= 1u << q;
+  }
+  float sel_v = 0.f, top = 0.f, den = 0.f;
+  int my_id = -1;                            // lane j < k keeps the j-th selected expert
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
 #pragma unroll
-      for (int q = 0; q < kMaxPerLane; ++q)
-        if (!(taken >> q & 1u) && v[q] > bv) {   // ascending q: ties keep the lower index
-          bv = v[q];
-          bi = q * kWave + lane;
-        }
-      const float vmax = wave_max(bv);
-      const uint64_t tie = __ballot(bi != 0x7FFFFFFF && bv == vmax);
-      int win;
-      if (__popcll(tie) == 1) {
-        win = __builtin_amdgcn_readlane(bi, __ffsll((unsigned long long)tie) - 1);
-      } else {                                   // several lanes hold the maximum
-        win = 0x7FFFFFFF;
-        for (uint64_t m = tie; m; m &= m - 1) {
-          const int l = __ffsll((unsigned long long)m) - 1;
-          const int c = __builtin_amdgcn_readlane(bi, l);
-          win = c < win ? c : win;
-        }
+    for (int q = 0; q < kMaxPerLane; ++q)
+      if (!(taken >> q & 1u) && v[q] > bv) {   // ascending q: ties keep the lower index
+        bv = v[q];
+        bi = q * kWave + lane;
       }
-      if ((win & 63) == lane) taken |= 1u << (win >> 6);
-      if (j == 0) top = vmax;
-      den += expf(vmax - top);
-      if (lane == j) {
-        my_id = win;
-        sel_v = vmax;
+    const float vmax = wave_max(bv);
+    const uint64_t tie = __ballot(bi != 0x7FFFFFFF && bv == vmax);
+    int win;
+    if (__popcll(tie) == 1) {
+      win = __builtin_amdgcn_readlane(bi, __ffsll((unsigned long long)tie) - 1);
+    } else {                                   // several lanes hold the maximum
+      win = 0x7FFFFFFF;
+      for (uint64_t m = tie; m; m &= m - 1) {
+        const int l = __ffsll((unsigned long long)m) - 1;
+        const int c = __builtin_amdgcn_readlane(bi, l);
+        win = c < win ? c : win;
       }
     }
-    if (lane < k) {
-      ids[(int64_t)t * k + lane] = my_id;
-      w[(int64_t)t * k + lane] = expf(sel_v - top) / den;
-      atomicOr(&masks[my_id], 1ull << tl);
+    if ((win & 63) == lane) taken |= 1u << (win >> 6);
+    if (j == 0) top = vmax;
+    den += expf(vmax - top);
+    if (lane == j) {
+      my_id = win;
+      sel_v = vmax;
     }
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x)
-    chunk_masks[(int64_t)chunk * E + e] = masks[e];
+  if (lane < k) {
+    ids[(int64_t)t * k + lane] = my_id;
+    w[(int64_t)t * k + lane] = expf(sel_v - top) / den;
+    atomicOr(reinterpret_cast<unsigned long long*>(chunk_masks) + (int64_t)(t / kChunk) * E + my_id,
+             1ull << (t % kChunk));
+  }
 }
 
 // Exclusive prefix sum over the block (blockDim.x a multiple of 64, <= 1024).
@@ -176,26 +174,30 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(SortParams p) {
 __global__ __launch_bounds__(64) void sort_scatter_kernel(SortParams p) {
   const int chunk = blockIdx.x, lane = threadIdx.x;
   const int t = chunk * kChunk + lane;
-  if (t >= p.T) return;
-  const uint64_t below = lanemask_lt(lane);
-  for (int j = 0; j < p.k; ++j) {
-    const int a = t * p.k + j;
-    const int e = p.ids[a];
-    const uint64_t m = p.chunk_masks[(int64_t)chunk * p.E + e];
-    const int pos = p.offsets[e] + p.chunk_base[(int64_t)chunk * p.E + e] + __popcll(m & below);
-    p.sorted_assign[pos] = a;
-    p.inv[a] = pos;
+  if (t < p.T) {
+    const uint64_t below = lanemask_lt(lane);
+    for (int j = 0; j < p.k; ++j) {
+      const int a = t * p.k + j;
+      const int e = p.ids[a];
+      const uint64_t m = p.chunk_masks[(int64_t)chunk * p.E + e];
+      const int pos = p.offsets[e] + p.chunk_base[(int64_t)chunk * p.E + e] + __popcll(m & below);
+      p.sorted_assign[pos] = a;
+      p.inv[a] = pos;
+    }
   }
+  // The chunk's masks are read only here (after the scan): clear them for the
+  // next call's atomic ORs, once every lane has read its own.
+  __syncthreads();
+  for (int e = lane; e < p.E; e += kChunk) p.chunk_masks[(int64_t)chunk * p.E + e] = 0ull;
 }
 
 }  // namespace
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                        uint64_t* chunk_masks, hipStream_t s) {
-  const int n_chunks = (T + kChunk - 1) / kChunk;
-  if (n_chunks == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(n_chunks), dim3(1024), 0, s, logits, T, E, k, ids, w,
-                     chunk_masks);
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_kernel, dim3((T + kTopkWaves - 1) / kTopkWaves), dim3(kTopkWaves * 64), 0, s,
+                     logits, T, E, k, ids, w, chunk_masks);
   return hipGetLastError();
 }
 
