@@ -81,8 +81,8 @@ Plan make_plan(const lmoe_config& c) {
   int64_t part = 0;
   if (c.act_dtype == LMOE_BF16) {
     const int64_t Ts = Tm < dense_stream_max_tokens() ? Tm : dense_stream_max_tokens();
-    const int64_t a = Ts * (Dp + E) * dense_stream_slices(c.d_model);
-    const int64_t b = Ts * (int64_t)c.d_model * dense_stream_slices(c.d_pooled);
+    const int64_t a = dense_stream_part_floats((int)Ts, Dp + E, c.d_model);
+    const int64_t b = dense_stream_part_floats((int)Ts, c.d_model, c.d_pooled);
     part = (a > b ? a : b) * 4;
   }
   p.part = grow(cur, part);
@@ -369,7 +369,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   // Small batches: the dense projections stream their weights with split-K.
   const bool dense_stream = bf16 && T <= dense_stream_max_tokens();
   float* part = reinterpret_cast<float*>(ws + pl.part);
-  const int slices_in = dense_stream_slices(D), slices_un = dense_stream_slices(Dp);
+  const int slices_in = dense_stream_slices(Dp + E, D), slices_un = dense_stream_slices(D, Dp);
 
   // Larger batches: the dense projections on 256 x 256 tiles (bf16; K a
   // multiple of 128, the pooler's rows a multiple of 256, 32-bit offsets).

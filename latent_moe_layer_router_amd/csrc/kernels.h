@@ -68,7 +68,8 @@ int stream_max_rows();
 hipError_t launch_stream(const StreamParams& p, EpiKind epi, hipStream_t s);
 
 // Dense C = A . B^T for T <= dense_stream_max_tokens() rows (bf16), split over
-// K-slices into fp32 partials, then reduced in slice order.
+// K-slices into fp32 partials, then reduced in slice order. n_split must be a
+// multiple of 64.
 struct DenseStreamParams {
   const void* A;
   int64_t lda;
@@ -77,8 +78,8 @@ struct DenseStreamParams {
   int n_split;
   int64_t ldb;
   int T, N, K;
-  int slices;                  // from dense_stream_slices(K)
-  float* part;                 // [slices][T][N] scratch
+  int slices;                  // from dense_stream_slices(N, K)
+  float* part;                 // dense_stream_part_floats(T, N, K) floats of scratch
   void* out0;                  // [T][ldo0] fp32, or bf16 if out0_bf16
   int64_t ldo0;
   int out0_bf16;
@@ -87,7 +88,8 @@ struct DenseStreamParams {
   const float* bias1;
 };
 int dense_stream_max_tokens();
-int dense_stream_slices(int K);   // 0 if K does not split evenly
+int dense_stream_slices(int N, int K);               // K a multiple of 64
+int64_t dense_stream_part_floats(int T, int N, int K);
 hipError_t launch_dense_stream(const DenseStreamParams& p, hipStream_t s);
 
 // Large-tile (256 x 256) GEMM (bf16). Grouped (M == 0), for experts with many

@@ -202,71 +202,133 @@ __global__ __launch_bounds__(64) void stream_kernel(StreamParams p) {
 }
 
 // Dense projections of a small batch (router + pooler, unpooler at decode
-// sizes): one wave per (group of 64 weight rows, K-slice), all T <= 128 tokens
-// held as up to 8 MFMA row tiles, weights streamed once. Each wave writes its
-// fp32 partial sums to part[slice][t][n]; splitk_reduce adds the slices in
-// slice order (deterministic), then applies the bias and the output type.
-constexpr int MTD = 8;
-constexpr int UD = 2;
+// sizes). A workgroup of 4 waves takes 128 weight rows (32 per wave) over one
+// K-slice and all T <= 128 tokens: both operands reach LDS through direct
+// global-to-LDS loads in a four-stage pipeline of 64-wide K-steps; the token
+// slice is loaded once per workgroup and shared by its waves, each weight byte
+// is read once. Each workgroup writes its fp32 partial sums to
+// part[slice][t][n] (n padded to whole groups); splitk_reduce adds the slices
+// in slice order (deterministic), then applies the bias and the output type.
+constexpr int DW = 4;                  // waves per workgroup
+constexpr int DR = 32;                 // weight rows per wave
+constexpr int DS = 4;                  // pipeline stages
+constexpr int DN = DW * DR;            // weight rows per workgroup
+constexpr int MTD = 8;                 // token tiles of 16 (T <= 128)
+constexpr int DSW = DW * DR * 128;     // weight bytes per stage
+constexpr int DST = 128 * 128;         // token bytes per stage
+constexpr int WJ = DR / 8, LPS = WJ + 4;
+constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past every extent
 
-__global__ __launch_bounds__(64) void dense_stream_kernel(DenseStreamParams p) {
+__shared__ __attribute__((aligned(16))) unsigned char dw0[DSW], dt0[DST], dw1[DSW], dt1[DST],
+    dw2[DSW], dt2[DST], dw3[DSW], dt3[DST];
+
+__global__ __launch_bounds__(DW * 64) void dense_stream_kernel(DenseStreamParams p) {
   const int grp = blockIdx.x / p.slices, sl = blockIdx.x % p.slices;
-  const int lane = threadIdx.x, r16 = lane & 15, kq = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, kq = lane >> 4, lrow = lane >> 3, lc = lane & 7;
   const int n_mt = (p.T + 15) >> 4;
-  const int kspan = p.K / p.slices, k0 = sl * kspan;
-  const bf16_t* brow[4];
+  // stages of 64 K-columns: slice sl takes [c0, c1) of nct
+  const int nct = p.K / KC;
+  const int c0 = (int)((int64_t)nct * sl / p.slices), c1 = (int)((int64_t)nct * (sl + 1) / p.slices);
+  const int nc = c1 - c0;
+
+  // This wave's 32 weight rows lie in B0 or in B1 (n_split is a multiple of 64).
+  const int nw = grp * DN + wave * DR;
+  const bool in1 = nw >= p.n_split;
+  const bf16_t* Bw = in1 ? static_cast<const bf16_t*>(p.B1) + (int64_t)(nw - p.n_split) * p.ldb
+                         : static_cast<const bf16_t*>(p.B0) + (int64_t)nw * p.ldb;
+  int valid = (in1 ? p.N : p.n_split) - nw;  // rows of this wave that exist
+  valid = valid < 0 ? 0 : (valid > DR ? DR : valid);
+  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(Bw), (short)0, valid * (int)p.ldb * 2, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.A), (short)0, p.T * (int)p.lda * 2, kBufWord3);
+  // Load j of a stage moves LDS rows 32*wave + 8j .. +7 of both operands
+  // (lane: row + lrow, stored chunk position lc = logical chunk ^ swz8(row)).
+  uint32_t wo[WJ], to[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int n = grp * 64 + t * 16 + r16;
-    const bf16_t* b;
-    if (n < p.n_split) b = static_cast<const bf16_t*>(p.B0) + (int64_t)n * p.ldb;
-    else if (n < p.N) b = static_cast<const bf16_t*>(p.B1) + (int64_t)(n - p.n_split) * p.ldb;
-    else b = static_cast<const bf16_t*>(p.B0);            // past N: a valid row, never stored
-    brow[t] = b + k0 + kq * 8;
+  for (int j = 0; j < WJ; ++j) {
+    const int lr = 8 * j + lrow;
+    const uint32_t ch = (uint32_t)((lc ^ swz8(lr)) << 4);
+    wo[j] = lr < valid ? (uint32_t)lr * (uint32_t)(p.ldb * 2) + ch : kOutOfRange;
   }
-  const bf16_t* arow[MTD];
 #pragma unroll
-  for (int mt = 0; mt < MTD; ++mt) {
-    int i = mt * 16 + r16;
-    if (i >= p.T) i = p.T - 1;
-    arow[mt] = static_cast<const bf16_t*>(p.A) + (int64_t)i * p.lda + k0 + kq * 8;
+  for (int j = 0; j < 4; ++j) {
+    const int r = wave * 32 + 8 * j + lrow;
+    const uint32_t ch = (uint32_t)((lc ^ swz8(r)) << 4);
+    to[j] = r < p.T ? (uint32_t)r * (uint32_t)(p.lda * 2) + ch : kOutOfRange;
   }
-  f32x4 acc[MTD][4];
+  const int dbase = wave * DR * 128, tbase = wave * 32 * 128;
+#define LMOE_DISSUE(c, SW, ST)                                                                   \
+  {                                                                                             \
+    const int ko_ = (c0 + (c)) * KC * 2;                                                        \
+    _Pragma("unroll") for (int j = 0; j < WJ; ++j)                                              \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (LMOE_AS3 void*)((SW) + dbase + 1024 * j), 16, \
+                                               (int)wo[j], ko_, 0, 2);                          \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                               \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (LMOE_AS3 void*)((ST) + tbase + 1024 * j), 16, \
+                                               (int)to[j], ko_, 0, 0);                          \
+  }
+  constexpr int NTW = DR / 16;
+  f32x4 acc[MTD][NTW];
 #pragma unroll
   for (int mt = 0; mt < MTD; ++mt)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < kspan; k += 32 * UD) {
-    uint4 b[UD][4], a[UD][MTD];
+    for (int t = 0; t < NTW; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int fo[2];
 #pragma unroll
-    for (int u = 0; u < UD; ++u)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) b[u][t] = load_stream16(brow[t] + k + 32 * u);
-#pragma unroll
-    for (int u = 0; u < UD; ++u)
-#pragma unroll
-      for (int mt = 0; mt < MTD; ++mt)
-        if (mt < n_mt) a[u][mt] = *reinterpret_cast<const uint4*>(arow[mt] + k + 32 * u);
-#pragma unroll
-    for (int u = 0; u < UD; ++u)
-#pragma unroll
-      for (int mt = 0; mt < MTD; ++mt)
-        if (mt < n_mt)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) mfma16(a[u][mt], b[u][t], acc[mt][t]);
+  for (int u = 0; u < 2; ++u) fo[u] = r16 * 128 + (((4 * u + kq) ^ swz8(r16)) << 4);
+  const int wrow = wave * DR * 128;              // this wave's weight tiles in a stage
+#define LMOE_DCOMPUTE(SW, ST)                                                                    \
+  _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                               \
+    uint4 b[NTW];                                                                               \
+    _Pragma("unroll") for (int t = 0; t < NTW; ++t)                                             \
+      b[t] = *reinterpret_cast<const uint4*>((SW) + wrow + t * 2048 + fo[u]);                   \
+    _Pragma("unroll") for (int mt = 0; mt < MTD; ++mt)                                          \
+      if (mt < n_mt) {                                                                          \
+        const uint4 a = *reinterpret_cast<const uint4*>((ST) + mt * 2048 + fo[u]);              \
+        _Pragma("unroll") for (int t = 0; t < NTW; ++t) mfma16(a, b[t], acc[mt][t]);            \
+      }                                                                                         \
   }
-  float* part = p.part + (int64_t)sl * p.T * p.N;
+  // Stage c: this wave's loads of stage c have landed (at most the two later
+  // stages' 16 loads outstanding) and its reads of stage c - 1 are done; after
+  // the barrier every wave's part of stage c is in LDS and nobody reads the
+  // buffer of stage c - 1 any more, which then takes stage c + 3.
+#define LMOE_DSTAGE(c, SW, ST, NW, NT)                                                           \
+  if ((c) < nc) {                                                                               \
+    __builtin_amdgcn_s_waitcnt(vm_wait((DS - 2) * LPS) & ~(15 << 8));                            \
+    __builtin_amdgcn_s_barrier();                                                               \
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");                            \
+    LMOE_DISSUE(((c) + DS - 1 < nc ? (c) + DS - 1 : nc - 1), NW, NT)                             \
+    LMOE_DCOMPUTE(SW, ST)                                                                       \
+  }
+  LMOE_DISSUE(0, dw0, dt0)
+  LMOE_DISSUE((1 < nc ? 1 : nc - 1), dw1, dt1)
+  LMOE_DISSUE((2 < nc ? 2 : nc - 1), dw2, dt2)
+  for (int c = 0; c < nc; c += 4) {
+    LMOE_DSTAGE(c, dw0, dt0, dw3, dt3)
+    LMOE_DSTAGE(c + 1, dw1, dt1, dw0, dt0)
+    LMOE_DSTAGE(c + 2, dw2, dt2, dw1, dt1)
+    LMOE_DSTAGE(c + 3, dw3, dt3, dw2, dt2)
+  }
+#undef LMOE_DSTAGE
+#undef LMOE_DCOMPUTE
+#undef LMOE_DISSUE
+  __builtin_amdgcn_s_waitcnt(0);             // the last (repeated) loads have landed
+
+  // partials: acc[mt][t][v] is token 16 mt + 4 kq + v, column nw + 16 t + r16
+  const int np = p.slices > 0 ? ((p.N + DN - 1) / DN) * DN : 0;
+  float* part = p.part + (int64_t)sl * p.T * np;
 #pragma unroll
   for (int mt = 0; mt < MTD; ++mt) {
     if (mt >= n_mt) break;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int i = mt * 16 + 4 * kq + v;
-      if (i >= p.T) continue;
+      if (i < p.T) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int n = grp * 64 + t * 16 + r16;
-        if (n < p.N) part[(int64_t)i * p.N + n] = acc[mt][t][v];
+        for (int t = 0; t < NTW; ++t) part[(int64_t)i * np + nw + t * 16 + r16] = acc[mt][t][v];
       }
     }
   }
@@ -274,19 +336,29 @@ __global__ __launch_bounds__(64) void dense_stream_kernel(DenseStreamParams p) {
 
 // out = sum over slices of part[slice][t][n] (slice order), split like EPI_F32:
 // columns [0, n_split) -> out0 (fp32, or bf16 if out0_bf16), [n_split, N) -> out1 + bias1.
+// One thread per 4 consecutive columns of a token.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(DenseStreamParams p) {
-  const int64_t total = (int64_t)p.T * p.N;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    float s = 0.f;
-    for (int sl = 0; sl < p.slices; ++sl) s += p.part[sl * total + i];
-    const int t = (int)(i / p.N), n = (int)(i % p.N);
-    if (n < p.n_split) {
-      if (p.out0_bf16) static_cast<bf16_t*>(p.out0)[(int64_t)t * p.ldo0 + n] = f32_to_bf16(s);
-      else static_cast<float*>(p.out0)[(int64_t)t * p.ldo0 + n] = s;
-    } else {
-      const int c = n - p.n_split;
-      static_cast<float*>(p.out1)[(int64_t)t * p.ldo1 + c] = s + (p.bias1 ? p.bias1[c] : 0.f);
+  const int np = ((p.N + DN - 1) / DN) * DN;
+  const int64_t total = (int64_t)p.T * np, q = total / 4;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < q; i += (int64_t)gridDim.x * blockDim.x) {
+    float4 s = *reinterpret_cast<const float4*>(p.part + 4 * i);
+    for (int sl = 1; sl < p.slices; ++sl) {
+      const float4 v = *reinterpret_cast<const float4*>(p.part + sl * total + 4 * i);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    const int t = (int)(4 * i / np), n0 = (int)(4 * i % np);
+    const float sv[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int n = n0 + e;
+      if (n >= p.N) break;
+      if (n < p.n_split) {
+        if (p.out0_bf16) static_cast<bf16_t*>(p.out0)[(int64_t)t * p.ldo0 + n] = f32_to_bf16(sv[e]);
+        else static_cast<float*>(p.out0)[(int64_t)t * p.ldo0 + n] = sv[e];
+      } else {
+        const int c = n - p.n_split;
+        static_cast<float*>(p.out1)[(int64_t)t * p.ldo1 + c] = sv[e] + (p.bias1 ? p.bias1[c] : 0.f);
+      }
     }
   }
 }
@@ -296,21 +368,27 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(DenseStreamParams p)
 int stream_max_rows() { return MT * 16; }
 int dense_stream_max_tokens() { return MTD * 16; }
 
-int dense_stream_slices(int K) {
-  int s = K / 512;
+// Slices for an N x K projection: about one workgroup per CU (256), at least one
+// 64-wide K-step per slice.
+int dense_stream_slices(int N, int K) {
+  const int groups = (N + DN - 1) / DN;
+  int s = 256 / groups;
   if (s < 1) s = 1;
-  while (s > 1 && K % (s * 32 * UD) != 0) --s;
-  return K % (s * 32 * UD) == 0 ? s : 0;
+  if (s > K / KC) s = K / KC;
+  return s;
+}
+int64_t dense_stream_part_floats(int T, int N, int K) {
+  return (int64_t)dense_stream_slices(N, K) * T * (((N + DN - 1) / DN) * DN);
 }
 
 hipError_t launch_dense_stream(const DenseStreamParams& p, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
-  const int groups = (p.N + 63) / 64;
-  hipLaunchKernelGGL(dense_stream_kernel, dim3(groups * p.slices), dim3(64), 0, s, p);
+  const int groups = (p.N + DN - 1) / DN;
+  hipLaunchKernelGGL(dense_stream_kernel, dim3(groups * p.slices), dim3(DW * 64), 0, s, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int64_t total = (int64_t)p.T * p.N;
-  const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+  const int64_t q = (int64_t)p.T * (((p.N + DN - 1) / DN) * DN) / 4;
+  const int blocks = (int)((q + 255) / 256 < 2048 ? (q + 255) / 256 : 2048);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
