@@ -44,6 +44,7 @@ def load(path: str = LIB_PATH):
         "orc_expert_assign": [_P, _I, _P, _P, _I, _I, _P, _P, _P, _P, _I, _P, _D, _I, _I, _P, _P],
         "orc_mx_quant_e4m3": [_P, _I, _P, _P, _P],
         "orc_mx_quant_e2m1": [_P, _I, _P, _P, _P],
+        "orc_nvfp4_to_mxfp4": [_P, _P, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -170,6 +171,21 @@ class Oracle:
         self.lib.orc_mx_quant_e2m1(v.ctypes.data, n, packed.ctypes.data, scales.ctypes.data,
                                    deq.ctypes.data)
         return packed, scales, deq
+
+    def nvfp4_to_mxfp4(self, codes, scales16, g):
+        """codes [M][R][C/2] u8, scales16 [M][R][C/16] u8, g [M] f32 ->
+        (codes [M][R][C/2], scales [M][R][C/32]) of the MXFP4 re-encoding."""
+        codes = self._c(codes, np.uint8)
+        scales16 = self._c(scales16, np.uint8)
+        g = self._c(g, np.float32)
+        M, R, half = codes.shape
+        C = 2 * half
+        assert scales16.shape == (M, R, C // 16) and g.shape == (M,) and C % 32 == 0
+        oc = np.empty_like(codes)
+        os_ = np.empty((M, R, C // 32), np.uint8)
+        self.lib.orc_nvfp4_to_mxfp4(codes.ctypes.data, scales16.ctypes.data, g.ctypes.data, M, R, C,
+                                    oc.ctypes.data, os_.ctypes.data)
+        return oc, os_
 
     def round_bf16(self, v: float) -> float:
         return self.lib.orc_round_bf16(float(v))

@@ -201,6 +201,62 @@ void orc_mx_quant_e2m1(const double* v, int n, uint8_t* packed, uint8_t* scales,
   }
 }
 
+/* ---------------------------------------------------------------------------
+ * NVFP4 -> MXFP4 requantization of expert weights at load.
+ *
+ * NVFP4 (blog, "NVFP4 as a third MMA type"): dense E2M1 values with one UE4M3
+ * block scale per 16 elements (instead of MXFP4's one UE8M0 per 32); a stored
+ * checkpoint also carries one FP32 scale per weight matrix. The blog's "AMD
+ * support" section serves the NVFP4 checkpoint on MI355X through the MXFP4
+ * quantization path and reports an "NVFP4 Requant" accuracy column, i.e. the
+ * NVFP4 weights are re-encoded as MXFP4 for the MI355X kernels.
+ *
+ * Reading (the pages give no formula): each element's NVFP4 value
+ * e2m1(code) * ue4m3(scale16) * g is formed in FP32 (the product of the two
+ * minifloats is exact; the multiplication by the FP32 matrix scale g rounds to
+ * nearest-even), then every 32-element block is MX-quantized exactly as
+ * orc_mx_quant_e2m1 does. The block-scale byte is unsigned (its top bit is
+ * ignored). A block whose scales or g are NaN (UE4M3 0x7F, non-finite g), or
+ * whose values overflow FP32, gets the E8M0 NaN scale 0xFF and zero codes.
+ *
+ * codes [n_mats][rows][cols/2] (element 2i in the low nibble), scales16
+ * [n_mats][rows][cols/16], g [n_mats] -> out_codes [n_mats][rows][cols/2],
+ * out_scales [n_mats][rows][cols/32]; cols a multiple of 32.
+ * ------------------------------------------------------------------------- */
+void orc_nvfp4_to_mxfp4(const uint8_t* codes, const uint8_t* scales16, const float* g,
+                        int64_t n_mats, int64_t rows, int64_t cols, uint8_t* out_codes,
+                        uint8_t* out_scales) {
+  const int64_t nb = cols / 32;
+  for (int64_t m = 0; m < n_mats; ++m) {
+    const float gm = g[m];
+    for (int64_t r = 0; r < rows; ++r) {
+      const int64_t row = m * rows + r;
+      for (int64_t b = 0; b < nb; ++b) {
+        double v[32];
+        int bad = !isfinite(gm);
+        for (int i = 0; i < 32; ++i) {
+          const int64_t k = 32 * b + i;
+          const uint8_t byte = codes[row * (cols / 2) + k / 2];
+          const uint8_t c = (k % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+          const uint8_t sc = scales16[row * (cols / 16) + k / 16] & 0x7F;
+          if (sc == 0x7F) bad = 1;
+          const float p = (float)orc_e2m1_value(c) * (float)orc_e4m3_value(sc);
+          const float x = p * gm;
+          if (!isfinite(x)) bad = 1;
+          v[i] = (double)x;
+        }
+        uint8_t* oc = out_codes + row * (cols / 2) + 16 * b;
+        if (bad) {
+          for (int i = 0; i < 16; ++i) oc[i] = 0;
+          out_scales[row * nb + b] = 0xFF;
+        } else {
+          orc_mx_quant_e2m1(v, 32, oc, out_scales + row * nb + b, NULL);
+        }
+      }
+    }
+  }
+}
+
 /* Row r of an expert weight matrix with K columns, dequantized into out[K]. */
 static void load_row(const void* w, const uint8_t* scales, int dt, size_t r, int K, double* out) {
   if (dt == ORC_MXFP4) {

@@ -377,6 +377,88 @@ def pin_mx_codec(O):
     assert np.array_equal(packed, codes_s.ravel()) and np.array_equal(scales, scales_s.ravel())
 
 
+def nvfp4_block(codes16x2, sc0, sc1):
+    """One 32-element NVFP4 block: 32 E2M1 codes (element order) packed two per
+    byte (low nibble first), and its two per-16 scale bytes."""
+    c = np.asarray(codes16x2, np.uint8)
+    return (c[0::2] | (c[1::2] << 4)).astype(np.uint8), np.array([sc0, sc1], np.uint8)
+
+
+def unpack4(b):
+    b = np.asarray(b, np.uint8).ravel()
+    out = np.empty(2 * b.size, np.uint8)
+    out[0::2], out[1::2] = b & 0xF, b >> 4
+    return out
+
+
+def pin_nvfp4_requant(O):
+    """P13: NVFP4 -> MXFP4 re-encoding. (a) Power-of-two block scales: with both
+    per-16 scales 2^a and the matrix scale 2^b, and a +-6 in the block, the MXFP4
+    block is the same codes with E8M0 exponent a + b (nibble order, per-16 scale
+    indexing and the shared-exponent rule all show). (b) Hand-worked blocks:
+    halves at scales 2^a and 2^(a-1); a non-power-of-two scale 1.5; a value that
+    the FP32 product puts exactly on a tie of the E2M1 grid; NaN and overflow
+    blocks; an all-zero block."""
+    rng = np.random.default_rng(13)
+    # (a) identity for power-of-two scales, 3 matrices x 5 rows x 128 columns
+    M, R, C = 3, 5, 128
+    codes = rng.integers(0, 16, size=(M, R, C)).astype(np.uint8)
+    codes[:, :, ::32] = 7                                  # a +6 in every block
+    a = rng.integers(-6, 9, size=(M, R, C // 32))          # UE4M3 2^a: exponent field a + 7
+    sc16 = np.repeat(((a + 7) << 3).astype(np.uint8), 2, axis=2)
+    bexp = np.array([0, -20, 9])
+    g = np.ldexp(1.0, bexp).astype(np.float32)
+    packed = (codes[:, :, 0::2] | (codes[:, :, 1::2] << 4)).astype(np.uint8)
+    oc, osc = O.nvfp4_to_mxfp4(packed, sc16, g)
+    # negative zero (code 8) re-encodes as +0 (code 0); everything else is unchanged
+    want = np.where(codes == 8, 0, codes)
+    assert np.array_equal(unpack4(oc).reshape(M, R, C), want)
+    assert np.array_equal(osc, (a + bexp[:, None, None] + 127).astype(np.uint8))
+
+    def one(c32, s0, s1, gm=1.0):
+        pk, s = nvfp4_block(c32, s0, s1)
+        o, os_ = O.nvfp4_to_mxfp4(pk.reshape(1, 1, 16), s.reshape(1, 1, 2), np.array([gm], np.float32))
+        return unpack4(o), int(os_.ravel()[0])
+
+    # (b1) half 0 at 2^2 (code 0x48) holding 6 -> amax 24, X = 4 - 2 = 2; half 1 at
+    # 2^1 (0x40): value c * 2 / 2^2 = c / 2, so 6 -> 3 (code 5), 4 -> 2 (4), 2 -> 1 (2),
+    # 1 -> 0.5 (1), 0.5 -> 0.25 = tie -> 0 (even), -3 -> -1.5 (code 11)
+    c = [7, 1, 2] + [0] * 13 + [7, 6, 4, 2, 1, 13] + [0] * 10
+    got, sc = one(c, 0x48, 0x40)
+    assert sc == 127 + 2
+    assert list(got[:3]) == [7, 1, 2] and list(got[16:22]) == [5, 4, 2, 1, 0, 11]
+    # (b2) scale 1.5 (0x3C) on both halves: amax 6 * 1.5 = 9, X = 3 - 2 = 1; elements
+    # v / 2: 6 -> 4.5 -> 4 (code 6); 1.5 -> 1.125 -> 1 (2); 3 -> 2.25 -> 2 (4);
+    # 4 -> 3 (5); 0.5 -> 0.375 -> 0.5 (1); 1 -> 0.75 = tie -> 1 (2, even); 2 -> 1.5 (3)
+    c = [7, 3, 5, 6, 1, 2, 4] + [0] * 25
+    got, sc = one(c, 0x3C, 0x3C)
+    assert sc == 128 and list(got[:7]) == [6, 2, 4, 5, 1, 2, 3]
+    # (b3) FP32 products on ties of the grid: g = the float just above 5/6
+    # (0x1.aaaaacp-1, 5/6 + 2^-24 * 2/3), scale 1.0. Code 7 (6) gives 6g = 5 + 2.4e-7,
+    # which FP32 rounds to 5.0: amax 5 -> X = 0, and 5 is a tie between 4 (code 6,
+    # even) and 6 (code 7) -> 6. Code 5 (3) gives 3g = 2.5 + 1.2e-7 -> 2.5 in FP32, a
+    # tie between 2 (code 4, even) and 3 (code 5) -> 4. (Formed in double both would
+    # sit above their ties and give 7 and 5.)
+    gm = np.float32(float.fromhex("0x1.aaaaacp-1"))
+    c = [7, 5] + [0] * 30
+    got, sc = one(c, 0x38, 0x38, gm)
+    assert sc == 127 and got[0] == 6 and got[1] == 4
+    # (b4) NaN scale (0x7F, also with the ignored top bit 0xFF), non-finite matrix
+    # scale, FP32 overflow -> E8M0 NaN (0xFF) and zero codes
+    for s0, s1, gmv in ((0x7F, 0x38, 1.0), (0x38, 0xFF, 1.0), (0x38, 0x38, np.inf),
+                        (0x38, 0x38, np.nan), (0x7E, 0x7E, 3.0e38)):
+        got, sc = one([7] * 32, s0, s1, gmv)
+        assert sc == 255 and not got.any(), (s0, s1, gmv)
+    # top bit of a finite scale byte is ignored: 0xB8 acts as 0x38
+    g1, s1_ = one([7, 1] + [0] * 30, 0xB8, 0xB8)
+    g2, s2_ = one([7, 1] + [0] * 30, 0x38, 0x38)
+    assert s1_ == s2_ == 127 and np.array_equal(g1, g2)
+    # (b5) all-zero block (+0 and -0 codes): smallest scale, zero codes
+    got, sc = one([0, 8] * 16, 0x38, 0x38)
+    assert sc == 0 and not got.any()
+
+
 PINS = [pin_bruteforce, pin_bruteforce_mx, pin_dense_e1k1, pin_topk, pin_weights,
         pin_permutation, pin_rms_unit, pin_token_permutation, pin_norm_before_combine,
-        pin_pool_norm_invariance, pin_identical_experts, pin_round_bf16, pin_mx_codec]
+        pin_pool_norm_invariance, pin_identical_experts, pin_round_bf16, pin_mx_codec,
+        pin_nvfp4_requant]

@@ -57,6 +57,13 @@ MUTANTS = [
      "  if (0) orc_mx_quant_e4m3(h, F, NULL, NULL, h);\n  else if (rnd && !mx_act)"),
     ("mxfp4_nibble_order", "uint8_t c = (i % 2 == 0) ? (row[i / 2] & 0xF) : (row[i / 2] >> 4);",
      "uint8_t c = (i % 2 == 1) ? (row[i / 2] & 0xF) : (row[i / 2] >> 4);"),
+    ("nvfp4_nibble_order", "const uint8_t c = (k % 2 == 0) ? (byte & 0xF) : (byte >> 4);",
+     "const uint8_t c = (k % 2 == 1) ? (byte & 0xF) : (byte >> 4);"),
+    ("nvfp4_scale_per_32", "scales16[row * (cols / 16) + k / 16]", "scales16[row * (cols / 16) + k / 32]"),
+    ("nvfp4_product_in_double", "v[i] = (double)x;",
+     "v[i] = orc_e2m1_value(c) * orc_e4m3_value(sc) * (double)gm;"),
+    ("nvfp4_matrix_scale_dropped", "const float x = p * gm;", "const float x = p;"),
+    ("nvfp4_sign_bit_kept", "& 0x7F;\n          if (sc == 0x7F) bad = 1;", ";\n          if ((sc & 0x7F) == 0x7F) bad = 1;"),
 ]
 
 
