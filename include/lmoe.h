@@ -152,6 +152,35 @@ lmoe_status lmoe_destroy(lmoe_handle h);
 lmoe_status lmoe_mx_quantize_e4m3(const float* x, int64_t n, uint8_t* codes, uint8_t* scales,
                                   void* hip_stream);
 
+/* Re-encode NVFP4 expert weights as MXFP4 (the form lmoe_create takes with
+ * expert_wdtype LMOE_MXFP4), for checkpoints stored in NVFP4.
+ * NVFP4 as the LMSYS blog's "NVFP4 as a third MMA type" section describes it:
+ * E2M1 values with one UE4M3 block scale per 16 elements, plus one FP32 scale
+ * per weight matrix; its "AMD support" section runs such a checkpoint on
+ * MI355X through the MXFP4 path. Each element's value e2m1 * ue4m3 * g is
+ * formed in FP32 (the minifloat product is exact; the product with g rounds to
+ * nearest-even), then every 32-element block is MX-quantized as OCP
+ * Microscaling v1.0 gives it for MXFP4: shared exponent X = floor(log2(amax))
+ * - 2, clamped to [-127, 127] (an all-zero block takes -127); each element is
+ * the E2M1 code of v / 2^X, nearest with ties to even, saturated at 6; -0 is
+ * stored as +0. The UE4M3 byte's top bit is ignored. A block with a NaN scale
+ * (0x7F), a non-finite g or a value that overflows FP32 gets the E8M0 NaN
+ * scale 0xFF and zero codes.
+ * Layouts (device, row-major; element 2i of a row in the low nibble of byte i):
+ *   codes        [n_mats][rows][cols/2]   E2M1, 16-byte aligned
+ *   scales16     [n_mats][rows][cols/16]  UE4M3, 2-byte aligned
+ *   global_scale [n_mats]                 FP32 (one per matrix), 4-byte aligned
+ *   out_codes    [n_mats][rows][cols/2]   E2M1, 16-byte aligned; may be codes
+ *                                         itself (in place), else disjoint
+ *   out_scales   [n_mats][rows][cols/32]  E8M0, disjoint from everything else
+ * cols must be a multiple of 32; a zero size enqueues nothing. For a layer's
+ * experts, n_mats = E with rows = 2F, cols = Dp (gate/up) or rows = Dp,
+ * cols = F (down). Asynchronous on hip_stream; LMOE_E_INVAL on bad arguments
+ * (nothing enqueued); the caller owns every buffer. */
+lmoe_status lmoe_nvfp4_to_mxfp4(const uint8_t* codes, const uint8_t* scales16, const float* global_scale,
+                                int64_t n_mats, int64_t rows, int64_t cols, uint8_t* out_codes,
+                                uint8_t* out_scales, void* hip_stream);
+
 /* Device workspace bytes a handle with this configuration allocates. */
 lmoe_status lmoe_workspace_bytes(const lmoe_config* cfg, size_t* out);
 

@@ -26,7 +26,7 @@ LMOE_NUM_STAGES = len(STAGES)
 
 EXPORTS = ["lmoe_create", "lmoe_forward", "lmoe_destroy", "lmoe_workspace_bytes",
            "lmoe_set_timing", "lmoe_get_timing", "lmoe_status_str", "lmoe_last_error",
-           "lmoe_mx_quantize_e4m3"]
+           "lmoe_mx_quantize_e4m3", "lmoe_nvfp4_to_mxfp4"]
 
 
 class lmoe_config(ctypes.Structure):
@@ -76,8 +76,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lmoe_set_timing.argtypes = [P, ctypes.c_int]
     lib.lmoe_get_timing.argtypes = [P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(I32)]
     lib.lmoe_mx_quantize_e4m3.argtypes = [P, ctypes.c_int64, P, P, P]
+    lib.lmoe_nvfp4_to_mxfp4.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P, P]
     for f in ("lmoe_create", "lmoe_forward", "lmoe_destroy", "lmoe_workspace_bytes",
-              "lmoe_set_timing", "lmoe_get_timing", "lmoe_mx_quantize_e4m3"):
+              "lmoe_set_timing", "lmoe_get_timing", "lmoe_mx_quantize_e4m3", "lmoe_nvfp4_to_mxfp4"):
         getattr(lib, f).restype = ctypes.c_int
     lib.lmoe_status_str.argtypes = [ctypes.c_int]
     lib.lmoe_status_str.restype = ctypes.c_char_p
@@ -135,6 +136,12 @@ def lmoe_get_timing(h: int):
 
 def lmoe_mx_quantize_e4m3(x: int, n: int, codes: int, scales: int, stream: int = 0):
     _check(load().lmoe_mx_quantize_e4m3(x, n, codes, scales, stream), "lmoe_mx_quantize_e4m3")
+
+
+def lmoe_nvfp4_to_mxfp4(codes: int, scales16: int, global_scale: int, n_mats: int, rows: int, cols: int,
+                        out_codes: int, out_scales: int, stream: int = 0):
+    _check(load().lmoe_nvfp4_to_mxfp4(codes, scales16, global_scale, n_mats, rows, cols, out_codes,
+                                      out_scales, stream), "lmoe_nvfp4_to_mxfp4")
 
 
 def make_config(D, Dp, F, E, k, max_tokens, act="bf16", eps_pool=1e-6, eps_expert=1e-6,

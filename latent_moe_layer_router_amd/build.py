@@ -8,7 +8,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "liblmoe.so")
-SOURCES = ["api.hip", "gemm.hip", "gemm256.hip", "gemm256_mx.hip", "stream.hip", "route.hip", "norm.hip"]
+SOURCES = ["api.hip", "gemm.hip", "gemm256.hip", "gemm256_mx.hip", "stream.hip", "route.hip", "norm.hip",
+           "convert.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

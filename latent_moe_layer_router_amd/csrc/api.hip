@@ -180,6 +180,38 @@ lmoe_status lmoe_mx_quantize_e4m3(const float* x, int64_t n, uint8_t* codes, uin
   return LMOE_OK;
 }
 
+lmoe_status lmoe_nvfp4_to_mxfp4(const uint8_t* codes, const uint8_t* scales16, const float* global_scale,
+                                int64_t n_mats, int64_t rows, int64_t cols, uint8_t* out_codes,
+                                uint8_t* out_scales, void* hip_stream) {
+  g_last_error.clear();
+  if (n_mats < 0 || rows < 0 || cols < 0 || cols % 32)
+    return fail(LMOE_E_INVAL, "n_mats and rows must be >= 0 and cols a non-negative multiple of 32");
+  if (n_mats == 0 || rows == 0 || cols == 0) return LMOE_OK;
+  if (!codes || !scales16 || !global_scale || !out_codes || !out_scales)
+    return fail(LMOE_E_INVAL, "codes, scales16, global_scale, out_codes and out_scales must not be NULL");
+  if (!aligned16(codes) || !aligned16(out_codes) || (reinterpret_cast<uintptr_t>(scales16) & 1) ||
+      !aligned4(global_scale))
+    return fail(LMOE_E_INVAL, "codes and out_codes must be 16-byte, scales16 2-byte, global_scale 4-byte aligned");
+  if (rows > INT64_MAX / n_mats || n_mats * rows > INT64_MAX / cols)
+    return fail(LMOE_E_INVAL, "size overflow");
+  const int64_t nc = n_mats * rows * (cols / 2), n16 = n_mats * rows * (cols / 16),
+                n32 = n_mats * rows * (cols / 32);
+  auto overlap = [](const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+  };
+  if (out_codes != codes && overlap(out_codes, nc, codes, nc))
+    return fail(LMOE_E_INVAL, "out_codes must be codes itself or not overlap it");
+  if (overlap(out_scales, n32, codes, nc) || overlap(out_scales, n32, scales16, n16) ||
+      overlap(out_scales, n32, out_codes, nc) || overlap(out_codes, nc, scales16, n16) ||
+      overlap(out_scales, n32, global_scale, 4 * n_mats) || overlap(out_codes, nc, global_scale, 4 * n_mats))
+    return fail(LMOE_E_INVAL, "outputs overlap the inputs");
+  const hipError_t e = launch_nvfp4_to_mxfp4(codes, scales16, global_scale, n_mats, rows, cols, out_codes,
+                                             out_scales, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(LMOE_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+  return LMOE_OK;
+}
+
 lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, lmoe_handle* out) {
   g_last_error.clear();
   if (!out) return fail(LMOE_E_INVAL, "out is NULL");

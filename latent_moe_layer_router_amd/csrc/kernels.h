@@ -193,6 +193,14 @@ hipError_t launch_pool_norm_mx(const float* P, const float* g, int T, int Dp, fl
 // n fp32 values (n a multiple of 32) -> MXFP8 E4M3 codes [n] and scales [n/32].
 hipError_t launch_mx_quant(const float* x, int64_t n, uint8_t* codes, uint8_t* scales, hipStream_t s);
 
+// NVFP4 expert weights (E2M1 codes [M][rows][cols/2], UE4M3 scales per 16
+// [M][rows][cols/16], FP32 scale per matrix [M]) re-encoded as MXFP4 (codes
+// [M][rows][cols/2], E8M0 scales [M][rows][cols/32]); cols a multiple of 32.
+// out_codes may be codes itself.
+hipError_t launch_nvfp4_to_mxfp4(const uint8_t* codes, const uint8_t* scales16, const float* gscale,
+                                 int64_t n_mats, int64_t rows, int64_t cols, uint8_t* out_codes,
+                                 uint8_t* out_scales, hipStream_t s);
+
 // u[t] = sum_j w[t][j] * rsqrt(sum(ss[inv[t,j]]) / Dp + eps) * g_e * y[inv[t,j]]
 struct CombineParams {
   const void* y;           // [T*k][Dp] sorted rows

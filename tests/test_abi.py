@@ -98,3 +98,36 @@ def test_mx_quantize_rejects_bad_arguments(n, ptr):
         lmoe.lmoe_mx_quantize_e4m3(ptr, n, ptr, ptr)
     assert e.value.status == lmoe.LMOE_E_INVAL
     lmoe.lmoe_mx_quantize_e4m3(0, 0, 0, 0)     # empty: nothing to do
+
+
+@pytest.mark.parametrize("args", [
+    (1, 1, 48),                      # cols not a multiple of 32
+    (-1, 1, 32), (1, -1, 32),        # negative sizes
+])
+def test_nvfp4_to_mxfp4_rejects_bad_sizes(args):
+    """Checked on the host before anything is enqueued (no GPU needed)."""
+    m, r, c = args
+    buf = 1 << 20
+    with pytest.raises(lmoe.LmoeError) as e:
+        lmoe.lmoe_nvfp4_to_mxfp4(buf, buf + 4096, buf + 8192, m, r, c, buf, buf + 16384)
+    assert e.value.status == lmoe.LMOE_E_INVAL
+
+
+def test_nvfp4_to_mxfp4_rejects_bad_pointers():
+    base = 1 << 24
+    codes, s16, g, oc, os_ = base, base + (1 << 16), base + (1 << 17), base + (1 << 18), base + (1 << 19)
+    cases = [
+        (0, s16, g, oc, os_),            # NULL codes
+        (codes, s16, g, oc, 0),          # NULL out_scales
+        (codes + 8, s16, g, oc, os_),    # codes misaligned
+        (codes, s16 + 1, g, oc, os_),    # scales16 misaligned
+        (codes, s16, g + 2, oc, os_),    # global_scale misaligned
+        (codes, s16, g, codes + 16, os_),  # out_codes overlaps codes without being it
+        (codes, s16, g, oc, codes + 4),  # out_scales inside codes
+        (codes, s16, g, oc, s16),        # out_scales inside scales16
+    ]
+    for c in cases:
+        with pytest.raises(lmoe.LmoeError) as e:
+            lmoe.lmoe_nvfp4_to_mxfp4(c[0], c[1], c[2], 2, 4, 64, c[3], c[4])
+        assert e.value.status == lmoe.LMOE_E_INVAL, c
+    lmoe.lmoe_nvfp4_to_mxfp4(0, 0, 0, 0, 4, 64, 0, 0)   # empty: nothing to do
