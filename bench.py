@@ -1,14 +1,15 @@
 """Benchmark of the latent-MoE block forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_bf16]
-                    [--also prefill_bf16,mxfp4] [--no-cpu-baseline]
+                    [--also prefill_bf16,mxfp4] [--no-cpu-baseline] [--no-convert]
 
 A step is one lmoe_forward over one batch of synthetic tokens already resident
 in HBM: routing, permutation, pooler, experts, combine, unpooler. The headline
 workload is decode-sized (T=128 tokens; D=8192, Dp=4096, F=4096, E=256, k=8,
 bf16), which streams the touched experts' weights and is bound by HBM; the
 prefill chunk (T=16384) is reported beside it against the bf16 MFMA peak, and
-the same chunk with MXFP4 experts (MXFP8 expert inputs) against the fp8 peak.
+the same chunk with MXFP4 experts (MXFP8 expert inputs) against the fp8 peak,
+and the load-time NVFP4 -> MXFP4 re-encoding of a layer's experts against HBM.
 Prints one JSON line. Weights are random-initialized (seed 0) with the model's
 shapes; inputs are synthetic (see synth/).
 """
@@ -164,6 +165,47 @@ def cpu_baseline(synth, w):
                       f"{dt:.1f} s in total"}
 
 
+def nvfp4_convert(lmoe, torch, dev, E=256, Dp=4096, F=4096, reps=5):
+    """Load-time re-encoding of a layer's NVFP4 expert weights as MXFP4: both
+    matrices of all E experts (gate/up [E][2F][Dp], down [E][Dp][F]) from seeded
+    random NVFP4 codes and scales, timed with HIP events on the launching stream.
+    Algorithmic bytes per element: 1/2 (codes) + 1/16 (UE4M3 scales) read,
+    1/2 (codes) + 1/32 (E8M0 scales) written."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    s = torch.cuda.current_stream()
+    shapes = [(E, 2 * F, Dp), (E, Dp, F)]
+    bufs = []
+    for m, r, c in shapes:
+        codes = torch.randint(0, 256, (m, r, c // 2), dtype=torch.uint8, device=dev, generator=gen)
+        s16 = torch.randint(0x18, 0x60, (m, r, c // 16), dtype=torch.uint8, device=dev, generator=gen)
+        g = torch.full((m,), 2.0 ** -7, dtype=torch.float32, device=dev)
+        bufs.append((codes, s16, g, torch.empty_like(codes),
+                     torch.empty((m, r, c // 32), dtype=torch.uint8, device=dev), m, r, c))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    times = []
+    for rep in range(reps + 1):
+        ev[0].record(s)
+        for i, (codes, s16, g, oc, os_, m, r, c) in enumerate(bufs):
+            lmoe.lmoe_nvfp4_to_mxfp4(codes.data_ptr(), s16.data_ptr(), g.data_ptr(), m, r, c,
+                                     oc.data_ptr(), os_.data_ptr(), s.cuda_stream)
+            ev[i + 1].record(s)
+        torch.cuda.synchronize()
+        if rep:
+            times.append(ev[0].elapsed_time(ev[2]))
+    n = sum(m * r * c for m, r, c in shapes)
+    byts = n * (1 / 2 + 1 / 16 + 1 / 2 + 1 / 32)
+    ms = sorted(times)[len(times) // 2]
+    gbs = byts / (ms * 1e-3) / 1e9
+    del bufs
+    torch.cuda.empty_cache()
+    return {"workload": "nvfp4_to_mxfp4", "what": f"all {E} experts' gate/up and down weights, "
+            "NVFP4 -> MXFP4 (load time, two launches)", "elements": n, "ms": round(ms, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "kernel": "nvfp4_to_mxfp4_kernel", "algorithmic_bytes": int(byts)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +215,8 @@ def main():
     ap.add_argument("--also", default="prefill_bf16,mxfp4",
                     help="comma-separated extra workloads, or ''")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-convert", action="store_true",
+                    help="skip timing the load-time NVFP4 -> MXFP4 weight re-encoding")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a kernel of "
                          "known traffic, to calibrate hardware byte counters against)")
@@ -245,10 +289,15 @@ def main():
         if not e.mx_act:
             entry["step_mfma_frac"] = round(ef / (ems * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
         also.append(entry)
-    res["also"] = also
     block.close()
     del tw
     torch.cuda.empty_cache()
+    if not args.no_convert:
+        conv = nvfp4_convert(lmoe, torch, dev)
+        print(f"[bench] nvfp4_to_mxfp4: {conv['ms']:.3f} ms, {conv['roofline']['achieved']} GB/s",
+              file=sys.stderr, flush=True)
+        also.append(conv)
+    res["also"] = also
     w = synth.WORKLOADS[args.workload]
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

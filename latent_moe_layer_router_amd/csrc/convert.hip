@@ -24,10 +24,10 @@ namespace lmoe {
 
 namespace {
 
-__device__ __forceinline__ float e2m1_value(uint32_t c) {
-  const uint32_t m = c & 7u;
-  uint32_t bits = m == 0 ? 0u : m == 1 ? 0x3F000000u : (((m >> 1) + 126u) << 23) | ((m & 1u) << 22);
-  return __uint_as_float(bits | ((c & 8u) << 28));
+// Twice the E2M1 magnitude of code m (0..7) is the integer 0, 1, 2, 3, 4, 6, 8
+// or 12: one byte permute picks it from two constant words.
+__device__ __forceinline__ float e2m1_twice(uint32_t m) {
+  return (float)(__builtin_amdgcn_perm(0x0C080604u, 0x03020100u, m) & 0xFFu);
 }
 
 // Unsigned E4M3 (bias 7; code 0x7F is NaN, handled by the caller).
@@ -37,25 +37,16 @@ __device__ __forceinline__ float ue4m3_value(uint32_t s) {
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
-// E2M1 code of v / 2^X: nearest, ties to even, saturating at 6.
-__device__ __forceinline__ uint32_t e2m1_code(float v, int X) {
-  // 2^-X for X in [-127, 125]: a normal float
-  const float q = fabsf(v) * __uint_as_float((uint32_t)(127 - X) << 23);
-  uint32_t code = 0;
-  if (q > 0.f) {
-    int e = (int)((__float_as_uint(q) >> 23) & 0xFF) - 127;   // floor(log2 q) for normal q
-    if (e < 0) e = 0;                                          // below 1: step 0.5
-    const float step = __uint_as_float((uint32_t)(e - 1 + 127) << 23);
-    float r = __builtin_rintf(q / step) * step;
-    if (r > 6.f) r = 6.f;
-    if (r == 0.5f) {
-      code = 1;
-    } else if (r > 0.f) {
-      const uint32_t rb = __float_as_uint(r);
-      code = ((((rb >> 23) & 0xFF) - 126u) << 1) | ((rb >> 22) & 1u);
-    }
-  }
-  return code | (v < 0.f ? 8u : 0u);
+// E2M1 magnitude code of q in [0, 8): nearest, ties to even, saturating at 6.
+// Below 1 the grid step is 0.5, so the code is rint(2q) (0, 1 or 2). From 1 up
+// the code is the float's exponent and top mantissa bit, so rounding q's bit
+// pattern to one mantissa bit (ties to even) gives it directly; 8 and above
+// saturate to code 7 (6.0).
+__device__ __forceinline__ uint32_t e2m1_mag_code(float q) {
+  const uint32_t b = __float_as_uint(q);
+  const uint32_t hi = ((b + 0x1FFFFFu + ((b >> 22) & 1u)) >> 22) - 252u;
+  const uint32_t lo = (uint32_t)__builtin_rintf(q + q);
+  return q < 1.f ? lo : (hi > 7u ? 7u : hi);
 }
 
 __global__ __launch_bounds__(256) void nvfp4_to_mxfp4_kernel(const uint8_t* codes, const uint8_t* scales16,
@@ -70,13 +61,16 @@ __global__ __launch_bounds__(256) void nvfp4_to_mxfp4_kernel(const uint8_t* code
     const uint32_t s2 = *reinterpret_cast<const uint16_t*>(scales16 + 2 * b);
     const uint32_t s0 = s2 & 0x7Fu, s1 = (s2 >> 8) & 0x7Fu;
     bool bad = !(fabsf(g) <= 3.402823466e38f) || s0 == 0x7Fu || s1 == 0x7Fu;
-    const float sc[2] = {ue4m3_value(s0), ue4m3_value(s1)};
+    // half the block scales: e2m1 * ue4m3 = (2 e2m1) * (ue4m3 / 2), both exact
+    const float hsc[2] = {0.5f * ue4m3_value(s0), 0.5f * ue4m3_value(s1)};
     const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
     float v[32];
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      const float p = e2m1_value((w[i >> 3] >> (4 * (i & 7))) & 15u) * sc[i >> 4];
+      const uint32_t c = (w[i >> 3] >> (4 * (i & 7))) & 15u;
+      const float mag = e2m1_twice(c & 7u) * hsc[i >> 4];
+      const float p = __uint_as_float(__float_as_uint(mag) ^ ((c & 8u) << 28));
       v[i] = p * g;
       amax = fmaxf(amax, fabsf(v[i]));
     }
@@ -91,8 +85,12 @@ __global__ __launch_bounds__(256) void nvfp4_to_mxfp4_kernel(const uint8_t* code
         X = X < -127 ? -127 : X;
       }
       scale = (uint8_t)(X + 127);
+      // 2^-X for X in [-127, 125] is a normal float; |v| * 2^-X is exact (or far
+      // below the grid's first step)
+      const float inv = __uint_as_float((uint32_t)(127 - X) << 23);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) o[i >> 3] |= e2m1_code(v[i], X) << (4 * (i & 7));
+      for (int i = 0; i < 32; ++i)
+        o[i >> 3] |= (e2m1_mag_code(fabsf(v[i]) * inv) | (v[i] < 0.f ? 8u : 0u)) << (4 * (i & 7));
     }
     *reinterpret_cast<uint4*>(out_codes + 16 * b) = uint4{o[0], o[1], o[2], o[3]};
     out_scales[b] = scale;
