@@ -54,6 +54,8 @@ def load(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = [ctypes.c_uint8]
         fn.restype = _D
+    lib.orc_set_flush_modes.argtypes = [ctypes.c_int]
+    lib.orc_set_flush_modes.restype = None
     lib.orc_round_bf16.argtypes = [_D]
     lib.orc_round_bf16.restype = _D
     return lib

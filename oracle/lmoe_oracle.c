@@ -62,6 +62,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#include <xmmintrin.h>
 
 enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_MXFP4 = 2 };
 
@@ -223,9 +224,27 @@ void orc_mx_quant_e2m1(const double* v, int n, uint8_t* packed, uint8_t* scales,
  * [n_mats][rows][cols/16], g [n_mats] -> out_codes [n_mats][rows][cols/2],
  * out_scales [n_mats][rows][cols/32]; cols a multiple of 32.
  * ------------------------------------------------------------------------- */
+/* IEEE arithmetic whatever the host process's SSE modes are: a library loaded
+   into the same process can switch it to flush-to-zero / denormals-are-zero
+   (code linked with fast-math does), which would change FP32 products below
+   2^-126. The modes are cleared for the call and restored after it. */
+static unsigned ieee_begin(void) {
+  const unsigned csr = _mm_getcsr();
+  _mm_setcsr(csr & ~0x8040u);                 /* FTZ (bit 15), DAZ (bit 6) */
+  return csr;
+}
+static void ieee_end(unsigned csr) { _mm_setcsr(csr); }
+
+/* Test hook: turn FTZ and DAZ on (1) or off (0) for the calling thread. */
+void orc_set_flush_modes(int on) {
+  const unsigned csr = _mm_getcsr();
+  _mm_setcsr(on ? (csr | 0x8040u) : (csr & ~0x8040u));
+}
+
 void orc_nvfp4_to_mxfp4(const uint8_t* codes, const uint8_t* scales16, const float* g,
                         int64_t n_mats, int64_t rows, int64_t cols, uint8_t* out_codes,
                         uint8_t* out_scales) {
+  const unsigned csr = ieee_begin();
   const int64_t nb = cols / 32;
   for (int64_t m = 0; m < n_mats; ++m) {
     const float gm = g[m];
@@ -255,6 +274,7 @@ void orc_nvfp4_to_mxfp4(const uint8_t* codes, const uint8_t* scales16, const flo
       }
     }
   }
+  ieee_end(csr);
 }
 
 /* Row r of an expert weight matrix with K columns, dequantized into out[K]. */

@@ -456,6 +456,24 @@ def pin_nvfp4_requant(O):
     # (b5) all-zero block (+0 and -0 codes): smallest scale, zero codes
     got, sc = one([0, 8] * 16, 0x38, 0x38)
     assert sc == 0 and not got.any()
+    # (b6) FP32 subnormals, also with flush-to-zero / denormals-are-zero switched on
+    # in the calling thread (as a fast-math library loaded into the process does):
+    # g = 2^-126, scale 1: 6 g = 6 * 2^-126 -> X = -126 + 2 - 2 = -126; 0.5 g = 2^-127
+    # (a subnormal product) / 2^-126 = 0.5 -> code 1. g = 2^-130 (a subnormal input):
+    # 6 g -> X = -130 clamped to -127, 6 * 2^-130 / 2^-127 = 0.75 -> 1.0 (code 2, tie
+    # to even); 4 g / 2^-127 = 0.5 -> code 1.
+    # (the matrix scales are made from their bit patterns, before the modes change)
+    g126, g130 = np.array([0x00800000, 0x00080000], np.uint32).view(np.float32)
+    assert float(g126) == 2.0 ** -126 and float(g130) == 2.0 ** -130
+    for flush in (0, 1):
+        O.lib.orc_set_flush_modes(flush)
+        try:
+            got, sc = one([7, 1] + [0] * 30, 0x38, 0x38, g126)
+            assert sc == 1 and list(got[:2]) == [7, 1], (flush, sc, got[:2])
+            got, sc = one([7, 6] + [0] * 30, 0x38, 0x38, g130)
+            assert sc == 0 and list(got[:2]) == [2, 1], (flush, sc, got[:2])
+        finally:
+            O.lib.orc_set_flush_modes(0)
 
 
 PINS = [pin_bruteforce, pin_bruteforce_mx, pin_dense_e1k1, pin_topk, pin_weights,

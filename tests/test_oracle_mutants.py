@@ -63,6 +63,7 @@ MUTANTS = [
     ("nvfp4_product_in_double", "v[i] = (double)x;",
      "v[i] = orc_e2m1_value(c) * orc_e4m3_value(sc) * (double)gm;"),
     ("nvfp4_matrix_scale_dropped", "const float x = p * gm;", "const float x = p;"),
+    ("nvfp4_host_flush_mode_kept", "_mm_setcsr(csr & ~0x8040u);                 /* FTZ", "_mm_setcsr(csr);                 /* FTZ"),
     ("nvfp4_sign_bit_kept", "& 0x7F;\n          if (sc == 0x7F) bad = 1;", ";\n          if ((sc & 0x7F) == 0x7F) bad = 1;"),
 ]
 
