@@ -46,9 +46,17 @@ __device__ __forceinline__ void store8(float* dst, const float (&v)[8]) {
   reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
   reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
-// Load 8 consecutive values (one 16-byte bf16 load, or two fp32).
-__device__ __forceinline__ void load8(const bf16_t* src, float (&v)[8]) {
-  const uint4 q = *reinterpret_cast<const uint4*>(src);
+// Load 8 consecutive fp32 values.
+__device__ __forceinline__ void load8(const float* src, float (&v)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(src)[0], b = reinterpret_cast<const float4*>(src)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// load8 with a non-temporal hint: for rows read exactly once, so that they do
+// not displace lines that are read again (the experts' gammas in the combine).
+__device__ __forceinline__ void load8_once(const bf16_t* src, float (&v)[8]) {
+  typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+  const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -56,8 +64,10 @@ __device__ __forceinline__ void load8(const bf16_t* src, float (&v)[8]) {
     v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
   }
 }
-__device__ __forceinline__ void load8(const float* src, float (&v)[8]) {
-  const float4 a = reinterpret_cast<const float4*>(src)[0], b = reinterpret_cast<const float4*>(src)[1];
+__device__ __forceinline__ void load8_once(const float* src, float (&v)[8]) {
+  typedef __attribute__((ext_vector_type(4))) float f32x4v;
+  const f32x4v a = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(src));
+  const f32x4v b = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(src) + 1);
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
@@ -172,36 +182,47 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   __shared__ float scale[16];
   __shared__ int pos[16];
   __shared__ int eid[16];
-  const int t = blockIdx.x;
+  const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nss = p.Dp / 64;
-  if (threadIdx.x < p.k) {
-    const int j = threadIdx.x;
+  // Slot j's scale: one wave reduces the row's partial sums of squares (lane q
+  // takes partials q, q + 64, ...; then a butterfly over the wave).
+  for (int j = wave; j < p.k; j += kThreads / kWave) {
     const int a = t * p.k + j;
     const int ps = p.inv[a];
     const float* ss = p.ss + (int64_t)ps * nss;
     float s = 0.f;
-    for (int q = 0; q < nss; ++q) s += ss[q];
-    scale[j] = p.w[a] / sqrtf(s / (float)p.Dp + p.eps);
-    pos[j] = ps;
-    eid[j] = p.ids[a];
+    for (int q = lane; q < nss; q += kWave) s += ss[q];
+    s = wave_sum(s);
+    if (lane == 0) {
+      scale[j] = p.w[a] / sqrtf(s / (float)p.Dp + p.eps);
+      pos[j] = ps;
+      eid[j] = p.ids[a];
+    }
   }
   __syncthreads();
   const T* y = static_cast<const T*>(p.y);
   T* u = static_cast<T*>(p.u) + (int64_t)t * p.Dp;
-  // 8 consecutive columns per thread (16-byte bf16 loads and stores); the k
-  // terms of each column are added in slot order.
+  // 8 consecutive columns per thread; the loads of up to 8 slots are issued
+  // before any is used, then the terms are added in slot order j = 0..k-1.
   for (int c = threadIdx.x * 8; c < p.Dp; c += kThreads * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < p.k; ++j) {
-      float yv[8];
-      load8(y + (int64_t)pos[j] * p.Dp + c, yv);
-      const float* gr = p.g_expert + (int64_t)eid[j] * p.Dp + c;
-      const float4 g0 = *reinterpret_cast<const float4*>(gr);
-      const float4 g1 = *reinterpret_cast<const float4*>(gr + 4);
-      const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-      const float s = scale[j];
+    for (int j0 = 0; j0 < p.k; j0 += 8) {
+      float yv[8][8], gv[8][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += s * gg[i] * yv[i];
+      for (int jj = 0; jj < 8; ++jj) {
+        if (j0 + jj < p.k) {
+          load8_once(y + (int64_t)pos[j0 + jj] * p.Dp + c, yv[jj]);
+          load8(p.g_expert + (int64_t)eid[j0 + jj] * p.Dp + c, gv[jj]);
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        if (j0 + jj < p.k) {
+          const float sj = scale[j0 + jj];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += sj * gv[jj][i] * yv[jj][i];
+        }
+      }
     }
     store8(u + c, acc);
   }

@@ -139,36 +139,69 @@ __device__ int block_exclusive_scan(int x, int* wave_tot, int* total) {
   return r;
 }
 
+// One workgroup of 1024 threads: thread (part q, expert e) with e < E_pad (E
+// rounded up to a wave) takes a contiguous share of the chunks, so that the
+// per-expert walk over the chunks runs in 1024 / E_pad parallel pieces.
 __global__ __launch_bounds__(1024) void sort_scan_kernel(SortParams p) {
   __shared__ int wave_tot[16];
   __shared__ int total;
-  const int e = threadIdx.x;
+  __shared__ int part_tot[1024];
+  const int e_pad = ((p.E + kWave - 1) / kWave) * kWave;
+  const int parts = blockDim.x / e_pad;
+  const int e = threadIdx.x % e_pad, q = threadIdx.x / e_pad;
+  const bool live = e < p.E && q < parts;
   const int n_chunks = (p.T + kChunk - 1) / kChunk;
-  int cnt = 0;
-  if (e < p.E) {
-    for (int c = 0; c < n_chunks; ++c) {
-      p.chunk_base[(int64_t)c * p.E + e] = cnt;
-      cnt += __popcll(p.chunk_masks[(int64_t)c * p.E + e]);
+  const int per = (n_chunks + parts - 1) / parts;
+  const int c0 = q * per, c1 = min(n_chunks, c0 + per);
+  // 1. this piece's count (eight mask loads in flight at a time)
+  int mine = 0;
+  if (live) {
+    for (int c = c0; c < c1; c += 8) {
+      uint64_t m[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m[i] = (c + i < c1) ? p.chunk_masks[(int64_t)(c + i) * p.E + e] : 0ull;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mine += __popcll(m[i]);
     }
-    p.counts[e] = cnt;
   }
-  const int off = block_exclusive_scan(e < p.E ? cnt : 0, wave_tot, &total);
-  if (e < p.E) p.offsets[e] = off;
-  if (e == 0) p.offsets[p.E] = total;
+  part_tot[threadIdx.x] = mine;
+  __syncthreads();
+  // 2. the piece's base within its expert, and the expert's count
+  int base = 0, cnt = 0;
+  for (int r = 0; r < parts; ++r) {
+    const int v = part_tot[r * e_pad + e];
+    base += r < q ? v : 0;
+    cnt += v;
+  }
+  // 3. per-chunk bases of this piece
+  if (live) {
+    int run = base;
+    for (int c = c0; c < c1; ++c) {
+      p.chunk_base[(int64_t)c * p.E + e] = run;
+      run += __popcll(p.chunk_masks[(int64_t)c * p.E + e]);
+    }
+  }
+  // Expert offsets and tile lists from the first piece of each expert (threads
+  // 0 .. E_pad-1, in expert order; the others add nothing to the scans).
+  const bool head = e < p.E && q == 0;
+  if (head) p.counts[e] = cnt;
+  const int off = block_exclusive_scan(head ? cnt : 0, wave_tot, &total);
+  if (head) p.offsets[e] = off;
+  if (threadIdx.x == 0) p.offsets[p.E] = total;
   // Grouped-GEMM tiles: expert e gets ceil(count / tile_m) row tiles, unless its
   // rows are few enough for the weight-streaming kernel.
-  const int nt = (e < p.E && cnt > p.small_max) ? (cnt + p.tile_m - 1) / p.tile_m : 0;
+  const int nt = (head && cnt > p.small_max) ? (cnt + p.tile_m - 1) / p.tile_m : 0;
   const int tbase = block_exclusive_scan(nt, wave_tot, &total);
-  for (int q = 0; q < nt; ++q) {
-    p.tiles[2 * (tbase + q)] = e;
-    p.tiles[2 * (tbase + q) + 1] = off + q * p.tile_m;
+  for (int i = 0; i < nt; ++i) {
+    p.tiles[2 * (tbase + i)] = e;
+    p.tiles[2 * (tbase + i) + 1] = off + i * p.tile_m;
   }
-  if (e == 0) *p.n_tiles = total;
+  if (threadIdx.x == 0) *p.n_tiles = total;
   // the large-tile GEMM: ceil(count / 256) row tiles
-  const int nt2 = (e < p.E && cnt > p.small_max) ? (cnt + p.tile_m2 - 1) / p.tile_m2 : 0;
+  const int nt2 = (head && cnt > p.small_max) ? (cnt + p.tile_m2 - 1) / p.tile_m2 : 0;
   const int mbase = block_exclusive_scan(nt2, wave_tot, &total);
-  if (e < p.E) p.mt_off[e] = mbase;
-  if (e == 0) p.mt_off[p.E] = total;
+  if (head) p.mt_off[e] = mbase;
+  if (threadIdx.x == 0) p.mt_off[p.E] = total;
 }
 
 __global__ __launch_bounds__(64) void sort_scatter_kernel(SortParams p) {
@@ -204,8 +237,7 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 hipError_t launch_sort(const SortParams& p, hipStream_t s) {
   const int n_chunks = (p.T + kChunk - 1) / kChunk;
   if (n_chunks == 0) return hipSuccess;
-  const int threads = ((p.E + 63) / 64) * 64;
-  hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(threads), 0, s, p);
+  hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), 0, s, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(sort_scatter_kernel, dim3(n_chunks), dim3(64), 0, s, p);
