@@ -107,11 +107,16 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
       if (p.ntiles_n * p.mt_off[mid] <= t) lo = mid; else hi = mid;
     }
     e = lo;
+    // The expert's rows are split evenly over its mt_e row tiles (each at most
+    // 256 rows), so that the tiles sharing a weight slice do the same work and
+    // stream that slice through L2 together; a short tail tile would race ahead
+    // and fetch every slice a second time.
     const int mt_e = p.mt_off[e + 1] - p.mt_off[e];
     const int tl = t - p.ntiles_n * p.mt_off[e];
+    const int mi = tl % mt_e, cnt = p.offsets[e + 1] - p.offsets[e];
     ntile = tl / mt_e;
-    m0 = p.offsets[e] + (tl % mt_e) * BM;
-    m_end = p.offsets[e + 1];
+    m0 = p.offsets[e] + (int)((int64_t)cnt * mi / mt_e);
+    m_end = p.offsets[e] + (int)((int64_t)cnt * (mi + 1) / mt_e);
   }
   const int n0 = ntile * (EPI == EPI_SWIGLU ? BNB / 2 : BNB);   // output column start
 
