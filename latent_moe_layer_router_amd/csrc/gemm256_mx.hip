@@ -101,12 +101,13 @@ __global__ __launch_bounds__(NT, 1) void gemm256_mx_kernel(Gemm256MxParams p) {
   const int e = lo;
   const int mt_e = p.mt_off[e + 1] - p.mt_off[e];
   const int tl = t - p.ntiles_n * p.mt_off[e];
-  // The expert's rows are split evenly over its row tiles (see the bf16
-  // 256-tile GEMM): tiles sharing a weight slice then run at the same pace.
+  // Row tiles of 256 from the expert's first row; the last may be short. (An
+  // even split over the tiles, as in the bf16 GEMM, costs time here: a tile of
+  // about 170 rows keeps one wave at full MFMA work behind the stage barriers,
+  // so three such tiles take longer than two full ones and a short tail.)
   const int ntile = tl / mt_e, mtile = tl % mt_e;
-  const int cnt = p.offsets[e + 1] - p.offsets[e];
-  const int m0 = p.offsets[e] + (int)((int64_t)cnt * mtile / mt_e);
-  const int m_end = p.offsets[e] + (int)((int64_t)cnt * (mtile + 1) / mt_e);
+  const int m0 = p.offsets[e] + mtile * BM;
+  const int m_end = p.offsets[e + 1];
   const int n0 = ntile * (EPI == EPI_SWIGLU ? BNB / 2 : BNB);   // output column start
   const int K = p.K;
 
