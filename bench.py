@@ -92,7 +92,8 @@ def run_workload(lmoe, torch, synth, sdev, block, w, steps, warmup, dev):
 CSRC = os.path.join(ROOT, "latent_moe_layer_router_amd", "csrc")
 GATE_UP_KERNEL = {"hbm": ("stream_kernel<EPI_SWIGLU>", ("stream.hip", "common.h")),
                   "mfma": ("gemm256_kernel<EPI_SWIGLU>", ("gemm256.hip", "common.h")),
-                  "mfma_mx": ("gemm256_mx_kernel<EPI_SWIGLU>", ("gemm256_mx.hip", "mx.h", "common.h"))}
+                  "mfma_mx": ("gemm256_mx_kernel<EPI_SWIGLU>", ("gemm256_mx.hip", "mx.h", "common.h")),
+                  "convert": ("nvfp4_to_mxfp4_kernel", ("convert.hip", "common.h"))}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.txt")
 
 
@@ -105,9 +106,11 @@ def kernel_digest(bound):
 
 
 def measured_traffic(workload, bound):
-    """HBM bytes per launch of the gate/up kernel, as read by the FETCH_SIZE and
-    WRITE_SIZE counters (each scaled by its plain-copy calibration factor) on
-    this workload. None unless they were taken on the kernel source as it is now."""
+    """Memory-side bytes per launch of the workload's dominant kernel, from the
+    profiles: reads from the L2's 32-, 64- and 128-byte read requests to memory
+    (TCC_EA0_RDREQ_32B/64B/128B; a 1 GiB device copy reads 1.00 GiB this way),
+    writes from WRITE_SIZE (the copy writes 1.00 GiB). None unless they were
+    taken on the kernel source as it is now."""
     try:
         with open(TRAFFIC_FILE) as fh:
             lines = fh.read().splitlines()
@@ -199,10 +202,12 @@ def nvfp4_convert(lmoe, torch, dev, E=256, Dp=4096, F=4096, reps=5):
     gbs = byts / (ms * 1e-3) / 1e9
     del bufs
     torch.cuda.empty_cache()
+    traffic = measured_traffic("nvfp4_to_mxfp4", "convert")   # both launches
     return {"workload": "nvfp4_to_mxfp4", "what": f"all {E} experts' gate/up and down weights, "
             "NVFP4 -> MXFP4 (load time, two launches)", "elements": n, "ms": round(ms, 4),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                         "traffic_over_algorithmic": None if traffic is None else round(traffic / byts, 3),
                          "kernel": "nvfp4_to_mxfp4_kernel", "algorithmic_bytes": int(byts)}}
 
 
