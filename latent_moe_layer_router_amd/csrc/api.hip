@@ -139,6 +139,7 @@ struct lmoe_ctx {
   Plan plan;
   unsigned char* ws;
   bool timing;
+  bool masks_dirty;                 // top-k ran without the sort that clears the masks
   std::vector<hipEvent_t> events;   // LMOE_NUM_STAGES + 1 per timed forward
   float acc_ms[LMOE_NUM_STAGES];
   int n_timed;
@@ -263,6 +264,7 @@ lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, lmoe_hand
     return fail(LMOE_E_HIP, "clearing the workspace failed");
   }
   h->timing = false;
+  h->masks_dirty = false;
   memset(h->acc_ms, 0, sizeof(h->acc_ms));
   h->n_timed = 0;
   *out = h;
@@ -393,10 +395,13 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     ++stage;
   };
 
+  // After the first failed launch nothing more is enqueued (later kernels would
+  // read tile lists and offsets that were never written).
   hipError_t err = hipSuccess;
-  auto run = [&](hipError_t e) {
-    if (err == hipSuccess) err = e;
-  };
+#define run(X)                    \
+  do {                            \
+    if (err == hipSuccess) err = (X); \
+  } while (0)
 
   // Small batches: the dense projections stream their weights with split-K.
   const bool dense_stream = bf16 && T <= dense_stream_max_tokens();
@@ -475,7 +480,14 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   // 2. top-k + softmax + chunk masks
   mark();
   uint64_t* masks = reinterpret_cast<uint64_t*>(ws + pl.masks);
+  // The top-k kernel ORs into the chunk masks and the sort clears them; if a
+  // previous call stopped between the two, clear them first.
+  if (h->masks_dirty) {
+    run(hipMemsetAsync(masks, 0, pl.chunk_base - pl.masks, s));
+    if (err == hipSuccess) h->masks_dirty = false;
+  }
   run(launch_topk(logits, T, E, k, ids, tw, masks, s));
+  if (err == hipSuccess) h->masks_dirty = true;
   // 3. counting sort + tile list
   mark();
   {
@@ -498,6 +510,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     sp.mt_off = mt_off;
     sp.tile_m2 = gemm256_tile_m();
     run(launch_sort(sp, s));
+    if (err == hipSuccess) h->masks_dirty = false;
   }
   // 4. pooled RMSNorm
   mark();
@@ -732,6 +745,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   if (aux && aux->sorted_assign)
     run(hipMemcpyAsync(aux->sorted_assign, sorted_assign, sizeof(int32_t) * (size_t)T * k,
                        hipMemcpyDeviceToDevice, s));
+#undef run
   if (timing) h->events.insert(h->events.end(), ev, ev + LMOE_NUM_STAGES + 1);
   if (cur != h->device) (void)hipSetDevice(cur);
   if (err != hipSuccess) return fail(LMOE_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));
