@@ -372,7 +372,9 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
                         (int64_t)T * k * Dp * 2 < ((int64_t)1 << 31) &&
                         (int64_t)2 * F * Dp * 2 < ((int64_t)1 << 31);
   const bool stream_ok = bf16 && !mx && Dp % 128 == 0 && F % 128 == 0 && off32_ok;
-  const int small_max = stream_ok ? stream_max_rows() : 0;
+  // MXFP4 experts: the create-time checks (Dp and F multiples of 1024, 32-bit
+  // byte extents) are all the MX weight-streaming kernel needs.
+  const int small_max = stream_ok ? stream_max_rows() : (mx ? stream_mx_max_rows() : 0);
   // Experts with many rows: the 256 x 256 tile GEMM (bf16, Dp % 256 == 0, F % 128 == 0).
   const bool big_ok = bf16 && !mx && Dp % 256 == 0 && F % 128 == 0 && off32_ok;
   int32_t* mt_off = reinterpret_cast<int32_t*>(ws + pl.mt_off);
@@ -540,6 +542,29 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     run(launch_stream(sp, EPI_SWIGLU, s));
   }
   if (mx) {
+    StreamMxParams sp{};
+    sp.A = xq;
+    sp.As = xs;
+    sp.B = static_cast<const uint8_t*>(h->w.w_gate_up);
+    sp.Bs = h->w.s_gate_up;
+    sp.N = 2 * F;
+    sp.offsets = offsets;
+    sp.n_experts = E;
+    sp.groups = F / 32;
+    sp.max_rows = small_max;
+    sp.K = Dp;
+    sp.F = F;
+    sp.a_bytes = (uint32_t)(A_ * Dp);
+    sp.as_bytes = (uint32_t)(A_ * Dp / 32);
+    sp.b_bytes = (uint32_t)((int64_t)F * Dp);
+    sp.bs_bytes = (uint32_t)((int64_t)2 * F * Dp / 32);
+    sp.out = hq;
+    sp.ldo = F;
+    sp.out_scales = hs;
+    sp.ldos = F / 32;
+    run(launch_stream_mx(sp, EPI_SWIGLU, s));
+  }
+  if (mx) {
     Gemm256MxParams g{};
     g.A = xq;
     g.As = xs;
@@ -619,6 +644,29 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     sp.ss_out = ss;
     sp.ss_ld = Dp / 64;
     run(launch_stream(sp, EPI_DOWN, s));
+  }
+  if (mx) {
+    StreamMxParams sp{};
+    sp.A = hq;
+    sp.As = hs;
+    sp.B = static_cast<const uint8_t*>(h->w.w_down);
+    sp.Bs = h->w.s_down;
+    sp.N = Dp;
+    sp.offsets = offsets;
+    sp.n_experts = E;
+    sp.groups = Dp / 64;
+    sp.max_rows = small_max;
+    sp.K = F;
+    sp.F = F;
+    sp.a_bytes = (uint32_t)(A_ * F);
+    sp.as_bytes = (uint32_t)(A_ * F / 32);
+    sp.b_bytes = (uint32_t)((int64_t)Dp * F / 2);
+    sp.bs_bytes = (uint32_t)((int64_t)Dp * F / 32);
+    sp.out = Y;
+    sp.ldo = Dp;
+    sp.ss_out = ss;
+    sp.ss_ld = Dp / 64;
+    run(launch_stream_mx(sp, EPI_DOWN, s));
   }
   if (mx) {
     Gemm256MxParams g{};

@@ -156,6 +156,36 @@ struct Gemm256MxParams {
 };
 hipError_t launch_gemm256_mx(const Gemm256MxParams& p, EpiKind epi, hipStream_t s);
 
+// Weight-streaming grouped GEMM of the MXFP4-expert path for experts with
+// 1..max_rows rows (max_rows <= stream_mx_max_rows()); one wave per (expert,
+// group of 64 weight rows). K a multiple of 1024.
+// Same operand and output formats as Gemm256MxParams.
+struct StreamMxParams {
+  const uint8_t* A;            // [rows][K] E4M3 codes, rows in sorted order
+  const uint8_t* As;           // [rows][K/32] E8M0 scales
+  const uint8_t* B;            // [E][N][K/2] E2M1 codes
+  const uint8_t* Bs;           // [E][N][K/32] E8M0 scales
+  int N;                       // B rows per expert (2F for gate/up, Dp for down)
+  const int32_t* offsets;      // [E+1]
+  int n_experts;
+  int groups;                  // F/32 for SwiGLU, Dp/64 for down
+  int max_rows;
+  int K;
+  int F;
+  uint32_t a_bytes;            // extents of A and As in bytes (below 2^31)
+  uint32_t as_bytes;
+  uint32_t b_bytes;            // extents of one expert's B and Bs in bytes (below 2^31)
+  uint32_t bs_bytes;
+  void* out;                   // EPI_SWIGLU: [rows][ldo] E4M3 codes; EPI_DOWN: [rows][ldo] bf16
+  int64_t ldo;
+  uint8_t* out_scales;         // EPI_SWIGLU: [rows][ldos] E8M0
+  int64_t ldos;
+  float* ss_out;               // EPI_DOWN: [rows][ss_ld]
+  int ss_ld;
+};
+int stream_mx_max_rows();
+hipError_t launch_stream_mx(const StreamMxParams& p, EpiKind epi, hipStream_t s);
+
 // Router top-k + softmax; also builds, per chunk of 64 tokens, a bitmask of
 // the chunk's tokens that selected each expert (ORed into chunk_masks, which
 // must be zero on entry; launch_sort leaves them zero again).

@@ -8,7 +8,11 @@ inputs on the block-scaled MFMA) against the CPU oracle.
   MXFP4 weights and quantizes xp and h to MXFP8 at the same points) within
   max|err|/RMS(out) <= 6e-2, at small multi-tile shapes and at the full size on
   a seeded 64-token subset of the 16K prefill chunk.
+* Experts with at most 32 rows take the MX weight-streaming kernel, the rest
+  the 256-row tiles: row counts at the boundaries (0, 1, 16, 17, 32, 33), both
+  GEMMs at K = 1024, 2048 and 4096, and the full-size decode batch (T=128).
 """
+import dataclasses
 import numpy as np
 import pytest
 import torch
@@ -19,7 +23,7 @@ import synth
 from synth import device as sdev
 from tests import harness as H
 from tests.pins import tiny
-from tests.test_gpu_parity import run_case
+from tests.test_gpu_parity import run_case, run_crafted
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -127,6 +131,58 @@ def test_mx_full_size_prefill_subset():
     keep = ~near[rows]
     err = H.out_error(got[rows][keep], ref[keep])
     H.say(f"[gpu]   mxfp4: max|err|/rms = {err:.3e} on {int(keep.sum())} tokens")
+    assert err <= H.tol(w), err
+    del tw
+    torch.cuda.empty_cache()
+
+
+def test_mx_stream_row_boundaries():
+    """Experts with 32 rows (the MX weight-streaming kernel's limit: two token
+    tiles), 33 (the tiled GEMM), 17 and 16 (two and one token tiles), 1 and 0
+    rows in one call."""
+    assign = np.array([0] * 32 + [1] * 33 + [2] * 17 + [3] * 16 + [4], np.int64)
+    w = mx_tiny(T=len(assign), D=256, Dp=1024, F_=1024, E=6, k=1, seed=220)
+    a = run_crafted(w, assign)
+    assert np.diff(a["expert_offsets"]).tolist() == [32, 33, 17, 16, 1, 0]
+
+
+@pytest.mark.parametrize("Dp,F_", [(2048, 1024), (1024, 4096), (4096, 2048)])
+def test_mx_stream_k_sizes(Dp, F_):
+    """A few rows per expert (all streamed), gate/up over K = Dp and down over
+    K = F of different sizes."""
+    w = mx_tiny(T=24, D=256, Dp=Dp, F_=F_, E=16, k=4, seed=230 + Dp // 1024 + F_ // 512)
+    _, a = run_case(w)
+    assert np.diff(a["expert_offsets"]).max() <= 32
+
+
+def test_mx_full_size_decode_subset():
+    """Full shapes (D=8192, Dp=F=4096, E=256, k=8) at the decode batch T=128,
+    MXFP4 experts: every expert gets a few rows, so both expert GEMMs stream
+    their weights. Selection and permutation on every token, the output on a
+    seeded 64-token subset."""
+    w = dataclasses.replace(synth.WORKLOADS["mxfp4"], T=128, name="mxfp4_decode")
+    H.say("[gpu] mxfp4 full size, T=128: uploading weights")
+    tw = sdev.upload_weights(w, DEV)
+    hw = H.host_weights(w, with_experts=False)
+    block = lmoe.LatentMoE(tw, w.k, w.T, w.eps_pool, w.eps_expert, out_dtype=torch.float32)
+    x = synth.x(w)
+    out, aux = block.forward(sdev.to_device(x, DEV), aux=True)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    a = {n: t.cpu().numpy() for n, t in aux.items()}
+    block.close()
+    counts = np.diff(a["expert_offsets"])
+    assert counts.max() <= 32, counts.max()
+    O = oracle.default()
+    logits = O.router(x, hw["w_router"], hw.get("b_router"))
+    ids, wts = O.topk_softmax(logits, w.k)
+    near = H.check_routing(a["topk_ids"], a["topk_w"], a["logits"], logits, ids, wts, w.k)
+    H.check_permutation(a["topk_ids"], a["expert_offsets"], a["sorted_assign"], w.E)
+    rows = synth.subset(w)
+    ref, _ = H.oracle_ref(w, x[rows], hw)
+    keep = ~near[rows]
+    err = H.out_error(got[rows][keep], ref[keep])
+    H.say(f"[gpu]   mxfp4 decode: max|err|/rms = {err:.3e} on {int(keep.sum())} tokens")
     assert err <= H.tol(w), err
     del tw
     torch.cuda.empty_cache()

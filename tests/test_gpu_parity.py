@@ -125,7 +125,7 @@ def run_crafted(w, assign):
     H.check_permutation(a["topk_ids"], a["expert_offsets"], a["sorted_assign"], w.E)
     err = H.out_error(got, ref)
     H.say(f"[gpu]   max|err|/rms = {err:.3e}")
-    assert err <= H.TOL[w.act]
+    assert err <= H.tol(w), err
     block.close()
     return a
 
