@@ -14,13 +14,15 @@
 // direct global-to-LDS loads of 8 rows x 128 bytes, non-temporal, with the
 // 16-byte chunk c of row r at position c ^ f(r), f(r) = ((r >> 1) ^ (r << 2)) & 7
 // (conflict-free fragment reads). Token rows (fp8, 256 bytes per stage) and
-// the scales of both operands (8 bytes per row and stage) go straight to
-// registers: the token rows are re-read by every wave of the expert and come
-// from L2, each weight-scale line is re-read over 16 stages, and keeping them
-// out of LDS leaves 16 KiB of LDS per wave. (Scale bytes read from LDS would
-// also sit behind the weight loads: the compiler cannot tell them apart from
-// the LDS being filled and waits for all loads first.) Two stages: the loads
-// of the next stage are in flight while the current one is multiplied.
+// the scales of both operands go straight to registers: the token rows are
+// re-read by every wave of the expert and come from L2, and keeping them out
+// of LDS leaves 16 KiB of LDS per wave. (Scale bytes read from LDS would also
+// sit behind the weight loads: the compiler cannot tell them apart from the
+// LDS being filled and waits for all loads first.) The scales come 32 bytes
+// per row at a time, every 4 stages: loading 8 bytes per row every stage
+// issued as many requests as the weights themselves and cost about a fifth of
+// the rate. Two stages: the loads of the next stage are in flight while the
+// current one is multiplied.
 //
 // Scaled-MFMA operand layout (gfx950, 16x16x128; lane l: row r = l % 16 of the
 // operand, group q = l / 16):
@@ -99,10 +101,15 @@ __device__ __forceinline__ void stream_mx_body(const StreamMxParams& p, int e, i
     const int lr = 8 * j + lrow;
     wo[j] = (uint32_t)wrow(lr) * (uint32_t)wrow_bytes + (uint32_t)((lc ^ swz8(lr)) << 4);
   }
-  // Weight scales: tile t, row t*16 + r16; 8 bytes per stage.
+  // Scales, per group of 4 stages (1024 K-columns: 32 bytes of each row): lane
+  // (r16, q) loads bytes [8q, 8q + 8) of the group's 32 for row r16 of every
+  // weight tile and token tile, so that one load covers 16 rows x 32 contiguous
+  // bytes. The byte a lane needs for K-step ks of stage c (K-block
+  // 8c + 4 ks + q) then sits in lane r16 + 16 (c % 4), word ks, byte q, and a
+  // lane shuffle fetches it.
   uint32_t wso[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) wso[t] = (uint32_t)wrow(t * 16 + r16) * (uint32_t)rs;
+  for (int t = 0; t < 4; ++t) wso[t] = (uint32_t)wrow(t * 16 + r16) * (uint32_t)rs + 8 * q;
   // Tokens: tile mt, row r16 (rows past the expert's end read its last row;
   // never stored), the lane's 16-byte column q.
   uint32_t ao[NMT], aso[NMT];
@@ -111,24 +118,29 @@ __device__ __forceinline__ void stream_mx_body(const StreamMxParams& p, int e, i
     const int tr = mt * 16 + r16;
     const int pos = lo + (tr < m_e ? tr : m_e - 1);
     ao[mt] = (uint32_t)pos * (uint32_t)K + 16 * q;
-    aso[mt] = (uint32_t)pos * (uint32_t)rs;
+    aso[mt] = (uint32_t)pos * (uint32_t)rs + 8 * q;
   }
 
-#define LMOE_ISSUE(c, SW, TA, TS, WS)                                                                \
+  // Loads of stage c: weights through LDS, tokens to registers; with SC, also
+  // the scales of group g.
+#define LMOE_ISSUE(c, SW, TA, SC, g, WS, TS)                                                      \
   {                                                                                               \
     const int c_ = (c);                                                                           \
     _Pragma("unroll") for (int j = 0; j < 8; ++j)                                                 \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (LMOE_AS3 void*)((SW) + 1024 * j), 16,        \
                                                (int)wo[j], c_ * 128, 0, 2);                       \
-    _Pragma("unroll") for (int mt = 0; mt < NMT; ++mt) {                                          \
+    _Pragma("unroll") for (int mt = 0; mt < NMT; ++mt)                                            \
       _Pragma("unroll") for (int ks = 0; ks < 2; ++ks)                                            \
         _Pragma("unroll") for (int h = 0; h < 2; ++h)                                             \
           TA[mt][ks].h[h] = __builtin_amdgcn_raw_buffer_load_b128(rsA, (int)ao[mt] + 128 * ks + 64 * h, \
                                                                   c_ * XKC, 0);                  \
-      TS[mt] = __builtin_amdgcn_raw_buffer_load_b64(rsAs, (int)aso[mt], c_ * 8, 0);              \
+    if (SC) {                                                                                     \
+      const int g_ = (g);                                                                         \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t)                                               \
+        WS[t] = __builtin_amdgcn_raw_buffer_load_b64(rsBs, (int)wso[t], g_ * 32, 0);              \
+      _Pragma("unroll") for (int mt = 0; mt < NMT; ++mt)                                          \
+        TS[mt] = __builtin_amdgcn_raw_buffer_load_b64(rsAs, (int)aso[mt], g_ * 32, 0);            \
     }                                                                                             \
-    _Pragma("unroll") for (int t = 0; t < 4; ++t)                                                 \
-      WS[t] = __builtin_amdgcn_raw_buffer_load_b64(rsBs, (int)wso[t], c_ * 8, 0);                 \
   }
 
   f32x4_t acc[NMT][4];
@@ -143,22 +155,22 @@ __device__ __forceinline__ void stream_mx_body(const StreamMxParams& p, int e, i
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) fo[ks] = r16 * 128 + (((4 * ks + q) ^ swz8(r16)) << 4);
 
-// The scale byte of the lane for K-step ks is byte q of word ks of the stage's
-// 8 bytes (K-block 8c + 4 ks + q).
-#define LMOE_COMPUTE(SW, TA, TS, WS)                                                              \
+  // Stage c = 4 g + i of its group (i static).
+#define LMOE_COMPUTE(i, SW, TA, WS, TS)                                                           \
   {                                                                                               \
+    const int src_ = 4 * (r16 + 16 * (i));                                                        \
     _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                            \
       uint4 b[4];                                                                                 \
       int sb[4];                                                                                  \
       _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                             \
         b[t] = *reinterpret_cast<const uint4*>((SW) + t * 2048 + fo[ks]);                         \
-        sb[t] = (int)(WS[t][ks] >> (8 * q));                                                      \
+        sb[t] = __builtin_amdgcn_ds_bpermute(src_, (int)WS[t][ks]) >> (8 * q);                    \
       }                                                                                           \
       _Pragma("unroll") for (int mt = 0; mt < NMT; ++mt) {                                        \
         const i32x8_t av = {(int)TA[mt][ks].h[0].x, (int)TA[mt][ks].h[0].y, (int)TA[mt][ks].h[0].z,  \
                             (int)TA[mt][ks].h[0].w, (int)TA[mt][ks].h[1].x, (int)TA[mt][ks].h[1].y,  \
                             (int)TA[mt][ks].h[1].z, (int)TA[mt][ks].h[1].w};                      \
-        const int sa = (int)(TS[mt][ks] >> (8 * q));                                              \
+        const int sa = __builtin_amdgcn_ds_bpermute(src_, (int)TS[mt][ks]) >> (8 * q);            \
         _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                           \
           const i32x8_t bv = {(int)b[t].x, (int)b[t].y, (int)b[t].z, (int)b[t].w, 0, 0, 0, 0};    \
           acc[mt][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mt][t], 0, 4, 0, sa, \
@@ -167,27 +179,41 @@ __device__ __forceinline__ void stream_mx_body(const StreamMxParams& p, int e, i
       }                                                                                           \
     }                                                                                             \
   }
-  // One stage: the previous reads of the weight buffer about to be refilled are
-  // done (all LDS reads complete), start the next stage's loads (at the end a
-  // harmless repeat of the last stage into buffers no later stage reads), wait
-  // until only those are outstanding, then an LDS acquire fence keeps the
-  // stage's reads below the wait, and multiply.
-#define LMOE_STAGE(c, SW, TA, TS, WS, NW, NTA, NTS, NWS)                                          \
+  // One stage (c = 4 g + i): the previous reads of the weight buffer about to
+  // be refilled are done (all LDS reads complete), start the next stage's loads
+  // (with the next group's scales after the group's last stage; at the end a
+  // harmless repeat of the last stage and group into buffers no later stage
+  // reads), wait until only those are outstanding, then an LDS acquire fence
+  // keeps the stage's reads below the wait, and multiply. The scheduling
+  // barrier keeps every load of the next stage ahead of the current stage's
+  // work (which otherwise gets hoisted between them, with waits for its
+  // operands).
+#define LMOE_STAGE(c, i, SW, TA, WS, TS, NW, NTA, NWS, NTS)                                       \
   {                                                                                               \
     __builtin_amdgcn_s_waitcnt(kLdsIdle);                                                         \
-    LMOE_ISSUE(((c) + 1 < nc ? (c) + 1 : nc - 1), NW, NTA, NTS, NWS)                               \
+    LMOE_ISSUE(((c) + 1 < nc ? (c) + 1 : nc - 1), NW, NTA, (i) == 3,                              \
+               ((c) + 1 < nc ? ((c) + 1) / 4 : nc / 4 - 1), NWS, NTS)                             \
     __builtin_amdgcn_sched_barrier(0);                                                            \
-    __builtin_amdgcn_s_waitcnt(vm_wait(12 + 5 * NMT));                                            \
+    __builtin_amdgcn_s_waitcnt(vm_wait(8 + 4 * NMT + ((i) == 3 ? 4 + NMT : 0)));                  \
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");                              \
-    LMOE_COMPUTE(SW, TA, TS, WS)                                                                  \
+    LMOE_COMPUTE(i, SW, TA, WS, TS)                                                               \
   }
   const int nc = K / XKC;                     // a multiple of 4 (K % 1024 == 0)
   TokStep ta0[NMT][2], ta1[NMT][2];
-  u32x2_t ts0[NMT], ts1[NMT], ws0[4], ws1[4];
-  LMOE_ISSUE(0, xw0, ta0, ts0, ws0)
-  for (int c = 0; c < nc; c += 2) {
-    LMOE_STAGE(c, xw0, ta0, ts0, ws0, xw1, ta1, ts1, ws1)
-    LMOE_STAGE(c + 1, xw1, ta1, ts1, ws1, xw0, ta0, ts0, ws0)
+  u32x2_t ws0[4], ws1[4], ts0[NMT], ts1[NMT];
+  LMOE_ISSUE(0, xw0, ta0, true, 0, ws0, ts0)
+  for (int c = 0; c < nc; c += 8) {
+    // group c / 4 (scales in ws0, ts0), then group c / 4 + 1 (ws1, ts1) if any
+    LMOE_STAGE(c, 0, xw0, ta0, ws0, ts0, xw1, ta1, ws1, ts1)
+    LMOE_STAGE(c + 1, 1, xw1, ta1, ws0, ts0, xw0, ta0, ws1, ts1)
+    LMOE_STAGE(c + 2, 2, xw0, ta0, ws0, ts0, xw1, ta1, ws1, ts1)
+    LMOE_STAGE(c + 3, 3, xw1, ta1, ws0, ts0, xw0, ta0, ws1, ts1)
+    if (c + 4 < nc) {
+      LMOE_STAGE(c + 4, 0, xw0, ta0, ws1, ts1, xw1, ta1, ws0, ts0)
+      LMOE_STAGE(c + 5, 1, xw1, ta1, ws1, ts1, xw0, ta0, ws0, ts0)
+      LMOE_STAGE(c + 6, 2, xw0, ta0, ws1, ts1, xw1, ta1, ws0, ts0)
+      LMOE_STAGE(c + 7, 3, xw1, ta1, ws1, ts1, xw0, ta0, ws0, ts0)
+    }
   }
 #undef LMOE_STAGE
 #undef LMOE_COMPUTE
