@@ -1,7 +1,7 @@
 """Benchmark of the latent-MoE block forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_bf16]
-                    [--also prefill_bf16,mxfp4] [--no-cpu-baseline] [--no-convert]
+                    [--also prefill_bf16,mxfp4,mxfp4_decode] [--no-cpu-baseline] [--no-convert]
 
 A step is one lmoe_forward over one batch of synthetic tokens already resident
 in HBM: routing, permutation, pooler, experts, combine, unpooler. The headline
@@ -9,7 +9,8 @@ workload is decode-sized (T=128 tokens; D=8192, Dp=4096, F=4096, E=256, k=8,
 bf16), which streams the touched experts' weights and is bound by HBM; the
 prefill chunk (T=16384) is reported beside it against the bf16 MFMA peak, and
 the same chunk with MXFP4 experts (MXFP8 expert inputs) against the fp8 peak,
-and the load-time NVFP4 -> MXFP4 re-encoding of a layer's experts against HBM.
+the decode batch with MXFP4 experts against HBM, and the load-time NVFP4 ->
+MXFP4 re-encoding of a layer's experts against HBM.
 Prints one JSON line. Weights are random-initialized (seed 0) with the model's
 shapes; inputs are synthetic (see synth/).
 """
@@ -87,10 +88,11 @@ def run_workload(lmoe, torch, synth, sdev, block, w, steps, warmup, dev):
 
 
 # The gate/up kernel of each regime and the sources that define it: the
-# weight-streaming kernel for decode-sized batches, the 256 x 256 tile GEMM for
-# prefill-sized ones.
+# weight-streaming kernels for decode-sized batches, the 256 x 256 tile GEMMs
+# for prefill-sized ones (bf16 or MXFP4 experts).
 CSRC = os.path.join(ROOT, "latent_moe_layer_router_amd", "csrc")
 GATE_UP_KERNEL = {"hbm": ("stream_kernel<EPI_SWIGLU>", ("stream.hip", "common.h")),
+                  "hbm_mx": ("stream_mx_kernel<EPI_SWIGLU>", ("stream_mx.hip", "mx.h", "common.h")),
                   "mfma": ("gemm256_kernel<EPI_SWIGLU>", ("gemm256.hip", "common.h")),
                   "mfma_mx": ("gemm256_mx_kernel<EPI_SWIGLU>", ("gemm256_mx.hip", "mx.h", "common.h")),
                   "convert": ("nvfp4_to_mxfp4_kernel", ("convert.hip", "common.h"))}
@@ -132,7 +134,7 @@ def roofline(w, stage_ms, n_active, bound):
               "traffic": traffic, "algorithmic_bytes": byts,
               "traffic_over_algorithmic": None if traffic is None else round(traffic / byts, 3),
               "avg_ms": round(stage_ms["gate_up"], 4)}
-    if bound == "hbm":
+    if bound in ("hbm", "hbm_mx"):
         ach = byts / t / 1e9
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), **common}
@@ -140,6 +142,15 @@ def roofline(w, stage_ms, n_active, bound):
     peak = PEAK_FP8_TFLOPS if bound == "mfma_mx" else PEAK_BF16_TFLOPS
     return {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
             "frac": round(ach / peak, 4), "algorithmic_flops": flops, **common}
+
+
+def regime(w):
+    """The gate/up kernel a workload runs on: weight streaming when every expert
+    gets a few rows (decode batches: T * k / E = 4 here), else the tiles."""
+    decode = w.T * w.k <= 4 * w.E
+    if w.mx_act:
+        return "hbm_mx" if decode else "mfma_mx"
+    return "hbm" if decode else "mfma"
 
 
 def cpu_baseline(synth, w):
@@ -217,7 +228,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_bf16")
-    ap.add_argument("--also", default="prefill_bf16,mxfp4",
+    ap.add_argument("--also", default="prefill_bf16,mxfp4,mxfp4_decode",
                     help="comma-separated extra workloads, or ''")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-convert", action="store_true",
@@ -265,7 +276,7 @@ def main():
         "config": {"workload": w.name, "T": w.T, "D": w.D, "Dp": w.Dp, "F": w.F, "E": w.E, "k": w.k,
                    "out_dtype": "f32", "active_experts": n_active},
         "step_hbm_frac": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "roofline": roofline(w, stage_ms, n_active, "hbm"),
+        "roofline": roofline(w, stage_ms, n_active, regime(w)),
         "stages_ms": {s: round(v, 4) for s, v in stage_ms.items()},
     }
     also = []
@@ -289,7 +300,7 @@ def main():
         entry = {"workload": e.name, "T": e.T, "expert_weights": e.expert_w,
                  "value": round(e.T / (ems * 1e-3), 1), "unit": "tokens/s",
                  "ms_per_step": round(ems, 4), "step_tflops": round(ef / (ems * 1e-3) / 1e12, 1),
-                 "roofline": roofline(e, est, ena, "mfma_mx" if e.mx_act else "mfma"),
+                 "roofline": roofline(e, est, ena, regime(e)),
                  "stages_ms": {s: round(v, 4) for s, v in est.items()}}
         if not e.mx_act:
             entry["step_mfma_frac"] = round(ef / (ems * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)

@@ -67,6 +67,7 @@ WORKLOADS = {
     "skewed_bf16": Workload("skewed_bf16", 4096, 8192, 4096, 4096, 256, 8, BF16, BF16, x_seed=3,
                             skew=True),
     "mxfp4": Workload("mxfp4", 16384, 8192, 4096, 4096, 256, 8, BF16, MXFP4, x_seed=2),
+    "mxfp4_decode": Workload("mxfp4_decode", 128, 8192, 4096, 4096, 256, 8, BF16, MXFP4, x_seed=1),
 }
 
 

@@ -12,7 +12,6 @@ inputs on the block-scaled MFMA) against the CPU oracle.
   the 256-row tiles: row counts at the boundaries (0, 1, 16, 17, 32, 33), both
   GEMMs at K = 1024, 2048 and 4096, and the full-size decode batch (T=128).
 """
-import dataclasses
 import numpy as np
 import pytest
 import torch
@@ -160,7 +159,7 @@ def test_mx_full_size_decode_subset():
     MXFP4 experts: every expert gets a few rows, so both expert GEMMs stream
     their weights. Selection and permutation on every token, the output on a
     seeded 64-token subset."""
-    w = dataclasses.replace(synth.WORKLOADS["mxfp4"], T=128, name="mxfp4_decode")
+    w = synth.WORKLOADS["mxfp4_decode"]
     H.say("[gpu] mxfp4 full size, T=128: uploading weights")
     tw = sdev.upload_weights(w, DEV)
     hw = H.host_weights(w, with_experts=False)
