@@ -17,18 +17,23 @@
 // one scale byte out, so consecutive threads touch consecutive bytes. A thread
 // reads its whole block before it writes, which lets the output codes overwrite
 // the input codes in place.
+//
+// The E2M1 steps use gfx950's scaled FP4 conversions. With a scale of 1 the
+// FP4 -> FP32 conversion gives the signed E2M1 values (two per instruction);
+// with a power-of-two scale 2^X the FP32 -> FP4 conversion gives v / 2^X
+// rounded to the E2M1 grid, ties to even, saturating at 6: on the device this
+// matched that rule on every value tried (dense sweeps over [0, 8] with
+// scales 2^-127 .. 2^127, both neighbours of every tie, infinities, FP32
+// subnormals). Both conversions take only the exponent of the scale, so the
+// UE4M3 block scale is applied by a multiply. The conversion keeps the sign of
+// a negative zero (code 8) where the rule above gives code 0 (a sign bit only
+// for values below zero), so negative zeros are cleared first.
 #include "common.h"
 #include "kernels.h"
 
 namespace lmoe {
 
 namespace {
-
-// Twice the E2M1 magnitude of code m (0..7) is the integer 0, 1, 2, 3, 4, 6, 8
-// or 12: one byte permute picks it from two constant words.
-__device__ __forceinline__ float e2m1_twice(uint32_t m) {
-  return (float)(__builtin_amdgcn_perm(0x0C080604u, 0x03020100u, m) & 0xFFu);
-}
 
 // Unsigned E4M3 (bias 7; code 0x7F is NaN, handled by the caller).
 __device__ __forceinline__ float ue4m3_value(uint32_t s) {
@@ -37,42 +42,50 @@ __device__ __forceinline__ float ue4m3_value(uint32_t s) {
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
-// E2M1 magnitude code of q in [0, 8): nearest, ties to even, saturating at 6.
-// Below 1 the grid step is 0.5, so the code is rint(2q) (0, 1 or 2). From 1 up
-// the code is the float's exponent and top mantissa bit, so rounding q's bit
-// pattern to one mantissa bit (ties to even) gives it directly; 8 and above
-// saturate to code 7 (6.0).
-__device__ __forceinline__ uint32_t e2m1_mag_code(float q) {
-  const uint32_t b = __float_as_uint(q);
-  const uint32_t hi = ((b + 0x1FFFFFu + ((b >> 22) & 1u)) >> 22) - 252u;
-  const uint32_t lo = (uint32_t)__builtin_rintf(q + q);
-  return q < 1.f ? lo : (hi > 7u ? 7u : hi);
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+
+// The two E2M1 values of byte S of w (low nibble first) as floats.
+template <int S>
+__device__ __forceinline__ f32x2_t fp4_pair(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, S);
+}
+// w with byte S replaced by the E2M1 codes of a / sx (low nibble) and b / sx.
+template <int S>
+__device__ __forceinline__ uint32_t fp4_put(uint32_t w, float a, float b, float sx) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, sx, S);
 }
 
 __global__ __launch_bounds__(256) void nvfp4_to_mxfp4_kernel(const uint8_t* codes, const uint8_t* scales16,
-                                                             const float* __restrict__ gscale, int64_t rows,
-                                                             int64_t nb, int64_t total, uint8_t* out_codes,
+                                                             const float* __restrict__ gscale, int64_t n_mats,
+                                                             int64_t per_mat, uint8_t* out_codes,
                                                              uint8_t* __restrict__ out_scales) {
-  for (int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; b < total;
-       b += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t m = b / (rows * nb);
-    const float g = gscale[m];
+  // matrices over grid rows, each matrix's blocks over the grid's columns
+  for (int64_t m = blockIdx.y; m < n_mats; m += gridDim.y) {
+  const float g = gscale[m];
+  for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < per_mat;
+       bi += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t b = m * per_mat + bi;
     const uint4 cw = *reinterpret_cast<const uint4*>(codes + 16 * b);
     const uint32_t s2 = *reinterpret_cast<const uint16_t*>(scales16 + 2 * b);
     const uint32_t s0 = s2 & 0x7Fu, s1 = (s2 >> 8) & 0x7Fu;
     bool bad = !(fabsf(g) <= 3.402823466e38f) || s0 == 0x7Fu || s1 == 0x7Fu;
-    // half the block scales: e2m1 * ue4m3 = (2 e2m1) * (ue4m3 / 2), both exact
-    const float hsc[2] = {0.5f * ue4m3_value(s0), 0.5f * ue4m3_value(s1)};
+    const float sc[2] = {ue4m3_value(s0), ue4m3_value(s1)};
     const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
     float v[32];
     float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint32_t c = (w[i >> 3] >> (4 * (i & 7))) & 15u;
-      const float mag = e2m1_twice(c & 7u) * hsc[i >> 4];
-      const float p = __uint_as_float(__float_as_uint(mag) ^ ((c & 8u) << 28));
-      v[i] = p * g;
-      amax = fmaxf(amax, fabsf(v[i]));
+    for (int j = 0; j < 4; ++j) {
+      // elements 2i (low nibble) and 2i + 1 of byte i = 4j + t; e2m1 * ue4m3 is
+      // exact, the product with g rounds once (an fma with +0, which also turns
+      // a negative zero into +0)
+      const f32x2_t e[4] = {fp4_pair<0>(w[j]), fp4_pair<1>(w[j]), fp4_pair<2>(w[j]), fp4_pair<3>(w[j])};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int i = 4 * j + t;
+        v[2 * i] = fmaf(e[t].x * sc[i >> 3], g, 0.f);
+        v[2 * i + 1] = fmaf(e[t].y * sc[i >> 3], g, 0.f);
+        amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
+      }
     }
     if (!(amax <= 3.402823466e38f)) bad = true;
     uint32_t o[4] = {0u, 0u, 0u, 0u};
@@ -85,15 +98,19 @@ __global__ __launch_bounds__(256) void nvfp4_to_mxfp4_kernel(const uint8_t* code
         X = X < -127 ? -127 : X;
       }
       scale = (uint8_t)(X + 127);
-      // 2^-X for X in [-127, 125] is a normal float; |v| * 2^-X is exact (or far
-      // below the grid's first step)
-      const float inv = __uint_as_float((uint32_t)(127 - X) << 23);
+      // 2^X as a float (2^-127 is the subnormal 0x00400000)
+      const float sx = __uint_as_float(X == -127 ? 0x00400000u : (uint32_t)(X + 127) << 23);
 #pragma unroll
-      for (int i = 0; i < 32; ++i)
-        o[i >> 3] |= (e2m1_mag_code(fabsf(v[i]) * inv) | (v[i] < 0.f ? 8u : 0u)) << (4 * (i & 7));
+      for (int j = 0; j < 4; ++j) {
+        o[j] = fp4_put<0>(o[j], v[8 * j], v[8 * j + 1], sx);
+        o[j] = fp4_put<1>(o[j], v[8 * j + 2], v[8 * j + 3], sx);
+        o[j] = fp4_put<2>(o[j], v[8 * j + 4], v[8 * j + 5], sx);
+        o[j] = fp4_put<3>(o[j], v[8 * j + 6], v[8 * j + 7], sx);
+      }
     }
     *reinterpret_cast<uint4*>(out_codes + 16 * b) = uint4{o[0], o[1], o[2], o[3]};
     out_scales[b] = scale;
+  }
   }
 }
 
@@ -102,12 +119,14 @@ __global__ __launch_bounds__(256) void nvfp4_to_mxfp4_kernel(const uint8_t* code
 hipError_t launch_nvfp4_to_mxfp4(const uint8_t* codes, const uint8_t* scales16, const float* gscale,
                                  int64_t n_mats, int64_t rows, int64_t cols, uint8_t* out_codes,
                                  uint8_t* out_scales, hipStream_t s) {
-  const int64_t nb = cols / 32, total = n_mats * rows * nb;
-  if (total == 0) return hipSuccess;
-  const int64_t want = (total + 255) / 256;
-  const int grid = (int)(want < 8192 ? want : 8192);
-  hipLaunchKernelGGL(nvfp4_to_mxfp4_kernel, dim3(grid), dim3(256), 0, s, codes, scales16, gscale, rows, nb,
-                     total, out_codes, out_scales);
+  const int64_t per = rows * (cols / 32);
+  if (n_mats == 0 || per == 0) return hipSuccess;
+  // about 8192 workgroups of 256 threads in all
+  const int gy = (int)(n_mats < 8192 ? n_mats : 8192);
+  const int64_t want_x = (per + 255) / 256, cap_x = (8192 + gy - 1) / gy;
+  const int gx = (int)(want_x < cap_x ? want_x : cap_x);
+  hipLaunchKernelGGL(nvfp4_to_mxfp4_kernel, dim3(gx, gy), dim3(256), 0, s, codes, scales16, gscale, n_mats, per,
+                     out_codes, out_scales);
   return hipGetLastError();
 }
 
