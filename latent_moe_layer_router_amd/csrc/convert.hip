@@ -43,6 +43,7 @@ __device__ __forceinline__ float ue4m3_value(uint32_t s) {
 }
 
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 
 // The two E2M1 values of byte S of w (low nibble first) as floats.
 template <int S>
@@ -65,8 +66,10 @@ __global__ __launch_bounds__(256) void nvfp4_to_mxfp4_kernel(const uint8_t* code
   for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < per_mat;
        bi += (int64_t)gridDim.x * blockDim.x) {
     const int64_t b = m * per_mat + bi;
-    const uint4 cw = *reinterpret_cast<const uint4*>(codes + 16 * b);
-    const uint32_t s2 = *reinterpret_cast<const uint16_t*>(scales16 + 2 * b);
+    // every byte is read and written once: non-temporal accesses
+    const u32x4_t cwv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(codes + 16 * b));
+    const uint4 cw = {cwv.x, cwv.y, cwv.z, cwv.w};
+    const uint32_t s2 = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(scales16 + 2 * b));
     const uint32_t s0 = s2 & 0x7Fu, s1 = (s2 >> 8) & 0x7Fu;
     bool bad = !(fabsf(g) <= 3.402823466e38f) || s0 == 0x7Fu || s1 == 0x7Fu;
     const float sc[2] = {ue4m3_value(s0), ue4m3_value(s1)};
@@ -108,8 +111,8 @@ __global__ __launch_bounds__(256) void nvfp4_to_mxfp4_kernel(const uint8_t* code
         o[j] = fp4_put<3>(o[j], v[8 * j + 6], v[8 * j + 7], sx);
       }
     }
-    *reinterpret_cast<uint4*>(out_codes + 16 * b) = uint4{o[0], o[1], o[2], o[3]};
-    out_scales[b] = scale;
+    __builtin_nontemporal_store(u32x4_t{o[0], o[1], o[2], o[3]}, reinterpret_cast<u32x4_t*>(out_codes + 16 * b));
+    __builtin_nontemporal_store(scale, out_scales + b);
   }
   }
 }
@@ -121,9 +124,9 @@ hipError_t launch_nvfp4_to_mxfp4(const uint8_t* codes, const uint8_t* scales16, 
                                  uint8_t* out_scales, hipStream_t s) {
   const int64_t per = rows * (cols / 32);
   if (n_mats == 0 || per == 0) return hipSuccess;
-  // about 8192 workgroups of 256 threads in all
-  const int gy = (int)(n_mats < 8192 ? n_mats : 8192);
-  const int64_t want_x = (per + 255) / 256, cap_x = (8192 + gy - 1) / gy;
+  // about 16384 workgroups of 256 threads in all
+  const int gy = (int)(n_mats < 16384 ? n_mats : 16384);
+  const int64_t want_x = (per + 255) / 256, cap_x = (16384 + gy - 1) / gy;
   const int gx = (int)(want_x < cap_x ? want_x : cap_x);
   hipLaunchKernelGGL(nvfp4_to_mxfp4_kernel, dim3(gx, gy), dim3(256), 0, s, codes, scales16, gscale, n_mats, per,
                      out_codes, out_scales);
