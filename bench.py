@@ -4,7 +4,10 @@
                     [--also prefill_bf16,mxfp4,mxfp4_decode] [--no-cpu-baseline] [--no-convert]
 
 A step is one lmoe_forward over one batch of synthetic tokens already resident
-in HBM: routing, permutation, pooler, experts, combine, unpooler. The headline
+in HBM: routing, permutation, pooler, experts, combine, unpooler. The timed
+steps are lmoe_forward calls back to back; the same steps as replays of one
+forward captured into a HIP graph are timed beside them (no faster: the host
+enqueues far enough ahead that launches leave no gaps). The headline
 workload is decode-sized (T=128 tokens; D=8192, Dp=4096, F=4096, E=256, k=8,
 bf16), which streams the touched experts' weights and is bound by HBM; the
 prefill chunk (T=16384) is reported beside it against the bf16 MFMA peak, and
@@ -63,7 +66,11 @@ def step_work(w, n_active: int):
     return byts, flops
 
 
-def run_workload(lmoe, torch, synth, sdev, block, w, steps, warmup, dev):
+def run_workload(lmoe, torch, synth, sdev, block, w, steps, warmup, dev, graph=True):
+    """Warmup, per-stage HIP-event times over `steps` forwards, then the timed
+    region: `steps` forwards back to back, bracketed by synchronizations (no
+    stage events inside). With `graph`, the same is timed again as replays of
+    one forward captured into a HIP graph (reported beside the eager time)."""
     x = sdev.upload_x(w, dev)
     out = torch.empty((w.T, w.D), dtype=torch.float32, device=dev)
     _, aux = block.forward(x, out=out, aux=True)
@@ -74,17 +81,55 @@ def run_workload(lmoe, torch, synth, sdev, block, w, steps, warmup, dev):
         block.forward(x, out=out)
     torch.cuda.synchronize()
     block.set_timing(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for _ in range(steps):
         block.forward(x, out=out)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     block.set_timing(False)
     stage_ms, n = block.get_timing()
     stage_ms = {s: v / n for s, v in stage_ms.items()}
-    ms = (t1 - t0) * 1e3 / steps
-    return ms, stage_ms, n_active, counts
+
+    def timed(step):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    ms = timed(lambda: block.forward(x, out=out))
+    graph_ms = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            block.forward(x, out=out)
+        for _ in range(warmup):
+            g.replay()
+        graph_ms = timed(g.replay)
+        del g
+    return ms, stage_ms, n_active, counts, graph_ms
+
+
+def cold_steps(torch, block, w, sdev, dev, n=10):
+    """Per-step times (HIP events on the launching stream) with the Infinity
+    Cache (256 MiB) flushed before each step by writing a 512 MiB buffer
+    outside the timed events. Median and minimum, ms."""
+    x = sdev.upload_x(w, dev)
+    out = torch.empty((w.T, w.D), dtype=torch.float32, device=dev)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream()
+    times = []
+    for i in range(n + 1):
+        scratch.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        block.forward(x, out=out, stream=s)
+        e1.record(s)
+        torch.cuda.synchronize()
+        if i:
+            times.append(e0.elapsed_time(e1))
+    del scratch
+    times.sort()
+    return round(times[len(times) // 2], 4), round(times[0], 4)
 
 
 # The gate/up kernel of each regime and the sources that define it: the
@@ -231,6 +276,8 @@ def main():
     ap.add_argument("--also", default="prefill_bf16,mxfp4,mxfp4_decode",
                     help="comma-separated extra workloads, or ''")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the extra timing of HIP graph replays")
     ap.add_argument("--no-convert", action="store_true",
                     help="skip timing the load-time NVFP4 -> MXFP4 weight re-encoding")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -264,13 +311,18 @@ def main():
     print(f"[bench] weights uploaded in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
     block = lmoe.LatentMoE(tw, w.k, max_tokens, w.eps_pool, w.eps_expert, out_dtype=torch.float32)
 
-    ms, stage_ms, n_active, _ = run_workload(lmoe, torch, synth, sdev, block, w, args.steps,
-                                             args.warmup, dev)
-    print(f"[bench] {w.name}: {ms:.3f} ms/step, stages {stage_ms}", file=sys.stderr, flush=True)
+    ms, stage_ms, n_active, _, graph_ms = run_workload(lmoe, torch, synth, sdev, block, w, args.steps,
+                                                       args.warmup, dev, graph=not args.no_graph)
+    print(f"[bench] {w.name}: {ms:.3f} ms/step (graph replay {graph_ms}), stages {stage_ms}", file=sys.stderr,
+          flush=True)
+    cold_med, cold_min = cold_steps(torch, block, w, sdev, dev)
+    print(f"[bench] {w.name} with the Infinity Cache flushed before each step: median {cold_med:.3f} ms, "
+          f"min {cold_min:.3f} ms", file=sys.stderr, flush=True)
     byts, flops = step_work(w, n_active)
     res = {
         "metric": METRIC, "value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "graph_replay_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) random-init weights)",
         "config": {"workload": w.name, "T": w.T, "D": w.D, "Dp": w.Dp, "F": w.F, "E": w.E, "k": w.k,
@@ -278,6 +330,8 @@ def main():
         "step_hbm_frac": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "roofline": roofline(w, stage_ms, n_active, regime(w)),
         "stages_ms": {s: round(v, 4) for s, v in stage_ms.items()},
+        "cold_cache_ms": {"median": cold_med, "min": cold_min,
+                          "what": "per-step HIP-event time, 512 MiB written between steps"},
     }
     also = []
     for e in extra:
@@ -294,12 +348,16 @@ def main():
             w = e
             block = lmoe.LatentMoE(tw, e.k, max_tokens, e.eps_pool, e.eps_expert,
                                    out_dtype=torch.float32)
-        ems, est, ena, _ = run_workload(lmoe, torch, synth, sdev, block, e, args.steps, args.warmup, dev)
-        print(f"[bench] {e.name}: {ems:.3f} ms/step, stages {est}", file=sys.stderr, flush=True)
+        ems, est, ena, _, gms = run_workload(lmoe, torch, synth, sdev, block, e, args.steps, args.warmup, dev,
+                                             graph=not args.no_graph)
+        print(f"[bench] {e.name}: {ems:.3f} ms/step (graph replay {gms}), stages {est}", file=sys.stderr,
+              flush=True)
         eb, ef = step_work(e, ena)
         entry = {"workload": e.name, "T": e.T, "expert_weights": e.expert_w,
                  "value": round(e.T / (ems * 1e-3), 1), "unit": "tokens/s",
-                 "ms_per_step": round(ems, 4), "step_tflops": round(ef / (ems * 1e-3) / 1e12, 1),
+                 "ms_per_step": round(ems, 4),
+                 "graph_replay_ms_per_step": None if gms is None else round(gms, 4),
+                 "step_tflops": round(ef / (ems * 1e-3) / 1e12, 1),
                  "roofline": roofline(e, est, ena, regime(e)),
                  "stages_ms": {s: round(v, 4) for s, v in est.items()}}
         if not e.mx_act:

@@ -133,7 +133,12 @@ lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, lmoe_hand
  * faults surface at the caller's next synchronization. T == 0 enqueues nothing
  * and returns LMOE_OK; T > max_tokens is LMOE_E_INVAL. out must not overlap x.
  * The handle's workspace is shared: calls on one handle must not overlap in time
- * (use one stream per handle). aux may be NULL. */
+ * (use one stream per handle). aux may be NULL.
+ * A call may be captured into a HIP graph (stream capture) and the graph
+ * replayed: it enqueues kernels only (no allocation, memset or host
+ * synchronization); a replay computes what the captured call computed, for the
+ * same x, out, T and aux pointers. Stage timing (lmoe_set_timing) records
+ * nothing while the stream captures. */
 lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, void* hip_stream,
                          const lmoe_aux* aux);
 

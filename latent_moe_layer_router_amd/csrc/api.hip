@@ -387,7 +387,12 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   const int mtiles_bound = (int)(A_ / 256 + n_big);
 
   hipEvent_t ev[LMOE_NUM_STAGES + 1] = {};
-  const bool timing = h->timing;
+  // Stage timing records events; a stream being captured into a graph gets
+  // none (the forward itself captures: kernels only, no allocation, memset or
+  // host synchronization).
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) return fail(LMOE_E_HIP, "hipStreamIsCapturing failed");
+  const bool timing = h->timing && cap == hipStreamCaptureStatusNone;
   if (timing)
     for (auto& e : ev)
       if (hipEventCreate(&e) != hipSuccess) return fail(LMOE_E_HIP, "hipEventCreate failed");
@@ -485,7 +490,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   // The top-k kernel ORs into the chunk masks and the sort clears them; if a
   // previous call stopped between the two, clear them first.
   if (h->masks_dirty) {
-    run(hipMemsetAsync(masks, 0, pl.chunk_base - pl.masks, s));
+    run(launch_clear_u64(masks, (int64_t)(pl.chunk_base - pl.masks) / 8, s));
     if (err == hipSuccess) h->masks_dirty = false;
   }
   run(launch_topk(logits, T, E, k, ids, tw, masks, s));

@@ -192,6 +192,9 @@ hipError_t launch_stream_mx(const StreamMxParams& p, EpiKind epi, hipStream_t s)
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                        uint64_t* chunk_masks, hipStream_t s);
 
+// p[0 .. n) = 0, as a kernel (no memset node when the forward is captured).
+hipError_t launch_clear_u64(uint64_t* p, int64_t n, hipStream_t s);
+
 // Counting sort of the T*k assignments by expert (stable), from the chunk masks.
 struct SortParams {
   const int32_t* ids;

@@ -224,7 +224,22 @@ __global__ __launch_bounds__(64) void sort_scatter_kernel(SortParams p) {
   for (int e = lane; e < p.E; e += kChunk) p.chunk_masks[(int64_t)chunk * p.E + e] = 0ull;
 }
 
+// Zero n 64-bit words (the chunk masks after an interrupted call). A kernel
+// rather than a memset, so that a forward captured into a HIP graph holds no
+// memset node.
+__global__ __launch_bounds__(256) void clear_u64_kernel(uint64_t* p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0ull;
+}
+
 }  // namespace
+
+hipError_t launch_clear_u64(uint64_t* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t want = (n + 255) / 256;
+  hipLaunchKernelGGL(clear_u64_kernel, dim3((int)(want < 1024 ? want : 1024)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                        uint64_t* chunk_masks, hipStream_t s) {
