@@ -379,7 +379,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   const bool big_ok = bf16 && !mx && Dp % 256 == 0 && F % 128 == 0 && off32_ok;
   int32_t* mt_off = reinterpret_cast<int32_t*>(ws + pl.mt_off);
   const int64_t A_ = (int64_t)T * k;
-  // Row tiles of 256 over the experts with more than small_max rows: at most
+  // Row tiles (at least 256 rows each) over the experts with more than small_max rows: at most
   // floor(A / 256) full ones plus one partial per such expert, and there are at
   // most floor(A / (small_max + 1)) such experts. The bound sizes the grid, so a
   // tight one keeps the launch cheap when few or no experts are large (decode).
@@ -515,7 +515,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     sp.tile_m = kGemmBM;
     sp.small_max = small_max;
     sp.mt_off = mt_off;
-    sp.tile_m2 = gemm256_tile_m();
+    sp.tile_m2 = mx ? gemm256_tile_m() : gemm_grouped_tile_m();
     run(launch_sort(sp, s));
     if (err == hipSuccess) h->masks_dirty = false;
   }
@@ -608,7 +608,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     g.F = F;
     g.out = H;
     g.ldo = F;
-    run(launch_gemm256(g, EPI_SWIGLU, s));
+    run(launch_gemm_grouped(g, EPI_SWIGLU, s));
   } else {
     GemmParams g{};
     g.N = F;
@@ -714,7 +714,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     g.ldo = Dp;
     g.ss_out = ss;
     g.ss_ld = Dp / 64;
-    run(launch_gemm256(g, EPI_DOWN, s));
+    run(launch_gemm_grouped(g, EPI_DOWN, s));
   } else {
     GemmParams g{};
     g.N = Dp;

@@ -129,6 +129,13 @@ struct Gemm256Params {
 int gemm256_tile_m();
 hipError_t launch_gemm256(const Gemm256Params& p, EpiKind epi, hipStream_t s);
 
+// Grouped expert GEMMs (bf16, M == 0) on row tiles of up to
+// gemm_grouped_tile_m() rows (each expert's rows split evenly over
+// ceil(rows / tile) tiles, mt_off counting them) x 256 weight rows; same
+// parameters as the grouped mode of launch_gemm256. EPI_SWIGLU or EPI_DOWN.
+int gemm_grouped_tile_m();
+hipError_t launch_gemm_grouped(const Gemm256Params& p, EpiKind epi, hipStream_t s);
+
 // The same tiling for the MXFP4-expert path: MXFP8 E4M3 activations x MXFP4
 // weights on the block-scaled MFMA. EPI_SWIGLU writes H as MXFP8 (codes to out,
 // scales to out_scales); EPI_DOWN writes y as bf16 and the sums of squares.
