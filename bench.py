@@ -133,12 +133,12 @@ def cold_steps(torch, block, w, sdev, dev, n=10):
 
 
 # The gate/up kernel of each regime and the sources that define it: the
-# weight-streaming kernels for decode-sized batches, the 256 x 256 tile GEMMs
+# weight-streaming kernels for decode-sized batches, the tiled grouped GEMMs
 # for prefill-sized ones (bf16 or MXFP4 experts).
 CSRC = os.path.join(ROOT, "latent_moe_layer_router_amd", "csrc")
 GATE_UP_KERNEL = {"hbm": ("stream_kernel<EPI_SWIGLU>", ("stream.hip", "common.h")),
                   "hbm_mx": ("stream_mx_kernel<EPI_SWIGLU>", ("stream_mx.hip", "mx.h", "common.h")),
-                  "mfma": ("gemm256_kernel<EPI_SWIGLU>", ("gemm256.hip", "common.h")),
+                  "mfma": ("gemm_grouped_kernel<EPI_SWIGLU>", ("gemm_grouped.hip", "common.h")),
                   "mfma_mx": ("gemm256_mx_kernel<EPI_SWIGLU>", ("gemm256_mx.hip", "mx.h", "common.h")),
                   "convert": ("nvfp4_to_mxfp4_kernel", ("convert.hip", "common.h"))}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.txt")

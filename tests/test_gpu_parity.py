@@ -139,6 +139,18 @@ def test_stream_path_row_boundaries():
     assert np.diff(a["expert_offsets"]).tolist() == [64, 65, 1, 0]
 
 
+def test_grouped_tile_boundaries():
+    """Experts at the grouped GEMM's row-tile boundaries (tiles of up to 320
+    rows, split evenly; each split again between two wave rows): 65 rows (the
+    smallest tiled expert), 320 (one full tile), 321 and 640 (two tiles), 641
+    and 1000 (three and four), 64 (streamed) and 0."""
+    counts = [65, 320, 321, 640, 641, 1000, 64, 0]
+    assign = np.repeat(np.arange(len(counts)), counts)
+    w = tiny(T=len(assign), D=256, Dp=256, F_=256, E=len(counts), k=1, seed=112, act=synth.BF16)
+    a = run_crafted(w, assign)
+    assert np.diff(a["expert_offsets"]).tolist() == counts
+
+
 def test_stream_and_tiled_mixed():
     """Uneven routing over 16 experts: some experts above 64 rows (tiled GEMM),
     the rest streamed, several token tiles per streamed expert."""
