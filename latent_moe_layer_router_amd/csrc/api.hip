@@ -515,7 +515,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     sp.tile_m = kGemmBM;
     sp.small_max = small_max;
     sp.mt_off = mt_off;
-    sp.tile_m2 = mx ? gemm256_tile_m() : gemm_grouped_tile_m();
+    sp.tile_m2 = mx ? gemm256_mx_tile_m() : gemm_grouped_tile_m();
     run(launch_sort(sp, s));
     if (err == hipSuccess) h->masks_dirty = false;
   }

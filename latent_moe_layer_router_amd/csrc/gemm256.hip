@@ -1,6 +1,6 @@
-// Large-tile grouped GEMM for experts with many rows (prefill): the two expert
-// GEMMs of the block (gate/up with the SwiGLU epilogue, down with the bf16
-// output and per-64-column sums of squares).
+// Large-tile dense GEMM (bf16): the router + pooler and the unpooler at
+// prefill sizes, out = A . B^T with fp32 out (and the router's columns, from a
+// second weight matrix plus a bias) or bf16 out.
 //
 // Tile 256 x 256 (A rows x B rows), 256 threads = 4 wave64 in a 2 x 2 grid,
 // each wave a 128 x 128 sub-tile of 4 x 4 MFMA 32x32x16 bf16 (accumulators in
@@ -12,13 +12,10 @@
 // for step k + 3 are issued while step k computes, so three steps of latency
 // (about 3000 cycles at full MFMA rate) are covered.
 //
-// Scheduling for the 8 XCDs: the tiles of all experts form one index space
-// ordered (expert, n-tile, m-tile); it is cut into 8 contiguous chunks and
-// workgroup b (dispatched to XCD b % 8) takes tile (b % 8) * chunk + b / 8. So
-// the CUs of one XCD work on the same expert at the same time and share its
-// weight slices and token rows in their L2.
-#include <type_traits>
-
+// Scheduling for the 8 XCDs: the tiles form one index space ordered (m-tile,
+// n-tile); it is cut into 8 contiguous chunks and workgroup b (dispatched to
+// XCD b % 8) takes tile (b % 8) * chunk + b / 8. So the CUs of one XCD share
+// row tiles of A in their L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -85,40 +82,17 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets in SGPRs
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- tile of this workgroup (XCD-chunked order) --------------------------
-  // Grouped (p.M == 0): tiles (expert, n-tile, m-tile) of the experts' sorted
-  // rows. Dense (p.M > 0): tiles (m-tile, n-tile) of an M x N product.
-  const bool dense = p.M > 0;
-  const int ntm = dense ? (p.M + BM - 1) / BM : 0;
-  const int total = dense ? ntm * p.ntiles_n : p.ntiles_n * p.mt_off[p.E];
+  // ---- tile of this workgroup (XCD-chunked order): (m-tile, n-tile) -------
+  const int ntm = (p.M + BM - 1) / BM;
+  const int total = ntm * p.ntiles_n;
   const int chunk = (total + 7) / 8;
   const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
   const int t = xcd * chunk + local;
   if (local >= chunk || t >= total) return;
-  int e = 0, ntile, m0, m_end;
-  if (dense) {
-    ntile = t % p.ntiles_n;
-    m0 = (t / p.ntiles_n) * BM;
-    m_end = p.M;
-  } else {
-    int lo = 0, hi = p.E;                    // expert e: ntiles_n*mt_off[e] <= t < ntiles_n*mt_off[e+1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.ntiles_n * p.mt_off[mid] <= t) lo = mid; else hi = mid;
-    }
-    e = lo;
-    // The expert's rows are split evenly over its mt_e row tiles (each at most
-    // 256 rows), so that the tiles sharing a weight slice do the same work and
-    // stream that slice through L2 together; a short tail tile would race ahead
-    // and fetch every slice a second time.
-    const int mt_e = p.mt_off[e + 1] - p.mt_off[e];
-    const int tl = t - p.ntiles_n * p.mt_off[e];
-    const int mi = tl % mt_e, cnt = p.offsets[e + 1] - p.offsets[e];
-    ntile = tl / mt_e;
-    m0 = p.offsets[e] + (int)((int64_t)cnt * mi / mt_e);
-    m_end = p.offsets[e] + (int)((int64_t)cnt * (mi + 1) / mt_e);
-  }
-  const int n0 = ntile * (EPI == EPI_SWIGLU ? BNB / 2 : BNB);   // output column start
+  const int ntile = t % p.ntiles_n;
+  const int m0 = (t / p.ntiles_n) * BM;
+  const int m_end = p.M;
+  const int n0 = ntile * BNB;                // output column start
 
   // ---- global-to-LDS loads ------------------------------------------------
   // Per stage each wave moves 4 x 16 rows of A and of B, one 1 KiB load each:
@@ -132,20 +106,11 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
   // wait counts around them.)
   const __amdgpu_buffer_rsrc_t rsA =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.A), (short)0, (int)p.a_bytes, kBufWord3);
-  // B rows of the tile: grouped, the expert's matrix (rows n0 + r, or the
-  // gate/up pairs); dense, the tile's own 256 rows from B (columns below
-  // n_split) or B1, the extent ending at row N (rows past it read as zero).
-  const bf16_t* Bt;
-  int b_ext;
-  if (dense) {
-    Bt = (n0 < p.n_split) ? static_cast<const bf16_t*>(p.B) + (int64_t)n0 * p.ldb
-                          : static_cast<const bf16_t*>(p.B1) + (int64_t)(n0 - p.n_split) * p.ldb;
-    const int rows = min(BNB, p.N - n0);
-    b_ext = rows * (int)p.ldb * 2;
-  } else {
-    Bt = static_cast<const bf16_t*>(p.B) + (int64_t)e * p.b_expert_stride;
-    b_ext = (int)p.b_bytes;
-  }
+  // B rows of the tile: its own 256 rows from B (columns below n_split) or B1,
+  // the extent ending at row N (rows past it read as zero).
+  const bf16_t* Bt = (n0 < p.n_split) ? static_cast<const bf16_t*>(p.B) + (int64_t)n0 * p.ldb
+                                      : static_cast<const bf16_t*>(p.B1) + (int64_t)(n0 - p.n_split) * p.ldb;
+  const int b_ext = min(BNB, p.N - n0) * (int)p.ldb * 2;
   const __amdgpu_buffer_rsrc_t rsB =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(Bt), (short)0, b_ext, kBufWord3);
   const int pos = lane & 3;
@@ -160,9 +125,8 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
     return (uint32_t)m * (uint32_t)(p.lda * 2) + c * 16;
   };
   auto b_off = [&](int r) -> uint32_t {
-    const int n = dense ? r : (EPI == EPI_SWIGLU) ? ((r < BNB / 2) ? (n0 + r) : (p.F + n0 + r - BNB / 2)) : (n0 + r);
     const uint32_t c = pos ^ (((r >> 1) ^ (r >> 3)) & 3);
-    return (uint32_t)n * (uint32_t)(p.ldb * 2) + c * 16;
+    return (uint32_t)r * (uint32_t)(p.ldb * 2) + c * 16;
   };
   const int rr = wave * 64 + (lane >> 2);    // row of load j is rr + 16 j
   const uint32_t ga0 = a_off(rr), ga1 = a_off(rr + 16), ga2 = a_off(rr + 32), ga3 = a_off(rr + 48);
@@ -193,14 +157,11 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
-  // LDS rows of this lane's MFMA operands: A rows wm*128 + 32 mi + l32; B rows:
-  // SwiGLU pairs gate (ni = 0, 1) and up (ni = 2, 3) of the same 64 columns.
+  // LDS rows of this lane's MFMA operands: A rows wm*128 + 32 mi + l32, B rows
+  // wn*128 + 32 ni + l32.
   const int l32 = lane & 31, half = lane >> 5;
   const int aoff0 = swz(wm * 128 + l32, half), aoff1 = swz(wm * 128 + l32, 2 + half);
-  auto brow_of = [&](int ni) {
-    return (EPI == EPI_SWIGLU) ? ((ni >> 1) * (BNB / 2) + wn * 64 + (ni & 1) * 32 + l32)
-                               : (wn * 128 + ni * 32 + l32);
-  };
+  auto brow_of = [&](int ni) { return wn * 128 + ni * 32 + l32; };
   const int b00 = swz(brow_of(0), half), b01 = swz(brow_of(0), 2 + half);
   const int b10 = swz(brow_of(1), half), b11 = swz(brow_of(1), 2 + half);
   const int b20 = swz(brow_of(2), half), b21 = swz(brow_of(2), 2 + half);
@@ -336,10 +297,9 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
     return;
   }
 
-  // ---- epilogue: stage [256][OBN] bf16 in LDS, 16-byte stores ----------------
+  // ---- bf16 out: stage [256][256] in LDS, 16-byte stores -------------------
   // The staging tile spans the stage buffers: rows [32 q, 32 q + 32) live in
   // buffer q (A0, B0, A1, ..., B3 in declaration order), 16 KiB each.
-  constexpr int OBN = (EPI == EPI_SWIGLU) ? BNB / 2 : BNB;
   auto srow = [&](int r) -> bf16_t* {
     unsigned char* b;
     switch (r >> 5) {
@@ -352,7 +312,7 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
       case 6: b = sA3; break;
       default: b = sB3; break;
     }
-    return reinterpret_cast<bf16_t*>(b) + (r & 31) * OBN;
+    return reinterpret_cast<bf16_t*>(b) + (r & 31) * BNB;
   };
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
@@ -360,55 +320,27 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(Gemm256Params p) {
     for (int v = 0; v < 16; ++v) {
       const int r = wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
       bf16_t* row = srow(r);
-      if (EPI == EPI_SWIGLU) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float g = acc[mi][h][v], u = acc[mi][2 + h][v];
-          row[wn * 64 + h * 32 + l32] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
-        }
-      } else {
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) row[wn * 128 + ni * 32 + l32] = f32_to_bf16(acc[mi][ni][v]);
-      }
+      for (int ni = 0; ni < 4; ++ni) row[wn * 128 + ni * 32 + l32] = f32_to_bf16(acc[mi][ni][v]);
     }
   __syncthreads();
-  constexpr int CPR = OBN / 8;
+  constexpr int CPR = BNB / 8;
   for (int i = tid; i < BM * CPR; i += NT) {
     const int r = i / CPR, c = (i % CPR) * 8;
     const int m = m0 + r;
-    if (m >= m_end || (dense && n0 + c >= p.N)) continue;
+    if (m >= m_end || n0 + c >= p.N) continue;
     *reinterpret_cast<uint4*>(static_cast<bf16_t*>(p.out) + (int64_t)m * p.ldo + n0 + c) =
         *reinterpret_cast<const uint4*>(srow(r) + c);
-  }
-  if (EPI == EPI_DOWN) {
-    // sums of squares of the stored bf16 values, per row and 64-column group
-    for (int i = tid; i < BM * (BNB / 64); i += NT) {
-      const int r = i / (BNB / 64), grp = i % (BNB / 64);
-      const int m = m0 + r;
-      if (m >= m_end) continue;
-      const bf16_t* row = srow(r) + grp * 64;
-      float ssq = 0.f;
-      for (int j = 0; j < 64; ++j) {
-        const float y = bf16_to_f32(row[j]);
-        ssq += y * y;
-      }
-      p.ss_out[(int64_t)m * p.ss_ld + (n0 + grp * 64) / 64] = ssq;
-    }
   }
 }
 
 }  // namespace
 
-int gemm256_tile_m() { return BM; }
-
 hipError_t launch_gemm256(const Gemm256Params& p, EpiKind epi, hipStream_t s) {
   if (p.max_tiles <= 0) return hipSuccess;
+  if (p.M <= 0) return hipErrorInvalidValue;
   const int grid = ((p.max_tiles + 7) / 8) * 8;
-  if (epi == EPI_SWIGLU)
-    hipLaunchKernelGGL(gemm256_kernel<EPI_SWIGLU>, dim3(grid), dim3(NT), 0, s, p);
-  else if (epi == EPI_DOWN)
-    hipLaunchKernelGGL(gemm256_kernel<EPI_DOWN>, dim3(grid), dim3(NT), 0, s, p);
-  else if (epi == EPI_F32 && p.M > 0)
+  if (epi == EPI_F32 && p.M > 0)
     hipLaunchKernelGGL(gemm256_kernel<EPI_F32>, dim3(grid), dim3(NT), 0, s, p);
   else if (epi == EPI_ACT && p.M > 0)
     hipLaunchKernelGGL(gemm256_kernel<EPI_ACT>, dim3(grid), dim3(NT), 0, s, p);

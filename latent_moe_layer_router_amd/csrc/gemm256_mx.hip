@@ -385,6 +385,8 @@ __global__ __launch_bounds__(NT, 1) void gemm256_mx_kernel(Gemm256MxParams p) {
 
 }  // namespace
 
+int gemm256_mx_tile_m() { return BM; }
+
 hipError_t launch_gemm256_mx(const Gemm256MxParams& p, EpiKind epi, hipStream_t s) {
   if (p.max_tiles <= 0) return hipSuccess;
   const int grid = ((p.max_tiles + 7) / 8) * 8;

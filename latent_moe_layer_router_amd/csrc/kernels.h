@@ -92,12 +92,13 @@ int dense_stream_slices(int N, int K);               // K a multiple of 64
 int64_t dense_stream_part_floats(int T, int N, int K);
 hipError_t launch_dense_stream(const DenseStreamParams& p, hipStream_t s);
 
-// Large-tile (256 x 256) GEMM (bf16). Grouped (M == 0), for experts with many
-// rows: expert e has mt_off[e+1] - mt_off[e] row tiles of 256 (in sorted row
-// order from offsets[e]; the last may be partial), each times ntiles_n column
-// tiles; EPI_SWIGLU or EPI_DOWN. Dense (M > 0): out = A . B^T over M rows and
-// N columns (ntiles_n tiles of 256, the last may be partial), rows [n_split, N)
-// of B^T taken from B1; EPI_F32 (fp32 out, out1 + bias1) or EPI_ACT (bf16 out).
+// Large-tile (256 x 256) dense GEMM (bf16, M > 0): out = A . B^T over M rows
+// and N columns (ntiles_n tiles of 256, the last may be partial), rows
+// [n_split, N) of B^T taken from B1; EPI_F32 (fp32 out, out1 + bias1) or
+// EPI_ACT (bf16 out). The grouped fields (M == 0: offsets, mt_off, E, F,
+// b_expert_stride, b_bytes, ss_out) serve launch_gemm_grouped: expert e has
+// mt_off[e+1] - mt_off[e] row tiles (its rows in sorted order from offsets[e],
+// split evenly), each times ntiles_n column tiles.
 struct Gemm256Params {
   const void* A;
   int64_t lda;
@@ -105,7 +106,7 @@ struct Gemm256Params {
   int64_t ldb;
   int64_t b_expert_stride;
   const int32_t* offsets;      // [E+1] rows per expert (sorted order)
-  const int32_t* mt_off;       // [E+1] exclusive prefix of 256-row tiles per expert
+  const int32_t* mt_off;       // [E+1] exclusive prefix of row tiles per expert (grouped)
   int E;
   int ntiles_n;                // F/128 (SwiGLU: 128 gate + 128 up rows per tile) or Dp/256
   int max_tiles;               // grid size, a bound on the tile count
@@ -126,7 +127,6 @@ struct Gemm256Params {
   int64_t ldo1;
   const float* bias1;
 };
-int gemm256_tile_m();
 hipError_t launch_gemm256(const Gemm256Params& p, EpiKind epi, hipStream_t s);
 
 // Grouped expert GEMMs (bf16, M == 0) on row tiles of up to
@@ -161,6 +161,7 @@ struct Gemm256MxParams {
   float* ss_out;               // EPI_DOWN
   int ss_ld;
 };
+int gemm256_mx_tile_m();      // rows per row tile (mt_off counts tiles of this height)
 hipError_t launch_gemm256_mx(const Gemm256MxParams& p, EpiKind epi, hipStream_t s);
 
 // Weight-streaming grouped GEMM of the MXFP4-expert path for experts with
@@ -216,8 +217,8 @@ struct SortParams {
   int32_t* n_tiles;             // [1]
   int T, E, k, tile_m;
   int small_max;                // experts with 1..small_max rows get no tiles (streamed instead)
-  int32_t* mt_off;              // [E+1] 256-row tile prefix for the large-tile GEMM
-  int tile_m2;                  // 256
+  int32_t* mt_off;              // [E+1] row-tile prefix for the large-tile grouped GEMM
+  int tile_m2;                  // its rows per tile
 };
 hipError_t launch_sort(const SortParams& p, hipStream_t s);
 
