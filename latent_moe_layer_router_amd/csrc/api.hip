@@ -515,7 +515,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     sp.tile_m = kGemmBM;
     sp.small_max = small_max;
     sp.mt_off = mt_off;
-    sp.tile_m2 = mx ? gemm256_mx_tile_m() : gemm_grouped_tile_m();
+    sp.tile_m2 = mx ? gemm_grouped_mx_tile_m() : gemm_grouped_tile_m();
     run(launch_sort(sp, s));
     if (err == hipSuccess) h->masks_dirty = false;
   }
@@ -589,7 +589,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     g.ldo = F;
     g.out_scales = hs;
     g.ldos = F / 32;
-    run(launch_gemm256_mx(g, EPI_SWIGLU, s));
+    run(launch_gemm_grouped_mx(g, EPI_SWIGLU, s));
   } else if (big_ok) {
     Gemm256Params g{};
     g.A = xp;
@@ -693,7 +693,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     g.ldo = Dp;
     g.ss_out = ss;
     g.ss_ld = Dp / 64;
-    run(launch_gemm256_mx(g, EPI_DOWN, s));
+    run(launch_gemm_grouped_mx(g, EPI_DOWN, s));
   } else if (big_ok) {
     Gemm256Params g{};
     g.A = H;

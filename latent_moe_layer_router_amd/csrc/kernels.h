@@ -164,6 +164,12 @@ struct Gemm256MxParams {
 int gemm256_mx_tile_m();      // rows per row tile (mt_off counts tiles of this height)
 hipError_t launch_gemm256_mx(const Gemm256MxParams& p, EpiKind epi, hipStream_t s);
 
+// The same GEMMs on row tiles of up to gemm_grouped_mx_tile_m() rows (each
+// expert's rows split evenly over ceil(rows / tile) tiles, mt_off counting
+// them); 8 waves per tile. K a multiple of 1024.
+int gemm_grouped_mx_tile_m();
+hipError_t launch_gemm_grouped_mx(const Gemm256MxParams& p, EpiKind epi, hipStream_t s);
+
 // Weight-streaming grouped GEMM of the MXFP4-expert path for experts with
 // 1..max_rows rows (max_rows <= stream_mx_max_rows()); one wave per (expert,
 // group of 64 weight rows). K a multiple of 1024.
