@@ -139,7 +139,7 @@ CSRC = os.path.join(ROOT, "latent_moe_layer_router_amd", "csrc")
 GATE_UP_KERNEL = {"hbm": ("stream_kernel<EPI_SWIGLU>", ("stream.hip", "common.h")),
                   "hbm_mx": ("stream_mx_kernel<EPI_SWIGLU>", ("stream_mx.hip", "mx.h", "common.h")),
                   "mfma": ("gemm_grouped_kernel<EPI_SWIGLU>", ("gemm_grouped.hip", "common.h")),
-                  "mfma_mx": ("gemm256_mx_kernel<EPI_SWIGLU>", ("gemm256_mx.hip", "mx.h", "common.h")),
+                  "mfma_mx": ("gemm_grouped_mx_kernel<EPI_SWIGLU>", ("gemm_grouped_mx.hip", "mx.h", "common.h")),
                   "convert": ("nvfp4_to_mxfp4_kernel", ("convert.hip", "common.h"))}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.txt")
 

@@ -136,9 +136,10 @@ hipError_t launch_gemm256(const Gemm256Params& p, EpiKind epi, hipStream_t s);
 int gemm_grouped_tile_m();
 hipError_t launch_gemm_grouped(const Gemm256Params& p, EpiKind epi, hipStream_t s);
 
-// The same tiling for the MXFP4-expert path: MXFP8 E4M3 activations x MXFP4
-// weights on the block-scaled MFMA. EPI_SWIGLU writes H as MXFP8 (codes to out,
-// scales to out_scales); EPI_DOWN writes y as bf16 and the sums of squares.
+// Grouped expert GEMMs of the MXFP4-expert path: MXFP8 E4M3 activations x
+// MXFP4 weights on the block-scaled MFMA. EPI_SWIGLU writes H as MXFP8 (codes
+// to out, scales to out_scales); EPI_DOWN writes y as bf16 and the sums of
+// squares.
 struct Gemm256MxParams {
   const uint8_t* A;            // [rows][K] E4M3 codes, rows in sorted order
   const uint8_t* As;           // [rows][K/32] E8M0 scales
@@ -161,12 +162,9 @@ struct Gemm256MxParams {
   float* ss_out;               // EPI_DOWN
   int ss_ld;
 };
-int gemm256_mx_tile_m();      // rows per row tile (mt_off counts tiles of this height)
-hipError_t launch_gemm256_mx(const Gemm256MxParams& p, EpiKind epi, hipStream_t s);
-
-// The same GEMMs on row tiles of up to gemm_grouped_mx_tile_m() rows (each
-// expert's rows split evenly over ceil(rows / tile) tiles, mt_off counting
-// them); 8 waves per tile. K a multiple of 1024.
+// Row tiles of up to gemm_grouped_mx_tile_m() rows (each expert's rows split
+// evenly over ceil(rows / tile) tiles, mt_off counting them) x 256 weight
+// rows; 8 waves per tile. K a multiple of 1024.
 int gemm_grouped_mx_tile_m();
 hipError_t launch_gemm_grouped_mx(const Gemm256MxParams& p, EpiKind epi, hipStream_t s);
 
