@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "liblmoe.so")
-SOURCES = ["api.hip", "gemm.hip", "gemm256.hip", "stream.hip", "route.hip", "norm.hip",
+SOURCES = ["api.hip", "gemm.hip", "stream.hip", "route.hip", "norm.hip",
            "convert.hip", "stream_mx.hip", "gemm_grouped.hip", "gemm_grouped_mx.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

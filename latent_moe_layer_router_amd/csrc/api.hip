@@ -415,7 +415,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   float* part = reinterpret_cast<float*>(ws + pl.part);
   const int slices_in = dense_stream_slices(Dp + E, D), slices_un = dense_stream_slices(D, Dp);
 
-  // Larger batches: the dense projections on 256 x 256 tiles (bf16; K a
+  // Larger batches: the dense projections on the tiled kernel (bf16; K a
   // multiple of 128, the pooler's rows a multiple of 256, 32-bit offsets).
   const bool dense256 = bf16 && !dense_stream && D % 128 == 0 && Dp % 256 == 0 &&
                         (int64_t)T * D * 2 < ((int64_t)1 << 31) && (int64_t)T * Dp * 2 < ((int64_t)1 << 31) &&
@@ -446,7 +446,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     g.out1 = logits;
     g.ldo1 = E;
     g.bias1 = h->w.b_router;
-    run(launch_gemm256(g, EPI_F32, s));
+    run(launch_gemm_grouped(g, EPI_F32, s));
   } else if (dense_stream && slices_in > 0) {
     DenseStreamParams d{};
     d.A = x;
@@ -760,7 +760,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     g.n_split = D;
     g.out = out;
     g.ldo = D;
-    run(launch_gemm256(g, out_f32 ? EPI_F32 : EPI_ACT, s));
+    run(launch_gemm_grouped(g, out_f32 ? EPI_F32 : EPI_ACT, s));
   } else if (dense_stream && slices_un > 0) {
     DenseStreamParams d{};
     d.A = u;

@@ -1,7 +1,8 @@
-// Grouped expert GEMMs (bf16) for experts with many rows (prefill): gate/up
-// with the SwiGLU epilogue, down with the bf16 output and per-64-column sums of
-// squares. Same pipeline as the 256 x 256 dense-projection kernel, with taller
-// row tiles.
+// Tiled bf16 GEMMs of the prefill path. Grouped (M == 0): the expert GEMMs for
+// experts with many rows, gate/up with the SwiGLU epilogue, down with the bf16
+// output and per-64-column sums of squares. Dense (M > 0): the router + pooler
+// (fp32 out, the router's columns from a second matrix plus a bias) and the
+// unpooler (fp32 or bf16 out), on row tiles of 256.
 //
 // Row tiles of up to 320 rows x 256 weight rows, 512 threads = 8 wave64 in a
 // 2 x 4 grid, each wave up to 160 x 64 = 5 x 2 MFMA 32x32x16 bf16 (160
@@ -84,24 +85,34 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(Gemm256Params p) {
   const int wm = wave >> 2, wn = wave & 3;
 
   // ---- tile of this workgroup (XCD-chunked order) --------------------------
-  const int total = p.ntiles_n * p.mt_off[p.E];
+  // Grouped: tiles (expert, n-tile, m-tile) of the experts' sorted rows. Dense:
+  // tiles (m-tile, n-tile) of an M x N product, row tiles of 256.
+  constexpr bool dense = (EPI == EPI_F32 || EPI == EPI_ACT);
+  const int total = dense ? ((p.M + 255) / 256) * p.ntiles_n : p.ntiles_n * p.mt_off[p.E];
   const int chunk = (total + 7) / 8;
   const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
   const int t = xcd * chunk + local;
   if (local >= chunk || t >= total) return;
-  int lo = 0, hi = p.E;                      // expert e: ntiles_n*mt_off[e] <= t < ntiles_n*mt_off[e+1]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.ntiles_n * p.mt_off[mid] <= t) lo = mid; else hi = mid;
+  int e = 0, ntile, m0, m_end;
+  if (dense) {
+    ntile = t % p.ntiles_n;
+    m0 = (t / p.ntiles_n) * 256;
+    m_end = min(p.M, m0 + 256);
+  } else {
+    int lo = 0, hi = p.E;                    // expert e: ntiles_n*mt_off[e] <= t < ntiles_n*mt_off[e+1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.ntiles_n * p.mt_off[mid] <= t) lo = mid; else hi = mid;
+    }
+    e = lo;
+    // the expert's rows split evenly over its row tiles (each at most 320 rows)
+    const int mt_e = p.mt_off[e + 1] - p.mt_off[e];
+    const int tl = t - p.ntiles_n * p.mt_off[e];
+    const int mi_t = tl % mt_e, cnt = p.offsets[e + 1] - p.offsets[e];
+    ntile = tl / mt_e;
+    m0 = p.offsets[e] + (int)((int64_t)cnt * mi_t / mt_e);
+    m_end = p.offsets[e] + (int)((int64_t)cnt * (mi_t + 1) / mt_e);
   }
-  const int e = lo;
-  // the expert's rows split evenly over its row tiles (each at most 320 rows)
-  const int mt_e = p.mt_off[e + 1] - p.mt_off[e];
-  const int tl = t - p.ntiles_n * p.mt_off[e];
-  const int mi_t = tl % mt_e, cnt = p.offsets[e + 1] - p.offsets[e];
-  const int ntile = tl / mt_e;
-  const int m0 = p.offsets[e] + (int)((int64_t)cnt * mi_t / mt_e);
-  const int m_end = p.offsets[e] + (int)((int64_t)cnt * (mi_t + 1) / mt_e);
   const int n0 = ntile * (EPI == EPI_SWIGLU ? GBN / 2 : GBN);   // output column start
   // the tile's rows split between the wave rows: wm = 0 takes the first r_half
   // (a multiple of 32, at least half), wm = 1 the rest; at most 160 each
@@ -114,9 +125,21 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(Gemm256Params p) {
   // ---- global-to-LDS loads --------------------------------------------------
   const __amdgpu_buffer_rsrc_t rsA =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.A), (short)0, (int)p.a_bytes, kBufWord3);
-  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(static_cast<const bf16_t*>(p.B) + (int64_t)e * p.b_expert_stride), (short)0,
-      (int)p.b_bytes, kBufWord3);
+  // B rows of the tile: grouped, the expert's matrix (rows n0 + r, or the
+  // gate/up pairs); dense, the tile's own 256 rows from B (columns below
+  // n_split) or B1, the extent ending at row N (rows past it read as zero).
+  const bf16_t* Bt;
+  int b_ext;
+  if (dense) {
+    Bt = (n0 < p.n_split) ? static_cast<const bf16_t*>(p.B) + (int64_t)n0 * p.ldb
+                          : static_cast<const bf16_t*>(p.B1) + (int64_t)(n0 - p.n_split) * p.ldb;
+    b_ext = min(GBN, p.N - n0) * (int)p.ldb * 2;
+  } else {
+    Bt = static_cast<const bf16_t*>(p.B) + (int64_t)e * p.b_expert_stride;
+    b_ext = (int)p.b_bytes;
+  }
+  const __amdgpu_buffer_rsrc_t rsB =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(Bt), (short)0, b_ext, kBufWord3);
   const int pos = lane & 3;
   // Rows past the tile's end get an offset beyond every extent: the load reads
   // nothing from memory. Those rows are never stored.
@@ -127,7 +150,7 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(Gemm256Params p) {
     return (uint32_t)m * (uint32_t)(p.lda * 2) + c * 16;
   };
   auto b_off = [&](int r) -> uint32_t {
-    const int n = (EPI == EPI_SWIGLU) ? ((r < GBN / 2) ? (n0 + r) : (p.F + n0 + r - GBN / 2)) : (n0 + r);
+    const int n = dense ? r : (EPI == EPI_SWIGLU) ? ((r < GBN / 2) ? (n0 + r) : (p.F + n0 + r - GBN / 2)) : (n0 + r);
     const uint32_t c = pos ^ (((r >> 1) ^ (r >> 3)) & 3);
     return (uint32_t)n * (uint32_t)(p.ldb * 2) + c * 16;
   };
@@ -263,6 +286,31 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(Gemm256Params p) {
 #undef LMOE_LD
   __syncthreads();   // every load has landed and every wave has finished reading
 
+  if (EPI == EPI_F32) {
+    // fp32 out, straight from the accumulators: the 32 lanes of a half-wave
+    // store 32 consecutive columns of a row (128 bytes). Columns below n_split
+    // go to out, the rest to out1 plus bias1 (router logits).
+#pragma unroll
+    for (int mi = 0; mi < GMI; ++mi)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = mi * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        if (r >= mrows) continue;
+        const int m = m0 + wrow0 + r;
+#pragma unroll
+        for (int ni = 0; ni < GNI; ++ni) {
+          const int n = n0 + wn * 64 + ni * 32 + l32;
+          if (n >= p.N) continue;
+          if (n < p.n_split)
+            static_cast<float*>(p.out)[(int64_t)m * p.ldo + n] = acc[mi][ni][v];
+          else
+            p.out1[(int64_t)m * p.ldo1 + (n - p.n_split)] =
+                acc[mi][ni][v] + (p.bias1 ? p.bias1[n - p.n_split] : 0.f);
+        }
+      }
+    return;
+  }
+
   // ---- epilogue, by wave row: stage [160][OBN] bf16 in LDS, 16-byte stores ---
   // Rows [32 q, 32 q + 32) of the staged half live in buffer q (gA0, gB0, gA1,
   // gB1, gA2: at least 16 KiB each, 32 rows of up to 512 bytes).
@@ -303,6 +351,7 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(Gemm256Params p) {
     constexpr int CPR = OBN / 8;
     for (int i = tid; i < hrows * CPR; i += GNT) {
       const int r = i / CPR, c = (i % CPR) * 8;
+      if (dense && n0 + c >= p.N) continue;
       *reinterpret_cast<uint4*>(static_cast<bf16_t*>(p.out) + (int64_t)(mh + r) * p.ldo + n0 + c) =
           *reinterpret_cast<const uint4*>(srow(r) + c);
     }
@@ -329,14 +378,18 @@ int gemm_grouped_tile_m() { return GBM; }
 
 hipError_t launch_gemm_grouped(const Gemm256Params& p, EpiKind epi, hipStream_t s) {
   if (p.max_tiles <= 0) return hipSuccess;
-  if (p.M != 0 || p.K % 128 != 0) return hipErrorInvalidValue;
+  if (p.K % 128 != 0) return hipErrorInvalidValue;
+  const bool dense = epi == EPI_F32 || epi == EPI_ACT;
+  if (dense != (p.M > 0) || (dense && p.n_split < p.N && p.n_split % GBN != 0)) return hipErrorInvalidValue;
   const int grid = ((p.max_tiles + 7) / 8) * 8;
   if (epi == EPI_SWIGLU)
     hipLaunchKernelGGL(gemm_grouped_kernel<EPI_SWIGLU>, dim3(grid), dim3(GNT), 0, s, p);
   else if (epi == EPI_DOWN)
     hipLaunchKernelGGL(gemm_grouped_kernel<EPI_DOWN>, dim3(grid), dim3(GNT), 0, s, p);
+  else if (epi == EPI_F32)
+    hipLaunchKernelGGL(gemm_grouped_kernel<EPI_F32>, dim3(grid), dim3(GNT), 0, s, p);
   else
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gemm_grouped_kernel<EPI_ACT>, dim3(grid), dim3(GNT), 0, s, p);
   return hipGetLastError();
 }
 

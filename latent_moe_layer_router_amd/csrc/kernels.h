@@ -92,12 +92,13 @@ int dense_stream_slices(int N, int K);               // K a multiple of 64
 int64_t dense_stream_part_floats(int T, int N, int K);
 hipError_t launch_dense_stream(const DenseStreamParams& p, hipStream_t s);
 
-// Large-tile (256 x 256) dense GEMM (bf16, M > 0): out = A . B^T over M rows
-// and N columns (ntiles_n tiles of 256, the last may be partial), rows
-// [n_split, N) of B^T taken from B1; EPI_F32 (fp32 out, out1 + bias1) or
-// EPI_ACT (bf16 out). The grouped fields (M == 0: offsets, mt_off, E, F,
-// b_expert_stride, b_bytes, ss_out) serve launch_gemm_grouped: expert e has
-// mt_off[e+1] - mt_off[e] row tiles (its rows in sorted order from offsets[e],
+// Tiled bf16 GEMMs of the prefill path (launch_gemm_grouped), 8 waves per tile.
+// Dense (M > 0; EPI_F32 or EPI_ACT): out = A . B^T over M rows (row tiles of
+// 256) and N columns (ntiles_n tiles of 256, the last may be partial), rows
+// [n_split, N) of B^T taken from B1 (n_split a multiple of 256, or N); EPI_F32
+// writes fp32 out and out1 + bias1, EPI_ACT bf16 out. Grouped (M == 0;
+// EPI_SWIGLU or EPI_DOWN): expert e has mt_off[e+1] - mt_off[e] row tiles of up
+// to gemm_grouped_tile_m() rows (its rows in sorted order from offsets[e],
 // split evenly), each times ntiles_n column tiles.
 struct Gemm256Params {
   const void* A;
@@ -127,12 +128,6 @@ struct Gemm256Params {
   int64_t ldo1;
   const float* bias1;
 };
-hipError_t launch_gemm256(const Gemm256Params& p, EpiKind epi, hipStream_t s);
-
-// Grouped expert GEMMs (bf16, M == 0) on row tiles of up to
-// gemm_grouped_tile_m() rows (each expert's rows split evenly over
-// ceil(rows / tile) tiles, mt_off counting them) x 256 weight rows; same
-// parameters as the grouped mode of launch_gemm256. EPI_SWIGLU or EPI_DOWN.
 int gemm_grouped_tile_m();
 hipError_t launch_gemm_grouped(const Gemm256Params& p, EpiKind epi, hipStream_t s);
 
