@@ -27,7 +27,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 // Byte layout of the workspace for a configuration (every region 256-byte aligned).
 struct Plan {
   size_t P, logits, ids, w, masks, chunk_base, counts, offsets, sorted_assign, inv,
-      tiles, n_tiles, mt_off, xp, H, xq, xs, hq, hs, Y, ss, u, part;
+      row_tok, scale, tiles, n_tiles, mt_off, xp, H, xq, xs, hq, hs, Y, ss, u, part;
   size_t total;
   int max_slots;
 };
@@ -61,17 +61,19 @@ Plan make_plan(const lmoe_config& c) {
   p.offsets = grow(cur, (E + 1) * 4);
   p.sorted_assign = grow(cur, A * 4);
   p.inv = grow(cur, A * 4);
+  p.row_tok = grow(cur, A * 4);
+  p.scale = grow(cur, A * 4);
   p.tiles = grow(cur, (size_t)p.max_slots * 8);
   p.n_tiles = grow(cur, 4);
   p.mt_off = grow(cur, (E + 1) * 4);
-  // Expert inputs, rows in sorted (expert-major) order: bf16/fp32 xp (each
-  // token's row once per selected expert) and H, or (MXFP4 experts) their
-  // MXFP8 codes and scales.
+  // Expert inputs: xp one row per token (the gate/up GEMMs gather it through
+  // row_tok), H one row per assignment in sorted (expert-major) order; bf16/fp32,
+  // or (MXFP4 experts) MXFP8 codes and scales.
   const bool mx = c.expert_wdtype == LMOE_MXFP4;
-  p.xp = grow(cur, mx ? 0 : A * Dp * es);
+  p.xp = grow(cur, mx ? 0 : Tm * Dp * es);
   p.H = grow(cur, mx ? 0 : A * F * es);
-  p.xq = grow(cur, mx ? A * Dp : 0);
-  p.xs = grow(cur, mx ? A * Dp / 32 : 0);
+  p.xq = grow(cur, mx ? Tm * Dp : 0);
+  p.xs = grow(cur, mx ? Tm * Dp / 32 : 0);
   p.hq = grow(cur, mx ? A * F : 0);
   p.hs = grow(cur, mx ? A * F / 32 : 0);
   p.Y = grow(cur, A * Dp * es);
@@ -108,7 +110,7 @@ lmoe_status check_config(const lmoe_config* c) {
     return fail(LMOE_E_UNSUPPORTED, "act_dtype must be LMOE_F32 or LMOE_BF16");
   if (c->expert_wdtype == LMOE_MXFP4) {
     // MXFP4 experts: bf16 activations elsewhere, MXFP8 expert inputs, the
-    // block-scaled 256-tile GEMM (K a multiple of 1024, 32-bit byte offsets).
+    // block-scaled tiled GEMM (K a multiple of 1024, 32-bit byte offsets).
     if (c->act_dtype != LMOE_BF16)
       return fail(LMOE_E_UNSUPPORTED, "MXFP4 experts need act_dtype LMOE_BF16");
     if (c->d_pooled % 1024 || c->d_ff % 1024)
@@ -354,6 +356,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   int32_t* tiles = reinterpret_cast<int32_t*>(ws + pl.tiles);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(ws + pl.n_tiles);
   int32_t* inv = reinterpret_cast<int32_t*>(ws + pl.inv);
+  int32_t* row_tok = reinterpret_cast<int32_t*>(ws + pl.row_tok);
   void* xp = ws + pl.xp;
   void* H = ws + pl.H;
   uint8_t* xq = ws + pl.xq;
@@ -375,7 +378,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   // MXFP4 experts: the create-time checks (Dp and F multiples of 1024, 32-bit
   // byte extents) are all the MX weight-streaming kernel needs.
   const int small_max = stream_ok ? stream_max_rows() : (mx ? stream_mx_max_rows() : 0);
-  // Experts with many rows: the 256 x 256 tile GEMM (bf16, Dp % 256 == 0, F % 128 == 0).
+  // Experts with many rows: the tiled grouped GEMM (bf16, Dp % 256 == 0, F % 128 == 0).
   const bool big_ok = bf16 && !mx && Dp % 256 == 0 && F % 128 == 0 && off32_ok;
   int32_t* mt_off = reinterpret_cast<int32_t*>(ws + pl.mt_off);
   const int64_t A_ = (int64_t)T * k;
@@ -507,6 +510,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     sp.offsets = offsets;
     sp.sorted_assign = sorted_assign;
     sp.inv = inv;
+    sp.row_tok = row_tok;
     sp.tiles = tiles;
     sp.n_tiles = n_tiles;
     sp.T = T;
@@ -522,15 +526,16 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   // 4. pooled RMSNorm
   mark();
   if (mx)
-    run(launch_pool_norm_mx(P, h->w.g_pool, T, Dp, c.eps_pool, inv, k, xq, xs, s));
+    run(launch_pool_norm_mx(P, h->w.g_pool, T, Dp, c.eps_pool, xq, xs, s));
   else
-    run(launch_pool_norm(P, h->w.g_pool, T, Dp, c.eps_pool, inv, k, xp, bf16, s));
+    run(launch_pool_norm(P, h->w.g_pool, T, Dp, c.eps_pool, xp, bf16, s));
   // 5. gate/up grouped GEMM + SwiGLU
   mark();
   if (stream_ok) {
     StreamParams sp{};
     sp.A = xp;
     sp.lda = Dp;
+    sp.a_rows = row_tok;
     sp.B = h->w.w_gate_up;
     sp.ldb = Dp;
     sp.b_expert_stride = (int64_t)2 * F * Dp;
@@ -540,7 +545,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     sp.max_rows = small_max;
     sp.K = Dp;
     sp.F = F;
-    sp.a_bytes = (uint32_t)(A_ * Dp * 2);
+    sp.a_bytes = (uint32_t)((int64_t)T * Dp * 2);
     sp.b_bytes = (uint32_t)((int64_t)2 * F * Dp * 2);
     sp.out = H;
     sp.ldo = F;
@@ -550,6 +555,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     StreamMxParams sp{};
     sp.A = xq;
     sp.As = xs;
+    sp.a_rows = row_tok;
     sp.B = static_cast<const uint8_t*>(h->w.w_gate_up);
     sp.Bs = h->w.s_gate_up;
     sp.N = 2 * F;
@@ -559,8 +565,8 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     sp.max_rows = small_max;
     sp.K = Dp;
     sp.F = F;
-    sp.a_bytes = (uint32_t)(A_ * Dp);
-    sp.as_bytes = (uint32_t)(A_ * Dp / 32);
+    sp.a_bytes = (uint32_t)((int64_t)T * Dp);
+    sp.as_bytes = (uint32_t)((int64_t)T * Dp / 32);
     sp.b_bytes = (uint32_t)((int64_t)F * Dp);
     sp.bs_bytes = (uint32_t)((int64_t)2 * F * Dp / 32);
     sp.out = hq;
@@ -573,6 +579,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     Gemm256MxParams g{};
     g.A = xq;
     g.As = xs;
+    g.a_rows = row_tok;
     g.B = static_cast<const uint8_t*>(h->w.w_gate_up);
     g.Bs = h->w.s_gate_up;
     g.N = 2 * F;
@@ -581,8 +588,8 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     g.E = E;
     g.ntiles_n = F / 128;
     g.max_tiles = g.ntiles_n * mtiles_bound;
-    g.a_bytes = (uint32_t)(A_ * Dp);
-    g.as_bytes = (uint32_t)(A_ * Dp / 32);
+    g.a_bytes = (uint32_t)((int64_t)T * Dp);
+    g.as_bytes = (uint32_t)((int64_t)T * Dp / 32);
     g.K = Dp;
     g.F = F;
     g.out = hq;
@@ -594,6 +601,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     Gemm256Params g{};
     g.A = xp;
     g.lda = Dp;
+    g.a_rows = row_tok;
     g.B = h->w.w_gate_up;
     g.ldb = Dp;
     g.b_expert_stride = (int64_t)2 * F * Dp;
@@ -602,7 +610,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     g.E = E;
     g.ntiles_n = F / 128;
     g.max_tiles = g.ntiles_n * mtiles_bound;
-    g.a_bytes = (uint32_t)(A_ * Dp * 2);
+    g.a_bytes = (uint32_t)((int64_t)T * Dp * 2);
     g.b_bytes = (uint32_t)((int64_t)2 * F * Dp * 2);
     g.K = Dp;
     g.F = F;
@@ -615,6 +623,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     g.K = Dp;
     g.A = xp;
     g.lda = Dp;
+    g.a_rows = row_tok;
     g.B0 = h->w.w_gate_up;
     g.ldb = Dp;
     g.b_expert_stride = (int64_t)2 * F * Dp;
@@ -741,6 +750,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     cp.y = Y;
     cp.ss = ss;
     cp.inv = inv;
+    cp.scale = reinterpret_cast<float*>(ws + pl.scale);
     cp.ids = ids;
     cp.w = tw;
     cp.g_expert = h->w.g_expert;

@@ -84,6 +84,7 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmParams p) {
   auto a_row = [&](int r) -> const unsigned char* {
     int m = m0 + r;
     if (m >= m_end) m = m_end - 1;          // rows past the end load a valid row; never stored
+    if (p.a_rows) m = p.a_rows[m];          // gathered rows (gate/up: the assignment's token)
     return reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.A) + (int64_t)m * p.lda) + lc * 16;
   };
   auto b_row = [&](int r) -> const unsigned char* {

@@ -147,7 +147,8 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(Gemm256Params p) {
     const int m = m0 + r;
     if (m >= m_end) return kOutOfRange;
     const uint32_t c = pos ^ (((r >> 1) ^ (r >> 3)) & 3);
-    return (uint32_t)m * (uint32_t)(p.lda * 2) + c * 16;
+    const int src = p.a_rows ? p.a_rows[m] : m;   // gathered rows (gate/up: the assignment's token)
+    return (uint32_t)src * (uint32_t)(p.lda * 2) + c * 16;
   };
   auto b_off = [&](int r) -> uint32_t {
     const int n = dense ? r : (EPI == EPI_SWIGLU) ? ((r < GBN / 2) ? (n0 + r) : (p.F + n0 + r - GBN / 2)) : (n0 + r);

@@ -139,6 +139,7 @@ __global__ __launch_bounds__(XNT, 1) void gemm_grouped_mx_kernel(Gemm256MxParams
   // Rows past the tile's end (tail rows) get offsets beyond every extent: their
   // loads read nothing from memory; they are never stored.
   auto a_live = [&](int r) { return m0 + r < m_end; };
+  auto a_src = [&](int r) { return (uint32_t)(p.a_rows ? p.a_rows[m0 + r] : m0 + r); };   // gathered rows
   auto b_row = [&](int r) -> uint32_t {     // B row of tile row r
     return (EPI == EPI_SWIGLU) ? (uint32_t)((r < XBN / 2) ? (n0 + r) : (p.F + n0 + r - XBN / 2))
                                : (uint32_t)(n0 + r);
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(XNT, 1) void gemm_grouped_mx_kernel(Gemm256MxParams
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
     const int r = 8 * (5 * wave + i) + (lane >> 3);
-    ga[i] = a_live(r) ? (uint32_t)(m0 + r) * (uint32_t)K + (uint32_t)(((lane & 7) ^ fa(r)) << 4) : kOutOfRange;
+    ga[i] = a_live(r) ? a_src(r) * (uint32_t)K + (uint32_t)(((lane & 7) ^ fa(r)) << 4) : kOutOfRange;
   }
   // B: 16 loads of 16 rows x 64 bytes per stage; wave w issues 2 w, 2 w + 1.
   uint32_t gb[2];
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(XNT, 1) void gemm_grouped_mx_kernel(Gemm256MxParams
   // B); wave w issues load w, and wave 0 also load 8.
   auto scale_off = [&](int s) -> uint32_t {
     const int r = 64 * (s < 5 ? s : s - 5) + lane;
-    if (s < 5) return a_live(r) ? (uint32_t)(m0 + r) * (uint32_t)(K / 32) : kOutOfRange;
+    if (s < 5) return a_live(r) ? a_src(r) * (uint32_t)(K / 32) : kOutOfRange;
     return b_row(r) * (uint32_t)(K / 32);
   };
   const uint32_t gs0 = scale_off(wave), gs1 = scale_off(8);

@@ -18,6 +18,7 @@ struct GemmParams {
   int M, N, K;                 // dense: M rows; N output columns; K inner
   const void* A;
   int64_t lda;                 // elements
+  const int32_t* a_rows;       // if set, product row m reads A row a_rows[m] (gate/up: its token)
   const void* B0;
   const void* B1;              // EPI_F32: rows [n_split, N) come from B1
   int n_split;
@@ -48,6 +49,7 @@ hipError_t launch_gemm(const GemmParams& p, EpiKind epi, bool bf16, hipStream_t 
 struct StreamParams {
   const void* A;
   int64_t lda;
+  const int32_t* a_rows;       // if set, product row m reads A row a_rows[m] (gate/up: its token)
   const void* B;
   int64_t ldb;
   int64_t b_expert_stride;
@@ -103,6 +105,7 @@ hipError_t launch_dense_stream(const DenseStreamParams& p, hipStream_t s);
 struct Gemm256Params {
   const void* A;
   int64_t lda;
+  const int32_t* a_rows;       // if set, product row m reads A row a_rows[m] (gate/up: its token)
   const void* B;
   int64_t ldb;
   int64_t b_expert_stride;
@@ -136,8 +139,9 @@ hipError_t launch_gemm_grouped(const Gemm256Params& p, EpiKind epi, hipStream_t 
 // to out, scales to out_scales); EPI_DOWN writes y as bf16 and the sums of
 // squares.
 struct Gemm256MxParams {
-  const uint8_t* A;            // [rows][K] E4M3 codes, rows in sorted order
+  const uint8_t* A;            // [rows][K] E4M3 codes (rows in sorted order, or gathered by a_rows)
   const uint8_t* As;           // [rows][K/32] E8M0 scales
+  const int32_t* a_rows;       // if set, product row m reads A row a_rows[m] (gate/up: its token)
   const uint8_t* B;            // [E][N][K/2] E2M1 codes, two per byte (low nibble first)
   const uint8_t* Bs;           // [E][N][K/32] E8M0 scales
   int N;                       // B rows per expert (2F for gate/up, Dp for down)
@@ -168,8 +172,9 @@ hipError_t launch_gemm_grouped_mx(const Gemm256MxParams& p, EpiKind epi, hipStre
 // group of 64 weight rows). K a multiple of 1024.
 // Same operand and output formats as Gemm256MxParams.
 struct StreamMxParams {
-  const uint8_t* A;            // [rows][K] E4M3 codes, rows in sorted order
+  const uint8_t* A;            // [rows][K] E4M3 codes (rows in sorted order, or gathered by a_rows)
   const uint8_t* As;           // [rows][K/32] E8M0 scales
+  const int32_t* a_rows;       // if set, product row m reads A row a_rows[m] (gate/up: its token)
   const uint8_t* B;            // [E][N][K/2] E2M1 codes
   const uint8_t* Bs;           // [E][N][K/32] E8M0 scales
   int N;                       // B rows per expert (2F for gate/up, Dp for down)
@@ -212,6 +217,7 @@ struct SortParams {
   int32_t* offsets;             // [E+1]
   int32_t* sorted_assign;       // [T*k]
   int32_t* inv;                 // [T*k]
+  int32_t* row_tok;             // [T*k] token of each sorted row
   int32_t* tiles;               // [max_slots][2]
   int32_t* n_tiles;             // [1]
   int T, E, k, tile_m;
@@ -221,15 +227,15 @@ struct SortParams {
 };
 hipError_t launch_sort(const SortParams& p, hipStream_t s);
 
-// xp = bf16/f32( P * rsqrt(mean(P^2) + eps) * g ), written to the token's k rows
-// of the sorted order: row inv[t*k + j] for j < k (the experts' input rows).
-hipError_t launch_pool_norm(const float* P, const float* g, int T, int Dp, float eps, const int32_t* inv,
-                            int k, void* xp, bool bf16, hipStream_t s);
+// xp[t] = bf16/f32( P[t] * rsqrt(mean(P[t]^2) + eps) * g ), one row per token;
+// the expert GEMMs gather the rows of their sorted assignments.
+hipError_t launch_pool_norm(const float* P, const float* g, int T, int Dp, float eps, void* xp, bool bf16,
+                            hipStream_t s);
 
 // MXFP4-expert path: xp quantized to MXFP8 E4M3 blocks of 32 (codes [T][Dp],
 // scales [T][Dp/32]) instead of stored as bf16.
-hipError_t launch_pool_norm_mx(const float* P, const float* g, int T, int Dp, float eps, const int32_t* inv,
-                               int k, uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_pool_norm_mx(const float* P, const float* g, int T, int Dp, float eps, uint8_t* codes,
+                               uint8_t* scales, hipStream_t s);
 // n fp32 values (n a multiple of 32) -> MXFP8 E4M3 codes [n] and scales [n/32].
 hipError_t launch_mx_quant(const float* x, int64_t n, uint8_t* codes, uint8_t* scales, hipStream_t s);
 
@@ -249,6 +255,7 @@ struct CombineParams {
   const int32_t* ids;      // [T][k]
   const float* w;          // [T][k]
   const float* g_expert;   // [E][Dp]
+  float* scale;            // [T*k] slot scales (scratch)
   void* u;                 // [T][Dp]
   int T, k, Dp;
   float eps;

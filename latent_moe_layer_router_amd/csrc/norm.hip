@@ -3,16 +3,17 @@
 // pool_norm — the pooled input is RMS-normalized before the experts run (LMSYS
 // blog, "MoE with pooler, unpooler and per-expert normalization"): one workgroup
 // per token reads the fp32 pooler output row, reduces its sum of squares and
-// writes xp = P / sqrt(mean(P^2) + eps) * g_pool in the expert GEMM's input type
-// to each of the token's k rows in the experts' sorted order.
+// writes xp = P / sqrt(mean(P^2) + eps) * g_pool in the expert GEMM's input type,
+// one row per token (the expert GEMMs gather the rows of their assignments).
 //
 // combine — the finalize step of the blog's "AMD support" section (unpermute +
-// per-expert RMSNorm + weighted sum in one kernel). One workgroup per token
-// gathers the token's k expert rows from their sorted positions, scales each by
-// w_j / sqrt(mean(y^2) + eps) — the mean coming from the down GEMM's per-64-column
-// partial sums of squares of the stored values ("Fused per-expert post-norm") —
-// and by that expert's gamma, and sums in fp32 in slot order j = 0..k-1 ("Miles"
-// RL backend: FP32 weighted sum).
+// per-expert RMSNorm + weighted sum; here a scale pass and a sum pass). Each
+// slot's scale is w_j / sqrt(mean(y^2) + eps), the mean coming from the down
+// GEMM's per-64-column partial sums of squares of the stored values ("Fused
+// per-expert post-norm"). A workgroup of the sum pass takes 1024 columns of one
+// token: it gathers the token's k expert rows from their sorted positions,
+// multiplies each by its scale and that expert's gamma, and sums in fp32 in slot
+// order j = 0..k-1 ("Miles" RL backend: FP32 weighted sum).
 #include "common.h"
 #include "kernels.h"
 #include "mx.h"
@@ -46,38 +47,10 @@ __device__ __forceinline__ void store8(float* dst, const float (&v)[8]) {
   reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
   reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
-// Load 8 consecutive fp32 values.
-__device__ __forceinline__ void load8(const float* src, float (&v)[8]) {
-  const float4 a = reinterpret_cast<const float4*>(src)[0], b = reinterpret_cast<const float4*>(src)[1];
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-
-// load8 with a non-temporal hint: for rows read exactly once, so that they do
-// not displace lines that are read again (the experts' gammas in the combine).
-__device__ __forceinline__ void load8_once(const bf16_t* src, float (&v)[8]) {
-  typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-  const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-  }
-}
-__device__ __forceinline__ void load8_once(const float* src, float (&v)[8]) {
-  typedef __attribute__((ext_vector_type(4))) float f32x4v;
-  const f32x4v a = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(src));
-  const f32x4v b = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(src) + 1);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-
-// The normalized row goes to the token's k rows of the sorted (expert-major)
-// order, inv[t*k + j], so that the expert GEMMs read their rows contiguously.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void pool_norm_kernel(const float* __restrict__ P,
                                                              const float* __restrict__ g, int Dp,
-                                                             float eps, const int32_t* __restrict__ inv,
-                                                             int k, T* __restrict__ xp) {
+                                                             float eps, T* __restrict__ xp) {
   __shared__ float red[kThreads / kWave];
   const int t = blockIdx.x;
   const float* row = P + (int64_t)t * Dp;
@@ -99,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void pool_norm_kernel(const float* __rest
       v[i + 2] = x.z * r * gg.z;
       v[i + 3] = x.w * r * gg.w;
     }
-    for (int j = 0; j < k; ++j) store8(xp + (int64_t)inv[t * k + j] * Dp + c, v);
+    store8(xp + (int64_t)t * Dp + c, v);
   }
 }
 
@@ -125,8 +98,7 @@ __device__ __forceinline__ void mx_store_block(const float (&v)[32], uint8_t* co
 // input. One thread per block after the row's sum of squares.
 __global__ __launch_bounds__(kThreads) void pool_norm_mx_kernel(const float* __restrict__ P,
                                                                 const float* __restrict__ g, int Dp,
-                                                                float eps, const int32_t* __restrict__ inv,
-                                                                int k, uint8_t* __restrict__ codes,
+                                                                float eps, uint8_t* __restrict__ codes,
                                                                 uint8_t* __restrict__ scales) {
   __shared__ float red[kThreads / kWave];
   const int t = blockIdx.x;
@@ -149,16 +121,7 @@ __global__ __launch_bounds__(kThreads) void pool_norm_mx_kernel(const float* __r
       v[i + 2] = x.z * r * gg.z;
       v[i + 3] = x.w * r * gg.w;
     }
-    // one quantization, stored to the token's k sorted rows
-    uint8_t* c0 = codes + (int64_t)inv[t * k] * Dp + 32 * b;
-    uint8_t* s0 = scales + (int64_t)inv[t * k] * (Dp / 32) + b;
-    mx_store_block(v, c0, s0);
-    for (int j = 1; j < k; ++j) {
-      const int64_t pos = inv[t * k + j];
-      reinterpret_cast<uint4*>(codes + pos * Dp + 32 * b)[0] = reinterpret_cast<const uint4*>(c0)[0];
-      reinterpret_cast<uint4*>(codes + pos * Dp + 32 * b)[1] = reinterpret_cast<const uint4*>(c0)[1];
-      scales[pos * (Dp / 32) + b] = *s0;
-    }
+    mx_store_block(v, codes + (int64_t)t * Dp + 32 * b, scales + (int64_t)t * (Dp / 32) + b);
   }
 }
 
@@ -177,76 +140,118 @@ __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const float* __restr
   mx_store_block(v, codes + 32 * b, scales + b);
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
-  __shared__ float scale[16];
-  __shared__ int pos[16];
-  __shared__ int eid[16];
-  const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Slot scales, one wave per assignment a: w_a / sqrt(mean(y_a^2) + eps), the
+// mean from the row's partial sums of squares (lane q adds partials q, q + 64,
+// ..., then a butterfly over the wave).
+__global__ __launch_bounds__(kThreads) void combine_scale_kernel(CombineParams p) {
+  const int a = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (a >= p.T * p.k) return;               // whole waves
   const int nss = p.Dp / 64;
-  // Slot j's scale: one wave reduces the row's partial sums of squares (lane q
-  // takes partials q, q + 64, ...; then a butterfly over the wave).
-  for (int j = wave; j < p.k; j += kThreads / kWave) {
-    const int a = t * p.k + j;
-    const int ps = p.inv[a];
-    const float* ss = p.ss + (int64_t)ps * nss;
-    float s = 0.f;
-    for (int q = lane; q < nss; q += kWave) s += ss[q];
-    s = wave_sum(s);
-    if (lane == 0) {
-      scale[j] = p.w[a] / sqrtf(s / (float)p.Dp + p.eps);
-      pos[j] = ps;
-      eid[j] = p.ids[a];
-    }
+  const float* ss = p.ss + (int64_t)p.inv[a] * nss;
+  float s = 0.f;
+  for (int q = lane; q < nss; q += kWave) s += ss[q];
+  s = wave_sum(s);
+  if (lane == 0) p.scale[a] = p.w[a] / sqrtf(s / (float)p.Dp + p.eps);
+}
+
+// One workgroup per (1024-column chunk, token). Consecutive workgroups take
+// consecutive tokens, token t starting at chunk t mod (Dp / 1024): the rows
+// being read at any time spread over all column offsets (and so over all HBM
+// channels; all workgroups on one chunk measured 10% slower). A thread sums 8
+// consecutive columns over the token's k slots in slot order.
+constexpr int kCombineThreads = 128, kCombineCols = kCombineThreads * 8;
+
+// The k slots' loads are all issued before any is used: raw 16-byte words per
+// slot (converted to fp32 only when summed, so each load keeps registers of its
+// own and stays in flight).
+__device__ __forceinline__ uint4 load16_once(const void* src) {
+  typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+  const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+  return make_uint4(q.x, q.y, q.z, q.w);
+}
+__device__ __forceinline__ void widen8(const uint4& q, float (&v)[8]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
   }
-  __syncthreads();
+}
+
+template <typename T>
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineParams p) {
+  const int nchunk = (p.Dp + kCombineCols - 1) / kCombineCols;
+  const int t = blockIdx.x % p.T, chunk = (blockIdx.x / p.T + t) % nchunk;
+  const int c = chunk * kCombineCols + threadIdx.x * 8;
+  if (c >= p.Dp) return;
+  constexpr int VW = 16 / sizeof(T);       // values per 16-byte word of y
   const T* y = static_cast<const T*>(p.y);
-  T* u = static_cast<T*>(p.u) + (int64_t)t * p.Dp;
-  // 8 consecutive columns per thread; the loads of up to 8 slots are issued
-  // before any is used, then the terms are added in slot order j = 0..k-1.
-  for (int c = threadIdx.x * 8; c < p.Dp; c += kThreads * 8) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < p.k; j0 += 8) {
-      float yv[8][8], gv[8][8];
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < p.k; j0 += 8) {
+    int pos[8], eid[8];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        if (j0 + jj < p.k) {
-          load8_once(y + (int64_t)pos[j0 + jj] * p.Dp + c, yv[jj]);
-          load8(p.g_expert + (int64_t)eid[j0 + jj] * p.Dp + c, gv[jj]);
-        }
-      }
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        if (j0 + jj < p.k) {
-          const float sj = scale[j0 + jj];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] += sj * gv[jj][i] * yv[jj][i];
-        }
+    for (int jj = 0; jj < 8; ++jj) {
+      if (j0 + jj < p.k) {
+        pos[jj] = p.inv[t * p.k + j0 + jj];
+        eid[jj] = p.ids[t * p.k + j0 + jj];
       }
     }
-    store8(u + c, acc);
+    uint4 yr[8][8 / VW];
+    float4 g0[8], g1[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if (j0 + jj < p.k) {
+        const T* yrow = y + (int64_t)pos[jj] * p.Dp + c;
+#pragma unroll
+        for (int h = 0; h < 8 / VW; ++h) yr[jj][h] = load16_once(yrow + h * VW);
+        const float4* gp = reinterpret_cast<const float4*>(p.g_expert + (int64_t)eid[jj] * p.Dp + c);
+        g0[jj] = gp[0];
+        g1[jj] = gp[1];
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if (j0 + jj < p.k) {
+        const float sj = p.scale[t * p.k + j0 + jj];
+        float yv[8];
+        if constexpr (VW == 8) {
+          widen8(yr[jj][0], yv);
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            yv[4 * h] = __uint_as_float(yr[jj][h].x);
+            yv[4 * h + 1] = __uint_as_float(yr[jj][h].y);
+            yv[4 * h + 2] = __uint_as_float(yr[jj][h].z);
+            yv[4 * h + 3] = __uint_as_float(yr[jj][h].w);
+          }
+        }
+        const float gv[8] = {g0[jj].x, g0[jj].y, g0[jj].z, g0[jj].w, g1[jj].x, g1[jj].y, g1[jj].z, g1[jj].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += sj * gv[i] * yv[i];
+      }
+    }
   }
+  store8(static_cast<T*>(p.u) + (int64_t)t * p.Dp + c, acc);
 }
 
 }  // namespace
 
-hipError_t launch_pool_norm(const float* P, const float* g, int T, int Dp, float eps, const int32_t* inv,
-                            int k, void* xp, bool bf16, hipStream_t s) {
+hipError_t launch_pool_norm(const float* P, const float* g, int T, int Dp, float eps, void* xp, bool bf16,
+                            hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (bf16)
-    hipLaunchKernelGGL(pool_norm_kernel<bf16_t>, dim3(T), dim3(kThreads), 0, s, P, g, Dp, eps, inv, k,
+    hipLaunchKernelGGL(pool_norm_kernel<bf16_t>, dim3(T), dim3(kThreads), 0, s, P, g, Dp, eps,
                        static_cast<bf16_t*>(xp));
   else
-    hipLaunchKernelGGL(pool_norm_kernel<float>, dim3(T), dim3(kThreads), 0, s, P, g, Dp, eps, inv, k,
+    hipLaunchKernelGGL(pool_norm_kernel<float>, dim3(T), dim3(kThreads), 0, s, P, g, Dp, eps,
                        static_cast<float*>(xp));
   return hipGetLastError();
 }
 
-hipError_t launch_pool_norm_mx(const float* P, const float* g, int T, int Dp, float eps, const int32_t* inv,
-                               int k, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+hipError_t launch_pool_norm_mx(const float* P, const float* g, int T, int Dp, float eps, uint8_t* codes,
+                               uint8_t* scales, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(pool_norm_mx_kernel, dim3(T), dim3(kThreads), 0, s, P, g, Dp, eps, inv, k, codes,
-                     scales);
+  hipLaunchKernelGGL(pool_norm_mx_kernel, dim3(T), dim3(kThreads), 0, s, P, g, Dp, eps, codes, scales);
   return hipGetLastError();
 }
 
@@ -260,10 +265,15 @@ hipError_t launch_mx_quant(const float* x, int64_t n, uint8_t* codes, uint8_t* s
 
 hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
+  const int64_t grid = (int64_t)((p.Dp + kCombineCols - 1) / kCombineCols) * p.T;
+  if (grid >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const int64_t n_assign = (int64_t)p.T * p.k;
+  hipLaunchKernelGGL(combine_scale_kernel, dim3((unsigned)((n_assign + kThreads / kWave - 1) / (kThreads / kWave))),
+                     dim3(kThreads), 0, s, p);
   if (bf16)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(p.T), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(grid), dim3(kCombineThreads), 0, s, p);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(p.T), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(grid), dim3(kCombineThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -216,6 +216,7 @@ __global__ __launch_bounds__(64) void sort_scatter_kernel(SortParams p) {
       const int pos = p.offsets[e] + p.chunk_base[(int64_t)chunk * p.E + e] + __popcll(m & below);
       p.sorted_assign[pos] = a;
       p.inv[a] = pos;
+      p.row_tok[pos] = t;
     }
   }
   // The chunk's masks are read only here (after the scan): clear them for the

@@ -86,7 +86,8 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int e, int gr
 #pragma unroll
   for (int i = 0; i < 2 * NMT; ++i) {
     const int tr = 8 * i + lrow;
-    const int pos = lo + (tr < m_e ? tr : m_e - 1);
+    int pos = lo + (tr < m_e ? tr : m_e - 1);
+    if (p.a_rows) pos = p.a_rows[pos];       // gathered rows (gate/up: the assignment's token)
     ao[i] = (uint32_t)pos * (uint32_t)(p.lda * 2) + (uint32_t)((lc ^ swz8(tr)) << 4);
   }
 #define LMOE_ISSUE(c, SW, SA)                                                                   \

@@ -116,7 +116,8 @@ __device__ __forceinline__ void stream_mx_body(const StreamMxParams& p, int e, i
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) {
     const int tr = mt * 16 + r16;
-    const int pos = lo + (tr < m_e ? tr : m_e - 1);
+    int pos = lo + (tr < m_e ? tr : m_e - 1);
+    if (p.a_rows) pos = p.a_rows[pos];       // gathered rows (gate/up: the assignment's token)
     ao[mt] = (uint32_t)pos * (uint32_t)K + 16 * q;
     aso[mt] = (uint32_t)pos * (uint32_t)rs + 8 * q;
   }

@@ -37,9 +37,10 @@ def test_status_strings_and_null_destroy():
 def test_workspace_bytes_full_size():
     cfg = lmoe.make_config(8192, 4096, 4096, 256, 8, 16384)
     n = lmoe.lmoe_workspace_bytes(cfg)
-    # intermediates: P fp32 (256 MiB); xp, H, Y in sorted order (1 GiB each, bf16);
-    # u (128 MiB), sum-of-squares partials, logits, routing arrays
-    assert 3.4 * 2 ** 30 < n < 3.5 * 2 ** 30
+    # intermediates: P fp32 (256 MiB); xp one row per token (128 MiB, bf16); H, Y
+    # in sorted order (1 GiB each); u (128 MiB), sum-of-squares partials, logits,
+    # routing arrays
+    assert 2.5 * 2 ** 30 < n < 2.65 * 2 ** 30
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -84,8 +85,8 @@ def test_mxfp4_config():
     codes + scales (1 + 1/32 bytes per value instead of 2)."""
     bf = lmoe.lmoe_workspace_bytes(lmoe.make_config(8192, 4096, 4096, 256, 8, 16384))
     mx = lmoe.lmoe_workspace_bytes(lmoe.make_config(8192, 4096, 4096, 256, 8, 16384, experts="mxfp4"))
-    A = 16384 * 8
-    assert bf - mx == pytest.approx((A * 4096 + A * 4096) * (2 - 1 - 1 / 32), abs=2 ** 20)
+    T, A = 16384, 16384 * 8      # xp: one row per token; H: one per assignment
+    assert bf - mx == pytest.approx((T * 4096 + A * 4096) * (2 - 1 - 1 / 32), abs=2 ** 20)
     cfg = lmoe.make_config(8192, 4096, 4096, 256, 8, 128, act="f32", experts="mxfp4")
     with pytest.raises(lmoe.LmoeError) as e:
         lmoe.lmoe_workspace_bytes(cfg)

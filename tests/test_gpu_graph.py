@@ -4,7 +4,7 @@ eager work (a fill of the output, an eager forward) and synchronizations between
 the replays. The forward is deterministic, so the comparison is exact.
 
 Cases cover the kernels a forward launches: the small-batch dense projections
-and the weight-streaming expert GEMMs (T <= 128), the 256-tile dense and grouped
+and the weight-streaming expert GEMMs (T <= 128), the tiled dense and grouped
 GEMMs (larger T, experts above the streaming limit), and the MXFP4 path.
 """
 import pytest
@@ -53,7 +53,7 @@ def test_graph_small_batch_bf16():
 
 
 def test_graph_tiled_bf16():
-    """T = 600 over 4 experts: 256-tile dense projections and grouped GEMMs."""
+    """T = 600 over 4 experts: tiled dense projections and grouped GEMMs."""
     replay_case(tiny(T=600, D=512, Dp=256, F_=256, E=4, k=2, seed=302, act=synth.BF16))
 
 

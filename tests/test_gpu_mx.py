@@ -9,7 +9,7 @@ inputs on the block-scaled MFMA) against the CPU oracle.
   max|err|/RMS(out) <= 6e-2, at small multi-tile shapes and at the full size on
   a seeded 64-token subset of the 16K prefill chunk.
 * Experts with at most 32 rows take the MX weight-streaming kernel, the rest
-  the 256-row tiles: row counts at the boundaries (0, 1, 16, 17, 32, 33), both
+  the tiled grouped GEMM (row tiles of up to 320): row counts at the boundaries (0, 1, 16, 17, 32, 33), both
   GEMMs at K = 1024, 2048 and 4096, and the full-size decode batch (T=128).
 """
 import numpy as np
@@ -88,8 +88,8 @@ def mx_tiny(**kw):
 @pytest.mark.parametrize("T,E,k", [(100, 8, 2), (600, 4, 2), (37, 16, 3)])
 def test_mx_small(T, E, k):
     """Dp = F = 1024 (the path needs multiples of 1024). T=600, E=4, k=2 puts
-    about 300 rows on each expert: full 256-row tiles plus ragged tails; the
-    others leave each expert one partial tile."""
+    about 300 rows on each expert: one tile of up to 320 rows split between
+    two wave rows with a ragged tail; the others leave each expert a few rows."""
     run_case(mx_tiny(T=T, D=256, Dp=1024, F_=1024, E=E, k=k, seed=200 + T))
 
 

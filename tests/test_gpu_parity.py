@@ -76,8 +76,8 @@ def test_multi_tile_fp32():
 def test_all_tokens_same_experts(Dp, F):
     """A router bias forces every token onto the same k experts: three full
     experts of 300 rows and every other expert empty. With Dp = F = 128 they
-    run as three 128-row tiles each; with Dp = F = 256 on the 256-row tiles,
-    one full tile plus a 44-row tail each."""
+    run as three 128-row tiles each; with Dp = F = 256 on the tiled grouped
+    GEMM, one tile of 300 rows each (160 + 140 between the wave rows)."""
     w = tiny(T=300, D=256, Dp=Dp, F_=F, E=16, k=3, seed=105, act=synth.BF16)
     wts = synth.dense_weights(w)
     b = np.zeros(w.E, np.float32)
