@@ -439,6 +439,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
 
   // 1. router + pooler: one GEMM over [W_pool; W_router]
   mark();
+  bool pooled = false;
   if (dense256) {
     Gemm256Params g = dense_params(x, D, Dp + E);
     g.B = h->w.w_pool;
@@ -468,7 +469,11 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     d.out1 = logits;
     d.ldo1 = E;
     d.bias1 = h->w.b_router;
-    run(launch_dense_stream(d, s));
+    // the split-K reduction, the pooled RMSNorm and the MXFP8 quantization of
+    // xp in one pass (xp is one row per token, so it needs no routing)
+    run(launch_dense_stream_partials(d, s));
+    run(launch_splitk_pool_norm(d, h->w.g_pool, c.eps_pool, mx ? static_cast<void*>(xq) : xp, mx ? 2 : 0, xs, s));
+    pooled = true;
   } else {
     GemmParams g{};
     g.M = T;
@@ -523,12 +528,14 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     run(launch_sort(sp, s));
     if (err == hipSuccess) h->masks_dirty = false;
   }
-  // 4. pooled RMSNorm
+  // 4. pooled RMSNorm (already done with the small-batch reduction)
   mark();
-  if (mx)
+  if (pooled) {
+  } else if (mx) {
     run(launch_pool_norm_mx(P, h->w.g_pool, T, Dp, c.eps_pool, xq, xs, s));
-  else
+  } else {
     run(launch_pool_norm(P, h->w.g_pool, T, Dp, c.eps_pool, xp, bf16, s));
+  }
   // 5. gate/up grouped GEMM + SwiGLU
   mark();
   if (stream_ok) {

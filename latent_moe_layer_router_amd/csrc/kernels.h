@@ -92,7 +92,11 @@ struct DenseStreamParams {
 int dense_stream_max_tokens();
 int dense_stream_slices(int N, int K);               // K a multiple of 64
 int64_t dense_stream_part_floats(int T, int N, int K);
+int dense_stream_part_ld(int N);                     // floats per token row of part
 hipError_t launch_dense_stream(const DenseStreamParams& p, hipStream_t s);
+// The split-K partials only (part, [slices][T][dense_stream_part_ld(N)]); the
+// reduction is left to the caller.
+hipError_t launch_dense_stream_partials(const DenseStreamParams& p, hipStream_t s);
 
 // Tiled bf16 GEMMs of the prefill path (launch_gemm_grouped), 8 waves per tile.
 // Dense (M > 0; EPI_F32 or EPI_ACT): out = A . B^T over M rows (row tiles of
@@ -231,6 +235,12 @@ hipError_t launch_sort(const SortParams& p, hipStream_t s);
 // the expert GEMMs gather the rows of their sorted assignments.
 hipError_t launch_pool_norm(const float* P, const float* g, int T, int Dp, float eps, void* xp, bool bf16,
                             hipStream_t s);
+
+// Router + pooler at small batches: reduce the split-K partials of d (fp32
+// out0 = P, out1 = logits + bias1) and normalize each P row into xp in one
+// kernel. mode 0: bf16 xp, 2: MXFP8 (codes to xp, scales).
+hipError_t launch_splitk_pool_norm(const DenseStreamParams& d, const float* g, float eps, void* xp, int mode,
+                                   uint8_t* scales, hipStream_t s);
 
 // MXFP4-expert path: xp quantized to MXFP8 E4M3 blocks of 32 (codes [T][Dp],
 // scales [T][Dp/32]) instead of stored as bf16.

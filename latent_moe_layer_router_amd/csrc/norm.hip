@@ -24,6 +24,7 @@ namespace {
 
 constexpr int kThreads = 256;
 
+template <int NT = kThreads>
 __device__ float block_sum(float v, float* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   v = wave_sum(v);
@@ -31,7 +32,7 @@ __device__ float block_sum(float v, float* red) {
   __syncthreads();
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < kThreads / kWave; ++i) s += red[i];
+  for (int i = 0; i < NT / kWave; ++i) s += red[i];
   __syncthreads();
   return s;
 }
@@ -47,21 +48,18 @@ __device__ __forceinline__ void store8(float* dst, const float (&v)[8]) {
   reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
   reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
-template <typename T>
-__global__ __launch_bounds__(kThreads) void pool_norm_kernel(const float* __restrict__ P,
-                                                             const float* __restrict__ g, int Dp,
-                                                             float eps, T* __restrict__ xp) {
-  __shared__ float red[kThreads / kWave];
-  const int t = blockIdx.x;
-  const float* row = P + (int64_t)t * Dp;
+// Normalize one fp32 row of P (the calling workgroup's NT threads) into xp.
+template <int NT, typename T>
+__device__ __forceinline__ void pool_norm_row(const float* __restrict__ row, const float* __restrict__ g,
+                                              int Dp, float eps, T* __restrict__ out, float* red) {
   float ss = 0.f;
-  for (int c = threadIdx.x * 4; c < Dp; c += kThreads * 4) {
+  for (int c = threadIdx.x * 4; c < Dp; c += NT * 4) {
     const float4 v = *reinterpret_cast<const float4*>(row + c);
     ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
   }
-  ss = block_sum(ss, red);
+  ss = block_sum<NT>(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)Dp + eps);
-  for (int c = threadIdx.x * 8; c < Dp; c += kThreads * 8) {
+  for (int c = threadIdx.x * 8; c < Dp; c += NT * 8) {
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; i += 4) {
@@ -72,8 +70,17 @@ __global__ __launch_bounds__(kThreads) void pool_norm_kernel(const float* __rest
       v[i + 2] = x.z * r * gg.z;
       v[i + 3] = x.w * r * gg.w;
     }
-    store8(xp + (int64_t)t * Dp + c, v);
+    store8(out + c, v);
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void pool_norm_kernel(const float* __restrict__ P,
+                                                             const float* __restrict__ g, int Dp,
+                                                             float eps, T* __restrict__ xp) {
+  __shared__ float red[kThreads / kWave];
+  const int t = blockIdx.x;
+  pool_norm_row<kThreads>(P + (int64_t)t * Dp, g, Dp, eps, xp + (int64_t)t * Dp, red);
 }
 
 // Quantize 32 values held by one thread to an MXFP8 E4M3 block: 32 code bytes
@@ -96,21 +103,18 @@ __device__ __forceinline__ void mx_store_block(const float (&v)[32], uint8_t* co
 // MX variant of pool_norm (MXFP4-expert path): the normalized row is quantized
 // to MXFP8 E4M3 blocks of 32 (codes [T][Dp], scales [T][Dp/32]) as the experts'
 // input. One thread per block after the row's sum of squares.
-__global__ __launch_bounds__(kThreads) void pool_norm_mx_kernel(const float* __restrict__ P,
-                                                                const float* __restrict__ g, int Dp,
-                                                                float eps, uint8_t* __restrict__ codes,
-                                                                uint8_t* __restrict__ scales) {
-  __shared__ float red[kThreads / kWave];
-  const int t = blockIdx.x;
-  const float* row = P + (int64_t)t * Dp;
+template <int NT>
+__device__ __forceinline__ void pool_norm_mx_row(const float* __restrict__ row, const float* __restrict__ g,
+                                                 int Dp, float eps, uint8_t* __restrict__ codes,
+                                                 uint8_t* __restrict__ scales, float* red) {
   float ss = 0.f;
-  for (int c = threadIdx.x * 4; c < Dp; c += kThreads * 4) {
+  for (int c = threadIdx.x * 4; c < Dp; c += NT * 4) {
     const float4 v = *reinterpret_cast<const float4*>(row + c);
     ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
   }
-  ss = block_sum(ss, red);
+  ss = block_sum<NT>(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)Dp + eps);
-  for (int b = threadIdx.x; b < Dp / 32; b += kThreads) {
+  for (int b = threadIdx.x; b < Dp / 32; b += NT) {
     float v[32];
 #pragma unroll
     for (int i = 0; i < 32; i += 4) {
@@ -121,8 +125,67 @@ __global__ __launch_bounds__(kThreads) void pool_norm_mx_kernel(const float* __r
       v[i + 2] = x.z * r * gg.z;
       v[i + 3] = x.w * r * gg.w;
     }
-    mx_store_block(v, codes + (int64_t)t * Dp + 32 * b, scales + (int64_t)t * (Dp / 32) + b);
+    mx_store_block(v, codes + 32 * b, scales + b);
   }
+}
+
+__global__ __launch_bounds__(kThreads) void pool_norm_mx_kernel(const float* __restrict__ P,
+                                                                const float* __restrict__ g, int Dp,
+                                                                float eps, uint8_t* __restrict__ codes,
+                                                                uint8_t* __restrict__ scales) {
+  __shared__ float red[kThreads / kWave];
+  const int t = blockIdx.x;
+  pool_norm_mx_row<kThreads>(P + (int64_t)t * Dp, g, Dp, eps, codes + (int64_t)t * Dp,
+                             scales + (int64_t)t * (Dp / 32), red);
+}
+
+// Small batches (router + pooler by split-K): one workgroup per token adds the
+// token's split-K partials in slice order (the pooler columns to P, the router
+// columns plus bias to the logits), then normalizes its P row into xp — the
+// reduction, the pooled norm and (MXFP4 experts) the quantization in one pass.
+// 1024 threads, so that the token's columns take about one pass of 4 per
+// thread, with the slice loads of a pass in flight together. The barrier
+// after the reduction orders the P columns before the norm reads them.
+constexpr int kSplitNormThreads = 1024;
+
+template <int MODE>   // 0: bf16 xp, 2: MXFP8 codes + scales
+__global__ __launch_bounds__(kSplitNormThreads) void splitk_pool_norm_kernel(DenseStreamParams d, int part_ld,
+                                                                            const float* __restrict__ g,
+                                                                            float eps, void* xp,
+                                                                            uint8_t* __restrict__ scales) {
+  constexpr int NT = kSplitNormThreads;
+  __shared__ float red[NT / kWave];
+  const int t = blockIdx.x;
+  const int64_t plane = (int64_t)d.T * part_ld;
+  float* P = static_cast<float*>(d.out0) + (int64_t)t * d.ldo0;
+  for (int n0 = threadIdx.x * 4; n0 < d.N; n0 += NT * 4) {
+    const float* src = d.part + (int64_t)t * part_ld + n0;
+    float4 s = *reinterpret_cast<const float4*>(src);
+#pragma unroll 8
+    for (int sl = 1; sl < d.slices; ++sl) {
+      const float4 v = *reinterpret_cast<const float4*>(src + sl * plane);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    const float sv[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int n = n0 + e;
+      if (n >= d.N) break;
+      if (n < d.n_split) {
+        P[n] = sv[e];
+      } else {
+        const int c = n - d.n_split;
+        d.out1[(int64_t)t * d.ldo1 + c] = sv[e] + (d.bias1 ? d.bias1[c] : 0.f);
+      }
+    }
+  }
+  __syncthreads();
+  const int Dp = d.n_split;
+  if (MODE == 2)
+    pool_norm_mx_row<NT>(P, g, Dp, eps, static_cast<uint8_t*>(xp) + (int64_t)t * Dp,
+                         scales + (int64_t)t * (Dp / 32), red);
+  else
+    pool_norm_row<NT>(P, g, Dp, eps, static_cast<bf16_t*>(xp) + (int64_t)t * Dp, red);
 }
 
 // Stand-alone MXFP8 E4M3 quantization of n fp32 values (n a multiple of 32).
@@ -252,6 +315,22 @@ hipError_t launch_pool_norm_mx(const float* P, const float* g, int T, int Dp, fl
                                uint8_t* scales, hipStream_t s) {
   if (T == 0) return hipSuccess;
   hipLaunchKernelGGL(pool_norm_mx_kernel, dim3(T), dim3(kThreads), 0, s, P, g, Dp, eps, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_pool_norm(const DenseStreamParams& d, const float* g, float eps, void* xp, int mode,
+                                   uint8_t* scales, hipStream_t s) {
+  if (d.T == 0) return hipSuccess;
+  if (d.out0_bf16 || d.n_split % 64 || d.N < d.n_split || (mode == 2 && !scales)) return hipErrorInvalidValue;
+  const int ld = dense_stream_part_ld(d.N);
+  if (mode == 0)
+    hipLaunchKernelGGL(splitk_pool_norm_kernel<0>, dim3(d.T), dim3(kSplitNormThreads), 0, s, d, ld, g, eps, xp,
+                       scales);
+  else if (mode == 2)
+    hipLaunchKernelGGL(splitk_pool_norm_kernel<2>, dim3(d.T), dim3(kSplitNormThreads), 0, s, d, ld, g, eps, xp,
+                       scales);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

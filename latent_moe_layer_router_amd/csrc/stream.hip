@@ -378,15 +378,21 @@ int dense_stream_slices(int N, int K) {
   if (s > K / KC) s = K / KC;
   return s;
 }
+int dense_stream_part_ld(int N) { return ((N + DN - 1) / DN) * DN; }
 int64_t dense_stream_part_floats(int T, int N, int K) {
-  return (int64_t)dense_stream_slices(N, K) * T * (((N + DN - 1) / DN) * DN);
+  return (int64_t)dense_stream_slices(N, K) * T * dense_stream_part_ld(N);
+}
+
+hipError_t launch_dense_stream_partials(const DenseStreamParams& p, hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  const int groups = (p.N + DN - 1) / DN;
+  hipLaunchKernelGGL(dense_stream_kernel, dim3(groups * p.slices), dim3(DW * 64), 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_dense_stream(const DenseStreamParams& p, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
-  const int groups = (p.N + DN - 1) / DN;
-  hipLaunchKernelGGL(dense_stream_kernel, dim3(groups * p.slices), dim3(DW * 64), 0, s, p);
-  hipError_t err = hipGetLastError();
+  hipError_t err = launch_dense_stream_partials(p, s);
   if (err != hipSuccess) return err;
   const int64_t q = (int64_t)p.T * (((p.N + DN - 1) / DN) * DN) / 4;
   const int blocks = (int)((q + 255) / 256 < 2048 ? (q + 255) / 256 : 2048);
