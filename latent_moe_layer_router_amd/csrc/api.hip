@@ -142,6 +142,7 @@ struct lmoe_ctx {
   unsigned char* ws;
   bool timing;
   bool masks_dirty;                 // top-k ran without the sort that clears the masks
+  int n_cu;                         // compute units of the device
   std::vector<hipEvent_t> events;   // LMOE_NUM_STAGES + 1 per timed forward
   float acc_ms[LMOE_NUM_STAGES];
   int n_timed;
@@ -267,6 +268,12 @@ lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, lmoe_hand
   }
   h->timing = false;
   h->masks_dirty = false;
+  h->n_cu = 256;
+  {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)
+      h->n_cu = prop.multiProcessorCount;
+  }
   memset(h->acc_ms, 0, sizeof(h->acc_ms));
   h->n_timed = 0;
   *out = h;
@@ -432,7 +439,8 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     g.M = T;
     g.N = N;
     g.ntiles_n = (N + 255) / 256;
-    g.max_tiles = g.ntiles_n * ((T + 255) / 256);
+    g.ntiles_m = gemm_grouped_dense_row_tiles(T, g.ntiles_n, h->n_cu);
+    g.max_tiles = g.ntiles_n * g.ntiles_m;
     g.a_bytes = (uint32_t)((int64_t)T * K * 2);
     return g;
   };

@@ -2,7 +2,8 @@
 // experts with many rows, gate/up with the SwiGLU epilogue, down with the bf16
 // output and per-64-column sums of squares. Dense (M > 0): the router + pooler
 // (fp32 out, the router's columns from a second matrix plus a bias) and the
-// unpooler (fp32 or bf16 out), on row tiles of 256.
+// unpooler (fp32 or bf16 out), M split evenly over ntiles_m row tiles of at
+// most 320 rows (the caller picks the count that fills whole rounds of tiles).
 //
 // Row tiles of up to 320 rows x 256 weight rows, 512 threads = 8 wave64 in a
 // 2 x 4 grid, each wave up to 160 x 64 = 5 x 2 MFMA 32x32x16 bf16 (160
@@ -86,9 +87,9 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(Gemm256Params p) {
 
   // ---- tile of this workgroup (XCD-chunked order) --------------------------
   // Grouped: tiles (expert, n-tile, m-tile) of the experts' sorted rows. Dense:
-  // tiles (m-tile, n-tile) of an M x N product, row tiles of 256.
+  // tiles (m-tile, n-tile) of an M x N product, M split evenly over ntiles_m.
   constexpr bool dense = (EPI == EPI_F32 || EPI == EPI_ACT);
-  const int total = dense ? ((p.M + 255) / 256) * p.ntiles_n : p.ntiles_n * p.mt_off[p.E];
+  const int total = dense ? p.ntiles_m * p.ntiles_n : p.ntiles_n * p.mt_off[p.E];
   const int chunk = (total + 7) / 8;
   const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
   const int t = xcd * chunk + local;
@@ -96,8 +97,9 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(Gemm256Params p) {
   int e = 0, ntile, m0, m_end;
   if (dense) {
     ntile = t % p.ntiles_n;
-    m0 = (t / p.ntiles_n) * 256;
-    m_end = min(p.M, m0 + 256);
+    const int mi_t = t / p.ntiles_n;
+    m0 = (int)((int64_t)p.M * mi_t / p.ntiles_m);
+    m_end = (int)((int64_t)p.M * (mi_t + 1) / p.ntiles_m);
   } else {
     int lo = 0, hi = p.E;                    // expert e: ntiles_n*mt_off[e] <= t < ntiles_n*mt_off[e+1]
     while (hi - lo > 1) {
@@ -377,11 +379,41 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(Gemm256Params p) {
 
 int gemm_grouped_tile_m() { return GBM; }
 
+// One tile per CU at a time (144 KiB of LDS). Measured at 16K rows, a tile's
+// time goes as (g + 1.5), g the 32-row groups of its larger wave row (4 for
+// 256 rows, 5 for 257..320): so choose the row-tile count (tiles of 128 to 320
+// rows) that minimizes ceil(tiles / n_cu) * (2 g + 3), and among equal costs
+// the smallest tiles. At M = 16384 and 17 column tiles (router + pooler) that
+// is 60 row tiles of about 273 rows, 4 full rounds (1.145 ms against 1.21 ms
+// for 64 tiles of 256 rows, 5 rounds); at 32 column tiles (unpooler) 64 tiles
+// of 256 rows stay best (56 tiles of 293 rows measured 2% slower).
+int gemm_grouped_dense_row_tiles(int M, int ntiles_n, int n_cu) {
+  if (M <= 0 || ntiles_n <= 0 || n_cu <= 0) return 1;
+  const int lo = (M + GBM - 1) / GBM;
+  const int hi = lo > (M + 127) / 128 ? lo : (M + 127) / 128;
+  int best = lo;
+  int64_t best_cost = -1, best_rows = 0;
+  for (int ntm = lo; ntm <= hi; ++ntm) {
+    const int64_t rows = (M + ntm - 1) / ntm;
+    const int64_t g = ((rows + 1) / 2 + 31) / 32;
+    const int64_t rounds = ((int64_t)ntm * ntiles_n + n_cu - 1) / n_cu;
+    const int64_t cost = rounds * (2 * g + 3);
+    if (best_cost < 0 || cost < best_cost || (cost == best_cost && rows < best_rows)) {
+      best = ntm;
+      best_cost = cost;
+      best_rows = rows;
+    }
+  }
+  return best;
+}
+
 hipError_t launch_gemm_grouped(const Gemm256Params& p, EpiKind epi, hipStream_t s) {
   if (p.max_tiles <= 0) return hipSuccess;
   if (p.K % 128 != 0) return hipErrorInvalidValue;
   const bool dense = epi == EPI_F32 || epi == EPI_ACT;
   if (dense != (p.M > 0) || (dense && p.n_split < p.N && p.n_split % GBN != 0)) return hipErrorInvalidValue;
+  if (dense && (p.ntiles_m < 1 || (int64_t)p.ntiles_m * GBM < p.M || p.ntiles_m * p.ntiles_n > p.max_tiles))
+    return hipErrorInvalidValue;
   const int grid = ((p.max_tiles + 7) / 8) * 8;
   if (epi == EPI_SWIGLU)
     hipLaunchKernelGGL(gemm_grouped_kernel<EPI_SWIGLU>, dim3(grid), dim3(GNT), 0, s, p);

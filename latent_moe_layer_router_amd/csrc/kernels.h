@@ -128,6 +128,7 @@ struct Gemm256Params {
   int ss_ld;
   // dense mode
   int M;                       // rows (0: grouped)
+  int ntiles_m;                // row tiles, M split evenly (at most gemm_grouped_tile_m() rows each)
   int N;                       // columns
   const void* B1;              // rows of B^T at n_split and above
   int n_split;                 // multiple of 256
@@ -136,6 +137,9 @@ struct Gemm256Params {
   const float* bias1;
 };
 int gemm_grouped_tile_m();
+// Dense mode: the row-tile count for an M-row product with ntiles_n column
+// tiles on n_cu compute units (tiles of at most gemm_grouped_tile_m() rows).
+int gemm_grouped_dense_row_tiles(int M, int ntiles_n, int n_cu);
 hipError_t launch_gemm_grouped(const Gemm256Params& p, EpiKind epi, hipStream_t s);
 
 // Grouped expert GEMMs of the MXFP4-expert path: MXFP8 E4M3 activations x
