@@ -431,7 +431,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
                         (int64_t)T * D * 2 < ((int64_t)1 << 31) && (int64_t)T * Dp * 2 < ((int64_t)1 << 31) &&
                         (int64_t)256 * D * 2 < ((int64_t)1 << 31);
   auto dense_params = [&](const void* A, int K, int N) {
-    Gemm256Params g{};
+    GroupedParams g{};
     g.A = A;
     g.lda = K;
     g.ldb = K;
@@ -449,7 +449,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   mark();
   bool pooled = false;
   if (dense256) {
-    Gemm256Params g = dense_params(x, D, Dp + E);
+    GroupedParams g = dense_params(x, D, Dp + E);
     g.B = h->w.w_pool;
     g.B1 = h->w.w_router;
     g.n_split = Dp;
@@ -591,7 +591,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     run(launch_stream_mx(sp, EPI_SWIGLU, s));
   }
   if (mx) {
-    Gemm256MxParams g{};
+    GroupedMxParams g{};
     g.A = xq;
     g.As = xs;
     g.a_rows = row_tok;
@@ -613,7 +613,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     g.ldos = F / 32;
     run(launch_gemm_grouped_mx(g, EPI_SWIGLU, s));
   } else if (big_ok) {
-    Gemm256Params g{};
+    GroupedParams g{};
     g.A = xp;
     g.lda = Dp;
     g.a_rows = row_tok;
@@ -698,7 +698,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     run(launch_stream_mx(sp, EPI_DOWN, s));
   }
   if (mx) {
-    Gemm256MxParams g{};
+    GroupedMxParams g{};
     g.A = hq;
     g.As = hs;
     g.B = static_cast<const uint8_t*>(h->w.w_down);
@@ -719,7 +719,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
     g.ss_ld = Dp / 64;
     run(launch_gemm_grouped_mx(g, EPI_DOWN, s));
   } else if (big_ok) {
-    Gemm256Params g{};
+    GroupedParams g{};
     g.A = H;
     g.lda = F;
     g.B = h->w.w_down;
@@ -779,7 +779,7 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   // 8. unpooler
   mark();
   if (dense256) {
-    Gemm256Params g = dense_params(u, Dp, D);
+    GroupedParams g = dense_params(u, Dp, D);
     g.B = h->w.w_unpool;
     g.B1 = h->w.w_unpool;
     g.n_split = D;

@@ -80,7 +80,7 @@ __device__ __forceinline__ void bar() {
 }
 
 template <int EPI>
-__global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(Gemm256Params p) {
+__global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
@@ -407,7 +407,7 @@ int gemm_grouped_dense_row_tiles(int M, int ntiles_n, int n_cu) {
   return best;
 }
 
-hipError_t launch_gemm_grouped(const Gemm256Params& p, EpiKind epi, hipStream_t s) {
+hipError_t launch_gemm_grouped(const GroupedParams& p, EpiKind epi, hipStream_t s) {
   if (p.max_tiles <= 0) return hipSuccess;
   if (p.K % 128 != 0) return hipErrorInvalidValue;
   const bool dense = epi == EPI_F32 || epi == EPI_ACT;

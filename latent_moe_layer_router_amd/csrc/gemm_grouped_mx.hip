@@ -94,7 +94,7 @@ __device__ __forceinline__ void bar() {
 }
 
 template <int EPI>
-__global__ __launch_bounds__(XNT, 1) void gemm_grouped_mx_kernel(Gemm256MxParams p) {
+__global__ __launch_bounds__(XNT, 1) void gemm_grouped_mx_kernel(GroupedMxParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(XNT, 1) void gemm_grouped_mx_kernel(Gemm256MxParams
 
 int gemm_grouped_mx_tile_m() { return XBM; }
 
-hipError_t launch_gemm_grouped_mx(const Gemm256MxParams& p, EpiKind epi, hipStream_t s) {
+hipError_t launch_gemm_grouped_mx(const GroupedMxParams& p, EpiKind epi, hipStream_t s) {
   if (p.max_tiles <= 0) return hipSuccess;
   if (p.K % 1024 != 0) return hipErrorInvalidValue;
   const int grid = ((p.max_tiles + 7) / 8) * 8;

@@ -106,7 +106,7 @@ hipError_t launch_dense_stream_partials(const DenseStreamParams& p, hipStream_t 
 // EPI_SWIGLU or EPI_DOWN): expert e has mt_off[e+1] - mt_off[e] row tiles of up
 // to gemm_grouped_tile_m() rows (its rows in sorted order from offsets[e],
 // split evenly), each times ntiles_n column tiles.
-struct Gemm256Params {
+struct GroupedParams {
   const void* A;
   int64_t lda;
   const int32_t* a_rows;       // if set, product row m reads A row a_rows[m] (gate/up: its token)
@@ -140,13 +140,13 @@ int gemm_grouped_tile_m();
 // Dense mode: the row-tile count for an M-row product with ntiles_n column
 // tiles on n_cu compute units (tiles of at most gemm_grouped_tile_m() rows).
 int gemm_grouped_dense_row_tiles(int M, int ntiles_n, int n_cu);
-hipError_t launch_gemm_grouped(const Gemm256Params& p, EpiKind epi, hipStream_t s);
+hipError_t launch_gemm_grouped(const GroupedParams& p, EpiKind epi, hipStream_t s);
 
 // Grouped expert GEMMs of the MXFP4-expert path: MXFP8 E4M3 activations x
 // MXFP4 weights on the block-scaled MFMA. EPI_SWIGLU writes H as MXFP8 (codes
 // to out, scales to out_scales); EPI_DOWN writes y as bf16 and the sums of
 // squares.
-struct Gemm256MxParams {
+struct GroupedMxParams {
   const uint8_t* A;            // [rows][K] E4M3 codes (rows in sorted order, or gathered by a_rows)
   const uint8_t* As;           // [rows][K/32] E8M0 scales
   const int32_t* a_rows;       // if set, product row m reads A row a_rows[m] (gate/up: its token)
@@ -173,12 +173,12 @@ struct Gemm256MxParams {
 // evenly over ceil(rows / tile) tiles, mt_off counting them) x 256 weight
 // rows; 8 waves per tile. K a multiple of 1024.
 int gemm_grouped_mx_tile_m();
-hipError_t launch_gemm_grouped_mx(const Gemm256MxParams& p, EpiKind epi, hipStream_t s);
+hipError_t launch_gemm_grouped_mx(const GroupedMxParams& p, EpiKind epi, hipStream_t s);
 
 // Weight-streaming grouped GEMM of the MXFP4-expert path for experts with
 // 1..max_rows rows (max_rows <= stream_mx_max_rows()); one wave per (expert,
 // group of 64 weight rows). K a multiple of 1024.
-// Same operand and output formats as Gemm256MxParams.
+// Same operand and output formats as GroupedMxParams.
 struct StreamMxParams {
   const uint8_t* A;            // [rows][K] E4M3 codes (rows in sorted order, or gathered by a_rows)
   const uint8_t* As;           // [rows][K/32] E8M0 scales
