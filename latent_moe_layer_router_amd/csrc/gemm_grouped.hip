@@ -22,8 +22,9 @@
 // pipeline of 32-wide K-steps (A 20 KiB + B 16 KiB per stage, 144 KiB): the
 // loads for step k + 3 are in flight while step k computes. A stage is 20 A
 // loads and 16 B loads of 16 rows x 64 bytes; wave w issues loads w, w + 8,
-// ... (waves 0-3 five per stage, waves 4-7 four). The 16-byte chunks of a row
-// are XOR-swizzled so that fragment reads are conflict-free.
+// ... (waves 0-3 five per stage, waves 4-7 four; A loads wholly past the
+// tile's last row are skipped). The 16-byte chunks of a row are XOR-swizzled
+// so that fragment reads are conflict-free.
 //
 // Tile order over the 8 XCDs: one index space (expert, n-tile, m-tile) cut
 // into 8 contiguous chunks, one per XCD, so that the CUs of an XCD share the
@@ -165,7 +166,11 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
   for (int i = 0; i < 3; ++i) ga[i] = (wave + 8 * i < LA) ? a_off(16 * (wave + 8 * i) + (lane >> 2)) : kOutOfRange;
 #pragma unroll
   for (int i = 0; i < 2; ++i) gb[i] = b_off(16 * (wave + 8 * i) + (lane >> 2));
-  const bool three_a = wave + 16 < LA;       // waves 0-3
+  // Waves 0-3 issue a third A load (rows 256 + 16 wave ..) only if some of its
+  // rows are in the tile: a 256-row tile then moves 32 rows per K-step instead
+  // of 36 x 16. The LDS rows a skipped load would have filled are read only
+  // for output rows past the tile's end, which are never stored.
+  const bool three_a = wave + 16 < LA && 16 * (wave + 16) < tile_rows;
 
 #define LMOE_LD(RS, OFF, DST, KO) \
   __builtin_amdgcn_raw_ptr_buffer_load_lds((RS), (LMOE_AS3 void*)(DST), 16, (int)(OFF), (KO), 0, 0);
