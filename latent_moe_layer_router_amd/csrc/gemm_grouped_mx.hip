@@ -167,19 +167,13 @@ __global__ __launch_bounds__(XNT, 1) void gemm_grouped_mx_kernel(GroupedMxParams
     return b_row(r) * (uint32_t)(K / 32);
   };
   const uint32_t gs0 = scale_off(wave), gs1 = scale_off(8);
-  // Loads wholly past the tile's last row are skipped (a 256-row tile: 32 of
-  // the 40 A loads, 4 of the 5 A scale loads); the LDS rows they would have
-  // filled are read only for output rows that are never stored.
-  const int na = min(5, max(0, (m_end - m0 + 7) / 8 - 5 * wave));
-  const bool s_live = wave >= 5 || 64 * wave < m_end - m0;
 
 #define LMOE_DATA(st, SA, SB)                                                                    \
   {                                                                                             \
     const int koa = (st) * RA, kob = (st) * RBB;                                                \
     _Pragma("unroll") for (int i = 0; i < 5; ++i)                                               \
-      if (i < na)                                                                               \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (LMOE_AS3 void*)((SA) + 1024 * (5 * wave + i)), \
-                                                 16, (int)ga[i], koa, 0, 0);                    \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (LMOE_AS3 void*)((SA) + 1024 * (5 * wave + i)), \
+                                               16, (int)ga[i], koa, 0, 0);                      \
     _Pragma("unroll") for (int i = 0; i < 2; ++i)                                               \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (LMOE_AS3 void*)((SB) + 1024 * (2 * wave + i)), \
                                                16, (int)gb[i], kob, 0, 0);                      \
@@ -187,9 +181,8 @@ __global__ __launch_bounds__(XNT, 1) void gemm_grouped_mx_kernel(GroupedMxParams
 #define LMOE_SCALES(g, SS)                                                                       \
   {                                                                                             \
     const int kos = (g) * 16;                                                                   \
-    if (s_live)                                                                                 \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 5 ? rAs : rBs,                            \
-                                               (LMOE_AS3 void*)((SS) + 1024 * wave), 16, (int)gs0, kos, 0, 0); \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 5 ? rAs : rBs,                              \
+                                             (LMOE_AS3 void*)((SS) + 1024 * wave), 16, (int)gs0, kos, 0, 0); \
     if (wave == 0)                                                                              \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, (LMOE_AS3 void*)((SS) + 1024 * 8), 16, (int)gs1, kos, 0, 0); \
   }
