@@ -208,8 +208,10 @@ __global__ __launch_bounds__(64) void stream_kernel(StreamParams p) {
 // global-to-LDS loads in a four-stage pipeline of 64-wide K-steps; the token
 // slice is loaded once per workgroup and shared by its waves, each weight byte
 // is read once. Each workgroup writes its fp32 partial sums to
-// part[slice][t][n] (n padded to whole groups); splitk_reduce adds the slices
-// in slice order (deterministic), then applies the bias and the output type.
+// part[slice][t][n] (n padded to whole groups); the reduction adds the slices
+// in slice order (deterministic), then applies the bias and the output type:
+// splitk_reduce here, or, for the router + pooler, the pooled-norm kernel that
+// also normalizes each P row (launch_splitk_pool_norm).
 constexpr int DW = 4;                  // waves per workgroup
 constexpr int DR = 32;                 // weight rows per wave
 constexpr int DS = 4;                  // pipeline stages
