@@ -22,7 +22,7 @@ import synth
 from synth import device as sdev
 from tests import harness as H
 from tests.pins import tiny
-from tests.test_gpu_parity import run_case, run_crafted
+from tests.test_gpu_parity import run_case, run_crafted, upload
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -185,3 +185,25 @@ def test_mx_full_size_decode_subset():
     assert err <= H.tol(w), err
     del tw
     torch.cuda.empty_cache()
+
+
+def test_mx_deterministic_and_token_permutation_invariant():
+    """MXFP4 experts: two runs give identical bits, and permuting the tokens
+    permutes the output rows bit-exactly. E = 24, k = 3 gives experts of about
+    42 rows, so both the streamed (<= 32 rows) and the tiled kernel run."""
+    w = mx_tiny(T=333, D=256, Dp=1024, F_=1024, E=24, k=3, seed=240)
+    block = lmoe.LatentMoE(upload(synth.dense_weights(w)), w.k, w.T)
+    x = sdev.to_device(synth.x(w), DEV)
+    H.say("[gpu] mxfp4 determinism: two runs, then permuted tokens")
+    o1, a1 = block.forward(x, aux=True)
+    o2, a2 = block.forward(x, aux=True)
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(w.T)).to(DEV)
+    o3 = block.forward(x[perm].contiguous())
+    torch.cuda.synchronize()
+    counts = np.diff(a1["expert_offsets"].cpu().numpy())
+    assert counts.min() <= 32 < counts.max(), counts
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    for n in a1:
+        assert torch.equal(a1[n], a2[n])
+    assert torch.equal(o1[perm].view(torch.int16), o3.view(torch.int16))
+    block.close()

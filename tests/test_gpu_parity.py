@@ -58,6 +58,14 @@ def test_small_bf16_ragged_T(T):
     run_case(tiny(T=T, D=256, Dp=128, F_=192, E=8, k=2, seed=101, act=synth.BF16), T=T)
 
 
+@pytest.mark.parametrize("T", [641, 1000])
+def test_dense_tiled_ragged_T(T):
+    """T > 128 with Dp a multiple of 256: the router + pooler and the unpooler run
+    on the tiled kernel's dense mode, M split evenly over the row-tile count the
+    host picks (641 rows: 6 tiles of 106-107; 1000 rows: 8 tiles of 125)."""
+    run_case(tiny(T=T, D=512, Dp=256, F_=256, E=8, k=2, seed=113, act=synth.BF16), T=T)
+
+
 @pytest.mark.parametrize("E,k", [(1, 1), (3, 3), (37, 5), (64, 16)])
 def test_small_bf16_expert_counts(E, k):
     run_case(tiny(T=77, D=128, Dp=64, F_=128, E=E, k=k, seed=102 + E, act=synth.BF16))
