@@ -116,8 +116,8 @@ typedef struct {
  * Filled by the same lmoe_forward call, asynchronously on its stream. */
 typedef struct {
   float* logits;            /* [T][E] fp32, bias included */
-  int32_t* topk_ids;        /* [T][k], logit descending, ties to the lower expert id */
-  float* topk_w;            /* [T][k] softmax of the selected logits */
+  int32_t* topk_ids;        /* [T][k], logit descending (NaN as -inf), ties to the lower expert id */
+  float* topk_w;            /* [T][k] softmax of the selected logits (non-finite: see below) */
   int32_t* expert_offsets;  /* [E+1] exclusive prefix sum of the per-expert counts */
   int32_t* sorted_assign;   /* [T*k] assignment t*k+j at each sorted position;
                                order (expert asc, token asc) */
@@ -127,6 +127,15 @@ typedef struct {
  * workspace for cfg->max_tokens on the current device. *out receives the handle
  * (NULL on error). */
 lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, lmoe_handle* out);
+
+/* Non-finite values. Router logits that are NaN (a NaN or an infinity in the
+ * token's x row makes them so) rank as -inf, and ties, -inf ones included, go
+ * to the lower expert id, so every token selects k distinct valid experts and
+ * the permutation stays exact. The weights are the softmax of the selected
+ * logits (NaN read as -inf); when the largest selected one is infinite (all
+ * -inf, e.g. a -inf router bias on every expert, or some +inf) they are equal
+ * shares among the slots holding it and 0 elsewhere. A token whose x row holds
+ * a NaN gets NaN outputs; rows never mix, so other tokens are unaffected. */
 
 /* Run the block on T tokens: x [T][D] -> out [T][D] (out_dtype), enqueued on
  * hip_stream (a hipStream_t; NULL is the null stream). Asynchronous: kernel

@@ -49,6 +49,14 @@ __device__ __forceinline__ float wave_max(float v) {
 // the winner the lowest index among the lanes holding it (usually one lane).
 // The token's bit goes into its chunk's mask of each selected expert with a
 // global atomic OR, which gives the same masks in any order.
+//
+// Non-finite logits: NaN scores as -inf, and a lane offers its first untaken
+// slot even when every untaken score it holds is -inf. Since k <= E, some
+// valid slot is untaken in each round, so some lane has an offer, the ballot
+// is never empty and every round selects a valid, distinct expert (with ties,
+// -inf ones included, going to the lower index). Weights: the softmax of the
+// selected scores; when the largest one is infinite (all selected -inf, or some
+// +inf), equal shares among the slots holding it, the softmax's limit.
 constexpr int kTopkWaves = 4;
 
 __global__ __launch_bounds__(kTopkWaves * 64) void topk_kernel(const float* __restrict__ logits, int T,
@@ -67,23 +75,25 @@ __global__ __launch_bounds__(kTopkWaves * 64) void topk_kernel(const float* __re
     const bool ok = q < per && e < E;
     // unconditional load from a clamped (valid) address, masked afterwards
     const float x = logits[(int64_t)t * E + (e < E ? e : E - 1)];
-    // NaN counts as -inf, so that every round selects a valid expert index.
     v[q] = (!ok || x != x) ? -INFINITY : x;
-    if (!ok) taken |= 1u << q;
+    if (!ok) taken |= 1u << q;               // slots past E are never offered
   }
   float sel_v = 0.f, top = 0.f, den = 0.f;
-  int my_id = -1;                            // lane j < k keeps the j-th selected expert
+  int n_top = 0;                             // selected slots whose score equals the first
+  int my_id = 0;                             // lane j < k keeps the j-th selected expert
   for (int j = 0; j < k; ++j) {
     float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+    int bi = 0x7FFFFFFF;                     // no offer yet
 #pragma unroll
     for (int q = 0; q < kMaxPerLane; ++q)
-      if (!(taken >> q & 1u) && v[q] > bv) {   // ascending q: ties keep the lower index
+      // ascending q: the first untaken slot is always offered, later ones only
+      // if strictly larger, so ties keep the lower index
+      if (!(taken >> q & 1u) && (bi == 0x7FFFFFFF || v[q] > bv)) {
         bv = v[q];
         bi = q * kWave + lane;
       }
     const float vmax = wave_max(bv);
-    const uint64_t tie = __ballot(bi != 0x7FFFFFFF && bv == vmax);
+    const uint64_t tie = __ballot(bi != 0x7FFFFFFF && bv == vmax);   // never empty (see above)
     int win;
     if (__popcll(tie) == 1) {
       win = __builtin_amdgcn_readlane(bi, __ffsll((unsigned long long)tie) - 1);
@@ -98,14 +108,16 @@ __global__ __launch_bounds__(kTopkWaves * 64) void topk_kernel(const float* __re
     if ((win & 63) == lane) taken |= 1u << (win >> 6);
     if (j == 0) top = vmax;
     den += expf(vmax - top);
+    n_top += vmax == top;
     if (lane == j) {
       my_id = win;
       sel_v = vmax;
     }
   }
   if (lane < k) {
+    const float wj = isinf(top) ? (sel_v == top ? 1.f / (float)n_top : 0.f) : expf(sel_v - top) / den;
     ids[(int64_t)t * k + lane] = my_id;
-    w[(int64_t)t * k + lane] = expf(sel_v - top) / den;
+    w[(int64_t)t * k + lane] = wj;
     atomicOr(reinterpret_cast<unsigned long long*>(chunk_masks) + (int64_t)(t / kChunk) * E + my_id,
              1ull << (t % kChunk));
   }

@@ -314,7 +314,18 @@ void orc_router(const void* x, const void* wr, int dt, const float* bias,
  * a top-k routing kernel emits expert ids and weights). Selection: the k largest
  * logits, ties to the lower index, listed in that order. Weights: softmax over
  * the k selected logits.
+ *
+ * Non-finite logits (the pages do not consider them; readings):
+ *  - a logit's routing score is the logit itself, except that NaN scores as
+ *    -inf: NaN ranks below every number and ties with -inf, so the k selected
+ *    ids are always k distinct valid experts (ties still go to the lower index);
+ *  - the weights are the softmax of the selected scores; when the largest
+ *    selected score m is infinite (every selected score is -inf, or some are
+ *    +inf) they are the softmax's limit as the logits equal to m move together
+ *    without bound: equal shares among the slots whose score is m, 0 elsewhere.
  * ------------------------------------------------------------------------- */
+static double route_score(float v) { return isnan(v) ? -INFINITY : (double)v; }
+
 void orc_topk_softmax(const float* logits, int T, int E, int k, int32_t* ids, double* w) {
   for (int t = 0; t < T; ++t) {
     const float* l = logits + (size_t)t * E;
@@ -325,15 +336,22 @@ void orc_topk_softmax(const float* logits, int T, int E, int k, int32_t* ids, do
         int taken = 0;
         for (int q = 0; q < j; ++q) taken |= (id[q] == e);
         if (taken) continue;
-        if (best < 0 || l[e] > l[best]) best = e;   /* strict '>' keeps the lower index on ties */
+        /* strict '>' keeps the lower index on ties */
+        if (best < 0 || route_score(l[e]) > route_score(l[best])) best = e;
       }
       id[j] = best;
     }
-    double m = l[id[0]];
-    for (int j = 1; j < k; ++j) m = fmax(m, (double)l[id[j]]);
+    double m = route_score(l[id[0]]);
+    for (int j = 1; j < k; ++j) m = fmax(m, route_score(l[id[j]]));
+    if (isinf(m)) {
+      int n = 0;
+      for (int j = 0; j < k; ++j) n += route_score(l[id[j]]) == m;
+      for (int j = 0; j < k; ++j) w[(size_t)t * k + j] = route_score(l[id[j]]) == m ? 1.0 / n : 0.0;
+      continue;
+    }
     double den = 0;
-    for (int j = 0; j < k; ++j) den += exp((double)l[id[j]] - m);
-    for (int j = 0; j < k; ++j) w[(size_t)t * k + j] = exp((double)l[id[j]] - m) / den;
+    for (int j = 0; j < k; ++j) den += exp(route_score(l[id[j]]) - m);
+    for (int j = 0; j < k; ++j) w[(size_t)t * k + j] = exp(route_score(l[id[j]]) - m) / den;
   }
 }
 

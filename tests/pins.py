@@ -184,7 +184,12 @@ def pin_dense_e1k1(O):
 
 def pin_topk(O):
     """P9: top-k equals a full library sort by (logit desc, index asc), including
-    exact ties; the weights are the library softmax of the selected logits."""
+    exact ties; the weights are the library softmax of the selected logits.
+    Non-finite logits: NaN sorts as -inf (so the ids are always k distinct valid
+    experts, ties to the lower index), and when the largest selected logit is
+    infinite the weights are equal shares among the slots holding it (the
+    softmax's limit) -- checked on rows of NaN, -inf and +inf against the same
+    library sort and these closed forms."""
     rng = np.random.default_rng(5)
     for E, k in ((8, 2), (16, 5), (256, 8), (5, 5), (1, 1)):
         l = rng.integers(-3, 4, size=(40, E)).astype(np.float32) * np.float32(0.25)   # many ties
@@ -193,6 +198,37 @@ def pin_topk(O):
         assert np.array_equal(ids, order[:, :k]), (E, k)
         ref = torch.softmax(torch.from_numpy(np.take_along_axis(l, ids, 1).astype(np.float64)), 1)
         assert np.abs(w - ref.numpy()).max() < 1e-14
+    # non-finite logits
+    nan, inf = np.float32(np.nan), np.float32(np.inf)
+    for E, k in ((8, 2), (16, 5), (256, 8), (5, 5), (70, 16)):
+        l = rng.standard_normal((12, E)).astype(np.float32)
+        l[0] = nan                                           # a NaN input row: every logit NaN
+        l[1] = -inf                                          # every expert biased to -inf
+        l[2, : E - k + 1] = -inf                             # only k - 1 finite logits
+        l[3, rng.choice(E, E // 2, replace=False)] = nan     # NaN mixed with numbers
+        l[4, 3 % E] = inf                                    # one +inf
+        l[5, [1 % E, (E - 1)]] = inf                         # two +inf (one if E == 1)
+        l[6, ::2] = -inf
+        l[6, 1::3] = nan                                     # NaN and -inf interleaved
+        l[7, : E - 1] = nan                                  # one number among NaNs
+        ids, w = O.topk_softmax(l, k)
+        score = np.where(np.isnan(l), -np.inf, l.astype(np.float64))
+        order = np.lexsort((np.broadcast_to(np.arange(E), l.shape), -score), axis=-1)
+        assert np.array_equal(ids, order[:, :k]), (E, k)
+        assert np.all((ids >= 0) & (ids < E))
+        assert all(len(set(r)) == k for r in ids.tolist())
+        sel = np.take_along_axis(score, ids, 1)
+        m = sel.max(1, keepdims=True)
+        fin = np.isfinite(m[:, 0])
+        ref = np.where(sel == m, 1.0, 0.0)
+        ref = ref / ref.sum(1, keepdims=True)                # equal shares (infinite maximum)
+        ref[fin] = torch.softmax(torch.from_numpy(sel[fin]), 1).numpy()
+        assert np.abs(w - ref).max() < 1e-14, (E, k)
+        assert np.array_equal(ids[0], np.arange(k)) and np.all(w[0] == 1.0 / k)
+        assert np.array_equal(ids[1], np.arange(k)) and np.all(w[1] == 1.0 / k)
+        assert ids[2, -1] == 0 and w[2, -1] == 0.0           # the lowest-id -inf expert, weight 0
+        assert ids[4, 0] == 3 % E and w[4, 0] == 1.0
+        assert np.abs(w.sum(1) - 1).max() <= 1e-15 * k
 
 
 def pin_weights(O):

@@ -17,9 +17,13 @@ from tests import pins
 SRC = os.path.join(os.path.dirname(oracle.__file__), "lmoe_oracle.c")
 
 MUTANTS = [
-    ("ties_to_higher_index", "if (best < 0 || l[e] > l[best])", "if (best < 0 || l[e] >= l[best])"),
-    ("softmax_over_all_logits", "for (int j = 0; j < k; ++j) den += exp((double)l[id[j]] - m);",
-     "for (int q = 0; q < E; ++q) den += exp((double)l[q] - m);"),
+    ("ties_to_higher_index", "if (best < 0 || route_score(l[e]) > route_score(l[best]))",
+     "if (best < 0 || route_score(l[e]) >= route_score(l[best]))"),
+    ("nan_kept_as_nan", "return isnan(v) ? -INFINITY : (double)v;", "return (double)v;"),
+    ("nan_ranked_as_plus_inf", "return isnan(v) ? -INFINITY : (double)v;", "return isnan(v) ? INFINITY : (double)v;"),
+    ("infinite_max_plain_softmax", "    if (isinf(m)) {", "    if (0) {"),
+    ("softmax_over_all_logits", "for (int j = 0; j < k; ++j) den += exp(route_score(l[id[j]]) - m);",
+     "for (int q = 0; q < E; ++q) den += exp(route_score(l[q]) - m);"),
     ("router_bias_dropped", "if (bias) s += (double)bias[e];", ""),
     ("pooled_norm_dropped", "double r = 1.0 / sqrt(ss / Dp + eps);\n    for (int c = 0; c < Dp; ++c) p[c] = p[c] * r",
      "double r = 1.0;\n    for (int c = 0; c < Dp; ++c) p[c] = p[c] * r"),
