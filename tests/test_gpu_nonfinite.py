@@ -70,8 +70,10 @@ def check(w, got, a, ref, raux, bad_rows=()):
     wg, wr = a["topk_w"].astype(np.float64), raux["w"]
     assert np.all(np.isfinite(wg))
     sel = np.take_along_axis(np.where(np.isnan(lg), -np.inf, lg), ids.astype(np.int64), 1)
-    dl = np.where(np.isfinite(sel), np.abs(sel - np.take_along_axis(np.where(np.isnan(lr), -np.inf, lr),
-                                                                      ids.astype(np.int64), 1)), 0)
+    sel_ref = np.take_along_axis(np.where(np.isnan(lr), -np.inf, lr), ids.astype(np.int64), 1)
+    fin_sel = np.isfinite(sel)
+    dl = np.zeros_like(sel)
+    dl[fin_sel] = np.abs(sel[fin_sel] - sel_ref[fin_sel])
     bound = 2 * wr * np.nan_to_num(dl).max(1, keepdims=True) + 1e-6
     assert np.all(np.abs(wg[~near] - wr[~near]) <= bound[~near])
     assert np.abs(wg.sum(1) - 1).max() <= 1e-5
