@@ -151,6 +151,26 @@ lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, lmoe_hand
 lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, void* hip_stream,
                          const lmoe_aux* aux);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward as lmoe_forward, with the same results bit for bit, but with no
+ * handle and no lmoe_create, and allocating nothing. cfg and w are checked as
+ * lmoe_create checks them (cfg->max_tokens bounds T) and are not kept; x, out,
+ * T, hip_stream and aux are as for lmoe_forward. The workspace is the
+ * library's static scratch of LMOE_NOALLOC_SCRATCH_BYTES per device (held by
+ * each GPU the library runs on until the process ends), laid out for T tokens;
+ * a T whose workspace (lmoe_workspace_bytes with max_tokens = T) exceeds it is
+ * LMOE_E_INVAL, with nothing enqueued. At the full Muse Spark Open shapes that
+ * admits T <= 301 with BF16 experts (36.4 MiB at T = 128) and T <= 382 with
+ * MXFP4 experts.
+ * Every call on a GPU shares that GPU's scratch: calls on one device must not
+ * overlap in time (one stream, or ordered streams), or they race. The first
+ * call on a device looks up the scratch's address there. */
+#define LMOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+lmoe_status lmoe_forward_noalloc(const lmoe_config* cfg, const lmoe_weights* w, const void* x, void* out,
+                                 int32_t T, void* hip_stream, const lmoe_aux* aux);
+
 /* Free the workspace and the handle. NULL is allowed (LMOE_OK). The caller must
  * make sure no enqueued forward on this handle is still running. */
 lmoe_status lmoe_destroy(lmoe_handle h);

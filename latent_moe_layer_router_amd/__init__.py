@@ -4,7 +4,7 @@ Argument marshalling only: every step of the block runs in the library's HIP
 kernels. The functions mirror the C ABI in include/lmoe.h one to one
 (lmoe_create, lmoe_forward, lmoe_destroy, lmoe_workspace_bytes,
 lmoe_set_timing, lmoe_get_timing, lmoe_status_str, lmoe_last_error,
-lmoe_mx_quantize_e4m3) and take raw
+lmoe_mx_quantize_e4m3, lmoe_nvfp4_to_mxfp4, lmoe_forward_noalloc) and take raw
 device pointers; LatentMoE wraps them for torch tensors, which serve only as
 device memory and streams. Importing works without a GPU; loading the library
 raises if it has not been built (there is no fallback path).
@@ -24,7 +24,9 @@ LMOE_FLAG_ROUTER_BIAS = 1
 STAGES = ["proj_in", "topk", "sort", "pool_norm", "gate_up", "down", "combine", "unpool"]
 LMOE_NUM_STAGES = len(STAGES)
 
-EXPORTS = ["lmoe_create", "lmoe_forward", "lmoe_destroy", "lmoe_workspace_bytes",
+LMOE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+EXPORTS = ["lmoe_create", "lmoe_forward", "lmoe_forward_noalloc", "lmoe_destroy", "lmoe_workspace_bytes",
            "lmoe_set_timing", "lmoe_get_timing", "lmoe_status_str", "lmoe_last_error",
            "lmoe_mx_quantize_e4m3", "lmoe_nvfp4_to_mxfp4"]
 
@@ -71,13 +73,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lmoe_create.argtypes = [ctypes.POINTER(lmoe_config), ctypes.POINTER(lmoe_weights),
                                 ctypes.POINTER(P)]
     lib.lmoe_forward.argtypes = [P, P, P, I32, P, ctypes.POINTER(lmoe_aux)]
+    lib.lmoe_forward_noalloc.argtypes = [ctypes.POINTER(lmoe_config), ctypes.POINTER(lmoe_weights), P, P, I32,
+                                         P, ctypes.POINTER(lmoe_aux)]
     lib.lmoe_destroy.argtypes = [P]
     lib.lmoe_workspace_bytes.argtypes = [ctypes.POINTER(lmoe_config), ctypes.POINTER(ctypes.c_size_t)]
     lib.lmoe_set_timing.argtypes = [P, ctypes.c_int]
     lib.lmoe_get_timing.argtypes = [P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(I32)]
     lib.lmoe_mx_quantize_e4m3.argtypes = [P, ctypes.c_int64, P, P, P]
     lib.lmoe_nvfp4_to_mxfp4.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P, P]
-    for f in ("lmoe_create", "lmoe_forward", "lmoe_destroy", "lmoe_workspace_bytes",
+    for f in ("lmoe_create", "lmoe_forward", "lmoe_forward_noalloc", "lmoe_destroy", "lmoe_workspace_bytes",
               "lmoe_set_timing", "lmoe_get_timing", "lmoe_mx_quantize_e4m3", "lmoe_nvfp4_to_mxfp4"):
         getattr(lib, f).restype = ctypes.c_int
     lib.lmoe_status_str.argtypes = [ctypes.c_int]
@@ -116,6 +120,13 @@ def lmoe_create(cfg: lmoe_config, weights: lmoe_weights) -> int:
 def lmoe_forward(h: int, x: int, out: int, T: int, stream: int = 0, aux: lmoe_aux | None = None):
     _check(load().lmoe_forward(h, x, out, T, stream, ctypes.byref(aux) if aux is not None else None),
            "lmoe_forward")
+
+
+def lmoe_forward_noalloc(cfg: lmoe_config, weights: lmoe_weights, x: int, out: int, T: int, stream: int = 0,
+                         aux: lmoe_aux | None = None):
+    _check(load().lmoe_forward_noalloc(ctypes.byref(cfg), ctypes.byref(weights), x, out, T, stream,
+                                       ctypes.byref(aux) if aux is not None else None),
+           "lmoe_forward_noalloc")
 
 
 def lmoe_destroy(h: int | None):

@@ -3,6 +3,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -132,6 +133,565 @@ lmoe_status check_config(const lmoe_config* c) {
   return LMOE_OK;
 }
 
+// Checks of one forward call's arguments against its configuration (before
+// anything is enqueued).
+lmoe_status check_forward_args(const lmoe_config& c, const void* x, void* out, int32_t T,
+                               const lmoe_aux* aux) {
+  if (T < 0 || T > c.max_tokens)
+    return fail(LMOE_E_INVAL, "T = " + std::to_string(T) + " outside [0, max_tokens = " +
+                                  std::to_string(c.max_tokens) + "]");
+  if (T == 0) return LMOE_OK;
+  if (!x || !out) return fail(LMOE_E_INVAL, "x or out is NULL");
+  if (!aligned16(x) || !aligned16(out)) return fail(LMOE_E_INVAL, "x or out is not 16-byte aligned");
+  const bool bf16 = c.act_dtype == LMOE_BF16;
+  const bool out_f32 = c.out_dtype == LMOE_F32;
+  const size_t x_bytes = (size_t)T * c.d_model * (bf16 ? 2 : 4);
+  const size_t o_bytes = (size_t)T * c.d_model * (out_f32 ? 4 : 2);
+  const uintptr_t xb = reinterpret_cast<uintptr_t>(x), ob = reinterpret_cast<uintptr_t>(out);
+  if (xb < ob + o_bytes && ob < xb + x_bytes) return fail(LMOE_E_INVAL, "out overlaps x");
+  if (aux) {
+    const void* ap[] = {aux->logits, aux->topk_ids, aux->topk_w, aux->expert_offsets, aux->sorted_assign};
+    for (const void* q : ap)
+      if (q && !aligned4(q)) return fail(LMOE_E_INVAL, "aux pointer is not 4-byte aligned");
+  }
+  return LMOE_OK;
+}
+
+// Validation of the weight pointers against a configuration.
+lmoe_status check_weights(const lmoe_config* cfg, const lmoe_weights* w) {
+  if (!w) return fail(LMOE_E_INVAL, "weights is NULL");
+  const void* req[] = {w->w_router, w->w_pool, w->g_pool, w->w_gate_up, w->w_down, w->g_expert,
+                       w->w_unpool};
+  const char* names[] = {"w_router", "w_pool", "g_pool", "w_gate_up", "w_down", "g_expert", "w_unpool"};
+  for (int i = 0; i < 7; ++i) {
+    if (!req[i]) return fail(LMOE_E_INVAL, std::string(names[i]) + " is NULL");
+    if (!aligned16(req[i])) return fail(LMOE_E_INVAL, std::string(names[i]) + " is not 16-byte aligned");
+  }
+  const bool has_bias = (cfg->flags & LMOE_FLAG_ROUTER_BIAS) != 0;
+  if (has_bias != (w->b_router != nullptr))
+    return fail(LMOE_E_INVAL, "b_router must be given iff LMOE_FLAG_ROUTER_BIAS is set");
+  if (w->b_router && !aligned4(w->b_router)) return fail(LMOE_E_INVAL, "b_router is misaligned");
+  if (cfg->expert_wdtype == LMOE_MXFP4) {
+    if (!w->s_gate_up || !w->s_down) return fail(LMOE_E_INVAL, "MXFP4 experts need s_gate_up and s_down");
+    if (!aligned16(w->s_gate_up) || !aligned16(w->s_down))
+      return fail(LMOE_E_INVAL, "s_gate_up / s_down are not 16-byte aligned");
+  } else if (w->s_gate_up || w->s_down) {
+    return fail(LMOE_E_INVAL, "MX scale pointers must be NULL unless expert_wdtype is LMOE_MXFP4");
+  }
+
+  return LMOE_OK;
+}
+
+// The launch sequence of one forward pass on stream s, over the workspace ws
+// laid out by pl (sized for at least T tokens). Arguments are already checked.
+// masks_dirty: whether the chunk masks may hold bits (they are cleared first
+// then); it is left true only if the call stopped between the top-k and the
+// sort. ev: null, or LMOE_NUM_STAGES + 1 created events recorded around the
+// stages. Returns the first failed launch's error (nothing more is enqueued
+// after it).
+hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Plan& pl, unsigned char* ws,
+                           int n_cu, bool& masks_dirty, hipEvent_t* ev, const void* x, void* out,
+                           int32_t T, hipStream_t s, const lmoe_aux* aux) {
+  const bool bf16 = c.act_dtype == LMOE_BF16;
+  const bool out_f32 = c.out_dtype == LMOE_F32;
+  const int E = c.n_experts, k = c.top_k, D = c.d_model, Dp = c.d_pooled, F = c.d_ff;
+  float* P = reinterpret_cast<float*>(ws + pl.P);
+  float* logits = (aux && aux->logits) ? aux->logits : reinterpret_cast<float*>(ws + pl.logits);
+  int32_t* ids = (aux && aux->topk_ids) ? aux->topk_ids : reinterpret_cast<int32_t*>(ws + pl.ids);
+  float* tw = (aux && aux->topk_w) ? aux->topk_w : reinterpret_cast<float*>(ws + pl.w);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + pl.offsets);
+  int32_t* sorted_assign = reinterpret_cast<int32_t*>(ws + pl.sorted_assign);
+  int32_t* tiles = reinterpret_cast<int32_t*>(ws + pl.tiles);
+  int32_t* n_tiles = reinterpret_cast<int32_t*>(ws + pl.n_tiles);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + pl.inv);
+  int32_t* row_tok = reinterpret_cast<int32_t*>(ws + pl.row_tok);
+  void* xp = ws + pl.xp;
+  void* H = ws + pl.H;
+  uint8_t* xq = ws + pl.xq;
+  uint8_t* xs = ws + pl.xs;
+  uint8_t* hq = ws + pl.hq;
+  uint8_t* hs = ws + pl.hs;
+  const bool mx = c.expert_wdtype == LMOE_MXFP4;
+  void* Y = ws + pl.Y;
+  float* ss = reinterpret_cast<float*>(ws + pl.ss);
+  void* u = ws + pl.u;
+  const int slots = slots_for(T, k, E);
+  // Experts with few rows go to the weight-streaming kernels (bf16, K multiple of 128).
+  // The grouped kernels' buffer loads take 32-bit byte offsets: the activations
+  // (xp, H) and one expert's weights must each stay below 2 GiB.
+  const bool off32_ok = (int64_t)T * k * F * 2 < ((int64_t)1 << 31) &&
+                        (int64_t)T * k * Dp * 2 < ((int64_t)1 << 31) &&
+                        (int64_t)2 * F * Dp * 2 < ((int64_t)1 << 31);
+  const bool stream_ok = bf16 && !mx && Dp % 128 == 0 && F % 128 == 0 && off32_ok;
+  // MXFP4 experts: the create-time checks (Dp and F multiples of 1024, 32-bit
+  // byte extents) are all the MX weight-streaming kernel needs.
+  const int small_max = stream_ok ? stream_max_rows() : (mx ? stream_mx_max_rows() : 0);
+  // Experts with many rows: the tiled grouped GEMM (bf16, Dp % 256 == 0, F % 128 == 0).
+  const bool big_ok = bf16 && !mx && Dp % 256 == 0 && F % 128 == 0 && off32_ok;
+  int32_t* mt_off = reinterpret_cast<int32_t*>(ws + pl.mt_off);
+  const int64_t A_ = (int64_t)T * k;
+  // Row tiles (at least 256 rows each) over the experts with more than small_max rows: at most
+  // floor(A / 256) full ones plus one partial per such expert, and there are at
+  // most floor(A / (small_max + 1)) such experts. The bound sizes the grid, so a
+  // tight one keeps the launch cheap when few or no experts are large (decode).
+  const int64_t n_big = A_ / (small_max + 1) < E ? A_ / (small_max + 1) : E;
+  const int mtiles_bound = (int)(A_ / 256 + n_big);
+
+  int stage = 0;
+  auto mark = [&]() {
+    if (ev) (void)hipEventRecord(ev[stage], s);
+    ++stage;
+  };
+
+  // After the first failed launch nothing more is enqueued (later kernels would
+  // read tile lists and offsets that were never written).
+  hipError_t err = hipSuccess;
+#define run(X)                    \
+  do {                            \
+    if (err == hipSuccess) err = (X); \
+  } while (0)
+
+  // Small batches: the dense projections stream their weights with split-K.
+  const bool dense_stream = bf16 && T <= dense_stream_max_tokens();
+  float* part = reinterpret_cast<float*>(ws + pl.part);
+  const int slices_in = dense_stream_slices(Dp + E, D), slices_un = dense_stream_slices(D, Dp);
+
+  // Larger batches: the dense projections on the tiled kernel (bf16; K a
+  // multiple of 128, the pooler's rows a multiple of 256, 32-bit offsets).
+  const bool dense256 = bf16 && !dense_stream && D % 128 == 0 && Dp % 256 == 0 &&
+                        (int64_t)T * D * 2 < ((int64_t)1 << 31) && (int64_t)T * Dp * 2 < ((int64_t)1 << 31) &&
+                        (int64_t)256 * D * 2 < ((int64_t)1 << 31);
+  auto dense_params = [&](const void* A, int K, int N) {
+    GroupedParams g{};
+    g.A = A;
+    g.lda = K;
+    g.ldb = K;
+    g.K = K;
+    g.M = T;
+    g.N = N;
+    g.ntiles_n = (N + 255) / 256;
+    g.ntiles_m = gemm_grouped_dense_row_tiles(T, g.ntiles_n, n_cu);
+    g.max_tiles = g.ntiles_n * g.ntiles_m;
+    g.a_bytes = (uint32_t)((int64_t)T * K * 2);
+    return g;
+  };
+
+  // 1. router + pooler: one GEMM over [W_pool; W_router]
+  mark();
+  bool pooled = false;
+  if (dense256) {
+    GroupedParams g = dense_params(x, D, Dp + E);
+    g.B = W.w_pool;
+    g.B1 = W.w_router;
+    g.n_split = Dp;
+    g.out = P;
+    g.ldo = Dp;
+    g.out1 = logits;
+    g.ldo1 = E;
+    g.bias1 = W.b_router;
+    run(launch_gemm_grouped(g, EPI_F32, s));
+  } else if (dense_stream && slices_in > 0) {
+    DenseStreamParams d{};
+    d.A = x;
+    d.lda = D;
+    d.B0 = W.w_pool;
+    d.B1 = W.w_router;
+    d.n_split = Dp;
+    d.ldb = D;
+    d.T = T;
+    d.N = Dp + E;
+    d.K = D;
+    d.slices = slices_in;
+    d.part = part;
+    d.out0 = P;
+    d.ldo0 = Dp;
+    d.out1 = logits;
+    d.ldo1 = E;
+    d.bias1 = W.b_router;
+    // the split-K reduction, the pooled RMSNorm and the MXFP8 quantization of
+    // xp in one pass (xp is one row per token, so it needs no routing)
+    run(launch_dense_stream_partials(d, s));
+    run(launch_splitk_pool_norm(d, W.g_pool, c.eps_pool, mx ? static_cast<void*>(xq) : xp, mx ? 2 : 0, xs, s));
+    pooled = true;
+  } else {
+    GemmParams g{};
+    g.M = T;
+    g.N = Dp + E;
+    g.K = D;
+    g.A = x;
+    g.lda = D;
+    g.B0 = W.w_pool;
+    g.B1 = W.w_router;
+    g.n_split = Dp;
+    g.ldb = D;
+    g.out0 = P;
+    g.ldo0 = Dp;
+    g.out1 = logits;
+    g.ldo1 = E;
+    g.bias1 = W.b_router;
+    run(launch_gemm(g, EPI_F32, bf16, s));
+  }
+  // 2. top-k + softmax + chunk masks
+  mark();
+  uint64_t* masks = reinterpret_cast<uint64_t*>(ws + pl.masks);
+  // The top-k kernel ORs into the chunk masks and the sort clears them; if a
+  // previous call stopped between the two, clear them first.
+  if (masks_dirty) {
+    run(launch_clear_u64(masks, (int64_t)(pl.chunk_base - pl.masks) / 8, s));
+    if (err == hipSuccess) masks_dirty = false;
+  }
+  run(launch_topk(logits, T, E, k, ids, tw, masks, s));
+  if (err == hipSuccess) masks_dirty = true;
+  // 3. counting sort + tile list
+  mark();
+  {
+    SortParams sp{};
+    sp.ids = ids;
+    sp.topk_w = tw;
+    sp.chunk_masks = masks;
+    sp.chunk_base = reinterpret_cast<int32_t*>(ws + pl.chunk_base);
+    sp.counts = reinterpret_cast<int32_t*>(ws + pl.counts);
+    sp.offsets = offsets;
+    sp.sorted_assign = sorted_assign;
+    sp.inv = inv;
+    sp.row_tok = row_tok;
+    sp.tiles = tiles;
+    sp.n_tiles = n_tiles;
+    sp.T = T;
+    sp.E = E;
+    sp.k = k;
+    sp.tile_m = kGemmBM;
+    sp.small_max = small_max;
+    sp.mt_off = mt_off;
+    sp.tile_m2 = mx ? gemm_grouped_mx_tile_m() : gemm_grouped_tile_m();
+    run(launch_sort(sp, s));
+    if (err == hipSuccess) masks_dirty = false;
+  }
+  // 4. pooled RMSNorm (already done with the small-batch reduction)
+  mark();
+  if (pooled) {
+  } else if (mx) {
+    run(launch_pool_norm_mx(P, W.g_pool, T, Dp, c.eps_pool, xq, xs, s));
+  } else {
+    run(launch_pool_norm(P, W.g_pool, T, Dp, c.eps_pool, xp, bf16, s));
+  }
+  // 5. gate/up grouped GEMM + SwiGLU
+  mark();
+  if (stream_ok) {
+    StreamParams sp{};
+    sp.A = xp;
+    sp.lda = Dp;
+    sp.a_rows = row_tok;
+    sp.B = W.w_gate_up;
+    sp.ldb = Dp;
+    sp.b_expert_stride = (int64_t)2 * F * Dp;
+    sp.offsets = offsets;
+    sp.n_experts = E;
+    sp.groups = F / 32;
+    sp.max_rows = small_max;
+    sp.K = Dp;
+    sp.F = F;
+    sp.a_bytes = (uint32_t)((int64_t)T * Dp * 2);
+    sp.b_bytes = (uint32_t)((int64_t)2 * F * Dp * 2);
+    sp.out = H;
+    sp.ldo = F;
+    run(launch_stream(sp, EPI_SWIGLU, s));
+  }
+  if (mx) {
+    StreamMxParams sp{};
+    sp.A = xq;
+    sp.As = xs;
+    sp.a_rows = row_tok;
+    sp.B = static_cast<const uint8_t*>(W.w_gate_up);
+    sp.Bs = W.s_gate_up;
+    sp.N = 2 * F;
+    sp.offsets = offsets;
+    sp.n_experts = E;
+    sp.groups = F / 32;
+    sp.max_rows = small_max;
+    sp.K = Dp;
+    sp.F = F;
+    sp.a_bytes = (uint32_t)((int64_t)T * Dp);
+    sp.as_bytes = (uint32_t)((int64_t)T * Dp / 32);
+    sp.b_bytes = (uint32_t)((int64_t)F * Dp);
+    sp.bs_bytes = (uint32_t)((int64_t)2 * F * Dp / 32);
+    sp.out = hq;
+    sp.ldo = F;
+    sp.out_scales = hs;
+    sp.ldos = F / 32;
+    run(launch_stream_mx(sp, EPI_SWIGLU, s));
+  }
+  if (mx) {
+    GroupedMxParams g{};
+    g.A = xq;
+    g.As = xs;
+    g.a_rows = row_tok;
+    g.B = static_cast<const uint8_t*>(W.w_gate_up);
+    g.Bs = W.s_gate_up;
+    g.N = 2 * F;
+    g.offsets = offsets;
+    g.mt_off = mt_off;
+    g.E = E;
+    g.ntiles_n = F / 128;
+    g.max_tiles = g.ntiles_n * mtiles_bound;
+    g.a_bytes = (uint32_t)((int64_t)T * Dp);
+    g.as_bytes = (uint32_t)((int64_t)T * Dp / 32);
+    g.K = Dp;
+    g.F = F;
+    g.out = hq;
+    g.ldo = F;
+    g.out_scales = hs;
+    g.ldos = F / 32;
+    run(launch_gemm_grouped_mx(g, EPI_SWIGLU, s));
+  } else if (big_ok) {
+    GroupedParams g{};
+    g.A = xp;
+    g.lda = Dp;
+    g.a_rows = row_tok;
+    g.B = W.w_gate_up;
+    g.ldb = Dp;
+    g.b_expert_stride = (int64_t)2 * F * Dp;
+    g.offsets = offsets;
+    g.mt_off = mt_off;
+    g.E = E;
+    g.ntiles_n = F / 128;
+    g.max_tiles = g.ntiles_n * mtiles_bound;
+    g.a_bytes = (uint32_t)((int64_t)T * Dp * 2);
+    g.b_bytes = (uint32_t)((int64_t)2 * F * Dp * 2);
+    g.K = Dp;
+    g.F = F;
+    g.out = H;
+    g.ldo = F;
+    run(launch_gemm_grouped(g, EPI_SWIGLU, s));
+  } else {
+    GemmParams g{};
+    g.N = F;
+    g.K = Dp;
+    g.A = xp;
+    g.lda = Dp;
+    g.a_rows = row_tok;
+    g.B0 = W.w_gate_up;
+    g.ldb = Dp;
+    g.b_expert_stride = (int64_t)2 * F * Dp;
+    g.tiles = tiles;
+    g.n_tiles = n_tiles;
+    g.offsets = offsets;
+    g.max_slots = slots;
+    g.out0 = H;
+    g.ldo0 = F;
+    g.F = F;
+    run(launch_gemm(g, EPI_SWIGLU, bf16, s));
+  }
+  // 6. down grouped GEMM + sum-of-squares partials
+  mark();
+  if (stream_ok) {
+    StreamParams sp{};
+    sp.A = H;
+    sp.lda = F;
+    sp.B = W.w_down;
+    sp.ldb = F;
+    sp.b_expert_stride = (int64_t)Dp * F;
+    sp.offsets = offsets;
+    sp.n_experts = E;
+    sp.groups = Dp / 64;
+    sp.max_rows = small_max;
+    sp.K = F;
+    sp.F = F;
+    sp.a_bytes = (uint32_t)(A_ * F * 2);
+    sp.b_bytes = (uint32_t)((int64_t)Dp * F * 2);
+    sp.out = Y;
+    sp.ldo = Dp;
+    sp.ss_out = ss;
+    sp.ss_ld = Dp / 64;
+    run(launch_stream(sp, EPI_DOWN, s));
+  }
+  if (mx) {
+    StreamMxParams sp{};
+    sp.A = hq;
+    sp.As = hs;
+    sp.B = static_cast<const uint8_t*>(W.w_down);
+    sp.Bs = W.s_down;
+    sp.N = Dp;
+    sp.offsets = offsets;
+    sp.n_experts = E;
+    sp.groups = Dp / 64;
+    sp.max_rows = small_max;
+    sp.K = F;
+    sp.F = F;
+    sp.a_bytes = (uint32_t)(A_ * F);
+    sp.as_bytes = (uint32_t)(A_ * F / 32);
+    sp.b_bytes = (uint32_t)((int64_t)Dp * F / 2);
+    sp.bs_bytes = (uint32_t)((int64_t)Dp * F / 32);
+    sp.out = Y;
+    sp.ldo = Dp;
+    sp.ss_out = ss;
+    sp.ss_ld = Dp / 64;
+    run(launch_stream_mx(sp, EPI_DOWN, s));
+  }
+  if (mx) {
+    GroupedMxParams g{};
+    g.A = hq;
+    g.As = hs;
+    g.B = static_cast<const uint8_t*>(W.w_down);
+    g.Bs = W.s_down;
+    g.N = Dp;
+    g.offsets = offsets;
+    g.mt_off = mt_off;
+    g.E = E;
+    g.ntiles_n = Dp / 256;
+    g.max_tiles = g.ntiles_n * mtiles_bound;
+    g.a_bytes = (uint32_t)(A_ * F);
+    g.as_bytes = (uint32_t)(A_ * F / 32);
+    g.K = F;
+    g.F = F;
+    g.out = Y;
+    g.ldo = Dp;
+    g.ss_out = ss;
+    g.ss_ld = Dp / 64;
+    run(launch_gemm_grouped_mx(g, EPI_DOWN, s));
+  } else if (big_ok) {
+    GroupedParams g{};
+    g.A = H;
+    g.lda = F;
+    g.B = W.w_down;
+    g.ldb = F;
+    g.b_expert_stride = (int64_t)Dp * F;
+    g.offsets = offsets;
+    g.mt_off = mt_off;
+    g.E = E;
+    g.ntiles_n = Dp / 256;
+    g.max_tiles = g.ntiles_n * mtiles_bound;
+    g.a_bytes = (uint32_t)(A_ * F * 2);
+    g.b_bytes = (uint32_t)((int64_t)Dp * F * 2);
+    g.K = F;
+    g.F = F;
+    g.out = Y;
+    g.ldo = Dp;
+    g.ss_out = ss;
+    g.ss_ld = Dp / 64;
+    run(launch_gemm_grouped(g, EPI_DOWN, s));
+  } else {
+    GemmParams g{};
+    g.N = Dp;
+    g.K = F;
+    g.A = H;
+    g.lda = F;
+    g.B0 = W.w_down;
+    g.ldb = F;
+    g.b_expert_stride = (int64_t)Dp * F;
+    g.tiles = tiles;
+    g.n_tiles = n_tiles;
+    g.offsets = offsets;
+    g.max_slots = slots;
+    g.out0 = Y;
+    g.ldo0 = Dp;
+    g.ss_out = ss;
+    g.ss_ld = Dp / 64;
+    run(launch_gemm(g, EPI_DOWN, bf16, s));
+  }
+  // 7. per-expert RMSNorm + weighted sum
+  mark();
+  {
+    CombineParams cp{};
+    cp.y = Y;
+    cp.ss = ss;
+    cp.inv = inv;
+    cp.scale = reinterpret_cast<float*>(ws + pl.scale);
+    cp.ids = ids;
+    cp.w = tw;
+    cp.g_expert = W.g_expert;
+    cp.u = u;
+    cp.T = T;
+    cp.k = k;
+    cp.Dp = Dp;
+    cp.eps = c.eps_expert;
+    run(launch_combine(cp, bf16, s));
+  }
+  // 8. unpooler
+  mark();
+  if (dense256) {
+    GroupedParams g = dense_params(u, Dp, D);
+    g.B = W.w_unpool;
+    g.B1 = W.w_unpool;
+    g.n_split = D;
+    g.out = out;
+    g.ldo = D;
+    run(launch_gemm_grouped(g, out_f32 ? EPI_F32 : EPI_ACT, s));
+  } else if (dense_stream && slices_un > 0) {
+    DenseStreamParams d{};
+    d.A = u;
+    d.lda = Dp;
+    d.B0 = W.w_unpool;
+    d.B1 = W.w_unpool;
+    d.n_split = D;
+    d.ldb = Dp;
+    d.T = T;
+    d.N = D;
+    d.K = Dp;
+    d.slices = slices_un;
+    d.part = part;
+    d.out0 = out;
+    d.ldo0 = D;
+    d.out0_bf16 = !out_f32;
+    run(launch_dense_stream(d, s));
+  } else {
+    GemmParams g{};
+    g.M = T;
+    g.N = D;
+    g.K = Dp;
+    g.A = u;
+    g.lda = Dp;
+    g.B0 = W.w_unpool;
+    g.ldb = Dp;
+    g.out0 = out;
+    g.ldo0 = D;
+    g.n_split = D;                       // EPI_F32: every column goes to out0 as fp32
+    run(launch_gemm(g, out_f32 ? EPI_F32 : EPI_ACT, bf16, s));
+  }
+  mark();
+  if (aux && aux->expert_offsets)
+    run(hipMemcpyAsync(aux->expert_offsets, offsets, sizeof(int32_t) * (E + 1), hipMemcpyDeviceToDevice, s));
+  if (aux && aux->sorted_assign)
+    run(hipMemcpyAsync(aux->sorted_assign, sorted_assign, sizeof(int32_t) * (size_t)T * k,
+                       hipMemcpyDeviceToDevice, s));
+#undef run
+  return err;
+}
+
+// Scratch of the no-allocation forward (lmoe_forward_noalloc): a file-scope
+// array in the code object's static device memory, so that each GPU the
+// library runs on holds its own copy from the code object's load until the
+// process ends. In host code the array's name is only a stand-in: kernels and
+// copies get the device address that hipGetSymbolAddress returns for the
+// current device, taken once per device.
+static __device__ __align__(256) unsigned char scratch[LMOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+struct NoallocDevice {
+  std::once_flag once;
+  unsigned char* ptr = nullptr;   // device address of this device's scratch
+  int n_cu = 0;
+  hipError_t err = hipSuccess;
+};
+NoallocDevice g_noalloc[kMaxDevices];
+
+// Set-up on the device that is current: the scratch's device address and the
+// compute-unit count, once per device.
+NoallocDevice& noalloc_device(int dev) {
+  NoallocDevice& d = g_noalloc[dev];
+  std::call_once(d.once, [&d, dev]() {
+    void* ptr = nullptr;
+    d.err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (d.err != hipSuccess) return;
+    d.ptr = static_cast<unsigned char*>(ptr);
+    int n = 0;
+    d.n_cu = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n
+                                                                                                          : 256;
+  });
+  return d;
+}
+
 }  // namespace
 
 struct lmoe_ctx {
@@ -222,25 +782,8 @@ lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, lmoe_hand
   *out = nullptr;
   lmoe_status st = check_config(cfg);
   if (st != LMOE_OK) return st;
-  if (!w) return fail(LMOE_E_INVAL, "weights is NULL");
-  const void* req[] = {w->w_router, w->w_pool, w->g_pool, w->w_gate_up, w->w_down, w->g_expert,
-                       w->w_unpool};
-  const char* names[] = {"w_router", "w_pool", "g_pool", "w_gate_up", "w_down", "g_expert", "w_unpool"};
-  for (int i = 0; i < 7; ++i) {
-    if (!req[i]) return fail(LMOE_E_INVAL, std::string(names[i]) + " is NULL");
-    if (!aligned16(req[i])) return fail(LMOE_E_INVAL, std::string(names[i]) + " is not 16-byte aligned");
-  }
-  const bool has_bias = (cfg->flags & LMOE_FLAG_ROUTER_BIAS) != 0;
-  if (has_bias != (w->b_router != nullptr))
-    return fail(LMOE_E_INVAL, "b_router must be given iff LMOE_FLAG_ROUTER_BIAS is set");
-  if (w->b_router && !aligned4(w->b_router)) return fail(LMOE_E_INVAL, "b_router is misaligned");
-  if (cfg->expert_wdtype == LMOE_MXFP4) {
-    if (!w->s_gate_up || !w->s_down) return fail(LMOE_E_INVAL, "MXFP4 experts need s_gate_up and s_down");
-    if (!aligned16(w->s_gate_up) || !aligned16(w->s_down))
-      return fail(LMOE_E_INVAL, "s_gate_up / s_down are not 16-byte aligned");
-  } else if (w->s_gate_up || w->s_down) {
-    return fail(LMOE_E_INVAL, "MX scale pointers must be NULL unless expert_wdtype is LMOE_MXFP4");
-  }
+  st = check_weights(cfg, w);
+  if (st != LMOE_OK) return st;
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(LMOE_E_HIP, "hipGetDevice failed");
@@ -326,76 +869,14 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
                          const lmoe_aux* aux) {
   g_last_error.clear();
   if (!h) return fail(LMOE_E_INVAL, "handle is NULL");
-  const lmoe_config& c = h->cfg;
-  if (T < 0 || T > c.max_tokens)
-    return fail(LMOE_E_INVAL, "T = " + std::to_string(T) + " outside [0, max_tokens = " +
-                                  std::to_string(c.max_tokens) + "]");
-  if (T == 0) return LMOE_OK;
-  if (!x || !out) return fail(LMOE_E_INVAL, "x or out is NULL");
-  if (!aligned16(x) || !aligned16(out)) return fail(LMOE_E_INVAL, "x or out is not 16-byte aligned");
-  const bool bf16 = c.act_dtype == LMOE_BF16;
-  const bool out_f32 = c.out_dtype == LMOE_F32;
-  const size_t x_bytes = (size_t)T * c.d_model * (bf16 ? 2 : 4);
-  const size_t o_bytes = (size_t)T * c.d_model * (out_f32 ? 4 : 2);
-  const uintptr_t xb = reinterpret_cast<uintptr_t>(x), ob = reinterpret_cast<uintptr_t>(out);
-  if (xb < ob + o_bytes && ob < xb + x_bytes) return fail(LMOE_E_INVAL, "out overlaps x");
-  if (aux) {
-    const void* ap[] = {aux->logits, aux->topk_ids, aux->topk_w, aux->expert_offsets, aux->sorted_assign};
-    for (const void* q : ap)
-      if (q && !aligned4(q)) return fail(LMOE_E_INVAL, "aux pointer is not 4-byte aligned");
-  }
+  lmoe_status st = check_forward_args(h->cfg, x, out, T, aux);
+  if (st != LMOE_OK || T == 0) return st;
 
   int cur = 0;
   if (hipGetDevice(&cur) != hipSuccess) return fail(LMOE_E_HIP, "hipGetDevice failed");
   if (cur != h->device && hipSetDevice(h->device) != hipSuccess)
     return fail(LMOE_E_HIP, "hipSetDevice failed");
-
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  const Plan& pl = h->plan;
-  unsigned char* ws = h->ws;
-  const int E = c.n_experts, k = c.top_k, D = c.d_model, Dp = c.d_pooled, F = c.d_ff;
-  float* P = reinterpret_cast<float*>(ws + pl.P);
-  float* logits = (aux && aux->logits) ? aux->logits : reinterpret_cast<float*>(ws + pl.logits);
-  int32_t* ids = (aux && aux->topk_ids) ? aux->topk_ids : reinterpret_cast<int32_t*>(ws + pl.ids);
-  float* tw = (aux && aux->topk_w) ? aux->topk_w : reinterpret_cast<float*>(ws + pl.w);
-  int32_t* offsets = reinterpret_cast<int32_t*>(ws + pl.offsets);
-  int32_t* sorted_assign = reinterpret_cast<int32_t*>(ws + pl.sorted_assign);
-  int32_t* tiles = reinterpret_cast<int32_t*>(ws + pl.tiles);
-  int32_t* n_tiles = reinterpret_cast<int32_t*>(ws + pl.n_tiles);
-  int32_t* inv = reinterpret_cast<int32_t*>(ws + pl.inv);
-  int32_t* row_tok = reinterpret_cast<int32_t*>(ws + pl.row_tok);
-  void* xp = ws + pl.xp;
-  void* H = ws + pl.H;
-  uint8_t* xq = ws + pl.xq;
-  uint8_t* xs = ws + pl.xs;
-  uint8_t* hq = ws + pl.hq;
-  uint8_t* hs = ws + pl.hs;
-  const bool mx = c.expert_wdtype == LMOE_MXFP4;
-  void* Y = ws + pl.Y;
-  float* ss = reinterpret_cast<float*>(ws + pl.ss);
-  void* u = ws + pl.u;
-  const int slots = slots_for(T, k, E);
-  // Experts with few rows go to the weight-streaming kernels (bf16, K multiple of 128).
-  // The grouped kernels' buffer loads take 32-bit byte offsets: the activations
-  // (xp, H) and one expert's weights must each stay below 2 GiB.
-  const bool off32_ok = (int64_t)T * k * F * 2 < ((int64_t)1 << 31) &&
-                        (int64_t)T * k * Dp * 2 < ((int64_t)1 << 31) &&
-                        (int64_t)2 * F * Dp * 2 < ((int64_t)1 << 31);
-  const bool stream_ok = bf16 && !mx && Dp % 128 == 0 && F % 128 == 0 && off32_ok;
-  // MXFP4 experts: the create-time checks (Dp and F multiples of 1024, 32-bit
-  // byte extents) are all the MX weight-streaming kernel needs.
-  const int small_max = stream_ok ? stream_max_rows() : (mx ? stream_mx_max_rows() : 0);
-  // Experts with many rows: the tiled grouped GEMM (bf16, Dp % 256 == 0, F % 128 == 0).
-  const bool big_ok = bf16 && !mx && Dp % 256 == 0 && F % 128 == 0 && off32_ok;
-  int32_t* mt_off = reinterpret_cast<int32_t*>(ws + pl.mt_off);
-  const int64_t A_ = (int64_t)T * k;
-  // Row tiles (at least 256 rows each) over the experts with more than small_max rows: at most
-  // floor(A / 256) full ones plus one partial per such expert, and there are at
-  // most floor(A / (small_max + 1)) such experts. The bound sizes the grid, so a
-  // tight one keeps the launch cheap when few or no experts are large (decode).
-  const int64_t n_big = A_ / (small_max + 1) < E ? A_ / (small_max + 1) : E;
-  const int mtiles_bound = (int)(A_ / 256 + n_big);
-
   hipEvent_t ev[LMOE_NUM_STAGES + 1] = {};
   // Stage timing records events; a stream being captured into a graph gets
   // none (the forward itself captures: kernels only, no allocation, memset or
@@ -406,426 +887,44 @@ lmoe_status lmoe_forward(lmoe_handle h, const void* x, void* out, int32_t T, voi
   if (timing)
     for (auto& e : ev)
       if (hipEventCreate(&e) != hipSuccess) return fail(LMOE_E_HIP, "hipEventCreate failed");
-  int stage = 0;
-  auto mark = [&]() {
-    if (timing) (void)hipEventRecord(ev[stage], s);
-    ++stage;
-  };
-
-  // After the first failed launch nothing more is enqueued (later kernels would
-  // read tile lists and offsets that were never written).
-  hipError_t err = hipSuccess;
-#define run(X)                    \
-  do {                            \
-    if (err == hipSuccess) err = (X); \
-  } while (0)
-
-  // Small batches: the dense projections stream their weights with split-K.
-  const bool dense_stream = bf16 && T <= dense_stream_max_tokens();
-  float* part = reinterpret_cast<float*>(ws + pl.part);
-  const int slices_in = dense_stream_slices(Dp + E, D), slices_un = dense_stream_slices(D, Dp);
-
-  // Larger batches: the dense projections on the tiled kernel (bf16; K a
-  // multiple of 128, the pooler's rows a multiple of 256, 32-bit offsets).
-  const bool dense256 = bf16 && !dense_stream && D % 128 == 0 && Dp % 256 == 0 &&
-                        (int64_t)T * D * 2 < ((int64_t)1 << 31) && (int64_t)T * Dp * 2 < ((int64_t)1 << 31) &&
-                        (int64_t)256 * D * 2 < ((int64_t)1 << 31);
-  auto dense_params = [&](const void* A, int K, int N) {
-    GroupedParams g{};
-    g.A = A;
-    g.lda = K;
-    g.ldb = K;
-    g.K = K;
-    g.M = T;
-    g.N = N;
-    g.ntiles_n = (N + 255) / 256;
-    g.ntiles_m = gemm_grouped_dense_row_tiles(T, g.ntiles_n, h->n_cu);
-    g.max_tiles = g.ntiles_n * g.ntiles_m;
-    g.a_bytes = (uint32_t)((int64_t)T * K * 2);
-    return g;
-  };
-
-  // 1. router + pooler: one GEMM over [W_pool; W_router]
-  mark();
-  bool pooled = false;
-  if (dense256) {
-    GroupedParams g = dense_params(x, D, Dp + E);
-    g.B = h->w.w_pool;
-    g.B1 = h->w.w_router;
-    g.n_split = Dp;
-    g.out = P;
-    g.ldo = Dp;
-    g.out1 = logits;
-    g.ldo1 = E;
-    g.bias1 = h->w.b_router;
-    run(launch_gemm_grouped(g, EPI_F32, s));
-  } else if (dense_stream && slices_in > 0) {
-    DenseStreamParams d{};
-    d.A = x;
-    d.lda = D;
-    d.B0 = h->w.w_pool;
-    d.B1 = h->w.w_router;
-    d.n_split = Dp;
-    d.ldb = D;
-    d.T = T;
-    d.N = Dp + E;
-    d.K = D;
-    d.slices = slices_in;
-    d.part = part;
-    d.out0 = P;
-    d.ldo0 = Dp;
-    d.out1 = logits;
-    d.ldo1 = E;
-    d.bias1 = h->w.b_router;
-    // the split-K reduction, the pooled RMSNorm and the MXFP8 quantization of
-    // xp in one pass (xp is one row per token, so it needs no routing)
-    run(launch_dense_stream_partials(d, s));
-    run(launch_splitk_pool_norm(d, h->w.g_pool, c.eps_pool, mx ? static_cast<void*>(xq) : xp, mx ? 2 : 0, xs, s));
-    pooled = true;
-  } else {
-    GemmParams g{};
-    g.M = T;
-    g.N = Dp + E;
-    g.K = D;
-    g.A = x;
-    g.lda = D;
-    g.B0 = h->w.w_pool;
-    g.B1 = h->w.w_router;
-    g.n_split = Dp;
-    g.ldb = D;
-    g.out0 = P;
-    g.ldo0 = Dp;
-    g.out1 = logits;
-    g.ldo1 = E;
-    g.bias1 = h->w.b_router;
-    run(launch_gemm(g, EPI_F32, bf16, s));
-  }
-  // 2. top-k + softmax + chunk masks
-  mark();
-  uint64_t* masks = reinterpret_cast<uint64_t*>(ws + pl.masks);
-  // The top-k kernel ORs into the chunk masks and the sort clears them; if a
-  // previous call stopped between the two, clear them first.
-  if (h->masks_dirty) {
-    run(launch_clear_u64(masks, (int64_t)(pl.chunk_base - pl.masks) / 8, s));
-    if (err == hipSuccess) h->masks_dirty = false;
-  }
-  run(launch_topk(logits, T, E, k, ids, tw, masks, s));
-  if (err == hipSuccess) h->masks_dirty = true;
-  // 3. counting sort + tile list
-  mark();
-  {
-    SortParams sp{};
-    sp.ids = ids;
-    sp.topk_w = tw;
-    sp.chunk_masks = masks;
-    sp.chunk_base = reinterpret_cast<int32_t*>(ws + pl.chunk_base);
-    sp.counts = reinterpret_cast<int32_t*>(ws + pl.counts);
-    sp.offsets = offsets;
-    sp.sorted_assign = sorted_assign;
-    sp.inv = inv;
-    sp.row_tok = row_tok;
-    sp.tiles = tiles;
-    sp.n_tiles = n_tiles;
-    sp.T = T;
-    sp.E = E;
-    sp.k = k;
-    sp.tile_m = kGemmBM;
-    sp.small_max = small_max;
-    sp.mt_off = mt_off;
-    sp.tile_m2 = mx ? gemm_grouped_mx_tile_m() : gemm_grouped_tile_m();
-    run(launch_sort(sp, s));
-    if (err == hipSuccess) h->masks_dirty = false;
-  }
-  // 4. pooled RMSNorm (already done with the small-batch reduction)
-  mark();
-  if (pooled) {
-  } else if (mx) {
-    run(launch_pool_norm_mx(P, h->w.g_pool, T, Dp, c.eps_pool, xq, xs, s));
-  } else {
-    run(launch_pool_norm(P, h->w.g_pool, T, Dp, c.eps_pool, xp, bf16, s));
-  }
-  // 5. gate/up grouped GEMM + SwiGLU
-  mark();
-  if (stream_ok) {
-    StreamParams sp{};
-    sp.A = xp;
-    sp.lda = Dp;
-    sp.a_rows = row_tok;
-    sp.B = h->w.w_gate_up;
-    sp.ldb = Dp;
-    sp.b_expert_stride = (int64_t)2 * F * Dp;
-    sp.offsets = offsets;
-    sp.n_experts = E;
-    sp.groups = F / 32;
-    sp.max_rows = small_max;
-    sp.K = Dp;
-    sp.F = F;
-    sp.a_bytes = (uint32_t)((int64_t)T * Dp * 2);
-    sp.b_bytes = (uint32_t)((int64_t)2 * F * Dp * 2);
-    sp.out = H;
-    sp.ldo = F;
-    run(launch_stream(sp, EPI_SWIGLU, s));
-  }
-  if (mx) {
-    StreamMxParams sp{};
-    sp.A = xq;
-    sp.As = xs;
-    sp.a_rows = row_tok;
-    sp.B = static_cast<const uint8_t*>(h->w.w_gate_up);
-    sp.Bs = h->w.s_gate_up;
-    sp.N = 2 * F;
-    sp.offsets = offsets;
-    sp.n_experts = E;
-    sp.groups = F / 32;
-    sp.max_rows = small_max;
-    sp.K = Dp;
-    sp.F = F;
-    sp.a_bytes = (uint32_t)((int64_t)T * Dp);
-    sp.as_bytes = (uint32_t)((int64_t)T * Dp / 32);
-    sp.b_bytes = (uint32_t)((int64_t)F * Dp);
-    sp.bs_bytes = (uint32_t)((int64_t)2 * F * Dp / 32);
-    sp.out = hq;
-    sp.ldo = F;
-    sp.out_scales = hs;
-    sp.ldos = F / 32;
-    run(launch_stream_mx(sp, EPI_SWIGLU, s));
-  }
-  if (mx) {
-    GroupedMxParams g{};
-    g.A = xq;
-    g.As = xs;
-    g.a_rows = row_tok;
-    g.B = static_cast<const uint8_t*>(h->w.w_gate_up);
-    g.Bs = h->w.s_gate_up;
-    g.N = 2 * F;
-    g.offsets = offsets;
-    g.mt_off = mt_off;
-    g.E = E;
-    g.ntiles_n = F / 128;
-    g.max_tiles = g.ntiles_n * mtiles_bound;
-    g.a_bytes = (uint32_t)((int64_t)T * Dp);
-    g.as_bytes = (uint32_t)((int64_t)T * Dp / 32);
-    g.K = Dp;
-    g.F = F;
-    g.out = hq;
-    g.ldo = F;
-    g.out_scales = hs;
-    g.ldos = F / 32;
-    run(launch_gemm_grouped_mx(g, EPI_SWIGLU, s));
-  } else if (big_ok) {
-    GroupedParams g{};
-    g.A = xp;
-    g.lda = Dp;
-    g.a_rows = row_tok;
-    g.B = h->w.w_gate_up;
-    g.ldb = Dp;
-    g.b_expert_stride = (int64_t)2 * F * Dp;
-    g.offsets = offsets;
-    g.mt_off = mt_off;
-    g.E = E;
-    g.ntiles_n = F / 128;
-    g.max_tiles = g.ntiles_n * mtiles_bound;
-    g.a_bytes = (uint32_t)((int64_t)T * Dp * 2);
-    g.b_bytes = (uint32_t)((int64_t)2 * F * Dp * 2);
-    g.K = Dp;
-    g.F = F;
-    g.out = H;
-    g.ldo = F;
-    run(launch_gemm_grouped(g, EPI_SWIGLU, s));
-  } else {
-    GemmParams g{};
-    g.N = F;
-    g.K = Dp;
-    g.A = xp;
-    g.lda = Dp;
-    g.a_rows = row_tok;
-    g.B0 = h->w.w_gate_up;
-    g.ldb = Dp;
-    g.b_expert_stride = (int64_t)2 * F * Dp;
-    g.tiles = tiles;
-    g.n_tiles = n_tiles;
-    g.offsets = offsets;
-    g.max_slots = slots;
-    g.out0 = H;
-    g.ldo0 = F;
-    g.F = F;
-    run(launch_gemm(g, EPI_SWIGLU, bf16, s));
-  }
-  // 6. down grouped GEMM + sum-of-squares partials
-  mark();
-  if (stream_ok) {
-    StreamParams sp{};
-    sp.A = H;
-    sp.lda = F;
-    sp.B = h->w.w_down;
-    sp.ldb = F;
-    sp.b_expert_stride = (int64_t)Dp * F;
-    sp.offsets = offsets;
-    sp.n_experts = E;
-    sp.groups = Dp / 64;
-    sp.max_rows = small_max;
-    sp.K = F;
-    sp.F = F;
-    sp.a_bytes = (uint32_t)(A_ * F * 2);
-    sp.b_bytes = (uint32_t)((int64_t)Dp * F * 2);
-    sp.out = Y;
-    sp.ldo = Dp;
-    sp.ss_out = ss;
-    sp.ss_ld = Dp / 64;
-    run(launch_stream(sp, EPI_DOWN, s));
-  }
-  if (mx) {
-    StreamMxParams sp{};
-    sp.A = hq;
-    sp.As = hs;
-    sp.B = static_cast<const uint8_t*>(h->w.w_down);
-    sp.Bs = h->w.s_down;
-    sp.N = Dp;
-    sp.offsets = offsets;
-    sp.n_experts = E;
-    sp.groups = Dp / 64;
-    sp.max_rows = small_max;
-    sp.K = F;
-    sp.F = F;
-    sp.a_bytes = (uint32_t)(A_ * F);
-    sp.as_bytes = (uint32_t)(A_ * F / 32);
-    sp.b_bytes = (uint32_t)((int64_t)Dp * F / 2);
-    sp.bs_bytes = (uint32_t)((int64_t)Dp * F / 32);
-    sp.out = Y;
-    sp.ldo = Dp;
-    sp.ss_out = ss;
-    sp.ss_ld = Dp / 64;
-    run(launch_stream_mx(sp, EPI_DOWN, s));
-  }
-  if (mx) {
-    GroupedMxParams g{};
-    g.A = hq;
-    g.As = hs;
-    g.B = static_cast<const uint8_t*>(h->w.w_down);
-    g.Bs = h->w.s_down;
-    g.N = Dp;
-    g.offsets = offsets;
-    g.mt_off = mt_off;
-    g.E = E;
-    g.ntiles_n = Dp / 256;
-    g.max_tiles = g.ntiles_n * mtiles_bound;
-    g.a_bytes = (uint32_t)(A_ * F);
-    g.as_bytes = (uint32_t)(A_ * F / 32);
-    g.K = F;
-    g.F = F;
-    g.out = Y;
-    g.ldo = Dp;
-    g.ss_out = ss;
-    g.ss_ld = Dp / 64;
-    run(launch_gemm_grouped_mx(g, EPI_DOWN, s));
-  } else if (big_ok) {
-    GroupedParams g{};
-    g.A = H;
-    g.lda = F;
-    g.B = h->w.w_down;
-    g.ldb = F;
-    g.b_expert_stride = (int64_t)Dp * F;
-    g.offsets = offsets;
-    g.mt_off = mt_off;
-    g.E = E;
-    g.ntiles_n = Dp / 256;
-    g.max_tiles = g.ntiles_n * mtiles_bound;
-    g.a_bytes = (uint32_t)(A_ * F * 2);
-    g.b_bytes = (uint32_t)((int64_t)Dp * F * 2);
-    g.K = F;
-    g.F = F;
-    g.out = Y;
-    g.ldo = Dp;
-    g.ss_out = ss;
-    g.ss_ld = Dp / 64;
-    run(launch_gemm_grouped(g, EPI_DOWN, s));
-  } else {
-    GemmParams g{};
-    g.N = Dp;
-    g.K = F;
-    g.A = H;
-    g.lda = F;
-    g.B0 = h->w.w_down;
-    g.ldb = F;
-    g.b_expert_stride = (int64_t)Dp * F;
-    g.tiles = tiles;
-    g.n_tiles = n_tiles;
-    g.offsets = offsets;
-    g.max_slots = slots;
-    g.out0 = Y;
-    g.ldo0 = Dp;
-    g.ss_out = ss;
-    g.ss_ld = Dp / 64;
-    run(launch_gemm(g, EPI_DOWN, bf16, s));
-  }
-  // 7. per-expert RMSNorm + weighted sum
-  mark();
-  {
-    CombineParams cp{};
-    cp.y = Y;
-    cp.ss = ss;
-    cp.inv = inv;
-    cp.scale = reinterpret_cast<float*>(ws + pl.scale);
-    cp.ids = ids;
-    cp.w = tw;
-    cp.g_expert = h->w.g_expert;
-    cp.u = u;
-    cp.T = T;
-    cp.k = k;
-    cp.Dp = Dp;
-    cp.eps = c.eps_expert;
-    run(launch_combine(cp, bf16, s));
-  }
-  // 8. unpooler
-  mark();
-  if (dense256) {
-    GroupedParams g = dense_params(u, Dp, D);
-    g.B = h->w.w_unpool;
-    g.B1 = h->w.w_unpool;
-    g.n_split = D;
-    g.out = out;
-    g.ldo = D;
-    run(launch_gemm_grouped(g, out_f32 ? EPI_F32 : EPI_ACT, s));
-  } else if (dense_stream && slices_un > 0) {
-    DenseStreamParams d{};
-    d.A = u;
-    d.lda = Dp;
-    d.B0 = h->w.w_unpool;
-    d.B1 = h->w.w_unpool;
-    d.n_split = D;
-    d.ldb = Dp;
-    d.T = T;
-    d.N = D;
-    d.K = Dp;
-    d.slices = slices_un;
-    d.part = part;
-    d.out0 = out;
-    d.ldo0 = D;
-    d.out0_bf16 = !out_f32;
-    run(launch_dense_stream(d, s));
-  } else {
-    GemmParams g{};
-    g.M = T;
-    g.N = D;
-    g.K = Dp;
-    g.A = u;
-    g.lda = Dp;
-    g.B0 = h->w.w_unpool;
-    g.ldb = Dp;
-    g.out0 = out;
-    g.ldo0 = D;
-    g.n_split = D;                       // EPI_F32: every column goes to out0 as fp32
-    run(launch_gemm(g, out_f32 ? EPI_F32 : EPI_ACT, bf16, s));
-  }
-  mark();
-  if (aux && aux->expert_offsets)
-    run(hipMemcpyAsync(aux->expert_offsets, offsets, sizeof(int32_t) * (E + 1), hipMemcpyDeviceToDevice, s));
-  if (aux && aux->sorted_assign)
-    run(hipMemcpyAsync(aux->sorted_assign, sorted_assign, sizeof(int32_t) * (size_t)T * k,
-                       hipMemcpyDeviceToDevice, s));
-#undef run
+  const hipError_t err = enqueue_forward(h->cfg, h->w, h->plan, h->ws, h->n_cu, h->masks_dirty,
+                                         timing ? ev : nullptr, x, out, T, s, aux);
   if (timing) h->events.insert(h->events.end(), ev, ev + LMOE_NUM_STAGES + 1);
   if (cur != h->device) (void)hipSetDevice(cur);
+  if (err != hipSuccess) return fail(LMOE_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));
+  return LMOE_OK;
+}
+
+lmoe_status lmoe_forward_noalloc(const lmoe_config* cfg, const lmoe_weights* w, const void* x, void* out,
+                                 int32_t T, void* hip_stream, const lmoe_aux* aux) {
+  g_last_error.clear();
+  lmoe_status st = check_config(cfg);
+  if (st != LMOE_OK) return st;
+  st = check_weights(cfg, w);
+  if (st != LMOE_OK) return st;
+  st = check_forward_args(*cfg, x, out, T, aux);
+  if (st != LMOE_OK || T == 0) return st;
+  // The scratch is laid out for exactly T tokens.
+  lmoe_config c = *cfg;
+  c.max_tokens = T;
+  const Plan pl = make_plan(c);
+  if (pl.total > (size_t)LMOE_NOALLOC_SCRATCH_BYTES)
+    return fail(LMOE_E_INVAL, "T = " + std::to_string(T) + " needs " + std::to_string(pl.total) +
+                                  " bytes of workspace, more than the " +
+                                  std::to_string((size_t)LMOE_NOALLOC_SCRATCH_BYTES) +
+                                  "-byte scratch of lmoe_forward_noalloc (use lmoe_create + lmoe_forward)");
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(LMOE_E_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LMOE_E_UNSUPPORTED, "device index beyond 63");
+  NoallocDevice& d = noalloc_device(dev);
+  if (d.err != hipSuccess)
+    return fail(LMOE_E_HIP, std::string("hipGetSymbolAddress of the scratch failed: ") + hipGetErrorString(d.err));
+  // The scratch keeps whatever the device's previous call (or another layout)
+  // left in it: the chunk masks, the only region that must start at zero, are
+  // cleared first by a kernel.
+  bool masks_dirty = true;
+  const hipError_t err = enqueue_forward(c, *w, pl, d.ptr, d.n_cu, masks_dirty, nullptr, x, out, T,
+                                         static_cast<hipStream_t>(hip_stream), aux);
   if (err != hipSuccess) return fail(LMOE_E_HIP, std::string("launch failed: ") + hipGetErrorString(err));
   return LMOE_OK;
 }

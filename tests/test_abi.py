@@ -132,3 +132,35 @@ def test_nvfp4_to_mxfp4_rejects_bad_pointers():
             lmoe.lmoe_nvfp4_to_mxfp4(c[0], c[1], c[2], 2, 4, 64, c[3], c[4])
         assert e.value.status == lmoe.LMOE_E_INVAL, c
     lmoe.lmoe_nvfp4_to_mxfp4(0, 0, 0, 0, 4, 64, 0, 0)   # empty: nothing to do
+
+
+def test_forward_noalloc_checks_before_touching_a_device():
+    """lmoe_forward_noalloc checks its configuration, weights and token count on
+    the host: a T whose workspace exceeds the static scratch is refused (the
+    limit at the full decode shape is T = 301), as are bad pointers, before any
+    device call."""
+    cfg = lmoe.make_config(8192, 4096, 4096, 256, 8, 1024)
+    base = 1 << 30
+    w = lmoe.lmoe_weights(*[base + (i << 20) for i in (0, 0, 1, 2, 3, 0, 4, 0, 5, 6)])
+    w.b_router = None
+    w.s_gate_up = None
+    w.s_down = None
+    x, out = base + (64 << 20), base + (256 << 20)
+    for T in (302, 1024):
+        with pytest.raises(lmoe.LmoeError) as e:
+            lmoe.lmoe_forward_noalloc(cfg, w, x, out, T)
+        assert e.value.status == lmoe.LMOE_E_INVAL and "scratch" in lmoe.lmoe_last_error()
+    c = lmoe.make_config(8192, 4096, 4096, 256, 8, 301)
+    assert lmoe.lmoe_workspace_bytes(c) <= lmoe.LMOE_NOALLOC_SCRATCH_BYTES
+    c.max_tokens = 302
+    assert lmoe.lmoe_workspace_bytes(c) > lmoe.LMOE_NOALLOC_SCRATCH_BYTES
+    with pytest.raises(lmoe.LmoeError) as e:
+        lmoe.lmoe_forward_noalloc(cfg, w, x, out, 2048)           # beyond max_tokens
+    assert e.value.status == lmoe.LMOE_E_INVAL
+    with pytest.raises(lmoe.LmoeError) as e:
+        lmoe.lmoe_forward_noalloc(cfg, lmoe.lmoe_weights(), x, out, 16)
+    assert e.value.status == lmoe.LMOE_E_INVAL
+    with pytest.raises(lmoe.LmoeError) as e:
+        lmoe.lmoe_forward_noalloc(cfg, w, x + 8, out, 16)        # misaligned x
+    assert e.value.status == lmoe.LMOE_E_INVAL
+    lmoe.lmoe_forward_noalloc(cfg, w, x, out, 0)                  # T = 0: nothing to do
