@@ -1,6 +1,8 @@
 // C ABI of the latent-MoE block (include/lmoe.h): argument checks, the
 // workspace plan and the launch sequence of one forward pass on one stream.
+#include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -28,7 +30,8 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 // Byte layout of the workspace for a configuration (every region 256-byte aligned).
 struct Plan {
   size_t P, logits, ids, w, masks, chunk_base, counts, offsets, sorted_assign, inv,
-      row_tok, scale, tiles, n_tiles, mt_off, xp, H, xq, xs, hq, hs, Y, ss, u, part;
+      row_tok, scale, tiles, n_tiles, mt_off, stream_items, n_stream, queue, xp, H, xq, xs, hq, hs, Y, ss,
+      u, part;
   size_t total;
   int max_slots;
 };
@@ -67,6 +70,9 @@ Plan make_plan(const lmoe_config& c) {
   p.tiles = grow(cur, (size_t)p.max_slots * 8);
   p.n_tiles = grow(cur, 4);
   p.mt_off = grow(cur, (E + 1) * 4);
+  p.stream_items = grow(cur, E * 4);
+  p.n_stream = grow(cur, 4);
+  p.queue = grow(cur, 4);
   // Expert inputs: xp one row per token (the gate/up GEMMs gather it through
   // row_tok), H one row per assignment in sorted (expert-major) order; bf16/fp32,
   // or (MXFP4 experts) MXFP8 codes and scales.
@@ -182,6 +188,22 @@ lmoe_status check_weights(const lmoe_config* cfg, const lmoe_weights* w) {
   return LMOE_OK;
 }
 
+// Whether the streamed experts (1..64 rows each) run on the fused kernel (both
+// GEMMs in one persistent launch, one expert per workgroup at a time) or on
+// two weight-streaming launches (one wave per 64 weight rows). The fused
+// kernel gives each expert to one compute unit, so it needs about as many
+// streamed experts as compute units: expected active experts
+// E (1 - (1 - 1/E)^(T k)) of at least 3/4 of them. The environment variable
+// LMOE_FUSED_EXPERTS = 1 or 0 overrides the choice (where the fused kernel
+// applies: bf16 experts, Dp a multiple of 256).
+bool want_fused_stream(int T, int k, int E, int n_cu) {
+  const char* env = getenv("LMOE_FUSED_EXPERTS");
+  if (env && env[0] == '1') return true;
+  if (env && env[0] == '0') return false;
+  const double active = E * (1.0 - pow(1.0 - 1.0 / E, (double)T * k));
+  return active >= 0.75 * n_cu;
+}
+
 // The launch sequence of one forward pass on stream s, over the workspace ws
 // laid out by pl (sized for at least T tokens). Arguments are already checked.
 // masks_dirty: whether the chunk masks may hold bits (they are cleared first
@@ -223,6 +245,7 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
                         (int64_t)T * k * Dp * 2 < ((int64_t)1 << 31) &&
                         (int64_t)2 * F * Dp * 2 < ((int64_t)1 << 31);
   const bool stream_ok = bf16 && !mx && Dp % 128 == 0 && F % 128 == 0 && off32_ok;
+  const bool fused = stream_ok && Dp % 256 == 0 && want_fused_stream(T, k, E, n_cu);
   // MXFP4 experts: the create-time checks (Dp and F multiples of 1024, 32-bit
   // byte extents) are all the MX weight-streaming kernel needs.
   const int small_max = stream_ok ? stream_max_rows() : (mx ? stream_mx_max_rows() : 0);
@@ -364,6 +387,11 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     sp.small_max = small_max;
     sp.mt_off = mt_off;
     sp.tile_m2 = mx ? gemm_grouped_mx_tile_m() : gemm_grouped_tile_m();
+    if (fused) {
+      sp.stream_items = reinterpret_cast<int32_t*>(ws + pl.stream_items);
+      sp.n_stream = reinterpret_cast<int32_t*>(ws + pl.n_stream);
+      sp.queue = reinterpret_cast<int32_t*>(ws + pl.queue);
+    }
     run(launch_sort(sp, s));
     if (err == hipSuccess) masks_dirty = false;
   }
@@ -375,8 +403,28 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
   } else {
     run(launch_pool_norm(P, W.g_pool, T, Dp, c.eps_pool, xp, bf16, s));
   }
-  // 5. gate/up grouped GEMM + SwiGLU
+  // 5. gate/up grouped GEMM + SwiGLU (with the fused kernel: both streamed GEMMs)
   mark();
+  StreamParams sp_down{};
+  if (stream_ok) {
+    sp_down.A = H;
+    sp_down.lda = F;
+    sp_down.B = W.w_down;
+    sp_down.ldb = F;
+    sp_down.b_expert_stride = (int64_t)Dp * F;
+    sp_down.offsets = offsets;
+    sp_down.n_experts = E;
+    sp_down.groups = Dp / 64;
+    sp_down.max_rows = small_max;
+    sp_down.K = F;
+    sp_down.F = F;
+    sp_down.a_bytes = (uint32_t)(A_ * F * 2);
+    sp_down.b_bytes = (uint32_t)((int64_t)Dp * F * 2);
+    sp_down.out = Y;
+    sp_down.ldo = Dp;
+    sp_down.ss_out = ss;
+    sp_down.ss_ld = Dp / 64;
+  }
   if (stream_ok) {
     StreamParams sp{};
     sp.A = xp;
@@ -395,7 +443,17 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     sp.b_bytes = (uint32_t)((int64_t)2 * F * Dp * 2);
     sp.out = H;
     sp.ldo = F;
-    run(launch_stream(sp, EPI_SWIGLU, s));
+    if (fused) {
+      FusedStreamParams f{};
+      f.gu = sp;
+      f.dn = sp_down;
+      f.items = reinterpret_cast<const int32_t*>(ws + pl.stream_items);
+      f.n_items = reinterpret_cast<const int32_t*>(ws + pl.n_stream);
+      f.queue = reinterpret_cast<int32_t*>(ws + pl.queue);
+      run(launch_fused_stream(f, n_cu, s));
+    } else {
+      run(launch_stream(sp, EPI_SWIGLU, s));
+    }
   }
   if (mx) {
     StreamMxParams sp{};
@@ -484,27 +542,7 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
   }
   // 6. down grouped GEMM + sum-of-squares partials
   mark();
-  if (stream_ok) {
-    StreamParams sp{};
-    sp.A = H;
-    sp.lda = F;
-    sp.B = W.w_down;
-    sp.ldb = F;
-    sp.b_expert_stride = (int64_t)Dp * F;
-    sp.offsets = offsets;
-    sp.n_experts = E;
-    sp.groups = Dp / 64;
-    sp.max_rows = small_max;
-    sp.K = F;
-    sp.F = F;
-    sp.a_bytes = (uint32_t)(A_ * F * 2);
-    sp.b_bytes = (uint32_t)((int64_t)Dp * F * 2);
-    sp.out = Y;
-    sp.ldo = Dp;
-    sp.ss_out = ss;
-    sp.ss_ld = Dp / 64;
-    run(launch_stream(sp, EPI_DOWN, s));
-  }
+  if (stream_ok && !fused) run(launch_stream(sp_down, EPI_DOWN, s));
   if (mx) {
     StreamMxParams sp{};
     sp.A = hq;

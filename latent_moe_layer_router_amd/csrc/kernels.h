@@ -69,6 +69,19 @@ struct StreamParams {
 int stream_max_rows();
 hipError_t launch_stream(const StreamParams& p, EpiKind epi, hipStream_t s);
 
+// Both expert GEMMs of the streamed experts in one persistent launch (n_cu
+// workgroups): gu as for launch_stream(EPI_SWIGLU), dn as for
+// launch_stream(EPI_DOWN), each with groups a multiple of 4. items lists the
+// experts to run (n_items of them, both on the device); queue is a counter
+// that must be zero at launch (the sort zeroes it).
+struct FusedStreamParams {
+  StreamParams gu, dn;
+  const int32_t* items;
+  const int32_t* n_items;
+  int32_t* queue;
+};
+hipError_t launch_fused_stream(const FusedStreamParams& f, int n_cu, hipStream_t s);
+
 // Dense C = A . B^T for T <= dense_stream_max_tokens() rows (bf16), split over
 // K-slices into fp32 partials, then reduced in slice order. n_split must be a
 // multiple of 64.
@@ -232,6 +245,9 @@ struct SortParams {
   int small_max;                // experts with 1..small_max rows get no tiles (streamed instead)
   int32_t* mt_off;              // [E+1] row-tile prefix for the large-tile grouped GEMM
   int tile_m2;                  // its rows per tile
+  int32_t* stream_items;        // if set: [E] the experts with 1..small_max rows, ascending
+  int32_t* n_stream;            //   [1] their number
+  int32_t* queue;               //   [1] set to zero (the fused kernel's ticket counter)
 };
 hipError_t launch_sort(const SortParams& p, hipStream_t s);
 

@@ -209,6 +209,16 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(SortParams p) {
     p.tiles[2 * (tbase + i) + 1] = off + i * p.tile_m;
   }
   if (threadIdx.x == 0) *p.n_tiles = total;
+  // the streamed experts (1..small_max rows), for the fused kernel's queue
+  if (p.stream_items) {
+    const int st = (head && cnt > 0 && cnt <= p.small_max) ? 1 : 0;
+    const int sbase = block_exclusive_scan(st, wave_tot, &total);
+    if (st) p.stream_items[sbase] = e;
+    if (threadIdx.x == 0) {
+      *p.n_stream = total;
+      *p.queue = 0;
+    }
+  }
   // the large-tile GEMM: ceil(count / 256) row tiles
   const int nt2 = (head && cnt > p.small_max) ? (cnt + p.tile_m2 - 1) / p.tile_m2 : 0;
   const int mbase = block_exclusive_scan(nt2, wave_tot, &total);

@@ -62,9 +62,14 @@ constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (
 // s_waitcnt immediate: no LDS (or scalar memory) operation outstanding.
 constexpr int kLdsIdle = 15 | (3 << 14) | (7 << 4);
 
+// One wave streams one (expert, group of 64 weight rows) through its own four
+// 8 KiB LDS buffers (weight and token stages 0 and 1; the epilogue stages the
+// output tile in sw0). Only this wave touches them.
 template <int EPI, int NMT>
-__device__ __forceinline__ void stream_body(const StreamParams& p, int e, int grp, int lo, int m_e) {
-  const int lane = threadIdx.x, r16 = lane & 15, kq = lane >> 4;
+__device__ __forceinline__ void stream_body(const StreamParams& p, int e, int grp, int lo, int m_e,
+                                            unsigned char* sw0, unsigned char* sw1, unsigned char* sa0,
+                                            unsigned char* sa1) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, kq = lane >> 4;
   const int lrow = lane >> 3, lc = lane & 7;
 
   // Weights: load j moves local rows 8j .. 8j+7 (lane: row 8j + lrow).
@@ -138,6 +143,8 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int e, int gr
     LMOE_COMPUTE(SW, SA)                                                                       \
   }
   const int nc = p.K / KC;                   // even (K % 128 == 0)
+  // the buffers' previous reads (an earlier group's epilogue) are done
+  __builtin_amdgcn_s_waitcnt(kLdsIdle);
   LMOE_ISSUE(0, sw0, sa0)
   for (int c = 0; c < nc; c += 2) {
     LMOE_STAGE(c, sw0, sa0, sw1, sa1)
@@ -178,7 +185,8 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int e, int gr
       }
     }
   }
-  __syncthreads();
+  // the tile is staged (this wave's LDS writes complete) before it is read back
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup", "local");
   constexpr int CPR = OC / 8;                // 16-byte chunks per output row
   const int col0 = grp * OC;
   for (int c = lane; c < m_e * CPR; c += 64) {
@@ -195,10 +203,76 @@ __global__ __launch_bounds__(64) void stream_kernel(StreamParams p) {
   const int m_e = p.offsets[e + 1] - lo;
   if (m_e == 0 || m_e > p.max_rows) return;
   switch ((m_e + 15) >> 4) {                 // token tiles in use (uniform)
-    case 1: stream_body<EPI, 1>(p, e, grp, lo, m_e); break;
-    case 2: stream_body<EPI, 2>(p, e, grp, lo, m_e); break;
-    case 3: stream_body<EPI, 3>(p, e, grp, lo, m_e); break;
-    default: stream_body<EPI, 4>(p, e, grp, lo, m_e); break;
+    case 1: stream_body<EPI, 1>(p, e, grp, lo, m_e, sw0, sw1, sa0, sa1); break;
+    case 2: stream_body<EPI, 2>(p, e, grp, lo, m_e, sw0, sw1, sa0, sa1); break;
+    case 3: stream_body<EPI, 3>(p, e, grp, lo, m_e, sw0, sw1, sa0, sa1); break;
+    default: stream_body<EPI, 4>(p, e, grp, lo, m_e, sw0, sw1, sa0, sa1); break;
+  }
+}
+
+// Fused expert kernel for decode-sized batches: both expert GEMMs of every
+// streamed expert (1..max_rows rows) in one launch. A persistent grid of one
+// workgroup of FW waves per CU takes whole experts from a device-side queue
+// (a ticket counter that the sort zeroes; the sort also lists the streamed
+// experts) and, for each, runs the weight-streaming gate/up GEMM with the
+// SwiGLU epilogue over all of the expert's 2F weight rows (wave w takes the
+// 64-row groups w, w + FW, ...), writes h to the expert's H rows, meets the
+// workgroup's other waves at a barrier (h complete and visible to them), then
+// streams the down GEMM over all Dp output columns with the bf16 and
+// sum-of-squares epilogue. No workgroup ever waits for another: a workgroup
+// only takes tickets and leaves once they run past the list, and an expert's
+// whole chain stays in one workgroup. One launch instead of two removes the
+// second kernel's ramp and tail, and each expert's 96 MiB of weights stream
+// as one unit of work.
+constexpr int FW = 4;                  // waves per workgroup (4 x 32 KiB of LDS)
+
+// Each wave's own buffers, separate objects (as in the single-wave kernel) so
+// that the compiler can tell them apart around the loads into LDS.
+__shared__ __attribute__((aligned(16))) unsigned char fw00[8192], fw01[8192], fa00[8192], fa01[8192];
+__shared__ __attribute__((aligned(16))) unsigned char fw10[8192], fw11[8192], fa10[8192], fa11[8192];
+__shared__ __attribute__((aligned(16))) unsigned char fw20[8192], fw21[8192], fa20[8192], fa21[8192];
+__shared__ __attribute__((aligned(16))) unsigned char fw30[8192], fw31[8192], fa30[8192], fa31[8192];
+
+template <int EPI>
+__device__ __forceinline__ void stream_groups(const StreamParams& p, int e, int lo, int m_e, int first,
+                                              unsigned char* w0, unsigned char* w1, unsigned char* a0,
+                                              unsigned char* a1) {
+  const int nmt = (m_e + 15) >> 4;           // token tiles in use (uniform)
+  for (int grp = first; grp < p.groups; grp += FW) {
+    switch (nmt) {
+      case 1: stream_body<EPI, 1>(p, e, grp, lo, m_e, w0, w1, a0, a1); break;
+      case 2: stream_body<EPI, 2>(p, e, grp, lo, m_e, w0, w1, a0, a1); break;
+      case 3: stream_body<EPI, 3>(p, e, grp, lo, m_e, w0, w1, a0, a1); break;
+      default: stream_body<EPI, 4>(p, e, grp, lo, m_e, w0, w1, a0, a1); break;
+    }
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ void stream_groups_of_wave(const StreamParams& p, int e, int lo, int m_e, int wave) {
+  switch (wave) {
+    case 0: stream_groups<EPI>(p, e, lo, m_e, 0, fw00, fw01, fa00, fa01); break;
+    case 1: stream_groups<EPI>(p, e, lo, m_e, 1, fw10, fw11, fa10, fa11); break;
+    case 2: stream_groups<EPI>(p, e, lo, m_e, 2, fw20, fw21, fa20, fa21); break;
+    default: stream_groups<EPI>(p, e, lo, m_e, 3, fw30, fw31, fa30, fa31); break;
+  }
+}
+
+__global__ __launch_bounds__(FW * 64) void fused_stream_kernel(FusedStreamParams f) {
+  __shared__ int ticket;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_items = *f.n_items;
+  for (;;) {
+    if (threadIdx.x == 0) ticket = atomicAdd(f.queue, 1);
+    __syncthreads();
+    const int item = ticket;
+    __syncthreads();                         // every wave has read it before the next one is taken
+    if (item >= n_items) break;              // uniform over the workgroup
+    const int e = f.items[item];
+    const int lo = f.gu.offsets[e], m_e = f.gu.offsets[e + 1] - lo;
+    stream_groups_of_wave<EPI_SWIGLU>(f.gu, e, lo, m_e, wave);
+    __syncthreads();                         // the expert's h rows are written and visible here
+    stream_groups_of_wave<EPI_DOWN>(f.dn, e, lo, m_e, wave);
   }
 }
 
@@ -399,6 +473,13 @@ hipError_t launch_dense_stream(const DenseStreamParams& p, hipStream_t s) {
   const int64_t q = (int64_t)p.T * (((p.N + DN - 1) / DN) * DN) / 4;
   const int blocks = (int)((q + 255) / 256 < 2048 ? (q + 255) / 256 : 2048);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_stream(const FusedStreamParams& f, int n_cu, hipStream_t s) {
+  if (f.gu.n_experts == 0 || n_cu <= 0) return hipSuccess;
+  if (f.gu.groups % FW || f.dn.groups % FW) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fused_stream_kernel, dim3(n_cu), dim3(FW * 64), 0, s, f);
   return hipGetLastError();
 }
 
