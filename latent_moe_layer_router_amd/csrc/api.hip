@@ -1,6 +1,5 @@
 // C ABI of the latent-MoE block (include/lmoe.h): argument checks, the
 // workspace plan and the launch sequence of one forward pass on one stream.
-#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -188,20 +187,17 @@ lmoe_status check_weights(const lmoe_config* cfg, const lmoe_weights* w) {
   return LMOE_OK;
 }
 
-// Whether the streamed experts (1..64 rows each) run on the fused kernel (both
-// GEMMs in one persistent launch, one expert per workgroup at a time) or on
-// two weight-streaming launches (one wave per 64 weight rows). The fused
-// kernel gives each expert to one compute unit, so it needs about as many
-// streamed experts as compute units: expected active experts
-// E (1 - (1 - 1/E)^(T k)) of at least 3/4 of them. The environment variable
-// LMOE_FUSED_EXPERTS = 1 or 0 overrides the choice (where the fused kernel
-// applies: bf16 experts, Dp a multiple of 256).
-bool want_fused_stream(int T, int k, int E, int n_cu) {
+// The fused expert kernel runs the streamed experts (1..64 rows each) whole,
+// one per workgroup, when there are at least this many of them (counted on
+// the device); otherwise the single-wave weight-streaming launches run them.
+// Each whole expert gets one compute unit, so that needs about as many
+// streamed experts as compute units (3/4 of them). The environment variable
+// LMOE_FUSED_EXPERTS = 1 (always whole experts) or 0 (never) overrides it.
+int fused_whole_min(int n_cu) {
   const char* env = getenv("LMOE_FUSED_EXPERTS");
-  if (env && env[0] == '1') return true;
-  if (env && env[0] == '0') return false;
-  const double active = E * (1.0 - pow(1.0 - 1.0 / E, (double)T * k));
-  return active >= 0.75 * n_cu;
+  if (env && env[0] == '1') return 0;
+  if (env && env[0] == '0') return INT32_MAX;
+  return (3 * n_cu + 3) / 4;
 }
 
 // The launch sequence of one forward pass on stream s, over the workspace ws
@@ -245,7 +241,12 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
                         (int64_t)T * k * Dp * 2 < ((int64_t)1 << 31) &&
                         (int64_t)2 * F * Dp * 2 < ((int64_t)1 << 31);
   const bool stream_ok = bf16 && !mx && Dp % 128 == 0 && F % 128 == 0 && off32_ok;
-  const bool fused = stream_ok && Dp % 256 == 0 && want_fused_stream(T, k, E, n_cu);
+  // The fused expert kernel (Dp a multiple of 256: whole groups of 4 waves),
+  // launched when the streamed experts may reach its threshold (there are at
+  // most T k of them); it and the single-wave launches then decide on the
+  // device which of them runs.
+  const int whole_min = fused_whole_min(n_cu);
+  const bool fused = stream_ok && Dp % 256 == 0 && (int64_t)T * k >= whole_min;
   // MXFP4 experts: the create-time checks (Dp and F multiples of 1024, 32-bit
   // byte extents) are all the MX weight-streaming kernel needs.
   const int small_max = stream_ok ? stream_max_rows() : (mx ? stream_mx_max_rows() : 0);
@@ -424,6 +425,10 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     sp_down.ldo = Dp;
     sp_down.ss_out = ss;
     sp_down.ss_ld = Dp / 64;
+    if (fused) {
+      sp_down.fused_n = reinterpret_cast<const int32_t*>(ws + pl.n_stream);
+      sp_down.whole_min = whole_min;
+    }
   }
   if (stream_ok) {
     StreamParams sp{};
@@ -450,10 +455,12 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
       f.items = reinterpret_cast<const int32_t*>(ws + pl.stream_items);
       f.n_items = reinterpret_cast<const int32_t*>(ws + pl.n_stream);
       f.queue = reinterpret_cast<int32_t*>(ws + pl.queue);
+      f.whole_min = whole_min;
       run(launch_fused_stream(f, n_cu, s));
-    } else {
-      run(launch_stream(sp, EPI_SWIGLU, s));
+      sp.fused_n = f.n_items;
+      sp.whole_min = whole_min;
     }
+    run(launch_stream(sp, EPI_SWIGLU, s));
   }
   if (mx) {
     StreamMxParams sp{};
@@ -542,7 +549,7 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
   }
   // 6. down grouped GEMM + sum-of-squares partials
   mark();
-  if (stream_ok && !fused) run(launch_stream(sp_down, EPI_DOWN, s));
+  if (stream_ok) run(launch_stream(sp_down, EPI_DOWN, s));
   if (mx) {
     StreamMxParams sp{};
     sp.A = hq;

@@ -65,20 +65,25 @@ struct StreamParams {
   int64_t ldo;
   float* ss_out;
   int ss_ld;
+  const int32_t* fused_n;      // if set: nothing to do when *fused_n >= whole_min (the fused
+  int whole_min;               // kernel ran the streamed experts whole)
 };
 int stream_max_rows();
 hipError_t launch_stream(const StreamParams& p, EpiKind epi, hipStream_t s);
 
-// Both expert GEMMs of the streamed experts in one persistent launch (n_cu
-// workgroups): gu as for launch_stream(EPI_SWIGLU), dn as for
-// launch_stream(EPI_DOWN), each with groups a multiple of 4. items lists the
-// experts to run (n_items of them, both on the device); queue is a counter
-// that must be zero at launch (the sort zeroes it).
+// The streamed experts' GEMMs in one persistent launch (n_cu workgroups): gu
+// as for launch_stream(EPI_SWIGLU), dn as for launch_stream(EPI_DOWN), each
+// with groups a multiple of 4. items lists the experts to run (n_items of
+// them, both on the device); queue is a counter that must be zero at launch
+// (the sort zeroes it). With n_items >= whole_min both GEMMs run here, whole
+// experts per workgroup; otherwise nothing, and launch_stream (both EPIs) with
+// fused_n = n_items and the same whole_min does the work.
 struct FusedStreamParams {
   StreamParams gu, dn;
   const int32_t* items;
   const int32_t* n_items;
   int32_t* queue;
+  int whole_min;
 };
 hipError_t launch_fused_stream(const FusedStreamParams& f, int n_cu, hipStream_t s);
 

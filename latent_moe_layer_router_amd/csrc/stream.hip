@@ -198,6 +198,7 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int e, int gr
 
 template <int EPI>
 __global__ __launch_bounds__(64) void stream_kernel(StreamParams p) {
+  if (p.fused_n && *p.fused_n >= p.whole_min) return;   // the fused kernel ran these experts whole
   const int e = blockIdx.x / p.groups, grp = blockIdx.x % p.groups;
   const int lo = p.offsets[e];
   const int m_e = p.offsets[e + 1] - lo;
@@ -211,19 +212,23 @@ __global__ __launch_bounds__(64) void stream_kernel(StreamParams p) {
 }
 
 // Fused expert kernel for decode-sized batches: both expert GEMMs of every
-// streamed expert (1..max_rows rows) in one launch. A persistent grid of one
-// workgroup of FW waves per CU takes whole experts from a device-side queue
-// (a ticket counter that the sort zeroes; the sort also lists the streamed
-// experts) and, for each, runs the weight-streaming gate/up GEMM with the
-// SwiGLU epilogue over all of the expert's 2F weight rows (wave w takes the
-// 64-row groups w, w + FW, ...), writes h to the expert's H rows, meets the
-// workgroup's other waves at a barrier (h complete and visible to them), then
-// streams the down GEMM over all Dp output columns with the bf16 and
-// sum-of-squares epilogue. No workgroup ever waits for another: a workgroup
-// only takes tickets and leaves once they run past the list, and an expert's
-// whole chain stays in one workgroup. One launch instead of two removes the
-// second kernel's ramp and tail, and each expert's 96 MiB of weights stream
-// as one unit of work.
+// streamed expert (1..max_rows rows) in one launch, when there are at least
+// whole_min of them (about as many as CUs, e.g. a decode batch; counted on the
+// device). A persistent grid of one workgroup of FW waves per CU takes whole
+// experts from a device-side queue (a ticket counter that the sort zeroes; the
+// sort also lists the streamed experts). For each, the workgroup runs the
+// weight-streaming gate/up GEMM with the SwiGLU epilogue over all of the
+// expert's 2F weight rows (wave w takes the 64-row groups w, w + FW, ...),
+// writes h to the expert's H rows, meets its other waves at a barrier (h
+// complete and visible to them), then streams the down GEMM over all Dp output
+// columns with the bf16 and sum-of-squares epilogue. With fewer streamed
+// experts (giving each a single CU would leave most of the GPU idle) the
+// kernel returns at once and the two single-wave launches that follow it do
+// the work; they return at once when it ran.
+// No workgroup ever waits for another: a workgroup only takes tickets and
+// leaves once they run past the list, an expert's whole chain stays inside one
+// workgroup, and every wave of a workgroup reaches its barriers equally often.
+// One launch instead of two removes the second kernel's ramp and tail.
 constexpr int FW = 4;                  // waves per workgroup (4 x 32 KiB of LDS)
 
 // Each wave's own buffers, separate objects (as in the single-wave kernel) so
@@ -262,6 +267,7 @@ __global__ __launch_bounds__(FW * 64) void fused_stream_kernel(FusedStreamParams
   __shared__ int ticket;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_items = *f.n_items;
+  if (n_items < f.whole_min) return;         // the single-wave launches take these experts
   for (;;) {
     if (threadIdx.x == 0) ticket = atomicAdd(f.queue, 1);
     __syncthreads();

@@ -1,11 +1,13 @@
-"""GPU parity of the fused expert kernel (both streamed expert GEMMs in one
-persistent launch, whole experts taken from a device-side queue).
+"""GPU parity of the fused expert kernel (the streamed experts' GEMMs in one
+persistent launch over a device-side queue).
 
-The fused kernel runs the same per-(expert, 64 weight rows) arithmetic as the
-two weight-streaming launches, in the same K order, so its results must equal
-theirs bit for bit; both are also compared with the oracle. The environment
-variable LMOE_FUSED_EXPERTS forces the choice (1: fused, 0: two launches),
-read by the library at every forward call. Cases: every token-tile count of a
+The kernel runs whole experts per workgroup (both GEMMs) when enough experts
+are streamed, else per-wave gate/up items followed by the down launch; the
+per-(expert, 64 weight rows) arithmetic and its K order are the same either
+way, so the two modes must give identical bits; both are also compared with
+the oracle. The environment variable LMOE_FUSED_EXPERTS forces the mode (1:
+whole experts, 0: per-wave items), read by the library at every forward call;
+unset, the count of streamed experts decides. Cases: every token-tile count of a
 streamed expert (1..64 rows, across the 16-row tile boundaries, beside a
 65-row tiled expert and an empty one), more streamed experts than workgroups
 (each workgroup takes several tickets), streamed and tiled experts mixed,
@@ -35,8 +37,8 @@ def fused(monkeypatch):
 
 
 def both_paths(monkeypatch, w, wts, x):
-    """The forward with the fused kernel and with two launches on the same
-    inputs; the outputs and routing must be identical."""
+    """The forward in both modes on the same inputs; outputs and routing must
+    be identical."""
     block = lmoe.LatentMoE(upload(wts), w.k, x.shape[0], w.eps_pool, w.eps_expert, out_dtype=torch.float32)
     xd = sdev.to_device(x, DEV)
     res = {}
@@ -48,7 +50,7 @@ def both_paths(monkeypatch, w, wts, x):
         res[flag] = (out, aux)
     monkeypatch.delenv("LMOE_FUSED_EXPERTS", raising=False)
     (o1, a1), (o0, a0) = res["1"], res["0"]
-    assert torch.equal(o1.view(torch.int32), o0.view(torch.int32)), "fused and two-launch outputs differ"
+    assert torch.equal(o1.view(torch.int32), o0.view(torch.int32)), "the two modes' outputs differ"
     for n in a1:
         assert torch.equal(a1[n], a0[n]), n
     block.close()
