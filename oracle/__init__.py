@@ -39,7 +39,6 @@ def load(path: str = LIB_PATH):
         "orc_permutation": [_P, _I, _I, _I, _P, _P, _P, _P],
         "orc_pool_norm": [_P, _P, _I, _P, _I, _I, _I, _D, _I, _I, _P],
         "orc_expert": [_P, _I, _I, _P, _P, _P, _P, _I, _P, _D, _I, _I, _P, _P],
-        "orc_expert_batch": [_P, _I, _I, _I, _P, _P, _P, _P, _I, _P, _D, _I, _I, _P, _P],
         "orc_combine_unpool": [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P],
         "orc_expert_assign": [_P, _I, _P, _P, _I, _I, _P, _P, _P, _P, _I, _P, _D, _I, _I, _P, _P],
         "orc_mx_quant_e4m3": [_P, _I, _P, _P, _P],
@@ -54,6 +53,10 @@ def load(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = [ctypes.c_uint8]
         fn.restype = _D
+    lib.orc_set_threads.argtypes = [ctypes.c_int]
+    lib.orc_set_threads.restype = None
+    lib.orc_get_threads.argtypes = []
+    lib.orc_get_threads.restype = ctypes.c_int
     lib.orc_set_flush_modes.argtypes = [ctypes.c_int]
     lib.orc_set_flush_modes.restype = None
     lib.orc_round_bf16.argtypes = [_D]
@@ -123,27 +126,6 @@ class Oracle:
                                eps, int(mx_act), int(rnd), xp.ctypes.data)
         return xp
 
-    def expert(self, xin, wgu, wd, ge, eps, mx_act=False, sgu=None, sd=None, rnd=False):
-        """Rows xin [n, Dp] through one expert. Returns z [n, Dp], rms_unit [n]."""
-        xin = self._c(np.atleast_2d(xin), np.float64)
-        n, Dp = xin.shape
-        ge = self._c(ge, np.float32)
-        wgu, wd = self._c(wgu), self._c(wd)
-        if sgu is not None:
-            wdt = ORC_MXFP4
-            F = wd.shape[1] * 2
-            sgu, sd = self._c(sgu), self._c(sd)
-        else:
-            wdt = self._dt(wgu)
-            F = wd.shape[1]
-        z = np.empty((n, Dp), np.float64)
-        rms = np.empty(n, np.float64)
-        self.lib.orc_expert_batch(xin.ctypes.data, n, Dp, F, wgu.ctypes.data,
-                                  None if sgu is None else sgu.ctypes.data, wd.ctypes.data,
-                                  None if sd is None else sd.ctypes.data, wdt, ge.ctypes.data, eps,
-                                  int(mx_act), int(rnd), z.ctypes.data, rms.ctypes.data)
-        return z, rms
-
     def combine_unpool(self, z, w, wun, rnd=False) -> np.ndarray:
         z, w, wun = self._c(z, np.float64), self._c(w, np.float64), self._c(wun)
         T, k, Dp = z.shape
@@ -188,6 +170,13 @@ class Oracle:
         self.lib.orc_nvfp4_to_mxfp4(codes.ctypes.data, scales16.ctypes.data, g.ctypes.data, M, R, C,
                                     oc.ctypes.data, os_.ctypes.data)
         return oc, os_
+
+    def set_threads(self, n: int):
+        """Threads of the parallel loops (timing only; results do not depend on it)."""
+        self.lib.orc_set_threads(int(n))
+
+    def threads(self) -> int:
+        return self.lib.orc_get_threads()
 
     def round_bf16(self, v: float) -> float:
         return self.lib.orc_round_bf16(float(v))

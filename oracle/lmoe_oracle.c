@@ -58,6 +58,7 @@
  * element 2i in the low nibble, plus uint8 E8M0 scales [rows][K/32]).
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -234,6 +235,11 @@ static unsigned ieee_begin(void) {
   return csr;
 }
 static void ieee_end(unsigned csr) { _mm_setcsr(csr); }
+
+/* Timing hooks: the number of threads the parallel loops over tokens and
+   assignments use (a CPU-baseline run single-threaded or on every core). */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int orc_get_threads(void) { return omp_get_max_threads(); }
 
 /* Test hook: turn FTZ and DAZ on (1) or off (0) for the calling thread. */
 void orc_set_flush_modes(int on) {
@@ -456,17 +462,6 @@ void orc_expert(const double* xin, int Dp, int F,
   if (rms_unit) *rms_unit = sqrt(su / Dp);
   free(row);
   free(h);
-}
-
-/* Step 5 for n tokens routed to the same expert (rows of xin [n][Dp]); z [n][Dp],
-   rms_unit [n] or NULL. Tokens are independent, so they run in parallel. */
-void orc_expert_batch(const double* xin, int n, int Dp, int F,
-                      const void* wgu, const uint8_t* sgu, const void* wd, const uint8_t* sd, int wdt,
-                      const float* ge, double eps, int mx_act, int rnd, double* z, double* rms_unit) {
-#pragma omp parallel for schedule(dynamic)
-  for (int i = 0; i < n; ++i)
-    orc_expert(xin + (size_t)i * Dp, Dp, F, wgu, sgu, wd, sd, wdt, ge, eps, mx_act, rnd,
-               z + (size_t)i * Dp, rms_unit ? rms_unit + i : NULL);
 }
 
 /* Step 5 for n (token, expert) assignments at once: assignment a runs token row
