@@ -18,13 +18,20 @@
 // more than the AGPR file, and the copies between AGPRs and VGPRs that follow
 // made it 2.2x slower.)
 //
-// Operands reach LDS through direct global-to-LDS buffer loads in a four-stage
-// pipeline of 32-wide K-steps (A 20 KiB + B 16 KiB per stage, 144 KiB): the
-// loads for step k + 3 are in flight while step k computes. A stage is 20 A
-// loads and 16 B loads of 16 rows x 64 bytes; wave w issues loads w, w + 8,
-// ... (waves 0-3 five per stage, waves 4-7 four; A loads wholly past the
-// tile's last row are skipped). The 16-byte chunks of a row are XOR-swizzled
-// so that fragment reads are conflict-free.
+// Operands reach LDS through direct global-to-LDS buffer loads. The token
+// rows (A) move in 32-wide K-steps, 64 bytes of each row, through three
+// buffers (20 KiB each): the loads for step k + 3 are issued at step k. The
+// weights (B) move in stages of two K-steps, whole 128-byte row segments, 8
+// rows per load, through three buffers (32 KiB each): the loads for steps
+// 2s + 6 and 2s + 7 are issued at step 2s + 1, once both halves of a buffer
+// are read (156 KiB in all). The weights come from HBM on their first touch,
+// the token rows mostly from L2: the weights run further ahead, and whole-line
+// loads halve their requests for the same bytes. A stage of A is 20 loads of
+// 16 rows x 64 bytes (wave w issues loads w, w + 8, w + 16: waves 0-3 three,
+// waves 4-7 two; A loads wholly past the tile's last row are skipped); a
+// stage of B is 32 loads of 8 rows x 128 bytes, four per wave. The 16-byte
+// chunks of each row are XOR-swizzled so that fragment reads are
+// conflict-free.
 //
 // Tile order over the 8 XCDs: one index space (expert, n-tile, m-tile) cut
 // into 8 contiguous chunks, one per XCD, so that the CUs of an XCD share the
@@ -40,18 +47,20 @@ constexpr int GW = 8;                  // waves
 constexpr int GNT = GW * 64;
 constexpr int GBM = 320, GBN = 256;    // A rows (max), B rows per tile
 constexpr int GMI = 5, GNI = 2;        // 32-row groups, 32-column groups per wave
-constexpr int RB = 64;                 // bytes of each tile row per stage (32 bf16)
-constexpr int GSA = GBM * RB, GSB = GBN * RB;
+constexpr int RB = 64;                 // bytes of each A row per stage (32 bf16)
+constexpr int RBB = 128;               // bytes of each B row per stage (two K-steps)
+constexpr int GSA = GBM * RB, GSB = GBN * RBB;
 constexpr int LA = GBM / 16;            // A loads of 16 rows per stage
 constexpr int kBufWord3 = 0x00020000;  // raw buffer descriptor, fourth word (CDNA)
 constexpr uint32_t kOutOfRange = 0x80000000u;   // past every extent used here
 
 #define LMOE_AS3 __attribute__((address_space(3)))
 
-// Four pipeline stages, separate LDS objects so that the compiler can tell
-// them apart when it orders reads against the loads still in flight.
+// Three A buffers and three B buffers, separate LDS objects so that the
+// compiler can tell them apart when it orders reads against the loads still in
+// flight.
 __shared__ __attribute__((aligned(16))) unsigned char gA0[GSA], gB0[GSB], gA1[GSA], gB1[GSB],
-    gA2[GSA], gB2[GSB], gA3[GSA], gB3[GSB];
+    gA2[GSA], gB2[GSB];
 
 // Byte offset of logical 16-byte chunk c (0..3) of tile row r (64-byte rows),
 // stored at position c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3: 32 lanes on 32
@@ -60,14 +69,21 @@ __device__ __forceinline__ int swz(int r, int c) {
   return r * RB + ((c ^ (((r >> 1) ^ (r >> 3)) & 3)) << 4);
 }
 
+// Byte offset of logical 16-byte chunk c (0..7) of B row r (128-byte rows),
+// stored at position c ^ g(r), g(r) = ((r >> 1) ^ (r << 2)) & 7: the chunk
+// positions of any 8 consecutive rows are a permutation of 0..7, so 32 lanes
+// reading 32 consecutive rows at one logical chunk are conflict-free.
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) ^ (r << 2)) & 7; }
+__device__ __forceinline__ int swzb(int r, int c) { return r * RBB + ((c ^ swz8(r)) << 4); }
+
 __device__ __forceinline__ void mfma32(const uint4& a, const uint4& b, f32x16_t& acc) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                 __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
 }
 
-// At most N global loads of this wave in flight (its two later stages) and no
-// LDS read outstanding: the scheduler may move the previous step's MFMAs (not
-// their reads) past the barrier that follows.
+// At most N global loads of this wave in flight (those issued after the last
+// one the next step needs) and no LDS read outstanding: the scheduler may move
+// the previous step's MFMAs (not their reads) past the barrier that follows.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
@@ -153,19 +169,27 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
     const int src = p.a_rows ? p.a_rows[m] : m;   // gathered rows (gate/up: the assignment's token)
     return (uint32_t)src * (uint32_t)(p.lda * 2) + c * 16;
   };
+  // B load j (of a stage) moves rows 8 j .. 8 j + 7, lane i row 8 j + i / 8 at
+  // chunk position i % 8 (which holds logical chunk (i % 8) ^ g(row)); wave w
+  // issues j = w, w + 8, w + 16, w + 24.
   auto b_off = [&](int r) -> uint32_t {
     const int n = dense ? r : (EPI == EPI_SWIGLU) ? ((r < GBN / 2) ? (n0 + r) : (p.F + n0 + r - GBN / 2)) : (n0 + r);
-    const uint32_t c = pos ^ (((r >> 1) ^ (r >> 3)) & 3);
+    const uint32_t c = (lane & 7) ^ swz8(r);
     return (uint32_t)n * (uint32_t)(p.ldb * 2) + c * 16;
   };
-  // load j (of a stage) moves rows 16 j .. 16 j + 15, lane i row 16 j + i / 4
-  // at chunk position i % 4; wave w issues j = w, w + 8, w + 16 (A, while j <
-  // 20) and j = w, w + 8 (B)
-  uint32_t ga[3], gb[2];
+  // A load j (of a stage) moves rows 16 j .. 16 j + 15, lane i row 16 j + i / 4
+  // at chunk position i % 4; wave w issues j = w, w + 8, w + 16 (while j < 20)
+  uint32_t ga[3];
 #pragma unroll
   for (int i = 0; i < 3; ++i) ga[i] = (wave + 8 * i < LA) ? a_off(16 * (wave + 8 * i) + (lane >> 2)) : kOutOfRange;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) gb[i] = b_off(16 * (wave + 8 * i) + (lane >> 2));
+  // The wave's four B loads (rows r, r + 64, r + 128, r + 192; the swizzle
+  // depends on the row's low 4 bits only) differ by whole rows: one offset
+  // register plus uniform row deltas in the scalar offset. SwiGLU rows 128..255
+  // are the up rows, F - 128 further on.
+  const uint32_t gb0 = b_off(8 * wave + (lane >> 3));
+  const int rowb = (int)p.ldb * 2;
+  const int up = (EPI == EPI_SWIGLU && !dense) ? (p.F - GBN / 2) * rowb : 0;
+  const int gbd1 = 64 * rowb, gbd2 = 128 * rowb + up, gbd3 = 192 * rowb + up;
   // Waves 0-3 issue a third A load (rows 256 + 16 wave ..) only if some of its
   // rows are in the tile: a 256-row tile then moves 32 rows per K-step instead
   // of 36 x 16. The LDS rows a skipped load would have filled are read only
@@ -174,20 +198,39 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
 
 #define LMOE_LD(RS, OFF, DST, KO) \
   __builtin_amdgcn_raw_ptr_buffer_load_lds((RS), (LMOE_AS3 void*)(DST), 16, (int)(OFF), (KO), 0, 0);
-#define LMOE_ISSUE(kt, SA, SBB)                                                                         \
+  // A for K-step kt (rotated), into buffer SA
+#define LMOE_ISSUE_A(kt, SA)                                                                            \
   {                                                                                                    \
     const int kr_ = (kt) + krot;                                                                       \
     const int ko = (kr_ >= nk ? kr_ - nk : kr_) * RB;                                                  \
     LMOE_LD(rsA, ga[0], (SA) + wave * 16 * RB, ko)                                                     \
     LMOE_LD(rsA, ga[1], (SA) + (wave + 8) * 16 * RB, ko)                                               \
     if (three_a) LMOE_LD(rsA, ga[2], (SA) + (wave + 16) * 16 * RB, ko)                                 \
-    LMOE_LD(rsB, gb[0], (SBB) + wave * 16 * RB, ko)                                                    \
-    LMOE_LD(rsB, gb[1], (SBB) + (wave + 8) * 16 * RB, ko)                                              \
   }
-  // two later stages of 5 (waves 0-3) or 4 loads
-#define LMOE_WAIT()                    \
-  if (three_a) wait_vm<10>();          \
-  else wait_vm<8>();
+  // B for K-steps 2 st and 2 st + 1 (rotated; krot is even, so the pair never
+  // wraps), into buffer SBB
+#define LMOE_ISSUE_B(st, SBB)                                                                           \
+  {                                                                                                    \
+    const int kr_ = 2 * (st) + krot;                                                                   \
+    const int ko = (kr_ >= nk ? kr_ - nk : kr_) * RB;                                                  \
+    LMOE_LD(rsB, gb0, (SBB) + wave * 8 * RBB, ko)                                                      \
+    LMOE_LD(rsB, gb0, (SBB) + (wave + 8) * 8 * RBB, ko + gbd1)                                         \
+    LMOE_LD(rsB, gb0, (SBB) + (wave + 16) * 8 * RBB, ko + gbd2)                                        \
+    LMOE_LD(rsB, gb0, (SBB) + (wave + 24) * 8 * RBB, ko + gbd3)                                        \
+  }
+  // Waits for the next step's operands. Loads are issued in blocks, one per
+  // step k: the B stage (odd k only) and then A for step k + 3. Counters drain
+  // in issue order, so a wait lets through the blocks issued after the last
+  // load it needs, which is always A for step k + 1 (block k - 2; the B stage
+  // holding step k + 1 came earlier): block k - 1, that is one A block, plus
+  // one B stage when k - 1 is odd. A blocks are 3 loads (waves with three_a)
+  // or 2, B stages 4.
+#define LMOE_WAIT_EVEN()               \
+  if (three_a) wait_vm<7>();           \
+  else wait_vm<6>();
+#define LMOE_WAIT_ODD()                \
+  if (three_a) wait_vm<3>();           \
+  else wait_vm<2>();
 
   f32x16_t acc[GMI][GNI];
 #pragma unroll
@@ -200,13 +243,20 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
   // LDS rows of this lane's MFMA operands: A rows wrow0 + 32 mi + l32 (the
   // swizzle depends on a row's low 5 bits only); B rows: SwiGLU the gate (ni =
   // 0) and up (ni = 1) rows of the same 32 output columns, down 64 columns.
+  // One offset register per operand (ao for A, bo0 and bo1 for the two B
+  // fragments) walks the logical chunks in place: the second 16-wide K-slice
+  // of a step is the first's chunk with bit 1 set (byte offset XOR 32), a B
+  // row's odd K-step its even one's with bit 2 set (XOR 64). The XORs are
+  // opaque to the compiler, which otherwise keeps every variant (and their
+  // sums with the buffers' LDS addresses) in registers and spills inside the
+  // K loop.
   const int l32 = lane & 31, half = lane >> 5;
-  const int aoff0 = swz(wrow0 + l32, half), aoff1 = swz(wrow0 + l32, 2 + half);
   auto brow_of = [&](int ni) {
     return (EPI == EPI_SWIGLU) ? (ni * (GBN / 2) + wn * 32 + l32) : (wn * 64 + ni * 32 + l32);
   };
-  const int b00 = swz(brow_of(0), half), b01 = swz(brow_of(0), 2 + half);
-  const int b10 = swz(brow_of(1), half), b11 = swz(brow_of(1), 2 + half);
+  int ao = swz(wrow0 + l32, half);           // A, first slice
+  int bo0 = swzb(brow_of(0), half), bo1 = swzb(brow_of(1), half);   // B, first slice, even step
+#define LMOE_XOR(X, IMM) __asm__ volatile("v_xor_b32 %0, " #IMM ", %0" : "+v"(X))
 
   // Operand fragments: two register sets, so that the LDS reads of the next
   // 16-wide K-slice are in flight while the MFMAs of the current one run.
@@ -229,36 +279,58 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
   if ((NMI) > 2) { mfma32(PA##2, PB##0, acc[2][0]); mfma32(PA##2, PB##1, acc[2][1]); }          \
   if ((NMI) > 3) { mfma32(PA##3, PB##0, acc[3][0]); mfma32(PA##3, PB##1, acc[3][1]); }          \
   if ((NMI) > 4) { mfma32(PA##4, PB##0, acc[4][0]); mfma32(PA##4, PB##1, acc[4][1]); }
-  // K-step k (stage k in SA/SBB, stage k + 1 in NA/NB). On entry stage k is
-  // visible to all waves, the loads of stages k + 1 .. k + 3 are in flight and
-  // the x registers hold the step's first K-slice. The step reads the second
-  // slice (y) and runs the first slice's MFMAs (x); waits for stage k + 1 and
-  // its own LDS reads, then the barrier: no wave reads stage k any more, so the
-  // loads of stage k + 4 go into its buffer (clamped to the last stage: a
-  // harmless re-read into a buffer no later step reads); reads the next step's
-  // first slice (x) and runs the second slice's MFMAs (y).
-#define LMOE_STEP(NMI, k, SA, SBB, NA, NB)                                                       \
+  // K-step k: A of step k in SA, of step k + 1 in NA; B of step k in SBB at
+  // parity PK (0: first K-step of the B stage, 1: second), of step k + 1 in
+  // NBB. On entry A and B of step k are visible to all waves and the x
+  // registers hold the step's first K-slice. The step reads the second slice
+  // (y) and runs the first slice's MFMAs (x); waits for step k + 1's operands
+  // and its own LDS reads, then the barrier: no wave reads step k's A buffer
+  // any more (nor, at an odd step, its B buffer), so those take the loads
+  // issued now (clamped to the last step or stage: a harmless re-read into a
+  // buffer no later step reads); reads the next step's first slice (x) and
+  // runs the second slice's MFMAs (y).
+#define LMOE_STEP(NMI, k, PK, SA, SBB, NA, NBB)                                                  \
   {                                                                                             \
-    LMOE_READ(NMI, SA, SBB, aoff1, b01, b11, ya, yb)                                            \
+    LMOE_XOR(ao, 32);                                                                           \
+    LMOE_XOR(bo0, 32);                                                                          \
+    LMOE_XOR(bo1, 32);                                                                          \
+    LMOE_READ(NMI, SA, SBB, ao, bo0, bo1, ya, yb)                                               \
     __builtin_amdgcn_sched_barrier(0);                                                          \
     LMOE_MFMA(NMI, xa, xb)                                                                      \
     __builtin_amdgcn_sched_barrier(0);                                                          \
-    LMOE_WAIT()                                                                                 \
+    if (PK) { LMOE_WAIT_ODD() } else { LMOE_WAIT_EVEN() }                                      \
     bar();                                                                                      \
-    LMOE_ISSUE(((k) + 4 < nk ? (k) + 4 : nk - 1), SA, SBB)                                      \
-    LMOE_READ(NMI, NA, NB, aoff0, b00, b10, xa, xb)                                             \
+    if (PK) LMOE_ISSUE_B(((k) + 5) / 2 < nk / 2 ? ((k) + 5) / 2 : nk / 2 - 1, SBB)            \
+    LMOE_ISSUE_A(((k) + 3 < nk ? (k) + 3 : nk - 1), SA)                                         \
+    LMOE_XOR(ao, 32);                                                                           \
+    LMOE_XOR(bo0, 96);                                                                          \
+    LMOE_XOR(bo1, 96);                                                                          \
+    LMOE_READ(NMI, NA, NBB, ao, bo0, bo1, xa, xb)                                               \
     __builtin_amdgcn_sched_barrier(0);                                                          \
     LMOE_MFMA(NMI, ya, yb)                                                                      \
     __builtin_amdgcn_sched_barrier(0);                                                          \
   }
+  // Six steps per iteration (the A buffers repeat every 3 steps, the B
+  // buffers every 6), then up to four more (K-steps are a multiple of 4).
 #define LMOE_KLOOP(NMI)                                                                          \
   {                                                                                             \
-    LMOE_READ(NMI, gA0, gB0, aoff0, b00, b10, xa, xb)                                           \
-    for (int k = 0; k < nk; k += 4) {                                                           \
-      LMOE_STEP(NMI, k, gA0, gB0, gA1, gB1)                                                     \
-      LMOE_STEP(NMI, k + 1, gA1, gB1, gA2, gB2)                                                 \
-      LMOE_STEP(NMI, k + 2, gA2, gB2, gA3, gB3)                                                 \
-      LMOE_STEP(NMI, k + 3, gA3, gB3, gA0, gB0)                                                 \
+    LMOE_READ(NMI, gA0, gB0, ao, bo0, bo1, xa, xb)                                              \
+    int k = 0;                                                                                  \
+    for (; k + 6 <= nk; k += 6) {                                                               \
+      LMOE_STEP(NMI, k, 0, gA0, gB0, gA1, gB0)                                                  \
+      LMOE_STEP(NMI, k + 1, 1, gA1, gB0, gA2, gB1)                                              \
+      LMOE_STEP(NMI, k + 2, 0, gA2, gB1, gA0, gB1)                                              \
+      LMOE_STEP(NMI, k + 3, 1, gA0, gB1, gA1, gB2)                                              \
+      LMOE_STEP(NMI, k + 4, 0, gA1, gB2, gA2, gB2)                                              \
+      LMOE_STEP(NMI, k + 5, 1, gA2, gB2, gA0, gB0)                                              \
+    }                                                                                           \
+    if (k < nk) {                                                                               \
+      LMOE_STEP(NMI, k, 0, gA0, gB0, gA1, gB0)                                                  \
+      LMOE_STEP(NMI, k + 1, 1, gA1, gB0, gA2, gB1)                                              \
+    }                                                                                           \
+    if (k + 2 < nk) {                                                                           \
+      LMOE_STEP(NMI, k + 2, 0, gA2, gB1, gA0, gB1)                                              \
+      LMOE_STEP(NMI, k + 3, 1, gA0, gB1, gA1, gB2)                                              \
     }                                                                                           \
   }
 
@@ -268,12 +340,18 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
   // a few steps apart. The order depends on the column tile only, so every
   // output element is summed in one fixed order, whatever the batch.
   const int krot = (ntile * 4) % nk;
-  LMOE_ISSUE(0, gA0, gB0)
-  LMOE_ISSUE(1, gA1, gB1)
-  LMOE_ISSUE(2, gA2, gB2)
-  LMOE_WAIT()
+  // Prologue: B stages 0..2 and A for steps 0..2 in the steady state's order
+  // (block k holds the B stage first), then wait for step 0's operands: A for
+  // step 0 and everything before it.
+  LMOE_ISSUE_B(0, gB0)
+  LMOE_ISSUE_B((1 < nk / 2 ? 1 : nk / 2 - 1), gB1)
+  LMOE_ISSUE_A(0, gA0)
+  LMOE_ISSUE_A(1, gA1)
+  LMOE_ISSUE_B((2 < nk / 2 ? 2 : nk / 2 - 1), gB2)
+  LMOE_ISSUE_A(2, gA2)
+  if (three_a) wait_vm<10>();
+  else wait_vm<8>();
   bar();
-  LMOE_ISSUE(3, gA3, gB3)
   // One K loop per number of live 32-row groups (uniform per wave; all waves
   // run the same barriers): 5, 4 (3 groups run it too), 2 (1-2 groups), none.
   if (nmi > 4) {
@@ -289,8 +367,11 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
 #undef LMOE_STEP
 #undef LMOE_MFMA
 #undef LMOE_READ
-#undef LMOE_WAIT
-#undef LMOE_ISSUE
+#undef LMOE_XOR
+#undef LMOE_WAIT_EVEN
+#undef LMOE_WAIT_ODD
+#undef LMOE_ISSUE_A
+#undef LMOE_ISSUE_B
 #undef LMOE_LD
   __syncthreads();   // every load has landed and every wave has finished reading
 
