@@ -151,6 +151,8 @@ CSRC = os.path.join(ROOT, "latent_moe_layer_router_amd", "csrc")
 KERNEL_SOURCES = {"fused_stream_kernel": ("stream.hip", "common.h"),
                   "stream_kernel": ("stream.hip", "common.h"),
                   "dense_stream_kernel": ("stream.hip", "norm.hip", "common.h"),
+                  "splitk_pool_norm_kernel": ("norm.hip", "mx.h", "common.h"),
+                  "splitk_reduce_kernel": ("stream.hip", "common.h"),
                   "stream_mx_kernel": ("stream_mx.hip", "mx.h", "common.h"),
                   "gemm_grouped_kernel": ("gemm_grouped.hip", "common.h"),
                   "gemm_grouped_mx_kernel": ("gemm_grouped_mx.hip", "mx.h", "common.h"),
@@ -169,35 +171,38 @@ def kernel_digest(kernel):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, kernel):
-    """Memory-side bytes per launch of a kernel in a workload, from the
-    profiles: reads from the L2's 32-, 64- and 128-byte read requests to memory
-    (TCC_EA0_RDREQ_32B/64B/128B; a 1 GiB device copy reads 1.00 GiB this way),
-    writes from WRITE_SIZE (the copy writes 1.00 GiB). None unless they were
-    taken on the kernel's sources as they are now."""
+def measured_traffic(workload, stages, launches=1):
+    """Memory-side bytes of the given stages of a workload, from the profiles:
+    the sum over every kernel those stages launch of its reads (the L2's 32-,
+    64- and 128-byte read requests to memory, TCC_EA0_RDREQ_32B/64B/128B; a
+    1 GiB device copy reads 1.00 GiB this way) and writes (WRITE_SIZE; the copy
+    writes 1.00 GiB), per launch, times `launches`. None unless every such
+    kernel was profiled on its sources as they are now."""
     try:
         with open(TRAFFIC_FILE) as fh:
             lines = fh.read().splitlines()
     except OSError:
         return None
-    digest = kernel_digest(kernel)
-    if digest is None:
-        return None
+    total, seen = 0, False
     for ln in lines:
         f = ln.split()
-        if len(f) == 5 and not ln.startswith("#") and f[0] == workload and f[1] == kernel and f[2] == digest:
-            return int(f[3]) + int(f[4])
-    return None
+        if ln.startswith("#") or len(f) != 6 or f[0] != workload or f[1] not in stages:
+            continue
+        if kernel_digest(f[2]) != f[3]:
+            return None
+        total += int(f[4]) + int(f[5])
+        seen = True
+    return total * launches if seen else None
 
 
-def roofline_entry(w, kernel, what, work, stage_ms, ms, mfma_peak, traffic_kernel=None):
+def roofline_entry(w, kernel, what, work, stages, ms, mfma_peak):
     """Roofline of one stage: its algorithmic bytes and flops over its HIP-event
     time, against the larger of bytes / HBM peak and flops / MFMA peak."""
     byts, flops = work
     t = ms * 1e-3
     t_hbm, t_mfma = byts / (PEAK_HBM_GBS * 1e9), flops / (mfma_peak * 1e12)
-    traffic = measured_traffic(w.name, traffic_kernel or kernel)
-    e = {"kernel": kernel, "what": what, "stages": stage_ms, "avg_ms": round(ms, 4),
+    traffic = measured_traffic(w.name, stages)
+    e = {"kernel": kernel, "what": what, "stages": stages, "avg_ms": round(ms, 4),
          "algorithmic_bytes": byts, "algorithmic_flops": flops, "traffic": traffic,
          "traffic_over_algorithmic": None if traffic is None else round(traffic / byts, 3)}
     if t_hbm >= t_mfma:
@@ -249,8 +254,7 @@ def kernel_rooflines(w, stage_ms, counts, n_cu):
                                   "down grouped GEMM + sums of squares", algorithmic(w, n_active, "down"),
                                   ["down"], stage_ms["down"], peak))
     out.append(roofline_entry(w, dense, "unpooler GEMM", algorithmic(w, n_active, "unpool"), ["unpool"],
-                              stage_ms["unpool"], PEAK_BF16_TFLOPS,
-                              traffic_kernel=dense + ":unpool"))
+                              stage_ms["unpool"], PEAK_BF16_TFLOPS))
     return out
 
 
@@ -390,7 +394,7 @@ def nvfp4_convert(lmoe, torch, dev, E=256, Dp=4096, F=4096, reps=5):
     gbs = byts / (ms * 1e-3) / 1e9
     del bufs
     torch.cuda.empty_cache()
-    traffic = measured_traffic("nvfp4_to_mxfp4", "nvfp4_to_mxfp4_kernel")   # both launches
+    traffic = measured_traffic("nvfp4_to_mxfp4", ["convert"], launches=2)   # profiled per launch
     return {"workload": "nvfp4_to_mxfp4", "what": f"all {E} experts' gate/up and down weights, "
             "NVFP4 -> MXFP4 (load time, two launches)", "elements": n, "ms": round(ms, 4),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
