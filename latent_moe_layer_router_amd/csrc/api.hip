@@ -313,7 +313,7 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     g.out1 = logits;
     g.ldo1 = E;
     g.bias1 = W.b_router;
-    run(launch_gemm_grouped(g, EPI_F32, s));
+    run(launch_gemm_grouped(g, EPI_F32, n_cu, s));
   } else if (dense_stream && slices_in > 0) {
     DenseStreamParams d{};
     d.A = x;
@@ -527,7 +527,7 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     g.F = F;
     g.out = H;
     g.ldo = F;
-    run(launch_gemm_grouped(g, EPI_SWIGLU, s));
+    run(launch_gemm_grouped(g, EPI_SWIGLU, n_cu, s));
   } else {
     GemmParams g{};
     g.N = F;
@@ -614,7 +614,7 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     g.ldo = Dp;
     g.ss_out = ss;
     g.ss_ld = Dp / 64;
-    run(launch_gemm_grouped(g, EPI_DOWN, s));
+    run(launch_gemm_grouped(g, EPI_DOWN, n_cu, s));
   } else {
     GemmParams g{};
     g.N = Dp;
@@ -661,7 +661,7 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     g.n_split = D;
     g.out = out;
     g.ldo = D;
-    run(launch_gemm_grouped(g, out_f32 ? EPI_F32 : EPI_ACT, s));
+    run(launch_gemm_grouped(g, out_f32 ? EPI_F32 : EPI_ACT, n_cu, s));
   } else if (dense_stream && slices_un > 0) {
     DenseStreamParams d{};
     d.A = u;

@@ -81,6 +81,21 @@ __device__ __forceinline__ void mfma32(const uint4& a, const uint4& b, f32x16_t&
                                                 __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
 }
 
+// Two fp32 values rounded to bf16 by the packed hardware conversion (to
+// nearest, ties to even, as f32_to_bf16 rounds every finite value; a NaN stays
+// a NaN), the first in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, b16x2_t));
+}
+
+// silu(g) * u with the hardware exponential and reciprocal (a few ulp of fp32,
+// far below the bf16 rounding that follows).
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 // At most N global loads of this wave in flight (those issued after the last
 // one the next step needs) and no LDS read outstanding: the scheduler may move
 // the previous step's MFMAs (not their reads) past the barrier that follows.
@@ -96,105 +111,139 @@ __device__ __forceinline__ void bar() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Stage hand-off barrier of the epilogue's LDS staging: the LDS writes (or
+// reads) before it are complete; global memory is left alone, so the next
+// tile's first loads stay in flight.
+__device__ __forceinline__ void lds_bar() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Tile t: its expert (grouped), column tile and rows [m0, m_end).
+struct TileGeo {
+  int e, ntile, m0, m_end;
+};
+
+template <bool kDense>
+__device__ __forceinline__ TileGeo tile_geo(const GroupedParams& p, int t) {
+  TileGeo g;
+  g.e = 0;
+  if (kDense) {
+    // tiles (m-tile, n-tile) of an M x N product, M split evenly over ntiles_m
+    g.ntile = t % p.ntiles_n;
+    const int mi_t = t / p.ntiles_n;
+    g.m0 = (int)((int64_t)p.M * mi_t / p.ntiles_m);
+    g.m_end = (int)((int64_t)p.M * (mi_t + 1) / p.ntiles_m);
+  } else {
+    // tiles (expert, n-tile, m-tile) of the experts' sorted rows: expert e has
+    // ntiles_n * mt_off[e] <= t < ntiles_n * mt_off[e + 1]
+    int lo = 0, hi = p.E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.ntiles_n * p.mt_off[mid] <= t) lo = mid; else hi = mid;
+    }
+    g.e = lo;
+    // the expert's rows split evenly over its row tiles (each at most 320 rows)
+    const int mt_e = p.mt_off[lo + 1] - p.mt_off[lo];
+    const int tl = t - p.ntiles_n * p.mt_off[lo];
+    const int mi_t = tl % mt_e, cnt = p.offsets[lo + 1] - p.offsets[lo];
+    g.ntile = tl / mt_e;
+    g.m0 = p.offsets[lo] + (int)((int64_t)cnt * mi_t / mt_e);
+    g.m_end = p.offsets[lo] + (int)((int64_t)cnt * (mi_t + 1) / mt_e);
+  }
+  return g;
+}
+
+// Persistent: each workgroup (one per CU) walks tiles of its XCD's chunk of
+// the tile order, a fixed stride apart. A tile's first B stage and A step are
+// issued before the previous tile's epilogue, which stages its output through
+// the other buffers, so their latency hides behind it.
 template <int EPI>
 __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
 
-  // ---- tile of this workgroup (XCD-chunked order) --------------------------
-  // Grouped: tiles (expert, n-tile, m-tile) of the experts' sorted rows. Dense:
-  // tiles (m-tile, n-tile) of an M x N product, M split evenly over ntiles_m.
+  // ---- tiles of this workgroup (XCD-chunked order) -------------------------
   constexpr bool dense = (EPI == EPI_F32 || EPI == EPI_ACT);
   const int total = dense ? p.ntiles_m * p.ntiles_n : p.ntiles_n * p.mt_off[p.E];
   const int chunk = (total + 7) / 8;
-  const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
-  const int t = xcd * chunk + local;
-  if (local >= chunk || t >= total) return;
-  int e = 0, ntile, m0, m_end;
-  if (dense) {
-    ntile = t % p.ntiles_n;
-    const int mi_t = t / p.ntiles_n;
-    m0 = (int)((int64_t)p.M * mi_t / p.ntiles_m);
-    m_end = (int)((int64_t)p.M * (mi_t + 1) / p.ntiles_m);
-  } else {
-    int lo = 0, hi = p.E;                    // expert e: ntiles_n*mt_off[e] <= t < ntiles_n*mt_off[e+1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.ntiles_n * p.mt_off[mid] <= t) lo = mid; else hi = mid;
-    }
-    e = lo;
-    // the expert's rows split evenly over its row tiles (each at most 320 rows)
-    const int mt_e = p.mt_off[e + 1] - p.mt_off[e];
-    const int tl = t - p.ntiles_n * p.mt_off[e];
-    const int mi_t = tl % mt_e, cnt = p.offsets[e + 1] - p.offsets[e];
-    ntile = tl / mt_e;
-    m0 = p.offsets[e] + (int)((int64_t)cnt * mi_t / mt_e);
-    m_end = p.offsets[e] + (int)((int64_t)cnt * (mi_t + 1) / mt_e);
-  }
-  const int n0 = ntile * (EPI == EPI_SWIGLU ? GBN / 2 : GBN);   // output column start
-  // the tile's rows split between the wave rows: wm = 0 takes the first r_half
-  // (a multiple of 32, at least half), wm = 1 the rest; at most 160 each
-  const int tile_rows = m_end - m0;
-  const int r_half = 32 * ((((tile_rows + 1) >> 1) + 31) >> 5);
-  const int wrow0 = wm * r_half;
-  const int mrows = wm == 0 ? min(r_half, tile_rows) : tile_rows - r_half;
-  const int nmi = __builtin_amdgcn_readfirstlane(mrows <= 0 ? 0 : (mrows >= 32 * GMI ? GMI : (mrows + 31) / 32));
+  const int xcd = blockIdx.x % 8, stride = gridDim.x / 8;
+  int local = blockIdx.x / 8;
+  if (local >= chunk || xcd * chunk + local >= total) return;
+  TileGeo geo = tile_geo<dense>(p, xcd * chunk + local);
 
-  // ---- global-to-LDS loads --------------------------------------------------
-  const __amdgpu_buffer_rsrc_t rsA =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.A), (short)0, (int)p.a_bytes, kBufWord3);
-  // B rows of the tile: grouped, the expert's matrix (rows n0 + r, or the
-  // gate/up pairs); dense, the tile's own 256 rows from B (columns below
-  // n_split) or B1, the extent ending at row N (rows past it read as zero).
-  const bf16_t* Bt;
-  int b_ext;
-  if (dense) {
-    Bt = (n0 < p.n_split) ? static_cast<const bf16_t*>(p.B) + (int64_t)n0 * p.ldb
-                          : static_cast<const bf16_t*>(p.B1) + (int64_t)(n0 - p.n_split) * p.ldb;
-    b_ext = min(GBN, p.N - n0) * (int)p.ldb * 2;
-  } else {
-    Bt = static_cast<const bf16_t*>(p.B) + (int64_t)e * p.b_expert_stride;
-    b_ext = (int)p.b_bytes;
-  }
-  const __amdgpu_buffer_rsrc_t rsB =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(Bt), (short)0, b_ext, kBufWord3);
-  const int pos = lane & 3;
-  // Rows past the tile's end get an offset beyond every extent: the load reads
-  // nothing from memory. Those rows are never stored.
-  auto a_off = [&](int r) -> uint32_t {
-    const int m = m0 + r;
-    if (m >= m_end) return kOutOfRange;
-    const uint32_t c = pos ^ (((r >> 1) ^ (r >> 3)) & 3);
-    const int src = p.a_rows ? p.a_rows[m] : m;   // gathered rows (gate/up: the assignment's token)
-    return (uint32_t)src * (uint32_t)(p.lda * 2) + c * 16;
-  };
-  // B load j (of a stage) moves rows 8 j .. 8 j + 7, lane i row 8 j + i / 8 at
-  // chunk position i % 8 (which holds logical chunk (i % 8) ^ g(row)); wave w
-  // issues j = w, w + 8, w + 16, w + 24.
-  auto b_off = [&](int r) -> uint32_t {
-    const int n = dense ? r : (EPI == EPI_SWIGLU) ? ((r < GBN / 2) ? (n0 + r) : (p.F + n0 + r - GBN / 2)) : (n0 + r);
-    const uint32_t c = (lane & 7) ^ swz8(r);
-    return (uint32_t)n * (uint32_t)(p.ldb * 2) + c * 16;
-  };
-  // A load j (of a stage) moves rows 16 j .. 16 j + 15, lane i row 16 j + i / 4
-  // at chunk position i % 4; wave w issues j = w, w + 8, w + 16 (while j < 20)
-  uint32_t ga[3];
-#pragma unroll
-  for (int i = 0; i < 3; ++i) ga[i] = (wave + 8 * i < LA) ? a_off(16 * (wave + 8 * i) + (lane >> 2)) : kOutOfRange;
+  const int nk = p.K / 32;                   // a multiple of 4 (K % 128 == 0)
+  const int rowb = (int)p.ldb * 2;
   // The wave's four B loads (rows r, r + 64, r + 128, r + 192; the swizzle
   // depends on the row's low 4 bits only) differ by whole rows: one offset
   // register plus uniform row deltas in the scalar offset. SwiGLU rows 128..255
   // are the up rows, F - 128 further on.
-  const uint32_t gb0 = b_off(8 * wave + (lane >> 3));
-  const int rowb = (int)p.ldb * 2;
   const int up = (EPI == EPI_SWIGLU && !dense) ? (p.F - GBN / 2) * rowb : 0;
   const int gbd1 = 64 * rowb, gbd2 = 128 * rowb + up, gbd3 = 192 * rowb + up;
-  // Waves 0-3 issue a third A load (rows 256 + 16 wave ..) only if some of its
-  // rows are in the tile: a 256-row tile then moves 32 rows per K-step instead
-  // of 36 x 16. The LDS rows a skipped load would have filled are read only
-  // for output rows past the tile's end, which are never stored.
-  const bool three_a = wave + 16 < LA && 16 * (wave + 16) < tile_rows;
+
+  // ---- global-to-LDS loads of a tile ----------------------------------------
+  __amdgpu_buffer_rsrc_t rsA, rsB;
+  uint32_t ga[3], gb0;
+  bool three_a;
+  int krot;
+  auto setup_loads = [&](const TileGeo& g) {
+    // the lane index, opaque: the offsets below are computed here for each
+    // tile, not hoisted out of the tile loop and kept live across it
+    int ln = lane;
+    __asm__ volatile("" : "+v"(ln));
+    const int n0 = g.ntile * (EPI == EPI_SWIGLU ? GBN / 2 : GBN);
+    rsA = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.A), (short)0, (int)p.a_bytes, kBufWord3);
+    // B rows of the tile: grouped, the expert's matrix (rows n0 + r, or the
+    // gate/up pairs); dense, the tile's own 256 rows from B (columns below
+    // n_split) or B1, the extent ending at row N (rows past it read as zero).
+    const bf16_t* Bt;
+    int b_ext;
+    if (dense) {
+      Bt = (n0 < p.n_split) ? static_cast<const bf16_t*>(p.B) + (int64_t)n0 * p.ldb
+                            : static_cast<const bf16_t*>(p.B1) + (int64_t)(n0 - p.n_split) * p.ldb;
+      b_ext = min(GBN, p.N - n0) * (int)p.ldb * 2;
+    } else {
+      Bt = static_cast<const bf16_t*>(p.B) + (int64_t)g.e * p.b_expert_stride;
+      b_ext = (int)p.b_bytes;
+    }
+    rsB = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(Bt), (short)0, b_ext, kBufWord3);
+    // A load j (of a stage) moves rows 16 j .. 16 j + 15, lane i row 16 j + i / 4
+    // at chunk position i % 4; wave w issues j = w, w + 8, w + 16 (while j < 20).
+    // Rows past the tile's end get an offset beyond every extent: the load reads
+    // nothing from memory. Those rows are never stored.
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int r = 16 * (wave + 8 * i) + (ln >> 2);
+      const int m = g.m0 + r;
+      uint32_t o = kOutOfRange;
+      if (wave + 8 * i < LA && m < g.m_end) {
+        const uint32_t c = (ln & 3) ^ (((r >> 1) ^ (r >> 3)) & 3);
+        const int src = p.a_rows ? p.a_rows[m] : m;   // gathered rows (gate/up: the assignment's token)
+        o = (uint32_t)src * (uint32_t)(p.lda * 2) + c * 16;
+      }
+      ga[i] = o;
+    }
+    // B load j (of a stage) moves rows 8 j .. 8 j + 7, lane i row 8 j + i / 8 at
+    // chunk position i % 8 (which holds logical chunk (i % 8) ^ g(row)); wave w
+    // issues j = w, w + 8, w + 16, w + 24.
+    {
+      const int r = 8 * wave + (ln >> 3);
+      const int n = dense ? r : n0 + r;
+      gb0 = (uint32_t)n * (uint32_t)rowb + (uint32_t)(((ln & 7) ^ swz8(r)) << 4);
+    }
+    // Waves 0-3 issue a third A load (rows 256 + 16 wave ..) only if some of its
+    // rows are in the tile: a 256-row tile then moves 32 rows per K-step instead
+    // of 36 x 16. The LDS rows a skipped load would have filled are read only
+    // for output rows past the tile's end, which are never stored.
+    three_a = wave + 16 < LA && 16 * (wave + 16) < g.m_end - g.m0;
+    // Each column tile walks K from its own starting step (4 steps further per
+    // column tile), so that the tiles sharing a row tile's token slice request
+    // it a few steps apart. The order depends on the column tile only, so every
+    // output element is summed in one fixed order, whatever the batch.
+    krot = (g.ntile * 4) % nk;
+  };
 
 #define LMOE_LD(RS, OFF, DST, KO) \
   __builtin_amdgcn_raw_ptr_buffer_load_lds((RS), (LMOE_AS3 void*)(DST), 16, (int)(OFF), (KO), 0, 0);
@@ -232,53 +281,44 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
   if (three_a) wait_vm<3>();           \
   else wait_vm<2>();
 
-  f32x16_t acc[GMI][GNI];
-#pragma unroll
-  for (int mi = 0; mi < GMI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < GNI; ++ni)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
-
   // LDS rows of this lane's MFMA operands: A rows wrow0 + 32 mi + l32 (the
   // swizzle depends on a row's low 5 bits only); B rows: SwiGLU the gate (ni =
   // 0) and up (ni = 1) rows of the same 32 output columns, down 64 columns.
-  // One offset register per operand (ao for A, bo0 and bo1 for the two B
-  // fragments) walks the logical chunks in place: the second 16-wide K-slice
+  // The second B fragment's row is the first's plus 128 (SwiGLU) or 32 (down)
+  // rows, a multiple of 8 that leaves the swizzle alone: a constant byte
+  // offset. One offset register per operand (ao for A, bo0 for B) walks the
+  // logical chunks in place: the second 16-wide K-slice
   // of a step is the first's chunk with bit 1 set (byte offset XOR 32), a B
   // row's odd K-step its even one's with bit 2 set (XOR 64). The XORs are
   // opaque to the compiler, which otherwise keeps every variant (and their
   // sums with the buffers' LDS addresses) in registers and spills inside the
   // K loop.
-  const int l32 = lane & 31, half = lane >> 5;
-  auto brow_of = [&](int ni) {
-    return (EPI == EPI_SWIGLU) ? (ni * (GBN / 2) + wn * 32 + l32) : (wn * 64 + ni * 32 + l32);
-  };
-  int ao = swz(wrow0 + l32, half);           // A, first slice
-  int bo0 = swzb(brow_of(0), half), bo1 = swzb(brow_of(1), half);   // B, first slice, even step
+  constexpr int kB1Off = ((EPI == EPI_SWIGLU) ? GBN / 2 : 32) * RBB;
 #define LMOE_XOR(X, IMM) __asm__ volatile("v_xor_b32 %0, " #IMM ", %0" : "+v"(X))
 
   // Operand fragments: two register sets, so that the LDS reads of the next
   // 16-wide K-slice are in flight while the MFMAs of the current one run.
   uint4 xa0, xa1, xa2, xa3, xa4, xb0, xb1;
   uint4 ya0, ya1, ya2, ya3, ya4, yb0, yb1;
+  f32x16_t acc[GMI][GNI];
 
-#define LMOE_READ(NMI, SA, SBB, AO, B0, B1, PA, PB)                                               \
+#define LMOE_READ(NMI, SA, SBB, AO, B0, PA, PB)                                                   \
   if ((NMI) > 0) {                                                                              \
     PB##0 = *reinterpret_cast<const uint4*>((SBB) + (B0));                                      \
-    PB##1 = *reinterpret_cast<const uint4*>((SBB) + (B1));                                      \
+    PB##1 = *reinterpret_cast<const uint4*>((SBB) + (B0) + kB1Off);                             \
     PA##0 = *reinterpret_cast<const uint4*>((SA) + (AO));                                       \
   }                                                                                             \
   if ((NMI) > 1) PA##1 = *reinterpret_cast<const uint4*>((SA) + (AO) + 32 * RB);                \
   if ((NMI) > 2) PA##2 = *reinterpret_cast<const uint4*>((SA) + (AO) + 64 * RB);                \
   if ((NMI) > 3) PA##3 = *reinterpret_cast<const uint4*>((SA) + (AO) + 96 * RB);                \
   if ((NMI) > 4) PA##4 = *reinterpret_cast<const uint4*>((SA) + (AO) + 128 * RB);
-#define LMOE_MFMA(NMI, PA, PB)                                                                   \
-  if ((NMI) > 0) { mfma32(PA##0, PB##0, acc[0][0]); mfma32(PA##0, PB##1, acc[0][1]); }          \
-  if ((NMI) > 1) { mfma32(PA##1, PB##0, acc[1][0]); mfma32(PA##1, PB##1, acc[1][1]); }          \
-  if ((NMI) > 2) { mfma32(PA##2, PB##0, acc[2][0]); mfma32(PA##2, PB##1, acc[2][1]); }          \
-  if ((NMI) > 3) { mfma32(PA##3, PB##0, acc[3][0]); mfma32(PA##3, PB##1, acc[3][1]); }          \
-  if ((NMI) > 4) { mfma32(PA##4, PB##0, acc[4][0]); mfma32(PA##4, PB##1, acc[4][1]); }
+  // MFMAs of 32-row groups LO..HI-1 (of the NMI live ones)
+#define LMOE_MFMA(NMI, PA, PB, LO, HI)                                                                            \
+  if ((NMI) > 0 && 0 >= (LO) && 0 < (HI)) { mfma32(PA##0, PB##0, acc[0][0]); mfma32(PA##0, PB##1, acc[0][1]); } \
+  if ((NMI) > 1 && 1 >= (LO) && 1 < (HI)) { mfma32(PA##1, PB##0, acc[1][0]); mfma32(PA##1, PB##1, acc[1][1]); } \
+  if ((NMI) > 2 && 2 >= (LO) && 2 < (HI)) { mfma32(PA##2, PB##0, acc[2][0]); mfma32(PA##2, PB##1, acc[2][1]); } \
+  if ((NMI) > 3 && 3 >= (LO) && 3 < (HI)) { mfma32(PA##3, PB##0, acc[3][0]); mfma32(PA##3, PB##1, acc[3][1]); } \
+  if ((NMI) > 4 && 4 >= (LO) && 4 < (HI)) { mfma32(PA##4, PB##0, acc[4][0]); mfma32(PA##4, PB##1, acc[4][1]); }
   // K-step k: A of step k in SA, of step k + 1 in NA; B of step k in SBB at
   // parity PK (0: first K-step of the B stage, 1: second), of step k + 1 in
   // NBB. On entry A and B of step k are visible to all waves and the x
@@ -287,34 +327,36 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
   // and its own LDS reads, then the barrier: no wave reads step k's A buffer
   // any more (nor, at an odd step, its B buffer), so those take the loads
   // issued now (clamped to the last step or stage: a harmless re-read into a
-  // buffer no later step reads); reads the next step's first slice (x) and
-  // runs the second slice's MFMAs (y).
+  // buffer no later step reads). The first 32-row group's second-slice MFMAs
+  // go right after the barrier, ahead of the loads, to keep the matrix cores
+  // fed while the loads issue; then the next step's first slice is read (x)
+  // and the remaining second-slice MFMAs run (y).
 #define LMOE_STEP(NMI, k, PK, SA, SBB, NA, NBB)                                                  \
   {                                                                                             \
     LMOE_XOR(ao, 32);                                                                           \
     LMOE_XOR(bo0, 32);                                                                          \
-    LMOE_XOR(bo1, 32);                                                                          \
-    LMOE_READ(NMI, SA, SBB, ao, bo0, bo1, ya, yb)                                               \
+    LMOE_READ(NMI, SA, SBB, ao, bo0, ya, yb)                                               \
     __builtin_amdgcn_sched_barrier(0);                                                          \
-    LMOE_MFMA(NMI, xa, xb)                                                                      \
+    LMOE_MFMA(NMI, xa, xb, 0, GMI)                                                              \
     __builtin_amdgcn_sched_barrier(0);                                                          \
     if (PK) { LMOE_WAIT_ODD() } else { LMOE_WAIT_EVEN() }                                      \
     bar();                                                                                      \
+    LMOE_MFMA(NMI, ya, yb, 0, 1)                                                                \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
     if (PK) LMOE_ISSUE_B(((k) + 5) / 2 < nk / 2 ? ((k) + 5) / 2 : nk / 2 - 1, SBB)            \
     LMOE_ISSUE_A(((k) + 3 < nk ? (k) + 3 : nk - 1), SA)                                         \
     LMOE_XOR(ao, 32);                                                                           \
     LMOE_XOR(bo0, 96);                                                                          \
-    LMOE_XOR(bo1, 96);                                                                          \
-    LMOE_READ(NMI, NA, NBB, ao, bo0, bo1, xa, xb)                                               \
+    LMOE_READ(NMI, NA, NBB, ao, bo0, xa, xb)                                               \
     __builtin_amdgcn_sched_barrier(0);                                                          \
-    LMOE_MFMA(NMI, ya, yb)                                                                      \
+    LMOE_MFMA(NMI, ya, yb, 1, GMI)                                                              \
     __builtin_amdgcn_sched_barrier(0);                                                          \
   }
   // Six steps per iteration (the A buffers repeat every 3 steps, the B
   // buffers every 6), then up to four more (K-steps are a multiple of 4).
 #define LMOE_KLOOP(NMI)                                                                          \
   {                                                                                             \
-    LMOE_READ(NMI, gA0, gB0, ao, bo0, bo1, xa, xb)                                              \
+    LMOE_READ(NMI, gA0, gB0, ao, bo0, xa, xb)                                              \
     int k = 0;                                                                                  \
     for (; k + 6 <= nk; k += 6) {                                                               \
       LMOE_STEP(NMI, k, 0, gA0, gB0, gA1, gB0)                                                  \
@@ -334,34 +376,186 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
     }                                                                                           \
   }
 
-  const int nk = p.K / 32;                   // a multiple of 4 (K % 128 == 0)
-  // Each column tile walks K from its own starting step (4 steps further per
-  // column tile), so that the tiles sharing a row tile's token slice request it
-  // a few steps apart. The order depends on the column tile only, so every
-  // output element is summed in one fixed order, whatever the batch.
-  const int krot = (ntile * 4) % nk;
-  // Prologue: B stages 0..2 and A for steps 0..2 in the steady state's order
-  // (block k holds the B stage first), then wait for step 0's operands: A for
-  // step 0 and everything before it.
+  // The first tile's B stage 0 and A step 0 (later tiles get theirs during the
+  // previous tile's epilogue).
+  setup_loads(geo);
   LMOE_ISSUE_B(0, gB0)
-  LMOE_ISSUE_B((1 < nk / 2 ? 1 : nk / 2 - 1), gB1)
   LMOE_ISSUE_A(0, gA0)
-  LMOE_ISSUE_A(1, gA1)
-  LMOE_ISSUE_B((2 < nk / 2 ? 2 : nk / 2 - 1), gB2)
-  LMOE_ISSUE_A(2, gA2)
-  if (three_a) wait_vm<10>();
-  else wait_vm<8>();
-  bar();
-  // One K loop per number of live 32-row groups (uniform per wave; all waves
-  // run the same barriers): 5, 4 (3 groups run it too), 2 (1-2 groups), none.
-  if (nmi > 4) {
-    LMOE_KLOOP(5)
-  } else if (nmi > 2) {
-    LMOE_KLOOP(4)
-  } else if (nmi > 0) {
-    LMOE_KLOOP(2)
-  } else {
-    LMOE_KLOOP(0)
+  for (;;) {
+    const int m0 = geo.m0, m_end = geo.m_end;
+    const int n0 = geo.ntile * (EPI == EPI_SWIGLU ? GBN / 2 : GBN);   // output column start
+    // the tile's rows split between the wave rows: wm = 0 takes the first r_half
+    // (a multiple of 32, at least half), wm = 1 the rest; at most 160 each
+    const int tile_rows = m_end - m0;
+    const int r_half = 32 * ((((tile_rows + 1) >> 1) + 31) >> 5);
+    const int wrow0 = wm * r_half;
+    const int mrows = wm == 0 ? min(r_half, tile_rows) : tile_rows - r_half;
+    const int nmi = __builtin_amdgcn_readfirstlane(mrows <= 0 ? 0 : (mrows >= 32 * GMI ? GMI : (mrows + 31) / 32));
+    // The lane index, opaque per tile: what derives from it (fragment and
+    // staging offsets) is computed where it is used, not hoisted out of the
+    // tile loop and kept live across the K loop.
+    int ln = lane;
+    __asm__ volatile("" : "+v"(ln));
+    const int l32 = ln & 31, half = ln >> 5;
+    auto brow_of = [&](int ni) {
+      return (EPI == EPI_SWIGLU) ? (ni * (GBN / 2) + wn * 32 + l32) : (wn * 64 + ni * 32 + l32);
+    };
+
+    // Prologue, continued: B stages 1 and 2 and A for steps 1 and 2 (the
+    // steady state's block order), then wait for step 0's operands: B stage 0,
+    // A step 0 and whatever was issued between them and these (the previous
+    // tile's output stores).
+    LMOE_ISSUE_B((1 < nk / 2 ? 1 : nk / 2 - 1), gB1)
+    LMOE_ISSUE_A(1, gA1)
+    LMOE_ISSUE_B((2 < nk / 2 ? 2 : nk / 2 - 1), gB2)
+    LMOE_ISSUE_A(2, gA2)
+    if (three_a) wait_vm<14>();
+    else wait_vm<12>();
+    bar();
+
+#pragma unroll
+    for (int mi = 0; mi < GMI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < GNI; ++ni)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+    int ao = swz(wrow0 + l32, half);           // A, first slice
+    int bo0 = swzb(brow_of(0), half);          // B, first slice, even step
+
+    // One K loop per number of live 32-row groups (uniform per wave; all waves
+    // run the same barriers): 5, 4 (3 groups run it too), 2 (1-2 groups), none.
+    if (nmi > 4) {
+      LMOE_KLOOP(5)
+    } else if (nmi > 2) {
+      LMOE_KLOOP(4)
+    } else if (nmi > 0) {
+      LMOE_KLOOP(2)
+    } else {
+      LMOE_KLOOP(0)
+    }
+    // every load has landed (including the clamped re-reads of the last
+    // steps) and every wave has finished reading the buffers
+    __builtin_amdgcn_s_waitcnt(0);
+    bar();
+
+    // The next tile's first B stage and A step, into buffers the epilogue
+    // does not use.
+    local += stride;
+    const bool more = local < chunk && xcd * chunk + local < total;
+    if (more) {
+      geo = tile_geo<dense>(p, xcd * chunk + local);
+      setup_loads(geo);
+      LMOE_ISSUE_B(0, gB0)
+      LMOE_ISSUE_A(0, gA0)
+    }
+
+    if (EPI == EPI_F32) {
+      // fp32 out, straight from the accumulators: the 32 lanes of a half-wave
+      // store 32 consecutive columns of a row (128 bytes). Columns below n_split
+      // go to out, the rest to out1 plus bias1 (router logits).
+#pragma unroll
+      for (int mi = 0; mi < GMI; ++mi)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = mi * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          if (r >= mrows) continue;
+          const int m = m0 + wrow0 + r;
+#pragma unroll
+          for (int ni = 0; ni < GNI; ++ni) {
+            const int n = n0 + wn * 64 + ni * 32 + l32;
+            if (n >= p.N) continue;
+            if (n < p.n_split)
+              static_cast<float*>(p.out)[(int64_t)m * p.ldo + n] = acc[mi][ni][v];
+            else
+              p.out1[(int64_t)m * p.ldo1 + (n - p.n_split)] =
+                  acc[mi][ni][v] + (p.bias1 ? p.bias1[n - p.n_split] : 0.f);
+          }
+        }
+    } else {
+      // ---- epilogue, by wave row: stage [160][OBN] bf16 in LDS, 16-byte stores
+      // Rows [0, 64) of the staged half live in gB1, [64, 128) in gB2, [128,
+      // 160) in gA1 (rows of up to 512 bytes: 32 KiB, 32 KiB, 16 KiB); gA0 and
+      // gB0 take the next tile's first loads meanwhile.
+      constexpr int OBN = (EPI == EPI_SWIGLU) ? GBN / 2 : GBN;
+      constexpr int RBO = OBN * 2;            // bytes per staged row
+      constexpr int CPR = OBN / 8;            // 16-byte chunks per staged row
+      // Byte b of staged row r sits at b ^ ((r & 4) << 4): the two half-waves
+      // write rows four apart, which then land 64 bytes apart (different banks).
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (wm == h) {
+#pragma unroll
+          for (int mi = 0; mi < GMI; ++mi) {
+            // rows 32 mi .. 32 mi + 31 of the half: a buffer known at compile time
+            unsigned char* buf = mi < 2 ? gB1 : (mi < 4 ? gB2 : gA1);
+            // rows r and r + 1 (v, v + 1) in one packed conversion; both have
+            // the same bit 2, so the same swizzle
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) {
+              const int r = (mi & 1) * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+              unsigned char* row = buf + r * RBO;
+              const int sw = (r & 4) << 4;
+              if (EPI == EPI_SWIGLU) {
+                const uint32_t pk = pack_bf16x2(swiglu(acc[mi][0][v], acc[mi][1][v]),
+                                                swiglu(acc[mi][0][v + 1], acc[mi][1][v + 1]));
+                const int b = ((wn * 32 + l32) * 2) ^ sw;
+                *reinterpret_cast<bf16_t*>(row + b) = static_cast<bf16_t>(pk);
+                *reinterpret_cast<bf16_t*>(row + RBO + b) = static_cast<bf16_t>(pk >> 16);
+              } else {
+#pragma unroll
+                for (int ni = 0; ni < GNI; ++ni) {
+                  const uint32_t pk = pack_bf16x2(acc[mi][ni][v], acc[mi][ni][v + 1]);
+                  const int b = ((wn * 64 + ni * 32 + l32) * 2) ^ sw;
+                  *reinterpret_cast<bf16_t*>(row + b) = static_cast<bf16_t>(pk);
+                  *reinterpret_cast<bf16_t*>(row + RBO + b) = static_cast<bf16_t>(pk >> 16);
+                }
+              }
+            }
+          }
+        }
+        lds_bar();
+        // rows of this half: tile rows [h r_half, h r_half + hrows); staged
+        // rows [0, 64) in gB1, [64, 128) in gB2, [128, 160) in gA1
+        const int hrows = h == 0 ? min(r_half, tile_rows) : tile_rows - r_half;
+        const int mh = m0 + h * r_half;
+        // the thread index, opaque (as the lane index above)
+        int td = tid;
+        __asm__ volatile("" : "+v"(td));
+        auto store_rows = [&](const unsigned char* buf, int r_lo, int r_hi) {
+          for (int i = td; i < (r_hi - r_lo) * CPR; i += GNT) {
+            const int r = i / CPR, c = i % CPR;
+            if (dense && n0 + 8 * c >= p.N) continue;
+            *reinterpret_cast<uint4*>(static_cast<bf16_t*>(p.out) + (int64_t)(mh + r_lo + r) * p.ldo + n0 + 8 * c) =
+                *reinterpret_cast<const uint4*>(buf + r * RBO + ((c * 16) ^ ((r & 4) << 4)));
+          }
+          if (EPI == EPI_DOWN) {
+            // sums of squares of the stored bf16 values, per row and 64-column
+            // group: 8 lanes per (row, group), 16 bytes each (the groups of a
+            // row on consecutive lanes), then a sum over the 8 lanes. Whole
+            // 8-lane sets are active together (the bound is a multiple of 32).
+            for (int i = td; i < (r_hi - r_lo) * 32; i += GNT) {
+              const int r = i >> 5, grp = (i >> 3) & 3, sub = i & 7;
+              const uint4 q = *reinterpret_cast<const uint4*>(buf + r * RBO + ((grp * 128 + sub * 16) ^ ((r & 4) << 4)));
+              float ssq = 0.f;
+              for (uint32_t w : {q.x, q.y, q.z, q.w}) {
+                const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xFFFF0000u);
+                ssq += lo * lo;
+                ssq += hi * hi;
+              }
+              ssq += __shfl_xor(ssq, 1);
+              ssq += __shfl_xor(ssq, 2);
+              ssq += __shfl_xor(ssq, 4);
+              if (sub == 0) p.ss_out[(int64_t)(mh + r_lo + r) * p.ss_ld + n0 / 64 + grp] = ssq;
+            }
+          }
+        };
+        store_rows(gB1, 0, min(hrows, 64));
+        store_rows(gB2, 64, max(64, min(hrows, 128)));
+        store_rows(gA1, 128, max(128, hrows));
+        lds_bar();   // the half is read out before the next one (or the next tile's loads) overwrite it
+      }
+    }
+    if (!more) break;
   }
 #undef LMOE_KLOOP
 #undef LMOE_STEP
@@ -373,92 +567,6 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
 #undef LMOE_ISSUE_A
 #undef LMOE_ISSUE_B
 #undef LMOE_LD
-  __syncthreads();   // every load has landed and every wave has finished reading
-
-  if (EPI == EPI_F32) {
-    // fp32 out, straight from the accumulators: the 32 lanes of a half-wave
-    // store 32 consecutive columns of a row (128 bytes). Columns below n_split
-    // go to out, the rest to out1 plus bias1 (router logits).
-#pragma unroll
-    for (int mi = 0; mi < GMI; ++mi)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = mi * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-        if (r >= mrows) continue;
-        const int m = m0 + wrow0 + r;
-#pragma unroll
-        for (int ni = 0; ni < GNI; ++ni) {
-          const int n = n0 + wn * 64 + ni * 32 + l32;
-          if (n >= p.N) continue;
-          if (n < p.n_split)
-            static_cast<float*>(p.out)[(int64_t)m * p.ldo + n] = acc[mi][ni][v];
-          else
-            p.out1[(int64_t)m * p.ldo1 + (n - p.n_split)] =
-                acc[mi][ni][v] + (p.bias1 ? p.bias1[n - p.n_split] : 0.f);
-        }
-      }
-    return;
-  }
-
-  // ---- epilogue, by wave row: stage [160][OBN] bf16 in LDS, 16-byte stores ---
-  // Rows [32 q, 32 q + 32) of the staged half live in buffer q (gA0, gB0, gA1,
-  // gB1, gA2: at least 16 KiB each, 32 rows of up to 512 bytes).
-  constexpr int OBN = (EPI == EPI_SWIGLU) ? GBN / 2 : GBN;
-  auto srow = [&](int r) -> bf16_t* {
-    unsigned char* b;
-    switch (r >> 5) {
-      case 0: b = gA0; break;
-      case 1: b = gB0; break;
-      case 2: b = gA1; break;
-      case 3: b = gB1; break;
-      default: b = gA2; break;
-    }
-    return reinterpret_cast<bf16_t*>(b) + (r & 31) * OBN;
-  };
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (wm == h) {
-#pragma unroll
-      for (int mi = 0; mi < GMI; ++mi)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = mi * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          bf16_t* row = srow(r);
-          if (EPI == EPI_SWIGLU) {
-            const float g = acc[mi][0][v], u = acc[mi][1][v];
-            row[wn * 32 + l32] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
-          } else {
-#pragma unroll
-            for (int ni = 0; ni < GNI; ++ni) row[wn * 64 + ni * 32 + l32] = f32_to_bf16(acc[mi][ni][v]);
-          }
-        }
-    }
-    __syncthreads();
-    // rows of this half: tile rows [h r_half, h r_half + hrows)
-    const int hrows = h == 0 ? min(r_half, tile_rows) : tile_rows - r_half;
-    const int mh = m0 + h * r_half;
-    constexpr int CPR = OBN / 8;
-    for (int i = tid; i < hrows * CPR; i += GNT) {
-      const int r = i / CPR, c = (i % CPR) * 8;
-      if (dense && n0 + c >= p.N) continue;
-      *reinterpret_cast<uint4*>(static_cast<bf16_t*>(p.out) + (int64_t)(mh + r) * p.ldo + n0 + c) =
-          *reinterpret_cast<const uint4*>(srow(r) + c);
-    }
-    if (EPI == EPI_DOWN) {
-      // sums of squares of the stored bf16 values, per row and 64-column group
-      for (int i = tid; i < hrows * (GBN / 64); i += GNT) {
-        const int r = i / (GBN / 64), grp = i % (GBN / 64);
-        const bf16_t* row = srow(r) + grp * 64;
-        float ssq = 0.f;
-        for (int j = 0; j < 64; ++j) {
-          const float y = bf16_to_f32(row[j]);
-          ssq += y * y;
-        }
-        p.ss_out[(int64_t)(mh + r) * p.ss_ld + (n0 + grp * 64) / 64] = ssq;
-      }
-    }
-    __syncthreads();   // the half is read out before the next one is staged
-  }
 }
 
 }  // namespace
@@ -493,14 +601,17 @@ int gemm_grouped_dense_row_tiles(int M, int ntiles_n, int n_cu) {
   return best;
 }
 
-hipError_t launch_gemm_grouped(const GroupedParams& p, EpiKind epi, hipStream_t s) {
+hipError_t launch_gemm_grouped(const GroupedParams& p, EpiKind epi, int n_cu, hipStream_t s) {
   if (p.max_tiles <= 0) return hipSuccess;
   if (p.K % 128 != 0) return hipErrorInvalidValue;
   const bool dense = epi == EPI_F32 || epi == EPI_ACT;
   if (dense != (p.M > 0) || (dense && p.n_split < p.N && p.n_split % GBN != 0)) return hipErrorInvalidValue;
   if (dense && (p.ntiles_m < 1 || (int64_t)p.ntiles_m * GBM < p.M || p.ntiles_m * p.ntiles_n > p.max_tiles))
     return hipErrorInvalidValue;
-  const int grid = ((p.max_tiles + 7) / 8) * 8;
+  // persistent: at most one workgroup per compute unit (a multiple of 8, one
+  // per XCD in turn), never more than the tile bound
+  const int cap = n_cu >= 8 ? (n_cu / 8) * 8 : 8;
+  const int grid = min(((p.max_tiles + 7) / 8) * 8, cap);
   if (epi == EPI_SWIGLU)
     hipLaunchKernelGGL(gemm_grouped_kernel<EPI_SWIGLU>, dim3(grid), dim3(GNT), 0, s, p);
   else if (epi == EPI_DOWN)

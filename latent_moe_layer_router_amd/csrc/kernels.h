@@ -158,7 +158,8 @@ int gemm_grouped_tile_m();
 // Dense mode: the row-tile count for an M-row product with ntiles_n column
 // tiles on n_cu compute units (tiles of at most gemm_grouped_tile_m() rows).
 int gemm_grouped_dense_row_tiles(int M, int ntiles_n, int n_cu);
-hipError_t launch_gemm_grouped(const GroupedParams& p, EpiKind epi, hipStream_t s);
+// n_cu: compute units of the device (the persistent grid's size).
+hipError_t launch_gemm_grouped(const GroupedParams& p, EpiKind epi, int n_cu, hipStream_t s);
 
 // Grouped expert GEMMs of the MXFP4-expert path: MXFP8 E4M3 activations x
 // MXFP4 weights on the block-scaled MFMA. EPI_SWIGLU writes H as MXFP8 (codes
