@@ -27,15 +27,19 @@
 // are read (156 KiB in all). The weights come from HBM on their first touch,
 // the token rows mostly from L2: the weights run further ahead, and whole-line
 // loads halve their requests for the same bytes. A stage of A is 20 loads of
-// 16 rows x 64 bytes (wave w issues loads w, w + 8, w + 16: waves 0-3 three,
-// waves 4-7 two; A loads wholly past the tile's last row are skipped); a
-// stage of B is 32 loads of 8 rows x 128 bytes, four per wave. The 16-byte
-// chunks of each row are XOR-swizzled so that fragment reads are
-// conflict-free.
+// 16 rows x 64 bytes (wave w issues loads w, w + 8, w + 16; waves 4-7's third
+// has no rows, and rows past the tile's last row read nothing); a stage of B is
+// 32 loads of 8 rows x 128 bytes, four per wave. The 16-byte chunks of each
+// row are XOR-swizzled so that fragment reads are conflict-free. Between two
+// barriers each wave's loads and LDS reads are interleaved one by one with its
+// MFMAs.
 //
 // Tile order over the 8 XCDs: one index space (expert, n-tile, m-tile) cut
 // into 8 contiguous chunks, one per XCD, so that the CUs of an XCD share the
-// expert's weight slices and token rows in their L2.
+// expert's weight slices and token rows in their L2. The workgroups are
+// persistent (one per CU, each walking its XCD's chunk at a stride of the
+// XCD's workgroup count), and a tile's first loads are issued before the
+// previous tile's epilogue.
 #include "common.h"
 #include "kernels.h"
 
@@ -61,6 +65,10 @@ constexpr uint32_t kOutOfRange = 0x80000000u;   // past every extent used here
 // flight.
 __shared__ __attribute__((aligned(16))) unsigned char gA0[GSA], gB0[GSB], gA1[GSA], gB1[GSB],
     gA2[GSA], gB2[GSB];
+// Target of the third A load of waves 4-7, which has no rows to move (1 KiB
+// per wave; the 160 KiB of LDS in all): every wave then issues the same loads,
+// and the K loop has no branch to split its instruction scheduling.
+__shared__ __attribute__((aligned(16))) unsigned char gAx[4 * 1024];
 
 // Byte offset of logical 16-byte chunk c (0..3) of tile row r (64-byte rows),
 // stored at position c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3: 32 lanes on 32
@@ -186,7 +194,6 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
   // ---- global-to-LDS loads of a tile ----------------------------------------
   __amdgpu_buffer_rsrc_t rsA, rsB;
   uint32_t ga[3], gb0;
-  bool three_a;
   int krot;
   auto setup_loads = [&](const TileGeo& g) {
     // the lane index, opaque: the offsets below are computed here for each
@@ -210,9 +217,10 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
     }
     rsB = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(Bt), (short)0, b_ext, kBufWord3);
     // A load j (of a stage) moves rows 16 j .. 16 j + 15, lane i row 16 j + i / 4
-    // at chunk position i % 4; wave w issues j = w, w + 8, w + 16 (while j < 20).
-    // Rows past the tile's end get an offset beyond every extent: the load reads
-    // nothing from memory. Those rows are never stored.
+    // at chunk position i % 4; wave w issues j = w, w + 8, w + 16 (j < 20; the
+    // third load of waves 4-7 has no rows and goes to gAx). Rows past the
+    // tile's end get an offset beyond every extent: the load reads nothing from
+    // memory. Those rows are never stored.
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       const int r = 16 * (wave + 8 * i) + (ln >> 2);
@@ -233,11 +241,6 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
       const int n = dense ? r : n0 + r;
       gb0 = (uint32_t)n * (uint32_t)rowb + (uint32_t)(((ln & 7) ^ swz8(r)) << 4);
     }
-    // Waves 0-3 issue a third A load (rows 256 + 16 wave ..) only if some of its
-    // rows are in the tile: a 256-row tile then moves 32 rows per K-step instead
-    // of 36 x 16. The LDS rows a skipped load would have filled are read only
-    // for output rows past the tile's end, which are never stored.
-    three_a = wave + 16 < LA && 16 * (wave + 16) < g.m_end - g.m0;
     // Each column tile walks K from its own starting step (4 steps further per
     // column tile), so that the tiles sharing a row tile's token slice request
     // it a few steps apart. The order depends on the column tile only, so every
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
     const int ko = (kr_ >= nk ? kr_ - nk : kr_) * RB;                                                  \
     LMOE_LD(rsA, ga[0], (SA) + wave * 16 * RB, ko)                                                     \
     LMOE_LD(rsA, ga[1], (SA) + (wave + 8) * 16 * RB, ko)                                               \
-    if (three_a) LMOE_LD(rsA, ga[2], (SA) + (wave + 16) * 16 * RB, ko)                                 \
+    LMOE_LD(rsA, ga[2], (wave < 4) ? (SA) + (wave + 16) * 16 * RB : gAx + (wave - 4) * 1024, ko)      \
   }
   // B for K-steps 2 st and 2 st + 1 (rotated; krot is even, so the pair never
   // wraps), into buffer SBB
@@ -272,14 +275,9 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
   // in issue order, so a wait lets through the blocks issued after the last
   // load it needs, which is always A for step k + 1 (block k - 2; the B stage
   // holding step k + 1 came earlier): block k - 1, that is one A block, plus
-  // one B stage when k - 1 is odd. A blocks are 3 loads (waves with three_a)
-  // or 2, B stages 4.
-#define LMOE_WAIT_EVEN()               \
-  if (three_a) wait_vm<7>();           \
-  else wait_vm<6>();
-#define LMOE_WAIT_ODD()                \
-  if (three_a) wait_vm<3>();           \
-  else wait_vm<2>();
+  // one B stage when k - 1 is odd. A blocks are 3 loads, B stages 4.
+#define LMOE_WAIT_EVEN() wait_vm<7>();
+#define LMOE_WAIT_ODD() wait_vm<3>();
 
   // LDS rows of this lane's MFMA operands: A rows wrow0 + 32 mi + l32 (the
   // swizzle depends on a row's low 5 bits only); B rows: SwiGLU the gate (ni =
@@ -319,37 +317,46 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
   if ((NMI) > 2 && 2 >= (LO) && 2 < (HI)) { mfma32(PA##2, PB##0, acc[2][0]); mfma32(PA##2, PB##1, acc[2][1]); } \
   if ((NMI) > 3 && 3 >= (LO) && 3 < (HI)) { mfma32(PA##3, PB##0, acc[3][0]); mfma32(PA##3, PB##1, acc[3][1]); } \
   if ((NMI) > 4 && 4 >= (LO) && 4 < (HI)) { mfma32(PA##4, PB##0, acc[4][0]); mfma32(PA##4, PB##1, acc[4][1]); }
+  // Scheduling of a stretch between two barriers: NM MFMAs, each followed by
+  // up to one global-to-LDS load (the first NV) and one LDS read (the first
+  // ND), so that a wave issues its loads and reads while its matrix core works
+  // instead of in a burst that leaves it idle (both waves of a SIMD reach the
+  // same barrier, so the other wave cannot fill the gap).
+#define LMOE_INTERLEAVE(NM, NV, ND)                                                              \
+  {                                                                                             \
+    _Pragma("unroll") for (int q_ = 0; q_ < (NM); ++q_) {                                        \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
+      if (q_ < (NV)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                          \
+      if (q_ < (ND)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                          \
+    }                                                                                           \
+  }
   // K-step k: A of step k in SA, of step k + 1 in NA; B of step k in SBB at
   // parity PK (0: first K-step of the B stage, 1: second), of step k + 1 in
   // NBB. On entry A and B of step k are visible to all waves and the x
   // registers hold the step's first K-slice. The step reads the second slice
-  // (y) and runs the first slice's MFMAs (x); waits for step k + 1's operands
+  // (y) while the first slice's MFMAs run (x); waits for step k + 1's operands
   // and its own LDS reads, then the barrier: no wave reads step k's A buffer
   // any more (nor, at an odd step, its B buffer), so those take the loads
   // issued now (clamped to the last step or stage: a harmless re-read into a
-  // buffer no later step reads). The first 32-row group's second-slice MFMAs
-  // go right after the barrier, ahead of the loads, to keep the matrix cores
-  // fed while the loads issue; then the next step's first slice is read (x)
-  // and the remaining second-slice MFMAs run (y).
+  // buffer no later step reads), which go out with the next step's first-slice
+  // reads (x) between the second slice's MFMAs (y).
 #define LMOE_STEP(NMI, k, PK, SA, SBB, NA, NBB)                                                  \
   {                                                                                             \
     LMOE_XOR(ao, 32);                                                                           \
     LMOE_XOR(bo0, 32);                                                                          \
-    LMOE_READ(NMI, SA, SBB, ao, bo0, ya, yb)                                               \
-    __builtin_amdgcn_sched_barrier(0);                                                          \
+    LMOE_READ(NMI, SA, SBB, ao, bo0, ya, yb)                                                    \
     LMOE_MFMA(NMI, xa, xb, 0, GMI)                                                              \
+    LMOE_INTERLEAVE(2 * (NMI), 0, (NMI) > 0 ? 2 + (NMI) : 0)                                    \
     __builtin_amdgcn_sched_barrier(0);                                                          \
-    if (PK) { LMOE_WAIT_ODD() } else { LMOE_WAIT_EVEN() }                                      \
-    bar();                                                                                      \
-    LMOE_MFMA(NMI, ya, yb, 0, 1)                                                                \
-    __builtin_amdgcn_sched_barrier(0);                                                          \
-    if (PK) LMOE_ISSUE_B(((k) + 5) / 2 < nk / 2 ? ((k) + 5) / 2 : nk / 2 - 1, SBB)            \
-    LMOE_ISSUE_A(((k) + 3 < nk ? (k) + 3 : nk - 1), SA)                                         \
     LMOE_XOR(ao, 32);                                                                           \
     LMOE_XOR(bo0, 96);                                                                          \
-    LMOE_READ(NMI, NA, NBB, ao, bo0, xa, xb)                                               \
-    __builtin_amdgcn_sched_barrier(0);                                                          \
-    LMOE_MFMA(NMI, ya, yb, 1, GMI)                                                              \
+    if (PK) { LMOE_WAIT_ODD() } else { LMOE_WAIT_EVEN() }                                      \
+    bar();                                                                                      \
+    if (PK) LMOE_ISSUE_B(((k) + 5) / 2 < nk / 2 ? ((k) + 5) / 2 : nk / 2 - 1, SBB)            \
+    LMOE_ISSUE_A(((k) + 3 < nk ? (k) + 3 : nk - 1), SA)                                         \
+    LMOE_READ(NMI, NA, NBB, ao, bo0, xa, xb)                                                    \
+    LMOE_MFMA(NMI, ya, yb, 0, GMI)                                                              \
+    LMOE_INTERLEAVE(2 * (NMI), (PK) ? 7 : 3, (NMI) > 0 ? 2 + (NMI) : 0)                         \
     __builtin_amdgcn_sched_barrier(0);                                                          \
   }
   // Six steps per iteration (the A buffers repeat every 3 steps, the B
@@ -409,8 +416,7 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
     LMOE_ISSUE_A(1, gA1)
     LMOE_ISSUE_B((2 < nk / 2 ? 2 : nk / 2 - 1), gB2)
     LMOE_ISSUE_A(2, gA2)
-    if (three_a) wait_vm<14>();
-    else wait_vm<12>();
+    wait_vm<14>();
     bar();
 
 #pragma unroll
@@ -559,6 +565,7 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
   }
 #undef LMOE_KLOOP
 #undef LMOE_STEP
+#undef LMOE_INTERLEAVE
 #undef LMOE_MFMA
 #undef LMOE_READ
 #undef LMOE_XOR
