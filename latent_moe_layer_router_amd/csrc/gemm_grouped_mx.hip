@@ -85,6 +85,20 @@ __device__ __forceinline__ void mfma_mx(const uint4& a0, const uint4& a1, const 
   acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 4, 0, sa, 0, sb);
 }
 
+// Two fp32 values rounded to bf16 by the packed hardware conversion (to
+// nearest, ties to even, as f32_to_bf16 rounds every finite value; a NaN stays
+// a NaN), the first in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, b16x2_t));
+}
+
+// silu(g) * u with the hardware exponential and reciprocal (a few ulp of fp32).
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 // s_waitcnt immediate: no vector-memory and no LDS operation outstanding.
 constexpr int kAllIdle = 7 << 4;
 
@@ -310,7 +324,7 @@ __global__ __launch_bounds__(XNT, 1) void gemm_grouped_mx_kernel(GroupedMxParams
 
   // ---- epilogue, by wave row (up to 160 rows each) ---------------------------
   // The staging area spans the two A stage buffers: rows [80 b, 80 b + 80) of
-  // the half live in buffer b, 512 bytes per row.
+  // the half live in buffer b, 512 bytes per row (128 fp32 or 256 bf16).
   auto srow = [&](int r) -> unsigned char* { return (r < 80 ? xA0 : xA1) + (r < 80 ? r : r - 80) * 512; };
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -318,21 +332,30 @@ __global__ __launch_bounds__(XNT, 1) void gemm_grouped_mx_kernel(GroupedMxParams
 #pragma unroll
       for (int mi = 0; mi < XMI; ++mi)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < 16; v += 2) {
+          // rows r and r + 1 (v, v + 1); both have the same bit 2
           const int r = mi * 32 + 8 * (v >> 2) + 4 * q + (v & 3);
           unsigned char* row = srow(r);
+          unsigned char* row1 = srow(r + 1);
           if (EPI == EPI_SWIGLU) {
             // fp32 h at column c (0..127), 16-byte chunk c / 4 stored at
             // position (c / 4) ^ (r & 7) of the row
-            const float g = acc[mi][0][v], u = acc[mi][1][v];
             const int c = wn * 32 + l32;
             *reinterpret_cast<float*>(row + ((((c >> 2) ^ (r & 7)) << 4) | ((c & 3) << 2))) =
-                g / (1.0f + __expf(-g)) * u;
+                swiglu(acc[mi][0][v], acc[mi][1][v]);
+            *reinterpret_cast<float*>(row1 + ((((c >> 2) ^ ((r + 1) & 7)) << 4) | ((c & 3) << 2))) =
+                swiglu(acc[mi][0][v + 1], acc[mi][1][v + 1]);
           } else {
-            // bf16 y at column c (0..255)
+            // bf16 y at column c (0..255), byte b of row r at b ^ ((r & 4) << 4):
+            // the two half-waves write rows four apart, 64 bytes apart
+            const int sw = (r & 4) << 4;
 #pragma unroll
-            for (int ni = 0; ni < XNI; ++ni)
-              reinterpret_cast<bf16_t*>(row)[wn * 64 + ni * 32 + l32] = f32_to_bf16(acc[mi][ni][v]);
+            for (int ni = 0; ni < XNI; ++ni) {
+              const uint32_t pk = pack_bf16x2(acc[mi][ni][v], acc[mi][ni][v + 1]);
+              const int b = ((wn * 64 + ni * 32 + l32) * 2) ^ sw;
+              *reinterpret_cast<bf16_t*>(row + b) = static_cast<bf16_t>(pk);
+              *reinterpret_cast<bf16_t*>(row1 + b) = static_cast<bf16_t>(pk >> 16);
+            }
           }
         }
     }
@@ -341,48 +364,46 @@ __global__ __launch_bounds__(XNT, 1) void gemm_grouped_mx_kernel(GroupedMxParams
     const int hrows = half == 0 ? min(r_half, tile_rows) : tile_rows - r_half;
     const int mh = m0 + half * r_half;
     if (EPI == EPI_SWIGLU) {
-      // one thread per (row, block of 32 columns): quantize to MXFP8 E4M3
-      for (int item = tid; item < hrows * 4; item += XNT) {
-        const int r = item >> 2, blk = item & 3;
-        const unsigned char* row = srow(r);
-        float v[32];
-#pragma unroll
-        for (int c4 = 0; c4 < 8; ++c4) {
-          const float4 f = *reinterpret_cast<const float4*>(row + (((blk * 8 + c4) ^ (r & 7)) << 4));
-          v[4 * c4] = f.x; v[4 * c4 + 1] = f.y; v[4 * c4 + 2] = f.z; v[4 * c4 + 3] = f.w;
-        }
-        float amax = 0.f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      // MXFP8 E4M3 blocks of 32 values: 8 lanes per (row, block), 4 values
+      // (one 16-byte chunk) each; the block's largest magnitude over the 8
+      // lanes, then each lane's 4 codes in one 32-bit store. Whole 8-lane sets
+      // are active together (the bound is a multiple of 32).
+      for (int i = tid; i < hrows * 32; i += XNT) {
+        const int r = i >> 5, blk = (i >> 3) & 3, sub = i & 7;
+        const float4 f = *reinterpret_cast<const float4*>(srow(r) + (((blk * 8 + sub) ^ (r & 7)) << 4));
+        float amax = fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w)));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        amax = fmaxf(amax, __shfl_xor(amax, 4));
         const int X = mx_e4m3_exponent(amax);
-        uint32_t w[8];
-#pragma unroll
-        for (int d = 0; d < 8; ++d)
-          w[d] = (uint32_t)mx_e4m3_code(v[4 * d], X) | ((uint32_t)mx_e4m3_code(v[4 * d + 1], X) << 8) |
-                 ((uint32_t)mx_e4m3_code(v[4 * d + 2], X) << 16) |
-                 ((uint32_t)mx_e4m3_code(v[4 * d + 3], X) << 24);
-        uint8_t* dst = static_cast<uint8_t*>(p.out) + (int64_t)(mh + r) * p.ldo + n0 + 32 * blk;
-        reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
-        p.out_scales[(int64_t)(mh + r) * p.ldos + n0 / 32 + blk] = mx_scale_code(X);
+        const uint32_t w = (uint32_t)mx_e4m3_code(f.x, X) | ((uint32_t)mx_e4m3_code(f.y, X) << 8) |
+                           ((uint32_t)mx_e4m3_code(f.z, X) << 16) | ((uint32_t)mx_e4m3_code(f.w, X) << 24);
+        uint8_t* dst = static_cast<uint8_t*>(p.out) + (int64_t)(mh + r) * p.ldo + n0 + 32 * blk + 4 * sub;
+        *reinterpret_cast<uint32_t*>(dst) = w;
+        if (sub == 0) p.out_scales[(int64_t)(mh + r) * p.ldos + n0 / 32 + blk] = mx_scale_code(X);
       }
     } else {
       // 16-byte stores of the bf16 rows, then the sums of squares of the stored
-      // values per row and 64-column group
+      // values per row and 64-column group: 8 lanes per (row, group), 16 bytes
+      // each (a row's groups on consecutive lanes), then a sum over the 8 lanes
       for (int i = tid; i < hrows * (XBN / 8); i += XNT) {
-        const int r = i / (XBN / 8), c = (i % (XBN / 8)) * 8;
-        *reinterpret_cast<uint4*>(static_cast<bf16_t*>(p.out) + (int64_t)(mh + r) * p.ldo + n0 + c) =
-            *reinterpret_cast<const uint4*>(srow(r) + 2 * c);
+        const int r = i / (XBN / 8), c = i % (XBN / 8);
+        *reinterpret_cast<uint4*>(static_cast<bf16_t*>(p.out) + (int64_t)(mh + r) * p.ldo + n0 + 8 * c) =
+            *reinterpret_cast<const uint4*>(srow(r) + ((c * 16) ^ ((r & 4) << 4)));
       }
-      for (int i = tid; i < hrows * (XBN / 64); i += XNT) {
-        const int r = i / (XBN / 64), grp = i % (XBN / 64);
-        const bf16_t* row = reinterpret_cast<const bf16_t*>(srow(r)) + grp * 64;
+      for (int i = tid; i < hrows * 32; i += XNT) {
+        const int r = i >> 5, grp = (i >> 3) & 3, sub = i & 7;
+        const uint4 qv = *reinterpret_cast<const uint4*>(srow(r) + ((grp * 128 + sub * 16) ^ ((r & 4) << 4)));
         float ssq = 0.f;
-        for (int j = 0; j < 64; ++j) {
-          const float y = bf16_to_f32(row[j]);
-          ssq += y * y;
+        for (uint32_t w : {qv.x, qv.y, qv.z, qv.w}) {
+          const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xFFFF0000u);
+          ssq += lo * lo;
+          ssq += hi * hi;
         }
-        p.ss_out[(int64_t)(mh + r) * p.ss_ld + (n0 + grp * 64) / 64] = ssq;
+        ssq += __shfl_xor(ssq, 1);
+        ssq += __shfl_xor(ssq, 2);
+        ssq += __shfl_xor(ssq, 4);
+        if (sub == 0) p.ss_out[(int64_t)(mh + r) * p.ss_ld + n0 / 64 + grp] = ssq;
       }
     }
     __syncthreads();   // the half is read out before the next one is staged

@@ -34,7 +34,10 @@ __device__ __forceinline__ uint8_t mx_e4m3_code(float v, int X) {
     if (((__float_as_uint(a) >> 23) & 0xFF) == 0) e = -127;
     if (e < -6) e = -6;                                            // subnormal range: step 2^-9
     const float step = __uint_as_float((uint32_t)(e - 3 + 127) << 23);
-    float q = __builtin_rintf(a / step) * step;                    // ties to even
+    // a / step is a power-of-two scaling (exact either way): multiply by the
+    // exact reciprocal instead of dividing
+    const float inv_step = __uint_as_float((uint32_t)(3 - e + 127) << 23);
+    float q = __builtin_rintf(a * inv_step) * step;                // ties to even
     if (q > 448.f) q = 448.f;
     if (q > 0.f) {
       const int qe = (int)((__float_as_uint(q) >> 23) & 0xFF) - 127;
