@@ -376,8 +376,7 @@ __global__ __launch_bounds__(XNT, 1) void gemm_grouped_mx_kernel(GroupedMxParams
         amax = fmaxf(amax, __shfl_xor(amax, 2));
         amax = fmaxf(amax, __shfl_xor(amax, 4));
         const int X = mx_e4m3_exponent(amax);
-        const uint32_t w = (uint32_t)mx_e4m3_code(f.x, X) | ((uint32_t)mx_e4m3_code(f.y, X) << 8) |
-                           ((uint32_t)mx_e4m3_code(f.z, X) << 16) | ((uint32_t)mx_e4m3_code(f.w, X) << 24);
+        const uint32_t w = mx_e4m3_code4(f.x, f.y, f.z, f.w, X);
         uint8_t* dst = static_cast<uint8_t*>(p.out) + (int64_t)(mh + r) * p.ldo + n0 + 32 * blk + 4 * sub;
         *reinterpret_cast<uint32_t*>(dst) = w;
         if (sub == 0) p.out_scales[(int64_t)(mh + r) * p.ldos + n0 / 32 + blk] = mx_scale_code(X);

@@ -52,6 +52,24 @@ __device__ __forceinline__ uint8_t mx_e4m3_code(float v, int X) {
   return (uint8_t)(code | (v < 0.f ? 0x80 : 0));
 }
 
+// Four E4M3 codes of v0..v3 / 2^X, exactly as mx_e4m3_code gives them, packed
+// into 32 bits (v0 in the low byte), by gfx950's packed fp8 conversion (OCP
+// E4M3, to nearest, ties to even) of the scaled values with the codec's
+// conventions applied first: a NaN codes as +0, magnitudes saturate at 448,
+// and -0 codes as +0 (checked against mx_e4m3_code on 2^24 values at seven
+// scales, edge values included).
+__device__ __forceinline__ uint32_t mx_e4m3_code4(float v0, float v1, float v2, float v3, int X) {
+  const float s = __uint_as_float((uint32_t)(127 - X) << 23 & 0x7F800000u);
+  auto prep = [s](float v) {
+    float a = v * s;
+    a = (a == a) ? a : 0.f;
+    return fminf(fmaxf(a, -448.f), 448.f) + 0.f;
+  };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(prep(v0), prep(v1), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(prep(v2), prep(v3), w, true);
+  return (uint32_t)w;
+}
+
 // The scale argument of X: an E8M0 byte.
 __device__ __forceinline__ uint8_t mx_scale_code(int X) { return (uint8_t)(X + 127); }
 

@@ -93,8 +93,7 @@ __device__ __forceinline__ void mx_store_block(const float (&v)[32], uint8_t* co
   uint32_t w[8];
 #pragma unroll
   for (int d = 0; d < 8; ++d)
-    w[d] = (uint32_t)mx_e4m3_code(v[4 * d], X) | ((uint32_t)mx_e4m3_code(v[4 * d + 1], X) << 8) |
-           ((uint32_t)mx_e4m3_code(v[4 * d + 2], X) << 16) | ((uint32_t)mx_e4m3_code(v[4 * d + 3], X) << 24);
+    w[d] = mx_e4m3_code4(v[4 * d], v[4 * d + 1], v[4 * d + 2], v[4 * d + 3], X);
   reinterpret_cast<uint4*>(codes)[0] = make_uint4(w[0], w[1], w[2], w[3]);
   reinterpret_cast<uint4*>(codes)[1] = make_uint4(w[4], w[5], w[6], w[7]);
   *scale = mx_scale_code(X);

@@ -241,8 +241,9 @@ __device__ __forceinline__ void stream_mx_body(const StreamMxParams& p, int e, i
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
         const int X = mx_e4m3_exponent(amax);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) stile[i * 32 + h * 16 + r16] = mx_e4m3_code(hv[h], X);
+        const uint32_t c2 = mx_e4m3_code4(hv[0], hv[1], 0.f, 0.f, X);
+        stile[i * 32 + r16] = (uint8_t)c2;
+        stile[i * 32 + 16 + r16] = (uint8_t)(c2 >> 8);
         if (r16 == 0 && i < m_e) p.out_scales[(int64_t)(lo + i) * p.ldos + grp] = mx_scale_code(X);
       }
     }
