@@ -31,8 +31,8 @@ DEV = "cuda:0"
 def quant_inputs(seed=7):
     """fp32 blocks of 32 covering the codec's cases: normal data at scales from
     2^-30 to 2^30, an all-zero block, exact ties of the E4M3 grid, values that
-    saturate at 448, values in the E4M3 subnormal range, and extreme blocks
-    (largest finite floats, fp32 subnormals)."""
+    saturate at 448, values in the E4M3 subnormal range, extreme blocks
+    (largest finite floats, fp32 subnormals), and signed zeros and NaNs."""
     rng = np.random.default_rng(seed)
     blocks = []
     for e in range(-30, 31, 3):
@@ -58,6 +58,12 @@ def quant_inputs(seed=7):
     # extremes
     blocks.append(rng.uniform(-3.4e38, 3.4e38, (1, 32)))
     blocks.append(rng.uniform(-1e-40, 1e-40, (1, 32)))
+    # signed zeros and NaNs: -0 codes as +0, a NaN codes as +0 and is left out
+    # of the block maximum
+    b = rng.standard_normal(32) * 4.0
+    b[[1, 7, 20]] = -0.0
+    b[[3, 11]] = np.nan
+    blocks.append(b[None, :])
     v = np.concatenate(blocks).astype(np.float32).ravel()
     return v
 
