@@ -120,8 +120,10 @@ __device__ __forceinline__ void bar() {
 }
 
 // Stage hand-off barrier of the epilogue's LDS staging: the LDS writes (or
-// reads) before it are complete; global memory is left alone, so the next
-// tile's first loads stay in flight.
+// reads) before it are complete. The release fence also covers this wave's
+// global-to-LDS loads (their LDS writes count), so the next tile's first loads
+// have landed by the first staging barrier; they land during the staging
+// anyway (a barrier without that wait measured the same).
 __device__ __forceinline__ void lds_bar() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
