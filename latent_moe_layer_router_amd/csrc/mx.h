@@ -26,6 +26,8 @@ __device__ __forceinline__ int mx_e4m3_exponent(float amax) {
 // E4M3 code (OCP: bias 7, max 448, no infinities) of v / 2^X: nearest, ties to
 // even, saturating. v / 2^X is formed exactly (a power-of-two scaling of a
 // float whose result is either exact or far below the smallest E4M3 step).
+// The codec's definition in plain arithmetic: the kernels call the packed
+// hardware form below (mx_e4m3_code4), which was checked against this one.
 __device__ __forceinline__ uint8_t mx_e4m3_code(float v, int X) {
   const float a = fabsf(v) * __uint_as_float((uint32_t)(127 - X) << 23 & 0x7F800000u);
   uint8_t code = 0;
