@@ -48,10 +48,45 @@ __device__ __forceinline__ void store8(float* dst, const float (&v)[8]) {
   reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
   reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
+// Store 4 consecutive values as bf16 (one 8-byte store) or fp32 (one 16-byte).
+__device__ __forceinline__ void store4(bf16_t* dst, const float4& v) {
+  *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
+                                              (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16));
+}
+__device__ __forceinline__ void store4(float* dst, const float4& v) { *reinterpret_cast<float4*>(dst) = v; }
+
+// Rows of up to 4 NT kRowChunks values stay in registers between the sum of
+// squares and the scaling, so P is read once: thread i holds the 16-byte chunks
+// i + NT j of the row, in the order the sum of squares takes them either way.
+constexpr int kRowChunks = 8;
+
 // Normalize one fp32 row of P (the calling workgroup's NT threads) into xp.
 template <int NT, typename T>
 __device__ __forceinline__ void pool_norm_row(const float* __restrict__ row, const float* __restrict__ g,
                                               int Dp, float eps, T* __restrict__ out, float* red) {
+  if (Dp <= 4 * NT * kRowChunks) {
+    float4 v[kRowChunks];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < kRowChunks; ++j) {
+      const int c = 4 * (threadIdx.x + NT * j);
+      if (c < Dp) {
+        v[j] = *reinterpret_cast<const float4*>(row + c);
+        ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+      }
+    }
+    ss = block_sum<NT>(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)Dp + eps);
+#pragma unroll
+    for (int j = 0; j < kRowChunks; ++j) {
+      const int c = 4 * (threadIdx.x + NT * j);
+      if (c < Dp) {
+        const float4 gg = *reinterpret_cast<const float4*>(g + c);
+        store4(out + c, make_float4(v[j].x * r * gg.x, v[j].y * r * gg.y, v[j].z * r * gg.z, v[j].w * r * gg.w));
+      }
+    }
+    return;
+  }
   float ss = 0.f;
   for (int c = threadIdx.x * 4; c < Dp; c += NT * 4) {
     const float4 v = *reinterpret_cast<const float4*>(row + c);
@@ -106,6 +141,40 @@ template <int NT>
 __device__ __forceinline__ void pool_norm_mx_row(const float* __restrict__ row, const float* __restrict__ g,
                                                  int Dp, float eps, uint8_t* __restrict__ codes,
                                                  uint8_t* __restrict__ scales, float* red) {
+  if (Dp <= 4 * NT * kRowChunks) {
+    // the row in registers as in pool_norm_row; an MXFP8 block of 32 values is
+    // the chunks of 8 consecutive lanes (NT j is a multiple of 8 and Dp of
+    // 32, so a block's 8 lanes are active together): its largest magnitude
+    // over those lanes, then each lane's 4 codes in one 32-bit store
+    float4 v[kRowChunks];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < kRowChunks; ++j) {
+      const int c = 4 * (threadIdx.x + NT * j);
+      if (c < Dp) {
+        v[j] = *reinterpret_cast<const float4*>(row + c);
+        ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+      }
+    }
+    ss = block_sum<NT>(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)Dp + eps);
+#pragma unroll
+    for (int j = 0; j < kRowChunks; ++j) {
+      const int c = 4 * (threadIdx.x + NT * j);
+      if (c < Dp) {
+        const float4 gg = *reinterpret_cast<const float4*>(g + c);
+        const float x0 = v[j].x * r * gg.x, x1 = v[j].y * r * gg.y, x2 = v[j].z * r * gg.z, x3 = v[j].w * r * gg.w;
+        float amax = fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3)));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        amax = fmaxf(amax, __shfl_xor(amax, 4));
+        const int X = mx_e4m3_exponent(amax);
+        *reinterpret_cast<uint32_t*>(codes + c) = mx_e4m3_code4(x0, x1, x2, x3, X);
+        if ((threadIdx.x & 7) == 0) scales[c / 32] = mx_scale_code(X);
+      }
+    }
+    return;
+  }
   float ss = 0.f;
   for (int c = threadIdx.x * 4; c < Dp; c += NT * 4) {
     const float4 v = *reinterpret_cast<const float4*>(row + c);
