@@ -99,6 +99,15 @@ def test_mx_small(T, E, k):
     run_case(mx_tiny(T=T, D=256, Dp=1024, F_=1024, E=E, k=k, seed=200 + T))
 
 
+@pytest.mark.parametrize("T", [136, 40])
+def test_mx_wide_pooled_rows(T):
+    """Dp = 9216: the MXFP8 pooled norm of T > 128 (256 threads) reads the row a
+    second time instead of keeping it in registers; at T = 40 the small-batch
+    kernel (1024 threads) keeps it, with a partial third chunk on some
+    threads, each MXFP8 block still the chunks of 8 consecutive lanes."""
+    run_case(mx_tiny(T=T, D=256, Dp=9216, F_=1024, E=4, k=1, seed=250 + T))
+
+
 def test_mx_all_tokens_same_experts():
     """Every token on the same two experts (300 rows each: one full tile and a
     44-row tail), every other expert empty."""

@@ -80,6 +80,17 @@ def test_multi_tile_fp32():
     run_case(tiny(T=300, D=512, Dp=256, F_=384, E=12, k=3, seed=104, act=synth.F32))
 
 
+@pytest.mark.parametrize("T,Dp", [(200, 8192), (200, 8448), (64, 8448)])
+def test_wide_pooled_rows(T, Dp):
+    """The pooled RMSNorm keeps a row in registers between its sum of squares
+    and its scaling when the row fits (8192 values for the 256 threads of the
+    T > 128 kernel, 32768 for the 1024 of the small-batch one). T = 200 with
+    Dp = 8192 fills those registers exactly; with Dp = 8448 the row is read a
+    second time; T = 64 with Dp = 8448 leaves some threads a partial third
+    chunk in the small-batch kernel."""
+    run_case(tiny(T=T, D=256, Dp=Dp, F_=256, E=4, k=2, seed=131 + T + Dp // 256, act=synth.BF16), T=T)
+
+
 @pytest.mark.parametrize("Dp,F", [(128, 128), (256, 256)])
 def test_all_tokens_same_experts(Dp, F):
     """A router bias forces every token onto the same k experts: three full
