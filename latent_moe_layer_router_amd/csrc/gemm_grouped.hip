@@ -587,7 +587,7 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
 
 int gemm_grouped_tile_m() { return GBM; }
 
-// One tile per CU at a time (144 KiB of LDS). Measured at 16K rows, a tile's
+// One tile per CU at a time (160 KiB of LDS). Measured at 16K rows, a tile's
 // time goes as (g + 1.5), g the 32-row groups of its larger wave row (4 for
 // 256 rows, 5 for 257..320): so choose the row-tile count (tiles of 128 to 320
 // rows) that minimizes ceil(tiles / n_cu) * (2 g + 3), and among equal costs
