@@ -403,6 +403,25 @@ def nvfp4_convert(lmoe, torch, dev, E=256, Dp=4096, F=4096, reps=5):
                          "kernel": "nvfp4_to_mxfp4_kernel", "algorithmic_bytes": int(byts)}}
 
 
+def pack_experts(lmoe, torch, tw):
+    """The bf16 expert weights re-laid out in place by lmoe_pack_experts (each
+    matrix through a one-matrix staging copy), timed with HIP events on the
+    stream it runs on. Nothing large is allocated or freed: releasing a second
+    25.8 GB copy slows HBM-bound kernels by a few percent for the next one to
+    three seconds on MI355X, which would land in the timed steps."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    tw = lmoe.pack_expert_weights(tw, s, in_place=True)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    byts = 4 * sum(tw[n].numel() * tw[n].element_size() for n in ("w_gate_up", "w_down"))
+    return tw, {"ms": round(ms, 2), "GB/s": round(byts / (ms * 1e-3) / 1e9, 1),
+                "what": "load-time re-layout of the bf16 expert weights in place (staging copy + pack: "
+                        "each byte read twice and written twice), not in a step"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -416,6 +435,8 @@ def main():
                     help="skip the extra timing of HIP graph replays")
     ap.add_argument("--no-convert", action="store_true",
                     help="skip timing the load-time NVFP4 -> MXFP4 weight re-encoding")
+    ap.add_argument("--row-major-experts", action="store_true",
+                    help="keep the bf16 expert weights row-major instead of packing them at load")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a kernel of "
                          "known traffic, to calibrate hardware byte counters against)")
@@ -446,7 +467,16 @@ def main():
     t0 = time.perf_counter()
     tw = sdev.upload_weights(w, dev)
     print(f"[bench] weights uploaded in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
-    block = lmoe.LatentMoE(tw, w.k, max_tokens, w.eps_pool, w.eps_expert, out_dtype=torch.float32)
+    packed = w.expert_w == synth.BF16 and not args.row_major_experts
+    pack = None
+    if packed:
+        # load-time re-layout of the expert weights into 64 x 64 blocks (not
+        # part of a step); the row-major copy is released
+        tw, pack = pack_experts(lmoe, torch, tw)
+        print(f"[bench] expert weights packed in {pack['ms']:.1f} ms ({pack['GB/s']} GB/s)", file=sys.stderr,
+              flush=True)
+    block = lmoe.LatentMoE(tw, w.k, max_tokens, w.eps_pool, w.eps_expert, out_dtype=torch.float32,
+                           packed=packed)
 
     ms, stage_ms, n_active, counts, graph_ms = run_workload(lmoe, torch, synth, sdev, block, w, args.steps,
                                                             args.warmup, dev, graph=not args.no_graph)
@@ -463,7 +493,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) random-init weights)",
         "config": {"workload": w.name, "T": w.T, "D": w.D, "Dp": w.Dp, "F": w.F, "E": w.E, "k": w.k,
-                   "out_dtype": "f32", "active_experts": n_active},
+                   "out_dtype": "f32", "active_experts": n_active,
+                   "expert_layout": "packed 64x64 blocks" if packed else "row-major"},
+        "pack_experts": pack,
         "cache": "warm: steps back to back, so the 132 MiB of dense weights can stay in the 256 MiB "
                  "Infinity Cache (the 25 GB of expert weights cannot); cold_cache_ms flushes it",
         "step_hbm_frac": head["step_hbm_frac"],
@@ -477,11 +509,15 @@ def main():
         "load": head["load"],
     }
     also = []
+    held = []            # handles kept open until the end (see below)
     for e in extra:
         if e.expert_w != w.expert_w:
             # another expert format (MXFP4): its own weights and handle, after
-            # the bf16 ones are released
-            block.close()
+            # the bf16 ones are released (the upload that follows takes longer
+            # than the clearing of the freed memory that slows kernels)
+            for b_ in held + [block]:
+                b_.close()
+            held = []
             del tw
             torch.cuda.empty_cache()
             t0 = time.perf_counter()
@@ -492,26 +528,30 @@ def main():
             block = lmoe.LatentMoE(tw, e.k, max_tokens, e.eps_pool, e.eps_expert,
                                    out_dtype=torch.float32)
         elif e.skew != w.skew:
-            # the skewed workload: the same model plus a router bias (its own handle)
-            block.close()
+            # the skewed workload: the same model plus a router bias (its own
+            # handle; the previous one stays open, since a freed workspace is
+            # cleared under the next timed steps)
             b = synth.router_bias(e)
             tw = dict(tw, b_router=None if b is None else sdev.to_device(b, dev))
             w = e
+            held.append(block)
             block = lmoe.LatentMoE(tw, e.k, max_tokens, e.eps_pool, e.eps_expert,
-                                   out_dtype=torch.float32)
+                                   out_dtype=torch.float32, packed=packed)
         ems, est, _, ecounts, gms = run_workload(lmoe, torch, synth, sdev, block, e, args.steps, args.warmup,
                                                  dev, graph=not args.no_graph)
         print(f"[bench] {e.name}: {ems:.3f} ms/step (graph replay {gms}), stages {est}", file=sys.stderr,
               flush=True)
         also.append(workload_entry(e, ems, est, ecounts.numpy(), n_cu, gms))
-    block.close()
-    del tw
-    torch.cuda.empty_cache()
     if not args.no_convert:
+        # timed before anything is released, for the same reason
         conv = nvfp4_convert(lmoe, torch, dev)
         print(f"[bench] nvfp4_to_mxfp4: {conv['ms']:.3f} ms, {conv['roofline']['achieved']} GB/s",
               file=sys.stderr, flush=True)
         also.append(conv)
+    for b_ in held + [block]:
+        b_.close()
+    del tw
+    torch.cuda.empty_cache()
     res["also"] = also
     w = synth.WORKLOADS[args.workload]
     if not args.no_cpu_baseline:

@@ -64,6 +64,12 @@ typedef enum {
 } lmoe_dtype;
 
 #define LMOE_FLAG_ROUTER_BIAS 1u   /* lmoe_weights.b_router is present */
+#define LMOE_FLAG_PACKED_EXPERTS 2u /* w_gate_up and w_down are in the packed expert
+                                       layout (lmoe_pack_experts); needs bf16
+                                       activations and experts, d_pooled a multiple
+                                       of 256, d_ff a multiple of 128, and
+                                       max_tokens * top_k * max(d_ff, d_pooled) * 2
+                                       and 4 * d_ff * d_pooled below 2^31 */
 
 /* Block configuration (host struct, copied at create).
  * Shapes: d_model (D), d_pooled (Dp), d_ff (F) must be multiples of 64;
@@ -214,6 +220,24 @@ lmoe_status lmoe_mx_quantize_e4m3(const float* x, int64_t n, uint8_t* codes, uin
 lmoe_status lmoe_nvfp4_to_mxfp4(const uint8_t* codes, const uint8_t* scales16, const float* global_scale,
                                 int64_t n_mats, int64_t rows, int64_t cols, uint8_t* out_codes,
                                 uint8_t* out_scales, void* hip_stream);
+
+/* Copy bf16 expert weights into the packed expert layout that lmoe_create
+ * reads with LMOE_FLAG_PACKED_EXPERTS (a load-time step, like the re-encoding
+ * above; the forward then streams each 64-row x 64-column piece of a weight
+ * matrix as one contiguous 8 KiB block instead of 64 row segments 2 cols bytes
+ * apart). Not a step of the block's computation: the same values, reordered.
+ * Each of the n_mats matrices is [rows][cols] bf16 row-major in src; in dst it
+ * is a sequence of blocks of 64 rows x 64 columns, block (g, s) (rows
+ * [64 g, 64 g + 64), columns [64 s, 64 s + 64)) at element offset
+ * (g * cols / 64 + s) * 4096 of the matrix, its row r at r * 64 and column c at
+ * c; matrices follow each other every rows * cols elements, as in src. rows and
+ * cols must be multiples of 64; src and dst are device pointers, 16-byte
+ * aligned, and must not overlap; a zero size enqueues nothing. For a layer's
+ * experts: n_mats = E with rows = 2F, cols = Dp (w_gate_up) and rows = Dp,
+ * cols = F (w_down). Asynchronous on hip_stream; LMOE_E_INVAL on bad arguments
+ * (nothing enqueued); the caller owns both buffers. */
+lmoe_status lmoe_pack_experts(const void* src, void* dst, int64_t n_mats, int64_t rows, int64_t cols,
+                              void* hip_stream);
 
 /* Device workspace bytes a handle with this configuration allocates. */
 lmoe_status lmoe_workspace_bytes(const lmoe_config* cfg, size_t* out);

@@ -21,6 +21,7 @@ LMOE_ABI_VERSION = 1
 LMOE_OK, LMOE_E_INVAL, LMOE_E_UNSUPPORTED, LMOE_E_NOMEM, LMOE_E_HIP = 0, -1, -2, -3, -4
 LMOE_F32, LMOE_BF16, LMOE_MXFP4, LMOE_MXFP8_E4M3 = 0, 1, 2, 3
 LMOE_FLAG_ROUTER_BIAS = 1
+LMOE_FLAG_PACKED_EXPERTS = 2
 STAGES = ["proj_in", "topk", "sort", "pool_norm", "gate_up", "down", "combine", "unpool"]
 LMOE_NUM_STAGES = len(STAGES)
 
@@ -28,7 +29,7 @@ LMOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ["lmoe_create", "lmoe_forward", "lmoe_forward_noalloc", "lmoe_destroy", "lmoe_workspace_bytes",
            "lmoe_set_timing", "lmoe_get_timing", "lmoe_status_str", "lmoe_last_error",
-           "lmoe_mx_quantize_e4m3", "lmoe_nvfp4_to_mxfp4"]
+           "lmoe_mx_quantize_e4m3", "lmoe_nvfp4_to_mxfp4", "lmoe_pack_experts"]
 
 
 class lmoe_config(ctypes.Structure):
@@ -81,8 +82,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lmoe_get_timing.argtypes = [P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(I32)]
     lib.lmoe_mx_quantize_e4m3.argtypes = [P, ctypes.c_int64, P, P, P]
     lib.lmoe_nvfp4_to_mxfp4.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P, P]
+    lib.lmoe_pack_experts.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P]
     for f in ("lmoe_create", "lmoe_forward", "lmoe_forward_noalloc", "lmoe_destroy", "lmoe_workspace_bytes",
-              "lmoe_set_timing", "lmoe_get_timing", "lmoe_mx_quantize_e4m3", "lmoe_nvfp4_to_mxfp4"):
+              "lmoe_set_timing", "lmoe_get_timing", "lmoe_mx_quantize_e4m3", "lmoe_nvfp4_to_mxfp4",
+              "lmoe_pack_experts"):
         getattr(lib, f).restype = ctypes.c_int
     lib.lmoe_status_str.argtypes = [ctypes.c_int]
     lib.lmoe_status_str.restype = ctypes.c_char_p
@@ -155,15 +158,49 @@ def lmoe_nvfp4_to_mxfp4(codes: int, scales16: int, global_scale: int, n_mats: in
                                       out_scales, stream), "lmoe_nvfp4_to_mxfp4")
 
 
+def lmoe_pack_experts(src: int, dst: int, n_mats: int, rows: int, cols: int, stream: int = 0):
+    _check(load().lmoe_pack_experts(src, dst, n_mats, rows, cols, stream), "lmoe_pack_experts")
+
+
 def make_config(D, Dp, F, E, k, max_tokens, act="bf16", eps_pool=1e-6, eps_expert=1e-6,
-                router_bias=False, out=None, experts=None) -> lmoe_config:
+                router_bias=False, out=None, experts=None, packed=False) -> lmoe_config:
     """act / out: "bf16" or "f32" (out defaults to act); experts: the expert
-    weight format, act (default) or "mxfp4"."""
+    weight format, act (default) or "mxfp4"; packed: the bf16 expert weights
+    are in the packed expert layout (lmoe_pack_experts)."""
     dts = {"bf16": LMOE_BF16, "f32": LMOE_F32, "mxfp4": LMOE_MXFP4}
     dt = dts[act]
     return lmoe_config(LMOE_ABI_VERSION, D, Dp, F, E, k, eps_pool, eps_expert, dt,
                        dts[experts or act], dts[out or act], max_tokens,
-                       LMOE_FLAG_ROUTER_BIAS if router_bias else 0)
+                       (LMOE_FLAG_ROUTER_BIAS if router_bias else 0) |
+                       (LMOE_FLAG_PACKED_EXPERTS if packed else 0))
+
+
+def pack_expert_weights(weights: dict, stream=None, in_place: bool = False) -> dict:
+    """A bf16 weight dict whose w_gate_up and w_down are in the packed expert
+    layout, filled by lmoe_pack_experts on `stream` (default: the current one);
+    the other tensors are shared. By default the packed tensors are new ones of
+    the same shapes. in_place: each expert matrix is copied to a one-matrix
+    staging buffer and packed back into its own storage, so no second copy of
+    the experts is allocated (or later freed); the given tensors are modified."""
+    import torch
+    out = dict(weights)
+    st = stream or torch.cuda.current_stream()
+    for name in ("w_gate_up", "w_down"):
+        w = weights[name]
+        assert w.dtype == torch.bfloat16 and w.is_contiguous() and w.dim() == 3
+        n, R, C = w.shape
+        if not in_place:
+            p = torch.empty_like(w)
+            lmoe_pack_experts(w.data_ptr(), p.data_ptr(), n, R, C, st.cuda_stream)
+            out[name] = p
+            continue
+        with torch.cuda.stream(st):
+            stage = torch.empty_like(w[0])
+            for e in range(n):
+                stage.copy_(w[e])
+                lmoe_pack_experts(stage.data_ptr(), w[e].data_ptr(), 1, R, C, st.cuda_stream)
+            stage.record_stream(st)
+    return out
 
 
 class LatentMoE:
@@ -174,10 +211,12 @@ class LatentMoE:
     (torch.bfloat16 or torch.float32), gammas and bias float32. MXFP4 experts:
     w_gate_up [E, 2F, Dp/2] and w_down [E, Dp, F/2] as uint8 E2M1 pairs plus
     s_gate_up [E, 2F, Dp/32] and s_down [E, Dp, F/32] uint8 E8M0 scales.
-    out_dtype: torch.float32 or the activation dtype (the default)."""
+    out_dtype: torch.float32 or the activation dtype (the default). packed: the
+    bf16 w_gate_up and w_down are in the packed expert layout
+    (pack_expert_weights)."""
 
     def __init__(self, weights: dict, top_k: int, max_tokens: int, eps_pool=1e-6, eps_expert=1e-6,
-                 out_dtype=None):
+                 out_dtype=None, packed: bool = False):
         import torch
         wp = weights["w_pool"]
         act = {torch.bfloat16: "bf16", torch.float32: "f32"}[wp.dtype]
@@ -193,7 +232,7 @@ class LatentMoE:
         self.max_tokens = max_tokens
         self.cfg = make_config(D, Dp, F, E, top_k, max_tokens, act, eps_pool, eps_expert,
                                weights.get("b_router") is not None, out,
-                               "mxfp4" if mx else None)
+                               "mxfp4" if mx else None, packed)
         ptr = lambda name: weights[name].data_ptr() if weights.get(name) is not None else None
         self.cw = lmoe_weights(ptr("w_router"), ptr("b_router"), ptr("w_pool"), ptr("g_pool"),
                                ptr("w_gate_up"), ptr("s_gate_up"), ptr("w_down"), ptr("s_down"),

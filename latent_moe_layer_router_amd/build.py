@@ -9,7 +9,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "liblmoe.so")
 SOURCES = ["api.hip", "gemm.hip", "stream.hip", "route.hip", "norm.hip",
-           "convert.hip", "stream_mx.hip", "gemm_grouped.hip", "gemm_grouped_mx.hip"]
+           "convert.hip", "stream_mx.hip", "gemm_grouped.hip", "gemm_grouped_mx.hip", "pack.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

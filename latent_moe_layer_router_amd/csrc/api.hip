@@ -134,7 +134,18 @@ lmoe_status check_config(const lmoe_config* c) {
   if ((int64_t)c->max_tokens * c->top_k > (int64_t)INT32_MAX / 2 ||
       (int64_t)c->max_tokens * c->top_k * c->d_ff > (int64_t)1 << 40)
     return fail(LMOE_E_UNSUPPORTED, "max_tokens too large");
-  if (c->flags & ~LMOE_FLAG_ROUTER_BIAS) return fail(LMOE_E_INVAL, "unknown flag bits");
+  if (c->flags & ~(LMOE_FLAG_ROUTER_BIAS | LMOE_FLAG_PACKED_EXPERTS)) return fail(LMOE_E_INVAL, "unknown flag bits");
+  if (c->flags & LMOE_FLAG_PACKED_EXPERTS) {
+    // Every expert GEMM must then run on the kernels that read the packed
+    // layout (the weight-streaming ones and the tiled grouped GEMM) at every T.
+    const int64_t A = (int64_t)c->max_tokens * c->top_k;
+    if (c->act_dtype != LMOE_BF16 || c->expert_wdtype != LMOE_BF16 || c->d_pooled % 256 || c->d_ff % 128 ||
+        A * c->d_ff * 2 >= ((int64_t)1 << 31) || A * c->d_pooled * 2 >= ((int64_t)1 << 31) ||
+        (int64_t)4 * c->d_ff * c->d_pooled >= ((int64_t)1 << 31))
+      return fail(LMOE_E_UNSUPPORTED,
+                  "packed expert weights need bf16 activations and experts, d_pooled a multiple of 256, d_ff a "
+                  "multiple of 128 and 32-bit byte offsets at max_tokens");
+  }
   return LMOE_OK;
 }
 
@@ -212,6 +223,9 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
                            int32_t T, hipStream_t s, const lmoe_aux* aux) {
   const bool bf16 = c.act_dtype == LMOE_BF16;
   const bool out_f32 = c.out_dtype == LMOE_F32;
+  // expert weights in the packed layout (create checked that only the
+  // weight-streaming and tiled grouped kernels run the expert GEMMs then)
+  const int packed = (c.flags & LMOE_FLAG_PACKED_EXPERTS) ? 1 : 0;
   const int E = c.n_experts, k = c.top_k, D = c.d_model, Dp = c.d_pooled, F = c.d_ff;
   float* P = reinterpret_cast<float*>(ws + pl.P);
   float* logits = (aux && aux->logits) ? aux->logits : reinterpret_cast<float*>(ws + pl.logits);
@@ -413,6 +427,7 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     sp_down.B = W.w_down;
     sp_down.ldb = F;
     sp_down.b_expert_stride = (int64_t)Dp * F;
+    sp_down.b_packed = packed;
     sp_down.offsets = offsets;
     sp_down.n_experts = E;
     sp_down.groups = Dp / 64;
@@ -438,6 +453,7 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     sp.B = W.w_gate_up;
     sp.ldb = Dp;
     sp.b_expert_stride = (int64_t)2 * F * Dp;
+    sp.b_packed = packed;
     sp.offsets = offsets;
     sp.n_experts = E;
     sp.groups = F / 32;
@@ -516,6 +532,7 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     g.B = W.w_gate_up;
     g.ldb = Dp;
     g.b_expert_stride = (int64_t)2 * F * Dp;
+    g.b_packed = packed;
     g.offsets = offsets;
     g.mt_off = mt_off;
     g.E = E;
@@ -601,6 +618,7 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     g.B = W.w_down;
     g.ldb = F;
     g.b_expert_stride = (int64_t)Dp * F;
+    g.b_packed = packed;
     g.offsets = offsets;
     g.mt_off = mt_off;
     g.E = E;
@@ -817,6 +835,26 @@ lmoe_status lmoe_nvfp4_to_mxfp4(const uint8_t* codes, const uint8_t* scales16, c
     return fail(LMOE_E_INVAL, "outputs overlap the inputs");
   const hipError_t e = launch_nvfp4_to_mxfp4(codes, scales16, global_scale, n_mats, rows, cols, out_codes,
                                              out_scales, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(LMOE_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+  return LMOE_OK;
+}
+
+lmoe_status lmoe_pack_experts(const void* src, void* dst, int64_t n_mats, int64_t rows, int64_t cols,
+                              void* hip_stream) {
+  g_last_error.clear();
+  if (n_mats < 0 || rows < 0 || cols < 0 || rows % 64 || cols % 64)
+    return fail(LMOE_E_INVAL, "n_mats must be >= 0, rows and cols non-negative multiples of 64");
+  if (n_mats == 0 || rows == 0 || cols == 0) return LMOE_OK;
+  if (!src || !dst) return fail(LMOE_E_INVAL, "src and dst must not be NULL");
+  if (!aligned16(src) || !aligned16(dst)) return fail(LMOE_E_INVAL, "src and dst must be 16-byte aligned");
+  if (rows > INT32_MAX || cols > INT32_MAX || rows > INT64_MAX / n_mats || n_mats * rows > INT64_MAX / (2 * cols))
+    return fail(LMOE_E_INVAL, "size overflow");
+  const int64_t bytes = n_mats * rows * cols * 2;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(src), y = reinterpret_cast<uintptr_t>(dst);
+  if (x < y + (uintptr_t)bytes && y < x + (uintptr_t)bytes) return fail(LMOE_E_INVAL, "src and dst overlap");
+  const hipError_t e = launch_pack_experts(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), n_mats,
+                                           (int)rows, (int)cols, static_cast<hipStream_t>(hip_stream));
+  if (e == hipErrorInvalidValue) return fail(LMOE_E_INVAL, "too many 64 x 64 blocks for one launch");
   if (e != hipSuccess) return fail(LMOE_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
   return LMOE_OK;
 }

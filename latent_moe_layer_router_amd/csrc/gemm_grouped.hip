@@ -190,8 +190,14 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
   // depends on the row's low 4 bits only) differ by whole rows: one offset
   // register plus uniform row deltas in the scalar offset. SwiGLU rows 128..255
   // are the up rows, F - 128 further on.
-  const int up = (EPI == EPI_SWIGLU && !dense) ? (p.F - GBN / 2) * rowb : 0;
-  const int gbd1 = 64 * rowb, gbd2 = 128 * rowb + up, gbd3 = 192 * rowb + up;
+  // In the packed expert layout (grouped mode only) rows come in groups of 64
+  // whose stage of two K-steps is one 8 KiB block: the row deltas are whole
+  // groups of K / 64 blocks, and a stage is 8 KiB further.
+  const bool bpk = !dense && p.b_packed;
+  const int rowu = bpk ? (p.K >> 6) * 8192 / 64 : rowb;   // bytes per row in whole-group deltas
+  const int up = (EPI == EPI_SWIGLU && !dense) ? (p.F - GBN / 2) * rowu : 0;
+  const int gbd1 = 64 * rowu, gbd2 = 128 * rowu + up, gbd3 = 192 * rowu + up;
+  const int kstep_b = bpk ? 4096 : RB;       // bytes per K-step of B (a stage is two)
 
   // ---- global-to-LDS loads of a tile ----------------------------------------
   __amdgpu_buffer_rsrc_t rsA, rsB;
@@ -241,7 +247,9 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
     {
       const int r = 8 * wave + (ln >> 3);
       const int n = dense ? r : n0 + r;
-      gb0 = (uint32_t)n * (uint32_t)rowb + (uint32_t)(((ln & 7) ^ swz8(r)) << 4);
+      gb0 = (bpk ? (uint32_t)(n >> 6) * (uint32_t)(p.K >> 6) * 8192u + (uint32_t)(n & 63) * 128u
+                 : (uint32_t)n * (uint32_t)rowb) +
+            (uint32_t)(((ln & 7) ^ swz8(r)) << 4);
     }
     // Dense products: each column tile walks K from its own starting step (4
     // steps further per column tile), so that the tiles sharing a row tile's
@@ -271,7 +279,7 @@ __global__ __launch_bounds__(GNT, 1) void gemm_grouped_kernel(GroupedParams p) {
 #define LMOE_ISSUE_B(st, SBB)                                                                           \
   {                                                                                                    \
     const int kr_ = 2 * (st) + krot;                                                                   \
-    const int ko = (kr_ >= nk ? kr_ - nk : kr_) * RB;                                                  \
+    const int ko = (kr_ >= nk ? kr_ - nk : kr_) * kstep_b;                                             \
     LMOE_LD(rsB, gb0, (SBB) + wave * 8 * RBB, ko)                                                      \
     LMOE_LD(rsB, gb0, (SBB) + (wave + 8) * 8 * RBB, ko + gbd1)                                         \
     LMOE_LD(rsB, gb0, (SBB) + (wave + 16) * 8 * RBB, ko + gbd2)                                        \

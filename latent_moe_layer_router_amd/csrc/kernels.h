@@ -67,9 +67,20 @@ struct StreamParams {
   int ss_ld;
   const int32_t* fused_n;      // if set: nothing to do when *fused_n >= whole_min (the fused
   int whole_min;               // kernel ran the streamed experts whole)
+  int b_packed;                // B in the packed expert layout (pack_experts; K a multiple of 64)
 };
 int stream_max_rows();
 hipError_t launch_stream(const StreamParams& p, EpiKind epi, hipStream_t s);
+
+// The packed expert layout of a bf16 [rows][cols] matrix (rows and cols
+// multiples of 64): blocks of 64 rows x 64 columns, 8 KiB each, block (g, s) at
+// byte (g * cols / 64 + s) * 8192, its row r at r * 128 and column c at c * 2;
+// element (i, j) at ((i / 64) * (cols / 64) + j / 64) * 8192 + (i % 64) * 128 +
+// (j % 64) * 2. A weight-streaming stage (64 rows x 64 columns) is then one
+// contiguous block. pack_experts copies n_mats such matrices from the row-major
+// src to dst (no overlap).
+hipError_t launch_pack_experts(const uint16_t* src, uint16_t* dst, int64_t n_mats, int rows, int cols,
+                               hipStream_t s);
 
 // The streamed experts' GEMMs in one persistent launch (n_cu workgroups): gu
 // as for launch_stream(EPI_SWIGLU), dn as for launch_stream(EPI_DOWN), each
@@ -153,6 +164,7 @@ struct GroupedParams {
   float* out1;
   int64_t ldo1;
   const float* bias1;
+  int b_packed;                // grouped: B in the packed expert layout (pack_experts)
 };
 int gemm_grouped_tile_m();
 // Dense mode: the row-tile count for an M-row product with ntiles_n column

@@ -72,7 +72,9 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int e, int gr
   const int lane = threadIdx.x & 63, r16 = lane & 15, kq = lane >> 4;
   const int lrow = lane >> 3, lc = lane & 7;
 
-  // Weights: load j moves local rows 8j .. 8j+7 (lane: row 8j + lrow).
+  // Weights: load j moves local rows 8j .. 8j+7 (lane: row 8j + lrow). In the
+  // packed layout a stage's 64 columns of a row group are one 8 KiB block, so
+  // each load moves 1 KiB of consecutive bytes; the stages are kw bytes apart.
   const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16_t*>(static_cast<const bf16_t*>(p.B) + (int64_t)e * p.b_expert_stride), (short)0,
       (int)p.b_bytes, kBufWord3);
@@ -81,8 +83,11 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int e, int gr
   for (int j = 0; j < 8; ++j) {
     const int lr = 8 * j + lrow;
     const int row = (EPI == EPI_SWIGLU) ? ((lr < 32 ? 0 : p.F - 32) + grp * 32 + lr) : (grp * 64 + lr);
-    wo[j] = (uint32_t)row * (uint32_t)(p.ldb * 2) + (uint32_t)((lc ^ swz8(lr)) << 4);
+    wo[j] = (p.b_packed ? (uint32_t)(row >> 6) * (uint32_t)(p.K >> 6) * 8192u + (uint32_t)(row & 63) * 128u
+                        : (uint32_t)row * (uint32_t)(p.ldb * 2)) +
+            (uint32_t)((lc ^ swz8(lr)) << 4);
   }
+  const int kw = p.b_packed ? 8192 : KC * 2;
   // Tokens: load i moves token rows 8i .. 8i+7 of the expert (rows past its end
   // load its last row; never stored).
   const __amdgpu_buffer_rsrc_t rsA =
@@ -97,10 +102,10 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int e, int gr
   }
 #define LMOE_ISSUE(c, SW, SA)                                                                   \
   {                                                                                            \
-    const int ko_ = (c) * KC * 2;                                                              \
+    const int ko_ = (c) * KC * 2, kow_ = (c) * kw;                                             \
     _Pragma("unroll") for (int j = 0; j < 8; ++j)                                              \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (LMOE_AS3 void*)((SW) + 1024 * j), 16,     \
-                                               (int)wo[j], ko_, 0, 2);                         \
+                                               (int)wo[j], kow_, 0, 2);                        \
     _Pragma("unroll") for (int i = 0; i < 2 * NMT; ++i)                                        \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (LMOE_AS3 void*)((SA) + 1024 * i), 16,     \
                                                (int)ao[i], ko_, 0, 0);                         \

@@ -56,7 +56,7 @@ def test_workspace_bytes_full_size():
     ("max_tokens", 0, lmoe.LMOE_E_INVAL),
     ("eps_pool", -1.0, lmoe.LMOE_E_INVAL),
     ("eps_expert", float("nan"), lmoe.LMOE_E_INVAL),
-    ("flags", 2, lmoe.LMOE_E_INVAL),
+    ("flags", 4, lmoe.LMOE_E_INVAL),
 ])
 def test_config_validation(field, value, status):
     cfg = lmoe.make_config(8192, 4096, 4096, 256, 8, 128, experts="mxfp4" if field == "d_ff" else None)
@@ -65,6 +65,50 @@ def test_config_validation(field, value, status):
         lmoe.lmoe_workspace_bytes(cfg)
     assert e.value.status == status
     assert lmoe.lmoe_last_error()
+
+
+@pytest.mark.parametrize("kw", [
+    dict(act="f32"),                         # packed weights are bf16
+    dict(experts="mxfp4"),                   # MXFP4 experts keep their layout
+    dict(Dp=4096 + 128),                     # d_pooled not a multiple of 256
+    dict(F=4096 + 64),                       # d_ff not a multiple of 128
+    dict(max_tokens=1 << 16),                # 32-bit offsets of H at max_tokens
+])
+def test_packed_experts_flag_validation(kw):
+    """The packed-layout flag is accepted only where every expert GEMM runs on
+    the kernels that read that layout."""
+    D, Dp, F = 8192, kw.pop("Dp", 4096), kw.pop("F", 4096)
+    T = kw.pop("max_tokens", 128)
+    lmoe.lmoe_workspace_bytes(lmoe.make_config(D, 4096, 4096, 256, 8, 128, packed=True))   # accepted
+    cfg = lmoe.make_config(D, Dp, F, 256, 8, T, packed=True, **kw)
+    with pytest.raises(lmoe.LmoeError) as e:
+        lmoe.lmoe_workspace_bytes(cfg)
+    assert e.value.status == lmoe.LMOE_E_UNSUPPORTED
+    assert "packed" in lmoe.lmoe_last_error()
+
+
+@pytest.mark.parametrize("args", [
+    (1, 32, 64), (1, 64, 96),                # rows, cols not multiples of 64
+    (-1, 64, 64), (1, -64, 64),              # negative sizes
+])
+def test_pack_experts_rejects_bad_sizes(args):
+    """Checked on the host before anything is enqueued (no GPU needed)."""
+    m, r, c = args
+    buf = 1 << 24
+    with pytest.raises(lmoe.LmoeError) as e:
+        lmoe.lmoe_pack_experts(buf, buf + (1 << 20), m, r, c)
+    assert e.value.status == lmoe.LMOE_E_INVAL
+
+
+def test_pack_experts_rejects_bad_pointers():
+    base = 1 << 24
+    n = 2 * 64 * 128 * 2                     # bytes of two 64 x 128 matrices
+    for src, dst in [(0, base), (base, 0), (base + 8, base + (1 << 20)), (base, base + (1 << 20) + 2),
+                     (base, base + n - 16), (base + 16, base)]:
+        with pytest.raises(lmoe.LmoeError) as e:
+            lmoe.lmoe_pack_experts(src, dst, 2, 64, 128)
+        assert e.value.status == lmoe.LMOE_E_INVAL, (src, dst)
+    lmoe.lmoe_pack_experts(0, 0, 0, 64, 64)      # empty: nothing to do
 
 
 def test_create_rejects_null_weights_before_touching_a_device():

@@ -120,3 +120,25 @@ def test_skewed_T4096(full):
           f"one-row experts {int((counts == 1).sum())}")
     assert (counts == 0).sum() >= 16 and counts.max() > 4 * counts.mean()
     block.close()
+
+
+def test_packed_experts_give_the_same_bits(full):
+    """The packed expert layout at the full sizes, in the benchmark's launch
+    configuration: the decode batch (the fused weight-streaming kernel over 253
+    experts) and a 4096-token prefill chunk (the tiled grouped GEMM) give the
+    row-major run's output bit for bit."""
+    tw, _, block = full
+    w = synth.WORKLOADS["decode_bf16"]
+    H.say("[gpu] full-size packed expert layout: packing 25.8 GB of experts")
+    pw = lmoe.pack_expert_weights(tw)
+    packed = lmoe.LatentMoE(pw, w.k, MAX_TOKENS, w.eps_pool, w.eps_expert, out_dtype=torch.float32,
+                            packed=True)
+    for xw, T in ((w, 128), (synth.WORKLOADS["prefill_bf16"], 4096)):
+        H.say(f"[gpu]   T={T}")
+        x = sdev.to_device(synth.x(xw, T=T), DEV)
+        o0, o1 = block.forward(x), packed.forward(x)
+        torch.cuda.synchronize()
+        assert torch.equal(o0.view(torch.int32), o1.view(torch.int32)), T
+    packed.close()
+    del pw
+    torch.cuda.empty_cache()
