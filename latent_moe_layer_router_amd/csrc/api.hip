@@ -29,7 +29,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 // Byte layout of the workspace for a configuration (every region 256-byte aligned).
 struct Plan {
   size_t P, logits, ids, w, masks, chunk_base, counts, offsets, sorted_assign, inv,
-      row_tok, scale, tiles, n_tiles, mt_off, stream_items, n_stream, queue, xp, H, xq, xs, hq, hs, Y, ss,
+      row_tok, tiles, n_tiles, mt_off, stream_items, n_stream, queue, xp, H, xq, xs, hq, hs, Y, ss,
       u, part;
   size_t total;
   int max_slots;
@@ -65,7 +65,6 @@ Plan make_plan(const lmoe_config& c) {
   p.sorted_assign = grow(cur, A * 4);
   p.inv = grow(cur, A * 4);
   p.row_tok = grow(cur, A * 4);
-  p.scale = grow(cur, A * 4);
   p.tiles = grow(cur, (size_t)p.max_slots * 8);
   p.n_tiles = grow(cur, 4);
   p.mt_off = grow(cur, (E + 1) * 4);
@@ -659,7 +658,6 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     cp.y = Y;
     cp.ss = ss;
     cp.inv = inv;
-    cp.scale = reinterpret_cast<float*>(ws + pl.scale);
     cp.ids = ids;
     cp.w = tw;
     cp.g_expert = W.g_expert;

@@ -303,7 +303,6 @@ struct CombineParams {
   const int32_t* ids;      // [T][k]
   const float* w;          // [T][k]
   const float* g_expert;   // [E][Dp]
-  float* scale;            // [T*k] slot scales (scratch)
   void* u;                 // [T][Dp]
   int T, k, Dp;
   float eps;

@@ -7,13 +7,13 @@
 // one row per token (the expert GEMMs gather the rows of their assignments).
 //
 // combine — the finalize step of the blog's "AMD support" section (unpermute +
-// per-expert RMSNorm + weighted sum; here a scale pass and a sum pass). Each
-// slot's scale is w_j / sqrt(mean(y^2) + eps), the mean coming from the down
-// GEMM's per-64-column partial sums of squares of the stored values ("Fused
-// per-expert post-norm"). A workgroup of the sum pass takes 1024 columns of one
-// token: it gathers the token's k expert rows from their sorted positions,
-// multiplies each by its scale and that expert's gamma, and sums in fp32 in slot
-// order j = 0..k-1 ("Miles" RL backend: FP32 weighted sum).
+// per-expert RMSNorm + weighted sum, one kernel). Each slot's scale is
+// w_j / sqrt(mean(y^2) + eps), the mean coming from the down GEMM's
+// per-64-column partial sums of squares of the stored values ("Fused per-expert
+// post-norm"). A workgroup takes 1024 columns of one token: it computes the
+// token's k slot scales, gathers its k expert rows from their sorted positions,
+// multiplies each by its scale and that expert's gamma, and sums in fp32 in
+// slot order j = 0..k-1 ("Miles" RL backend: FP32 weighted sum).
 #include "common.h"
 #include "kernels.h"
 #include "mx.h"
@@ -271,28 +271,18 @@ __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const float* __restr
   mx_store_block(v, codes + 32 * b, scales + b);
 }
 
-// Slot scales, one wave per assignment a: w_a / sqrt(mean(y_a^2) + eps), the
-// mean from the row's partial sums of squares (lane q adds partials q, q + 64,
-// ..., then a butterfly over the wave).
-__global__ __launch_bounds__(kThreads) void combine_scale_kernel(CombineParams p) {
-  const int a = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (a >= p.T * p.k) return;               // whole waves
-  const int nss = p.Dp / 64;
-  const float* ss = p.ss + (int64_t)p.inv[a] * nss;
-  float s = 0.f;
-  for (int q = lane; q < nss; q += kWave) s += ss[q];
-  s = wave_sum(s);
-  if (lane == 0) p.scale[a] = p.w[a] / sqrtf(s / (float)p.Dp + p.eps);
-}
+// One workgroup per (1024-column chunk, token). With the first y words in
+// flight, it computes the token's k slot scales, w_j / sqrt(mean(y_j^2) + eps), the mean from the row's partial
+// sums of squares: 16 threads per slot, thread q adding partials q, q + 16, ...,
+// then a butterfly over the 16; the scales go through LDS. A thread then sums 8
+// consecutive columns over the k slots in slot order. The workgroups of one
+// token are adjacent (its partials are read from L2 after the first), token t
+// starting at chunk t mod (Dp / 1024): the rows being read at any time spread
+// over all column offsets (and so over all HBM channels; all workgroups on one
+// chunk measured 10% slower).
+constexpr int kCombineThreads = 128, kCombineCols = kCombineThreads * 8, kMaxSlots = 16;
 
-// One workgroup per (1024-column chunk, token). Consecutive workgroups take
-// consecutive tokens, token t starting at chunk t mod (Dp / 1024): the rows
-// being read at any time spread over all column offsets (and so over all HBM
-// channels; all workgroups on one chunk measured 10% slower). A thread sums 8
-// consecutive columns over the token's k slots in slot order.
-constexpr int kCombineThreads = 128, kCombineCols = kCombineThreads * 8;
-
-// The k slots' loads are all issued before any is used: raw 16-byte words per
+// The slots' loads are all issued before any is used: raw 16-byte words per
 // slot (converted to fp32 only when summed, so each load keeps registers of its
 // own and stays in flight).
 __device__ __forceinline__ uint4 load16_once(const void* src) {
@@ -309,58 +299,86 @@ __device__ __forceinline__ void widen8(const uint4& q, float (&v)[8]) {
   }
 }
 
+// 8 columns of up to 8 slots j0 .. j0 + 7: the y words and the experts' gammas.
 template <typename T>
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineParams p) {
-  const int nchunk = (p.Dp + kCombineCols - 1) / kCombineCols;
-  const int t = blockIdx.x % p.T, chunk = (blockIdx.x / p.T + t) % nchunk;
-  const int c = chunk * kCombineCols + threadIdx.x * 8;
-  if (c >= p.Dp) return;
+struct SlotWords {
+  uint4 y[8][8 * sizeof(T) / 16];
+  float4 g0[8], g1[8];
+};
+
+template <typename T>
+__device__ __forceinline__ void combine_load(const CombineParams& p, int t, int c, int j0, SlotWords<T>& w) {
   constexpr int VW = 16 / sizeof(T);       // values per 16-byte word of y
   const T* y = static_cast<const T*>(p.y);
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    if (j0 + jj < p.k) {
+      const int pos = p.inv[t * p.k + j0 + jj], eid = p.ids[t * p.k + j0 + jj];
+      const T* yrow = y + (int64_t)pos * p.Dp + c;
+#pragma unroll
+      for (int h = 0; h < 8 / VW; ++h) w.y[jj][h] = load16_once(yrow + h * VW);
+      const float4* gp = reinterpret_cast<const float4*>(p.g_expert + (int64_t)eid * p.Dp + c);
+      w.g0[jj] = gp[0];
+      w.g1[jj] = gp[1];
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void combine_add(const CombineParams& p, const float* sc, int j0, const SlotWords<T>& w,
+                                            float (&acc)[8]) {
+  constexpr int VW = 16 / sizeof(T);
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    if (j0 + jj < p.k) {
+      const float sj = sc[j0 + jj];
+      float yv[8];
+      if constexpr (VW == 8) {
+        widen8(w.y[jj][0], yv);
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          yv[4 * h] = __uint_as_float(w.y[jj][h].x);
+          yv[4 * h + 1] = __uint_as_float(w.y[jj][h].y);
+          yv[4 * h + 2] = __uint_as_float(w.y[jj][h].z);
+          yv[4 * h + 3] = __uint_as_float(w.y[jj][h].w);
+        }
+      }
+      const float gv[8] = {w.g0[jj].x, w.g0[jj].y, w.g0[jj].z, w.g0[jj].w,
+                           w.g1[jj].x, w.g1[jj].y, w.g1[jj].z, w.g1[jj].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += sj * gv[i] * yv[i];
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineParams p) {
+  __shared__ float sc[kMaxSlots];
+  const int nchunk = (p.Dp + kCombineCols - 1) / kCombineCols;
+  const int t = blockIdx.x / nchunk, chunk = (blockIdx.x + t) % nchunk;
+  const int tid = threadIdx.x, nss = p.Dp / 64;
+  const int c = chunk * kCombineCols + tid * 8;
+  SlotWords<T> w;
+  if (c < p.Dp) combine_load<T>(p, t, c, 0, w);   // in flight while the scales are computed
+  for (int j0 = 0; j0 < p.k; j0 += kCombineThreads / 16) {
+    const int j = j0 + (tid >> 4), q0 = tid & 15;
+    float s = 0.f;
+    if (j < p.k) {
+      const int a = t * p.k + j;
+      const float* ss = p.ss + (int64_t)p.inv[a] * nss;
+      for (int q = q0; q < nss; q += 16) s += ss[q];
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+    if (j < p.k && q0 == 0) sc[j] = p.w[t * p.k + j] / sqrtf(s / (float)p.Dp + p.eps);
+  }
+  __syncthreads();
+  if (c >= p.Dp) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; j0 < p.k; j0 += 8) {
-    int pos[8], eid[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      if (j0 + jj < p.k) {
-        pos[jj] = p.inv[t * p.k + j0 + jj];
-        eid[jj] = p.ids[t * p.k + j0 + jj];
-      }
-    }
-    uint4 yr[8][8 / VW];
-    float4 g0[8], g1[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      if (j0 + jj < p.k) {
-        const T* yrow = y + (int64_t)pos[jj] * p.Dp + c;
-#pragma unroll
-        for (int h = 0; h < 8 / VW; ++h) yr[jj][h] = load16_once(yrow + h * VW);
-        const float4* gp = reinterpret_cast<const float4*>(p.g_expert + (int64_t)eid[jj] * p.Dp + c);
-        g0[jj] = gp[0];
-        g1[jj] = gp[1];
-      }
-    }
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      if (j0 + jj < p.k) {
-        const float sj = p.scale[t * p.k + j0 + jj];
-        float yv[8];
-        if constexpr (VW == 8) {
-          widen8(yr[jj][0], yv);
-        } else {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            yv[4 * h] = __uint_as_float(yr[jj][h].x);
-            yv[4 * h + 1] = __uint_as_float(yr[jj][h].y);
-            yv[4 * h + 2] = __uint_as_float(yr[jj][h].z);
-            yv[4 * h + 3] = __uint_as_float(yr[jj][h].w);
-          }
-        }
-        const float gv[8] = {g0[jj].x, g0[jj].y, g0[jj].z, g0[jj].w, g1[jj].x, g1[jj].y, g1[jj].z, g1[jj].w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += sj * gv[i] * yv[i];
-      }
-    }
+    if (j0) combine_load<T>(p, t, c, j0, w);
+    combine_add<T>(p, sc, j0, w, acc);
   }
   store8(static_cast<T*>(p.u) + (int64_t)t * p.Dp + c, acc);
 }
@@ -412,15 +430,13 @@ hipError_t launch_mx_quant(const float* x, int64_t n, uint8_t* codes, uint8_t* s
 
 hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
+  if (p.k > kMaxSlots || p.Dp % 64) return hipErrorInvalidValue;
   const int64_t grid = (int64_t)((p.Dp + kCombineCols - 1) / kCombineCols) * p.T;
   if (grid >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  const int64_t n_assign = (int64_t)p.T * p.k;
-  hipLaunchKernelGGL(combine_scale_kernel, dim3((unsigned)((n_assign + kThreads / kWave - 1) / (kThreads / kWave))),
-                     dim3(kThreads), 0, s, p);
   if (bf16)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(grid), dim3(kCombineThreads), 0, s, p);
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3((unsigned)grid), dim3(kCombineThreads), 0, s, p);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(grid), dim3(kCombineThreads), 0, s, p);
+    hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)grid), dim3(kCombineThreads), 0, s, p);
   return hipGetLastError();
 }
 
