@@ -36,6 +36,7 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA (the MXFP4 experts' fp8 x fp4 products)
 PEAK_FP4_TFLOPS = 10100.0    # MI355X dense fp4 / fp6 MFMA
 STREAM_MAX_ROWS = 64         # experts with at most this many rows are streamed (bf16)
+ALL_STREAMED_T = 128         # batches of at most this many tokens stream every expert
 
 
 def expert_bytes_per_weight(w):
@@ -218,15 +219,23 @@ def roofline_entry(w, kernel, what, work, stages, ms, mfma_peak):
     return e
 
 
+def stream_limit(w):
+    """The largest expert the weight-streaming kernels take in this workload."""
+    if w.T <= ALL_STREAMED_T:
+        return ALL_STREAMED_T
+    return 32 if w.mx_act else STREAM_MAX_ROWS
+
+
 def kernel_rooflines(w, stage_ms, counts, n_cu):
     """Every compute stage of a workload with its roofline. Expert stages name
     the kernel that carries their work, decided from the routing the way the
     library decides it: the fused expert kernel when at least 3/4 as many
     experts as CUs are streamed (at most 64 rows each, bf16), else the
-    weight-streaming kernels (MXFP4: at most 32 rows) and the tiled GEMMs."""
+    weight-streaming kernels (MXFP4: at most 32 rows) and the tiled GEMMs. A
+    batch of at most 128 tokens streams every expert (in passes)."""
     n_active = int((counts > 0).sum())
     mx = w.mx_act
-    small = 32 if mx else STREAM_MAX_ROWS
+    small = stream_limit(w)
     n_stream = int(((counts > 0) & (counts <= small)).sum())
     n_tiled = int((counts > small).sum())
     peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
@@ -285,7 +294,7 @@ def workload_entry(w, ms, stage_ms, counts, n_cu, graph_ms=None):
          "step_bound": "hbm" if byts / (PEAK_HBM_GBS * 1e9) >= flops / (peak * 1e12) else "mfma",
          "roofline": dom, "kernels": ks,
          "stages_ms": {s: round(v, 4) for s, v in stage_ms.items()},
-         "load": load_histogram(counts, 32 if w.mx_act else STREAM_MAX_ROWS)}
+         "load": load_histogram(counts, stream_limit(w))}
     if w.mx_act:
         e["step_mfma_frac_fp4"] = round(flops / t / 1e12 / PEAK_FP4_TFLOPS, 4)
     return e

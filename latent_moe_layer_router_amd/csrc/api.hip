@@ -203,6 +203,8 @@ lmoe_status check_weights(const lmoe_config* cfg, const lmoe_weights* w) {
 // Each whole expert gets one compute unit, so that needs about as many
 // streamed experts as compute units (3/4 of them). The environment variable
 // LMOE_FUSED_EXPERTS = 1 (always whole experts) or 0 (never) overrides it.
+constexpr int kAllStreamedT = 128;
+
 int fused_whole_min(int n_cu) {
   const char* env = getenv("LMOE_FUSED_EXPERTS");
   if (env && env[0] == '1') return 0;
@@ -262,7 +264,14 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
   const bool fused = stream_ok && Dp % 256 == 0 && (int64_t)T * k >= whole_min;
   // MXFP4 experts: the create-time checks (Dp and F multiples of 1024, 32-bit
   // byte extents) are all the MX weight-streaming kernel needs.
-  const int small_max = stream_ok ? stream_max_rows() : (mx ? stream_mx_max_rows() : 0);
+  // A batch of at most kAllStreamedT tokens gives no expert more than that many
+  // rows (the k experts of a token are distinct); then the weight-streaming
+  // kernels take every expert, in passes of their row limit, and the tiled
+  // kernels are not launched (their launches cost more than the rare extra
+  // pass over an expert's weights).
+  const int pass_rows = stream_ok ? stream_max_rows() : (mx ? stream_mx_max_rows() : 0);
+  const int small_max = pass_rows > 0 && T <= kAllStreamedT ? kAllStreamedT : pass_rows;
+  const bool tiled = T > small_max;
   // Experts with many rows: the tiled grouped GEMM (bf16, Dp % 256 == 0, F % 128 == 0).
   const bool big_ok = bf16 && !mx && Dp % 256 == 0 && F % 128 == 0 && off32_ok;
   int32_t* mt_off = reinterpret_cast<int32_t*>(ws + pl.mt_off);
@@ -501,7 +510,8 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     sp.ldos = F / 32;
     run(launch_stream_mx(sp, EPI_SWIGLU, s));
   }
-  if (mx) {
+  if (mx && !tiled) {
+  } else if (mx) {
     GroupedMxParams g{};
     g.A = xq;
     g.As = xs;
@@ -543,7 +553,7 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     g.F = F;
     g.out = H;
     g.ldo = F;
-    run(launch_gemm_grouped(g, EPI_SWIGLU, n_cu, s));
+    if (tiled) run(launch_gemm_grouped(g, EPI_SWIGLU, n_cu, s));
   } else {
     GemmParams g{};
     g.N = F;
@@ -589,7 +599,8 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     sp.ss_ld = Dp / 64;
     run(launch_stream_mx(sp, EPI_DOWN, s));
   }
-  if (mx) {
+  if (mx && !tiled) {
+  } else if (mx) {
     GroupedMxParams g{};
     g.A = hq;
     g.As = hs;
@@ -631,7 +642,7 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     g.ldo = Dp;
     g.ss_out = ss;
     g.ss_ld = Dp / 64;
-    run(launch_gemm_grouped(g, EPI_DOWN, n_cu, s));
+    if (tiled) run(launch_gemm_grouped(g, EPI_DOWN, n_cu, s));
   } else {
     GemmParams g{};
     g.N = Dp;

@@ -208,11 +208,17 @@ __global__ __launch_bounds__(64) void stream_kernel(StreamParams p) {
   const int lo = p.offsets[e];
   const int m_e = p.offsets[e + 1] - lo;
   if (m_e == 0 || m_e > p.max_rows) return;
-  switch ((m_e + 15) >> 4) {                 // token tiles in use (uniform)
-    case 1: stream_body<EPI, 1>(p, e, grp, lo, m_e, sw0, sw1, sa0, sa1); break;
-    case 2: stream_body<EPI, 2>(p, e, grp, lo, m_e, sw0, sw1, sa0, sa1); break;
-    case 3: stream_body<EPI, 3>(p, e, grp, lo, m_e, sw0, sw1, sa0, sa1); break;
-    default: stream_body<EPI, 4>(p, e, grp, lo, m_e, sw0, sw1, sa0, sa1); break;
+  // Passes of up to 64 rows, each streaming the group's weights again (more
+  // than one only when the host let experts above 64 rows come here: batches
+  // too small for the tiled kernel to be worth a launch).
+  for (int r0 = 0; r0 < m_e; r0 += MT * 16) {
+    const int m = m_e - r0 < MT * 16 ? m_e - r0 : MT * 16;
+    switch ((m + 15) >> 4) {                 // token tiles in use (uniform)
+      case 1: stream_body<EPI, 1>(p, e, grp, lo + r0, m, sw0, sw1, sa0, sa1); break;
+      case 2: stream_body<EPI, 2>(p, e, grp, lo + r0, m, sw0, sw1, sa0, sa1); break;
+      case 3: stream_body<EPI, 3>(p, e, grp, lo + r0, m, sw0, sw1, sa0, sa1); break;
+      default: stream_body<EPI, 4>(p, e, grp, lo + r0, m, sw0, sw1, sa0, sa1); break;
+    }
   }
 }
 
@@ -247,13 +253,15 @@ template <int EPI>
 __device__ __forceinline__ void stream_groups(const StreamParams& p, int e, int lo, int m_e, int first,
                                               unsigned char* w0, unsigned char* w1, unsigned char* a0,
                                               unsigned char* a1) {
-  const int nmt = (m_e + 15) >> 4;           // token tiles in use (uniform)
   for (int grp = first; grp < p.groups; grp += FW) {
-    switch (nmt) {
-      case 1: stream_body<EPI, 1>(p, e, grp, lo, m_e, w0, w1, a0, a1); break;
-      case 2: stream_body<EPI, 2>(p, e, grp, lo, m_e, w0, w1, a0, a1); break;
-      case 3: stream_body<EPI, 3>(p, e, grp, lo, m_e, w0, w1, a0, a1); break;
-      default: stream_body<EPI, 4>(p, e, grp, lo, m_e, w0, w1, a0, a1); break;
+    for (int r0 = 0; r0 < m_e; r0 += MT * 16) {     // passes of up to 64 rows, as above
+      const int m = m_e - r0 < MT * 16 ? m_e - r0 : MT * 16;
+      switch ((m + 15) >> 4) {               // token tiles in use (uniform)
+        case 1: stream_body<EPI, 1>(p, e, grp, lo + r0, m, w0, w1, a0, a1); break;
+        case 2: stream_body<EPI, 2>(p, e, grp, lo + r0, m, w0, w1, a0, a1); break;
+        case 3: stream_body<EPI, 3>(p, e, grp, lo + r0, m, w0, w1, a0, a1); break;
+        default: stream_body<EPI, 4>(p, e, grp, lo + r0, m, w0, w1, a0, a1); break;
+      }
     }
   }
 }

@@ -202,6 +202,8 @@ __device__ __forceinline__ void stream_mx_body(const StreamMxParams& p, int e, i
   const int nc = K / XKC;                     // a multiple of 4 (K % 1024 == 0)
   TokStep ta0[NMT][2], ta1[NMT][2];
   u32x2_t ws0[4], ws1[4], ts0[NMT], ts1[NMT];
+  // the buffers' previous reads (an earlier pass's epilogue) are done
+  __builtin_amdgcn_s_waitcnt(kLdsIdle);
   LMOE_ISSUE(0, xw0, ta0, true, 0, ws0, ts0)
   for (int c = 0; c < nc; c += 8) {
     // group c / 4 (scales in ws0, ts0), then group c / 4 + 1 (ws1, ts1) if any
@@ -289,10 +291,16 @@ __global__ __launch_bounds__(64) void stream_mx_kernel(StreamMxParams p) {
   const int lo = p.offsets[e];
   const int m_e = p.offsets[e + 1] - lo;
   if (m_e == 0 || m_e > p.max_rows) return;
-  if (m_e <= 16)
-    stream_mx_body<EPI, 1>(p, e, grp, lo, m_e);
-  else
-    stream_mx_body<EPI, 2>(p, e, grp, lo, m_e);
+  // Passes of up to 32 rows, each streaming the group's weights again (more
+  // than one only when the host let experts above 32 rows come here: batches
+  // too small for the tiled kernel to be worth a launch).
+  for (int r0 = 0; r0 < m_e; r0 += XMT * 16) {
+    const int m = m_e - r0 < XMT * 16 ? m_e - r0 : XMT * 16;
+    if (m <= 16)
+      stream_mx_body<EPI, 1>(p, e, grp, lo + r0, m);
+    else
+      stream_mx_body<EPI, 2>(p, e, grp, lo + r0, m);
+  }
 }
 
 }  // namespace
@@ -302,8 +310,7 @@ int stream_mx_max_rows() { return XMT * 16; }
 hipError_t launch_stream_mx(const StreamMxParams& p, EpiKind epi, hipStream_t s) {
   const int blocks = p.n_experts * p.groups;
   if (blocks == 0) return hipSuccess;
-  if (p.K % 1024 != 0 || p.max_rows > stream_mx_max_rows())
-    return hipErrorInvalidValue;
+  if (p.K % 1024 != 0) return hipErrorInvalidValue;
   if (epi == EPI_SWIGLU)
     hipLaunchKernelGGL(stream_mx_kernel<EPI_SWIGLU>, dim3(blocks), dim3(64), 0, s, p);
   else if (epi == EPI_DOWN)

@@ -68,6 +68,13 @@ def test_expert_stages_are_priced_on_the_kernel_that_runs():
     m = synth.WORKLOADS["mxfp4_decode"]
     ks = stage_kernels(m, [4] * 256)
     assert ("stream_mx_kernel<EPI_SWIGLU>", ["gate_up"]) in ks
+    # at most 128 tokens every expert is streamed (in passes), whatever its rows
+    ks = stage_kernels(m, [100] + [4] * 7 + [0] * 248)
+    assert ("stream_mx_kernel<EPI_DOWN>", ["down"]) in ks
+    ks = stage_kernels(d, [100] * 2 + [0] * 254)
+    assert ("stream_kernel<EPI_SWIGLU>", ["gate_up"]) in ks
+    assert bench.stream_limit(d) == 128 and bench.stream_limit(p) == 64
+    assert bench.stream_limit(synth.WORKLOADS["mxfp4"]) == 32
 
 
 def test_profiled_traffic_is_used_only_for_the_current_sources(tmp_path, monkeypatch):

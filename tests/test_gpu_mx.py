@@ -152,12 +152,25 @@ def test_mx_full_size_prefill_subset():
 
 def test_mx_stream_row_boundaries():
     """Experts with 32 rows (the MX weight-streaming kernel's limit: two token
-    tiles), 33 (the tiled GEMM), 17 and 16 (two and one token tiles), 1 and 0
-    rows in one call."""
-    assign = np.array([0] * 32 + [1] * 33 + [2] * 17 + [3] * 16 + [4], np.int64)
-    w = mx_tiny(T=len(assign), D=256, Dp=1024, F_=1024, E=6, k=1, seed=220)
+    tiles), 33 and 40 (the tiled GEMM), 17 and 16 (two and one token tiles), 1
+    and 0 rows in one call (139 tokens: above 128 the tiled GEMM takes the
+    experts with more than 32 rows)."""
+    counts = [32, 33, 17, 16, 1, 40, 0]
+    assign = np.repeat(np.arange(len(counts)), counts)
+    w = mx_tiny(T=len(assign), D=256, Dp=1024, F_=1024, E=len(counts), k=1, seed=220)
     a = run_crafted(w, assign)
-    assert np.diff(a["expert_offsets"]).tolist() == [32, 33, 17, 16, 1, 0]
+    assert np.diff(a["expert_offsets"]).tolist() == counts
+
+
+@pytest.mark.parametrize("counts", [[90, 33, 4, 1, 0], [128, 0, 0, 0, 0]])
+def test_mx_small_batch_experts_in_passes(counts):
+    """At most 128 tokens: the MX weight-streaming kernel takes every expert,
+    those above 32 rows in passes of 32 rows (90 = 32 + 32 + 26, 33 = 32 + 1,
+    128 = 4 x 32), and the tiled GEMM is not launched."""
+    assign = np.repeat(np.arange(len(counts)), counts)
+    w = mx_tiny(T=len(assign), D=256, Dp=1024, F_=1024, E=len(counts), k=1, seed=221 + counts[0])
+    a = run_crafted(w, assign)
+    assert np.diff(a["expert_offsets"]).tolist() == counts
 
 
 @pytest.mark.parametrize("Dp,F_", [(2048, 1024), (1024, 4096), (4096, 2048)])

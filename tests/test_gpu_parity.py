@@ -151,11 +151,26 @@ def run_crafted(w, assign):
 
 def test_stream_path_row_boundaries():
     """Experts with 64 rows (the weight-streaming kernel's limit), 65 rows (the
-    tiled GEMM), 1 row and 0 rows in one call."""
+    tiled GEMM), 1 row and 0 rows in one call (130 tokens: above 128 the
+    tiled GEMM takes the experts with more than 64 rows)."""
     assign = np.array([0] * 64 + [1] * 65 + [2], np.int64)
     w = tiny(T=len(assign), D=256, Dp=128, F_=256, E=4, k=1, seed=110, act=synth.BF16)
     a = run_crafted(w, assign)
     assert np.diff(a["expert_offsets"]).tolist() == [64, 65, 1, 0]
+
+
+@pytest.mark.parametrize("counts", [[100, 27, 1, 0], [128, 0, 0, 0], [64, 64, 0, 0], [65, 63, 0, 0]])
+@pytest.mark.parametrize("fused", ["0", "1"])
+def test_small_batch_experts_in_passes(monkeypatch, counts, fused):
+    """At most 128 tokens: the weight-streaming kernels take every expert, those
+    above 64 rows in passes of 64 rows (100 = 64 + 36, 128 = 64 + 64, 65 =
+    64 + 1), and the tiled GEMM is not launched; through the single-wave
+    kernels and through the fused kernel (forced by LMOE_FUSED_EXPERTS)."""
+    monkeypatch.setenv("LMOE_FUSED_EXPERTS", fused)
+    assign = np.repeat(np.arange(len(counts)), counts)
+    w = tiny(T=len(assign), D=256, Dp=256, F_=256, E=len(counts), k=1, seed=114 + counts[0], act=synth.BF16)
+    a = run_crafted(w, assign)
+    assert np.diff(a["expert_offsets"]).tolist() == counts
 
 
 def test_grouped_tile_boundaries():
