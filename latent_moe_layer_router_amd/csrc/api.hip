@@ -322,6 +322,10 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     return g;
   };
 
+  // The top-k ORs into the chunk masks and the sort clears them; if a previous
+  // call stopped between the two, they are cleared before the top-k.
+  uint64_t* masks = reinterpret_cast<uint64_t*>(ws + pl.masks);
+
   // 1. router + pooler: one GEMM over [W_pool; W_router]
   mark();
   bool pooled = false;
@@ -355,9 +359,15 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     d.ldo1 = E;
     d.bias1 = W.b_router;
     // the split-K reduction, the pooled RMSNorm and the MXFP8 quantization of
-    // xp in one pass (xp is one row per token, so it needs no routing)
+    // xp (one row per token, so it needs no routing) and the top-k in one pass
     run(launch_dense_stream_partials(d, s));
-    run(launch_splitk_pool_norm(d, W.g_pool, c.eps_pool, mx ? static_cast<void*>(xq) : xp, mx ? 2 : 0, xs, s));
+    if (masks_dirty) {
+      run(launch_clear_u64(masks, (int64_t)(pl.chunk_base - pl.masks) / 8, s));
+      if (err == hipSuccess) masks_dirty = false;
+    }
+    const TopkOut tk{ids, tw, masks, k};
+    run(launch_splitk_pool_norm(d, W.g_pool, c.eps_pool, mx ? static_cast<void*>(xq) : xp, mx ? 2 : 0, xs, tk, s));
+    if (err == hipSuccess) masks_dirty = true;
     pooled = true;
   } else {
     GemmParams g{};
@@ -377,17 +387,16 @@ hipError_t enqueue_forward(const lmoe_config& c, const lmoe_weights& W, const Pl
     g.bias1 = W.b_router;
     run(launch_gemm(g, EPI_F32, bf16, s));
   }
-  // 2. top-k + softmax + chunk masks
+  // 2. top-k + softmax + chunk masks (done above with the small-batch reduction)
   mark();
-  uint64_t* masks = reinterpret_cast<uint64_t*>(ws + pl.masks);
-  // The top-k kernel ORs into the chunk masks and the sort clears them; if a
-  // previous call stopped between the two, clear them first.
-  if (masks_dirty) {
-    run(launch_clear_u64(masks, (int64_t)(pl.chunk_base - pl.masks) / 8, s));
-    if (err == hipSuccess) masks_dirty = false;
+  if (!pooled) {
+    if (masks_dirty) {
+      run(launch_clear_u64(masks, (int64_t)(pl.chunk_base - pl.masks) / 8, s));
+      if (err == hipSuccess) masks_dirty = false;
+    }
+    run(launch_topk(logits, T, E, k, ids, tw, masks, s));
+    if (err == hipSuccess) masks_dirty = true;
   }
-  run(launch_topk(logits, T, E, k, ids, tw, masks, s));
-  if (err == hipSuccess) masks_dirty = true;
   // 3. counting sort + tile list
   mark();
   {

@@ -276,9 +276,17 @@ hipError_t launch_pool_norm(const float* P, const float* g, int T, int Dp, float
 
 // Router + pooler at small batches: reduce the split-K partials of d (fp32
 // out0 = P, out1 = logits + bias1) and normalize each P row into xp in one
-// kernel. mode 0: bf16 xp, 2: MXFP8 (codes to xp, scales).
+// kernel. mode 0: bf16 xp, 2: MXFP8 (codes to xp, scales). With tk.ids set,
+// each token's top-k (launch_topk's outputs) too, from the logits it reduced
+// (then out1 must be the [T][E] logits, ldo1 = E).
+struct TopkOut {
+  int32_t* ids;            // [T][k], or null: no top-k here
+  float* w;                // [T][k]
+  uint64_t* chunk_masks;   // [T/64][E], zero before the call
+  int k;
+};
 hipError_t launch_splitk_pool_norm(const DenseStreamParams& d, const float* g, float eps, void* xp, int mode,
-                                   uint8_t* scales, hipStream_t s);
+                                   uint8_t* scales, const TopkOut& tk, hipStream_t s);
 
 // MXFP4-expert path: xp quantized to MXFP8 E4M3 blocks of 32 (codes [T][Dp],
 // scales [T][Dp/32]) instead of stored as bf16.

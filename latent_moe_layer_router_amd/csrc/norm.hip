@@ -17,6 +17,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "mx.h"
+#include "route.h"
 
 namespace lmoe {
 
@@ -220,7 +221,8 @@ template <int MODE>   // 0: bf16 xp, 2: MXFP8 codes + scales
 __global__ __launch_bounds__(kSplitNormThreads) void splitk_pool_norm_kernel(DenseStreamParams d, int part_ld,
                                                                             const float* __restrict__ g,
                                                                             float eps, void* xp,
-                                                                            uint8_t* __restrict__ scales) {
+                                                                            uint8_t* __restrict__ scales,
+                                                                            TopkOut tk) {
   constexpr int NT = kSplitNormThreads;
   __shared__ float red[NT / kWave];
   const int t = blockIdx.x;
@@ -254,6 +256,9 @@ __global__ __launch_bounds__(kSplitNormThreads) void splitk_pool_norm_kernel(Den
                          scales + (int64_t)t * (Dp / 32), red);
   else
     pool_norm_row<NT>(P, g, Dp, eps, static_cast<bf16_t*>(xp) + (int64_t)t * Dp, red);
+  // the token's top-k on the logits this workgroup wrote before the barrier
+  if (tk.ids && threadIdx.x < kWave)
+    topk_token(d.out1 + (int64_t)t * d.ldo1, t, d.N - d.n_split, tk.k, tk.ids, tk.w, tk.chunk_masks);
 }
 
 // Stand-alone MXFP8 E4M3 quantization of n fp32 values (n a multiple of 32).
@@ -405,16 +410,17 @@ hipError_t launch_pool_norm_mx(const float* P, const float* g, int T, int Dp, fl
 }
 
 hipError_t launch_splitk_pool_norm(const DenseStreamParams& d, const float* g, float eps, void* xp, int mode,
-                                   uint8_t* scales, hipStream_t s) {
+                                   uint8_t* scales, const TopkOut& tk, hipStream_t s) {
   if (d.T == 0) return hipSuccess;
   if (d.out0_bf16 || d.n_split % 64 || d.N < d.n_split || (mode == 2 && !scales)) return hipErrorInvalidValue;
+  if (tk.ids && (d.ldo1 != d.N - d.n_split || !tk.w || !tk.chunk_masks)) return hipErrorInvalidValue;
   const int ld = dense_stream_part_ld(d.N);
   if (mode == 0)
     hipLaunchKernelGGL(splitk_pool_norm_kernel<0>, dim3(d.T), dim3(kSplitNormThreads), 0, s, d, ld, g, eps, xp,
-                       scales);
+                       scales, tk);
   else if (mode == 2)
     hipLaunchKernelGGL(splitk_pool_norm_kernel<2>, dim3(d.T), dim3(kSplitNormThreads), 0, s, d, ld, g, eps, xp,
-                       scales);
+                       scales, tk);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

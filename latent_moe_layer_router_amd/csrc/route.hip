@@ -21,106 +21,23 @@
 // deterministic.
 #include "common.h"
 #include "kernels.h"
+#include "route.h"
 
 namespace lmoe {
 
 namespace {
 
-constexpr int kChunk = 64;
-constexpr int kMaxE = 1024;
-constexpr int kMaxPerLane = kMaxE / kWave;  // 16
-
-// Wave-wide maximum with DPP moves (no LDS round trip): butterflies inside
-// quads, half-rows and rows of 16 lanes, then row broadcasts carry each row's
-// maximum upward; lane 63 ends with the wave's maximum.
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x141, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x140, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x142, 0xA, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x143, 0xC, 0xF, false)));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
-// One wave per token (4 per workgroup), so that even a decode-sized batch
-// spreads over the GPU: k rounds of a wave arg-max, each on the lanes' best
-// untaken logits (lowest index on ties) with the wave maximum from wave_max and
-// the winner the lowest index among the lanes holding it (usually one lane).
-// The token's bit goes into its chunk's mask of each selected expert with a
-// global atomic OR, which gives the same masks in any order.
-//
-// Non-finite logits: NaN scores as -inf, and a lane offers its first untaken
-// slot even when every untaken score it holds is -inf. Since k <= E, some
-// valid slot is untaken in each round, so some lane has an offer, the ballot
-// is never empty and every round selects a valid, distinct expert (with ties,
-// -inf ones included, going to the lower index). Weights: the softmax of the
-// selected scores; when the largest one is infinite (all selected -inf, or some
-// +inf), equal shares among the slots holding it, the softmax's limit.
+// One wave per token, 4 per workgroup, so that even a decode-sized batch
+// spreads over the GPU.
 constexpr int kTopkWaves = 4;
 
 __global__ __launch_bounds__(kTopkWaves * 64) void topk_kernel(const float* __restrict__ logits, int T,
                                                                int E, int k, int32_t* __restrict__ ids,
                                                                float* __restrict__ w,
                                                                uint64_t* __restrict__ chunk_masks) {
-  const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kTopkWaves + (threadIdx.x >> 6);
   if (t >= T) return;                        // whole waves
-  const int per = (E + kWave - 1) / kWave;
-  float v[kMaxPerLane];
-  unsigned taken = 0;
-#pragma unroll
-  for (int q = 0; q < kMaxPerLane; ++q) {
-    const int e = q * kWave + lane;
-    const bool ok = q < per && e < E;
-    // unconditional load from a clamped (valid) address, masked afterwards
-    const float x = logits[(int64_t)t * E + (e < E ? e : E - 1)];
-    v[q] = (!ok || x != x) ? -INFINITY : x;
-    if (!ok) taken |= 1u << q;               // slots past E are never offered
-  }
-  float sel_v = 0.f, top = 0.f, den = 0.f;
-  int n_top = 0;                             // selected slots whose score equals the first
-  int my_id = 0;                             // lane j < k keeps the j-th selected expert
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;                     // no offer yet
-#pragma unroll
-    for (int q = 0; q < kMaxPerLane; ++q)
-      // ascending q: the first untaken slot is always offered, later ones only
-      // if strictly larger, so ties keep the lower index
-      if (!(taken >> q & 1u) && (bi == 0x7FFFFFFF || v[q] > bv)) {
-        bv = v[q];
-        bi = q * kWave + lane;
-      }
-    const float vmax = wave_max(bv);
-    const uint64_t tie = __ballot(bi != 0x7FFFFFFF && bv == vmax);   // never empty (see above)
-    int win;
-    if (__popcll(tie) == 1) {
-      win = __builtin_amdgcn_readlane(bi, __ffsll((unsigned long long)tie) - 1);
-    } else {                                   // several lanes hold the maximum
-      win = 0x7FFFFFFF;
-      for (uint64_t m = tie; m; m &= m - 1) {
-        const int l = __ffsll((unsigned long long)m) - 1;
-        const int c = __builtin_amdgcn_readlane(bi, l);
-        win = c < win ? c : win;
-      }
-    }
-    if ((win & 63) == lane) taken |= 1u << (win >> 6);
-    if (j == 0) top = vmax;
-    den += expf(vmax - top);
-    n_top += vmax == top;
-    if (lane == j) {
-      my_id = win;
-      sel_v = vmax;
-    }
-  }
-  if (lane < k) {
-    const float wj = isinf(top) ? (sel_v == top ? 1.f / (float)n_top : 0.f) : expf(sel_v - top) / den;
-    ids[(int64_t)t * k + lane] = my_id;
-    w[(int64_t)t * k + lane] = wj;
-    atomicOr(reinterpret_cast<unsigned long long*>(chunk_masks) + (int64_t)(t / kChunk) * E + my_id,
-             1ull << (t % kChunk));
-  }
+  topk_token(logits + (int64_t)t * E, t, E, k, ids, w, chunk_masks);
 }
 
 // Exclusive prefix sum over the block (blockDim.x a multiple of 64, <= 1024).
@@ -154,6 +71,30 @@ __device__ int block_exclusive_scan(int x, int* wave_tot, int* total) {
 // One workgroup of 1024 threads: thread (part q, expert e) with e < E_pad (E
 // rounded up to a wave) takes a contiguous share of the chunks, so that the
 // per-expert walk over the chunks runs in 1024 / E_pad parallel pieces.
+// Chunk `chunk`'s assignments, by one wave: token t = 64 chunk + lane places
+// its k assignments, then the wave clears the chunk's masks for the next
+// call's atomic ORs (every lane's mask loads have returned by then: their
+// values fed the positions stored before).
+__device__ __forceinline__ void scatter_chunk(const SortParams& p, int chunk, int lane) {
+  const int t = chunk * kChunk + lane;
+  if (t < p.T) {
+    const uint64_t below = lanemask_lt(lane);
+    for (int j = 0; j < p.k; ++j) {
+      const int a = t * p.k + j;
+      const int e = p.ids[a];
+      const uint64_t m = p.chunk_masks[(int64_t)chunk * p.E + e];
+      const int pos = p.offsets[e] + p.chunk_base[(int64_t)chunk * p.E + e] + __popcll(m & below);
+      p.sorted_assign[pos] = a;
+      p.inv[a] = pos;
+      p.row_tok[pos] = t;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  for (int e = lane; e < p.E; e += kChunk) p.chunk_masks[(int64_t)chunk * p.E + e] = 0ull;
+}
+
+constexpr int kScanScatterChunks = 1024 / kWave;
+
 __global__ __launch_bounds__(1024) void sort_scan_kernel(SortParams p) {
   __shared__ int wave_tot[16];
   __shared__ int total;
@@ -224,27 +165,18 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(SortParams p) {
   const int mbase = block_exclusive_scan(nt2, wave_tot, &total);
   if (head) p.mt_off[e] = mbase;
   if (threadIdx.x == 0) p.mt_off[p.E] = total;
+  // Up to 16 chunks: the placement too, one wave per chunk, once the offsets
+  // and chunk bases written above are visible to every wave and every wave's
+  // reads of the masks are done.
+  if (n_chunks <= kScanScatterChunks) {
+    __syncthreads();
+    const int wave = threadIdx.x >> 6;
+    if (wave < n_chunks) scatter_chunk(p, wave, threadIdx.x & 63);
+  }
 }
 
 __global__ __launch_bounds__(64) void sort_scatter_kernel(SortParams p) {
-  const int chunk = blockIdx.x, lane = threadIdx.x;
-  const int t = chunk * kChunk + lane;
-  if (t < p.T) {
-    const uint64_t below = lanemask_lt(lane);
-    for (int j = 0; j < p.k; ++j) {
-      const int a = t * p.k + j;
-      const int e = p.ids[a];
-      const uint64_t m = p.chunk_masks[(int64_t)chunk * p.E + e];
-      const int pos = p.offsets[e] + p.chunk_base[(int64_t)chunk * p.E + e] + __popcll(m & below);
-      p.sorted_assign[pos] = a;
-      p.inv[a] = pos;
-      p.row_tok[pos] = t;
-    }
-  }
-  // The chunk's masks are read only here (after the scan): clear them for the
-  // next call's atomic ORs, once every lane has read its own.
-  __syncthreads();
-  for (int e = lane; e < p.E; e += kChunk) p.chunk_masks[(int64_t)chunk * p.E + e] = 0ull;
+  scatter_chunk(p, blockIdx.x, threadIdx.x);
 }
 
 // Zero n 64-bit words (the chunk masks after an interrupted call). A kernel
@@ -277,7 +209,7 @@ hipError_t launch_sort(const SortParams& p, hipStream_t s) {
   if (n_chunks == 0) return hipSuccess;
   hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), 0, s, p);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || n_chunks <= kScanScatterChunks) return err;
   hipLaunchKernelGGL(sort_scatter_kernel, dim3(n_chunks), dim3(64), 0, s, p);
   return hipGetLastError();
 }

@@ -9,10 +9,11 @@ slots holding the largest score when it is infinite. These cases check the
 GPU's ids, expert offsets and sorted order bit for bit against the oracle's,
 its weights against the oracle's, and that a NaN token leaves every other
 token's output within the bf16 tolerance (its own output is NaN, as the
-oracle's is). Cases run on the dense projections of both batch regimes (split-K
-streaming at T <= 128, tiled above) and on both expert kernels (weight
-streaming for a few rows per expert, tiled when the bias sends every token to
-the same experts).
+oracle's is). Cases run on both batch regimes (at T <= 128 split-K streaming
+dense projections, the top-k inside the pooled-norm kernel and every expert on
+the weight-streaming kernels; above, the tiled dense projections, the top-k
+kernel, and the tiled expert GEMM when the bias sends every token to the same
+experts).
 """
 import numpy as np
 import pytest
@@ -119,26 +120,30 @@ def test_minus_inf_bias_leaves_k_minus_1_experts(T):
     check(w, *run(w, wts, x), bad_rows=(7,))
 
 
-def test_all_minus_inf_bias():
+@pytest.mark.parametrize("T", [100, 200])
+def test_all_minus_inf_bias(T):
     """-inf bias on every expert: experts 0..k-1 with equal weights for every
-    token, so each of them gets all T rows (the tiled expert GEMMs)."""
-    w = workload(200)
+    token, so each of them gets all T rows (the tiled expert GEMMs at 200
+    tokens; at 100 the streaming kernels in two passes, after the top-k that
+    runs inside the small-batch pooled-norm kernel)."""
+    w = workload(T)
     wts = synth.dense_weights(w)
     wts["b_router"] = np.full(w.E, -np.inf, np.float32)
-    got, a, ref, raux = run(w, wts, synth.x(w, T=200))
+    got, a, ref, raux = run(w, wts, synth.x(w, T=T))
     assert np.all(a["topk_ids"] == np.arange(w.k)) and np.all(a["topk_w"] == np.float32(1 / w.k))
     check(w, got, a, ref, raux)
 
 
-def test_plus_inf_bias():
+@pytest.mark.parametrize("T", [100, 200])
+def test_plus_inf_bias(T):
     """+inf bias on two experts: both are selected first by every token and share
     the weight equally; the other slots get 0."""
-    w = workload(200)
+    w = workload(T)
     wts = synth.dense_weights(w)
     b = np.zeros(w.E, np.float32)
     b[[200, 9]] = np.inf
     wts["b_router"] = b
-    got, a, ref, raux = run(w, wts, synth.x(w, T=200))
+    got, a, ref, raux = run(w, wts, synth.x(w, T=T))
     assert np.all(a["topk_ids"][:, :2] == [9, 200])
     assert np.all(a["topk_w"][:, :2] == 0.5) and np.all(a["topk_w"][:, 2:] == 0)
     check(w, got, a, ref, raux)
