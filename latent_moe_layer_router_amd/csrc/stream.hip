@@ -315,8 +315,12 @@ constexpr int DST = 128 * 128;         // token bytes per stage
 constexpr int WJ = DR / 8, LPS = WJ + 4;
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past every extent
 
-__shared__ __attribute__((aligned(16))) unsigned char dw0[DSW], dt0[DST], dw1[DSW], dt1[DST],
-    dw2[DSW], dt2[DST], dw3[DSW], dt3[DST];
+// One object per stage (weights, then tokens at DSW): the compiler tells the
+// stages apart around the loads into LDS only while it tracks few enough
+// objects; with a weight and a token object per stage it waited for the later
+// stages' loads before reading the current one.
+__shared__ __attribute__((aligned(16))) unsigned char ds0[DSW + DST], ds1[DSW + DST], ds2[DSW + DST],
+    ds3[DSW + DST];
 
 __global__ __launch_bounds__(DW * 64) void dense_stream_kernel(DenseStreamParams p) {
   const int grp = blockIdx.x / p.slices, sl = blockIdx.x % p.slices;
@@ -376,15 +380,19 @@ __global__ __launch_bounds__(DW * 64) void dense_stream_kernel(DenseStreamParams
 #pragma unroll
   for (int u = 0; u < 2; ++u) fo[u] = r16 * 128 + (((4 * u + kq) ^ swz8(r16)) << 4);
   const int wrow = wave * DR * 128;              // this wave's weight tiles in a stage
+// All fragments of a K-half are read before its MFMAs (every token tile is in
+// the stage, zero past T), so the reads are in flight together instead of
+// one read, one wait, two MFMAs at a time.
 #define LMOE_DCOMPUTE(SW, ST)                                                                    \
   _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                               \
-    uint4 b[NTW];                                                                               \
+    uint4 b[NTW], a[MTD];                                                                       \
     _Pragma("unroll") for (int t = 0; t < NTW; ++t)                                             \
       b[t] = *reinterpret_cast<const uint4*>((SW) + wrow + t * 2048 + fo[u]);                   \
     _Pragma("unroll") for (int mt = 0; mt < MTD; ++mt)                                          \
+      a[mt] = *reinterpret_cast<const uint4*>((ST) + mt * 2048 + fo[u]);                        \
+    _Pragma("unroll") for (int mt = 0; mt < MTD; ++mt)                                          \
       if (mt < n_mt) {                                                                          \
-        const uint4 a = *reinterpret_cast<const uint4*>((ST) + mt * 2048 + fo[u]);              \
-        _Pragma("unroll") for (int t = 0; t < NTW; ++t) mfma16(a, b[t], acc[mt][t]);            \
+        _Pragma("unroll") for (int t = 0; t < NTW; ++t) mfma16(a[mt], b[t], acc[mt][t]);        \
       }                                                                                         \
   }
   // Stage c: this wave's loads of stage c have landed (at most the two later
@@ -399,14 +407,14 @@ __global__ __launch_bounds__(DW * 64) void dense_stream_kernel(DenseStreamParams
     LMOE_DISSUE(((c) + DS - 1 < nc ? (c) + DS - 1 : nc - 1), NW, NT)                             \
     LMOE_DCOMPUTE(SW, ST)                                                                       \
   }
-  LMOE_DISSUE(0, dw0, dt0)
-  LMOE_DISSUE((1 < nc ? 1 : nc - 1), dw1, dt1)
-  LMOE_DISSUE((2 < nc ? 2 : nc - 1), dw2, dt2)
+  LMOE_DISSUE(0, ds0, ds0 + DSW)
+  LMOE_DISSUE((1 < nc ? 1 : nc - 1), ds1, ds1 + DSW)
+  LMOE_DISSUE((2 < nc ? 2 : nc - 1), ds2, ds2 + DSW)
   for (int c = 0; c < nc; c += 4) {
-    LMOE_DSTAGE(c, dw0, dt0, dw3, dt3)
-    LMOE_DSTAGE(c + 1, dw1, dt1, dw0, dt0)
-    LMOE_DSTAGE(c + 2, dw2, dt2, dw1, dt1)
-    LMOE_DSTAGE(c + 3, dw3, dt3, dw2, dt2)
+    LMOE_DSTAGE(c, ds0, ds0 + DSW, ds3, ds3 + DSW)
+    LMOE_DSTAGE(c + 1, ds1, ds1 + DSW, ds0, ds0 + DSW)
+    LMOE_DSTAGE(c + 2, ds2, ds2 + DSW, ds1, ds1 + DSW)
+    LMOE_DSTAGE(c + 3, ds3, ds3 + DSW, ds2, ds2 + DSW)
   }
 #undef LMOE_DSTAGE
 #undef LMOE_DCOMPUTE
