@@ -8,10 +8,10 @@
 // Row tiles of up to 320 rows x 256 weight rows, 512 threads = 8 wave64 in a
 // 2 x 4 grid, each wave up to 160 x 64 = 5 x 2 MFMA 32x32x16 bf16 (160
 // accumulator registers of the 256 each of two waves per SIMD gets). An expert's rows
-// are split evenly over ceil(rows / 320) tiles and each tile's rows evenly
-// between its two wave rows (in multiples of 32), so a 512-row expert runs two
-// tiles of 256 (four 32-row groups per wave) and one of 513..640 rows still
-// two tiles (of up to five groups). With 256-row tiles, near-uniform routing
+// are split over ceil(rows / 320) tiles in whole units of 64 rows and each
+// tile's rows evenly between its two wave rows (in multiples of 32), so a
+// 512-row expert runs two tiles of 256 (four 32-row groups per wave) and one of
+// 513..640 rows two tiles of 320 and the rest (five and at most four groups). With 256-row tiles, near-uniform routing
 // (512 +- 23 rows per expert) gave half the experts a third tile that loads
 // the expert's whole weight slice once more; the loads bound this kernel.
 // (A 4-wave layout of the same tile needs 320 accumulator registers per lane,
@@ -154,13 +154,18 @@ __device__ __forceinline__ TileGeo tile_geo(const GroupedParams& p, int t) {
       if (p.ntiles_n * p.mt_off[mid] <= t) lo = mid; else hi = mid;
     }
     g.e = lo;
-    // the expert's rows split evenly over its row tiles (each at most 320 rows)
+    // the expert's rows split over its row tiles in whole units of 64 rows
+    // (each tile at most 320 rows): a tile's time goes with the 32-row groups
+    // of its larger wave row, ceil(rows / 64), so 530 rows run as 320 + 210
+    // (5 + 4 groups) rather than 265 + 265 (5 + 5)
     const int mt_e = p.mt_off[lo + 1] - p.mt_off[lo];
     const int tl = t - p.ntiles_n * p.mt_off[lo];
     const int mi_t = tl % mt_e, cnt = p.offsets[lo + 1] - p.offsets[lo];
+    const int G = (cnt + 63) >> 6;
+    const int g0 = (int)((int64_t)G * mi_t / mt_e), g1 = (int)((int64_t)G * (mi_t + 1) / mt_e);
     g.ntile = tl / mt_e;
-    g.m0 = p.offsets[lo] + (int)((int64_t)cnt * mi_t / mt_e);
-    g.m_end = p.offsets[lo] + (int)((int64_t)cnt * (mi_t + 1) / mt_e);
+    g.m0 = p.offsets[lo] + min(cnt, 64 * g0);
+    g.m_end = p.offsets[lo] + min(cnt, 64 * g1);
   }
   return g;
 }

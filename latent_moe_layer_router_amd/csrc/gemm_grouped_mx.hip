@@ -19,8 +19,8 @@
 //   result: register v of lane l at row 8 (v / 4) + 4q + v % 4, column l % 32.
 //
 // Row tiles as in the bf16 grouped GEMM: up to 320 rows x 256 weight rows, each
-// expert's rows split evenly over ceil(rows / 320) tiles and each tile's rows
-// between two wave rows. 512 threads = 8 wave64 in a 2 x 4 grid, each wave up
+// expert's rows split over ceil(rows / 320) tiles in whole units of 64 rows
+// and each tile's rows between two wave rows. 512 threads = 8 wave64 in a 2 x 4 grid, each wave up
 // to 160 x 64 = 5 x 2 MFMAs per K-step of 64 (160 accumulator registers, two
 // waves per SIMD). With 256-row tiles, near-uniform routing (512 +- 23 rows per
 // expert) gave half the experts a third row tile that loads the whole weight
@@ -129,8 +129,11 @@ __global__ __launch_bounds__(XNT, 1) void gemm_grouped_mx_kernel(GroupedMxParams
   const int tl = t - p.ntiles_n * p.mt_off[e];
   const int mi_t = tl % mt_e, cnt = p.offsets[e + 1] - p.offsets[e];
   const int ntile = tl / mt_e;
-  const int m0 = p.offsets[e] + (int)((int64_t)cnt * mi_t / mt_e);
-  const int m_end = p.offsets[e] + (int)((int64_t)cnt * (mi_t + 1) / mt_e);
+  // whole units of 64 rows per tile, as in the bf16 grouped GEMM
+  const int G = (cnt + 63) >> 6;
+  const int g0 = (int)((int64_t)G * mi_t / mt_e), g1 = (int)((int64_t)G * (mi_t + 1) / mt_e);
+  const int m0 = p.offsets[e] + min(cnt, 64 * g0);
+  const int m_end = p.offsets[e] + min(cnt, 64 * g1);
   const int n0 = ntile * (EPI == EPI_SWIGLU ? XBN / 2 : XBN);   // output column start
   const int K = p.K;
   // the tile's rows split between the wave rows: wm = 0 takes the first r_half

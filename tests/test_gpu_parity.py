@@ -175,9 +175,10 @@ def test_small_batch_experts_in_passes(monkeypatch, counts, fused):
 
 def test_grouped_tile_boundaries():
     """Experts at the grouped GEMM's row-tile boundaries (tiles of up to 320
-    rows, split evenly; each split again between two wave rows): 65 rows (the
-    smallest tiled expert), 320 (one full tile), 321 and 640 (two tiles), 641
-    and 1000 (three and four), 64 (streamed) and 0."""
+    rows, split in whole units of 64 rows; each split again between two wave
+    rows): 65 rows (the smallest tiled expert), 320 (one full tile), 321 (192 +
+    129) and 640 (two tiles of 320), 641 (192 + 256 + 193) and 1000 (four
+    tiles, the last 232 rows), 64 (streamed) and 0."""
     counts = [65, 320, 321, 640, 641, 1000, 64, 0]
     assign = np.repeat(np.arange(len(counts)), counts)
     w = tiny(T=len(assign), D=256, Dp=256, F_=256, E=len(counts), k=1, seed=112, act=synth.BF16)
