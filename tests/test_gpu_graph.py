@@ -4,8 +4,9 @@ eager work (a fill of the output, an eager forward) and synchronizations between
 the replays. The forward is deterministic, so the comparison is exact.
 
 Cases cover the kernels a forward launches: the small-batch dense projections
-and the weight-streaming expert GEMMs (T <= 128), the tiled dense and grouped
-GEMMs (larger T, experts above the streaming limit), and the MXFP4 path.
+and the weight-streaming expert GEMMs (T <= 128; also the fused expert kernel on
+packed weights), the tiled dense and grouped GEMMs (larger T, experts above the
+streaming limit), and the MXFP4 path.
 """
 import pytest
 import torch
@@ -21,10 +22,13 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def replay_case(w, replays=4):
-    H.say(f"[gpu] graph replay: T={w.T} D={w.D} Dp={w.Dp} F={w.F} E={w.E} k={w.k} experts={w.expert_w}")
-    wts = synth.dense_weights(w)
-    block = lmoe.LatentMoE(upload(wts), w.k, w.T, w.eps_pool, w.eps_expert, out_dtype=torch.float32)
+def replay_case(w, replays=4, packed=False):
+    H.say(f"[gpu] graph replay: T={w.T} D={w.D} Dp={w.Dp} F={w.F} E={w.E} k={w.k} experts={w.expert_w} "
+          f"packed={packed}")
+    tw = upload(synth.dense_weights(w))
+    if packed:
+        tw = lmoe.pack_expert_weights(tw)
+    block = lmoe.LatentMoE(tw, w.k, w.T, w.eps_pool, w.eps_expert, out_dtype=torch.float32, packed=packed)
     x = sdev.to_device(synth.x(w), DEV)
     ref = block.forward(x).clone()
     torch.cuda.synchronize()
@@ -50,6 +54,14 @@ def replay_case(w, replays=4):
 def test_graph_small_batch_bf16():
     """T = 100: dense projections by split-K streaming, all experts streamed."""
     replay_case(tiny(T=100, D=256, Dp=128, F_=192, E=8, k=2, seed=301, act=synth.BF16))
+
+
+def test_graph_fused_packed(monkeypatch):
+    """The fused expert kernel (forced by LMOE_FUSED_EXPERTS) on weights in the
+    packed expert layout, after the top-k inside the small-batch pooled-norm
+    kernel and the sort's one-launch placement."""
+    monkeypatch.setenv("LMOE_FUSED_EXPERTS", "1")
+    replay_case(tiny(T=96, D=256, Dp=512, F_=256, E=16, k=4, seed=303, act=synth.BF16), packed=True)
 
 
 def test_graph_tiled_bf16():
