@@ -58,6 +58,16 @@ def test_small_bf16_ragged_T(T):
     run_case(tiny(T=T, D=256, Dp=128, F_=192, E=8, k=2, seed=101, act=synth.BF16), T=T)
 
 
+@pytest.mark.parametrize("T", [128, 129, 1024, 1025])
+def test_regime_boundaries(T):
+    """Batch sizes at the host's switches: up to 128 tokens the split-K dense
+    projections with the top-k inside the pooled-norm kernel and every expert
+    streamed, from 129 the tiled projections, the top-k kernel and the tiled
+    expert GEMM; up to 1024 tokens (16 chunks of 64) the sort's scan workgroup
+    also places the assignments, from 1025 a second launch does."""
+    run_case(tiny(T=T, D=512, Dp=256, F_=256, E=16, k=2, seed=140 + T % 7, act=synth.BF16), T=T)
+
+
 @pytest.mark.parametrize("T", [641, 1000])
 def test_dense_tiled_ragged_T(T):
     """T > 128 with Dp a multiple of 256: the router + pooler and the unpooler run
