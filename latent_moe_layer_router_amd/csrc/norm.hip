@@ -225,10 +225,15 @@ __global__ __launch_bounds__(kSplitNormThreads) void splitk_pool_norm_kernel(Den
                                                                             TopkOut tk) {
   constexpr int NT = kSplitNormThreads;
   __shared__ float red[NT / kWave];
-  const int t = blockIdx.x;
+  // With the top-k, workgroups T .. 2T - 1 take the logit columns and the
+  // top-k of token blockIdx.x - T, beside the pooled-row workgroups (the two
+  // run at once instead of one after the other).
+  const bool topk_role = tk.ids && (int)blockIdx.x >= d.T;
+  const int t = topk_role ? blockIdx.x - d.T : blockIdx.x;
+  const int lo = topk_role ? d.n_split : 0, hi = (tk.ids && !topk_role) ? d.n_split : d.N;
   const int64_t plane = (int64_t)d.T * part_ld;
   float* P = static_cast<float*>(d.out0) + (int64_t)t * d.ldo0;
-  for (int n0 = threadIdx.x * 4; n0 < d.N; n0 += NT * 4) {
+  for (int n0 = lo + threadIdx.x * 4; n0 < hi; n0 += NT * 4) {
     const float* src = d.part + (int64_t)t * part_ld + n0;
     float4 s = *reinterpret_cast<const float4*>(src);
 #pragma unroll 8
@@ -240,7 +245,7 @@ __global__ __launch_bounds__(kSplitNormThreads) void splitk_pool_norm_kernel(Den
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int n = n0 + e;
-      if (n >= d.N) break;
+      if (n >= hi) break;
       if (n < d.n_split) {
         P[n] = sv[e];
       } else {
@@ -249,16 +254,19 @@ __global__ __launch_bounds__(kSplitNormThreads) void splitk_pool_norm_kernel(Den
       }
     }
   }
-  __syncthreads();
+  __syncthreads();                           // (uniform: a workgroup has one role)
+  if (topk_role) {
+    // the token's top-k on the logits this workgroup wrote before the barrier
+    if (threadIdx.x < kWave)
+      topk_token(d.out1 + (int64_t)t * d.ldo1, t, d.N - d.n_split, tk.k, tk.ids, tk.w, tk.chunk_masks);
+    return;
+  }
   const int Dp = d.n_split;
   if (MODE == 2)
     pool_norm_mx_row<NT>(P, g, Dp, eps, static_cast<uint8_t*>(xp) + (int64_t)t * Dp,
                          scales + (int64_t)t * (Dp / 32), red);
   else
     pool_norm_row<NT>(P, g, Dp, eps, static_cast<bf16_t*>(xp) + (int64_t)t * Dp, red);
-  // the token's top-k on the logits this workgroup wrote before the barrier
-  if (tk.ids && threadIdx.x < kWave)
-    topk_token(d.out1 + (int64_t)t * d.ldo1, t, d.N - d.n_split, tk.k, tk.ids, tk.w, tk.chunk_masks);
 }
 
 // Stand-alone MXFP8 E4M3 quantization of n fp32 values (n a multiple of 32).
@@ -416,11 +424,11 @@ hipError_t launch_splitk_pool_norm(const DenseStreamParams& d, const float* g, f
   if (tk.ids && (d.ldo1 != d.N - d.n_split || !tk.w || !tk.chunk_masks)) return hipErrorInvalidValue;
   const int ld = dense_stream_part_ld(d.N);
   if (mode == 0)
-    hipLaunchKernelGGL(splitk_pool_norm_kernel<0>, dim3(d.T), dim3(kSplitNormThreads), 0, s, d, ld, g, eps, xp,
-                       scales, tk);
+    hipLaunchKernelGGL(splitk_pool_norm_kernel<0>, dim3(tk.ids ? 2 * d.T : d.T), dim3(kSplitNormThreads), 0, s, d,
+                       ld, g, eps, xp, scales, tk);
   else if (mode == 2)
-    hipLaunchKernelGGL(splitk_pool_norm_kernel<2>, dim3(d.T), dim3(kSplitNormThreads), 0, s, d, ld, g, eps, xp,
-                       scales, tk);
+    hipLaunchKernelGGL(splitk_pool_norm_kernel<2>, dim3(tk.ids ? 2 * d.T : d.T), dim3(kSplitNormThreads), 0, s, d,
+                       ld, g, eps, xp, scales, tk);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -143,13 +143,16 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(SortParams p) {
   if (threadIdx.x == 0) p.offsets[p.E] = total;
   // Grouped-GEMM tiles: expert e gets ceil(count / tile_m) row tiles, unless its
   // rows are few enough for the weight-streaming kernel.
+  // (no expert has more than T rows: with T <= small_max the tile lists are
+  // empty, and their scans are skipped; the condition is uniform)
+  const bool tiled = p.T > p.small_max;
   const int nt = (head && cnt > p.small_max) ? (cnt + p.tile_m - 1) / p.tile_m : 0;
-  const int tbase = block_exclusive_scan(nt, wave_tot, &total);
+  const int tbase = tiled ? block_exclusive_scan(nt, wave_tot, &total) : 0;
   for (int i = 0; i < nt; ++i) {
     p.tiles[2 * (tbase + i)] = e;
     p.tiles[2 * (tbase + i) + 1] = off + i * p.tile_m;
   }
-  if (threadIdx.x == 0) *p.n_tiles = total;
+  if (threadIdx.x == 0) *p.n_tiles = tiled ? total : 0;
   // the streamed experts (1..small_max rows), for the fused kernel's queue
   if (p.stream_items) {
     const int st = (head && cnt > 0 && cnt <= p.small_max) ? 1 : 0;
@@ -162,9 +165,9 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(SortParams p) {
   }
   // the large-tile GEMM: ceil(count / 256) row tiles
   const int nt2 = (head && cnt > p.small_max) ? (cnt + p.tile_m2 - 1) / p.tile_m2 : 0;
-  const int mbase = block_exclusive_scan(nt2, wave_tot, &total);
+  const int mbase = tiled ? block_exclusive_scan(nt2, wave_tot, &total) : 0;
   if (head) p.mt_off[e] = mbase;
-  if (threadIdx.x == 0) p.mt_off[p.E] = total;
+  if (threadIdx.x == 0) p.mt_off[p.E] = tiled ? total : 0;
   // Up to 16 chunks: the placement too, one wave per chunk, once the offsets
   // and chunk bases written above are visible to every wave and every wave's
   // reads of the masks are done.
