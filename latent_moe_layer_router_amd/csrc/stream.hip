@@ -204,20 +204,25 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int e, int gr
 template <int EPI>
 __global__ __launch_bounds__(64) void stream_kernel(StreamParams p) {
   if (p.fused_n && *p.fused_n >= p.whole_min) return;   // the fused kernel ran these experts whole
-  const int e = blockIdx.x / p.groups, grp = blockIdx.x % p.groups;
+  // Two consecutive row groups of one expert per workgroup (groups is even):
+  // half the workgroups, so a launch with nothing to do costs half as much.
+  const int pairs = p.groups >> 1;
+  const int e = blockIdx.x / pairs, grp0 = 2 * (blockIdx.x % pairs);
   const int lo = p.offsets[e];
   const int m_e = p.offsets[e + 1] - lo;
   if (m_e == 0 || m_e > p.max_rows) return;
-  // Passes of up to 64 rows, each streaming the group's weights again (more
-  // than one only when the host let experts above 64 rows come here: batches
-  // too small for the tiled kernel to be worth a launch).
-  for (int r0 = 0; r0 < m_e; r0 += MT * 16) {
-    const int m = m_e - r0 < MT * 16 ? m_e - r0 : MT * 16;
-    switch ((m + 15) >> 4) {                 // token tiles in use (uniform)
-      case 1: stream_body<EPI, 1>(p, e, grp, lo + r0, m, sw0, sw1, sa0, sa1); break;
-      case 2: stream_body<EPI, 2>(p, e, grp, lo + r0, m, sw0, sw1, sa0, sa1); break;
-      case 3: stream_body<EPI, 3>(p, e, grp, lo + r0, m, sw0, sw1, sa0, sa1); break;
-      default: stream_body<EPI, 4>(p, e, grp, lo + r0, m, sw0, sw1, sa0, sa1); break;
+  for (int grp = grp0; grp < grp0 + 2; ++grp) {
+    // Passes of up to 64 rows, each streaming the group's weights again (more
+    // than one only when the host let experts above 64 rows come here:
+    // batches too small for the tiled kernel to be worth a launch).
+    for (int r0 = 0; r0 < m_e; r0 += MT * 16) {
+      const int m = m_e - r0 < MT * 16 ? m_e - r0 : MT * 16;
+      switch ((m + 15) >> 4) {               // token tiles in use (uniform)
+        case 1: stream_body<EPI, 1>(p, e, grp, lo + r0, m, sw0, sw1, sa0, sa1); break;
+        case 2: stream_body<EPI, 2>(p, e, grp, lo + r0, m, sw0, sw1, sa0, sa1); break;
+        case 3: stream_body<EPI, 3>(p, e, grp, lo + r0, m, sw0, sw1, sa0, sa1); break;
+        default: stream_body<EPI, 4>(p, e, grp, lo + r0, m, sw0, sw1, sa0, sa1); break;
+      }
     }
   }
 }
@@ -511,8 +516,9 @@ hipError_t launch_fused_stream(const FusedStreamParams& f, int n_cu, hipStream_t
 }
 
 hipError_t launch_stream(const StreamParams& p, EpiKind epi, hipStream_t s) {
-  const int blocks = p.n_experts * p.groups;
+  const int blocks = p.n_experts * (p.groups >> 1);
   if (blocks == 0) return hipSuccess;
+  if (p.groups & 1) return hipErrorInvalidValue;
   if (epi == EPI_SWIGLU)
     hipLaunchKernelGGL(stream_kernel<EPI_SWIGLU>, dim3(blocks), dim3(64), 0, s, p);
   else if (epi == EPI_DOWN)
