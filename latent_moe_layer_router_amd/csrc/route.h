@@ -41,15 +41,17 @@ __device__ __forceinline__ float wave_max(float v) {
 // Token t's top-k, by the calling wave (all 64 lanes): row points at its E
 // logits. Lane j < k writes the j-th selected expert and its weight, and ORs
 // the token's bit into its chunk's mask of that expert.
-__device__ __forceinline__ void topk_token(const float* __restrict__ row, int t, int E, int k,
-                                           int32_t* __restrict__ ids, float* __restrict__ w,
-                                           uint64_t* __restrict__ chunk_masks) {
+// MAXQ: the slots a lane holds at most (E <= 64 MAXQ); the rounds scan only those.
+template <int MAXQ>
+__device__ __forceinline__ void topk_token_q(const float* __restrict__ row, int t, int E, int k,
+                                             int32_t* __restrict__ ids, float* __restrict__ w,
+                                             uint64_t* __restrict__ chunk_masks) {
   const int lane = threadIdx.x & 63;
   const int per = (E + kWave - 1) / kWave;
-  float v[kMaxPerLane];
+  float v[MAXQ];
   unsigned taken = 0;
 #pragma unroll
-  for (int q = 0; q < kMaxPerLane; ++q) {
+  for (int q = 0; q < MAXQ; ++q) {
     const int e = q * kWave + lane;
     const bool ok = q < per && e < E;
     // unconditional load from a clamped (valid) address, masked afterwards
@@ -64,7 +66,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int t,
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;                     // no offer yet
 #pragma unroll
-    for (int q = 0; q < kMaxPerLane; ++q)
+    for (int q = 0; q < MAXQ; ++q)
       // ascending q: the first untaken slot is always offered, later ones only
       // if strictly larger, so ties keep the lower index
       if (!(taken >> q & 1u) && (bi == 0x7FFFFFFF || v[q] > bv)) {
@@ -100,6 +102,16 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int t,
     atomicOr(reinterpret_cast<unsigned long long*>(chunk_masks) + (int64_t)(t / kChunk) * E + my_id,
              1ull << (t % kChunk));
   }
+}
+
+// Token t's top-k (as topk_token_q), the per-lane slot count picked from E.
+__device__ __forceinline__ void topk_token(const float* __restrict__ row, int t, int E, int k,
+                                           int32_t* __restrict__ ids, float* __restrict__ w,
+                                           uint64_t* __restrict__ chunk_masks) {
+  if (E <= 4 * kWave)
+    topk_token_q<4>(row, t, E, k, ids, w, chunk_masks);
+  else
+    topk_token_q<kMaxPerLane>(row, t, E, k, ids, w, chunk_masks);
 }
 
 }  // namespace
