@@ -152,7 +152,7 @@ CSRC = os.path.join(ROOT, "latent_moe_layer_router_amd", "csrc")
 KERNEL_SOURCES = {"fused_stream_kernel": ("stream.hip", "common.h"),
                   "stream_kernel": ("stream.hip", "common.h"),
                   "dense_stream_kernel": ("stream.hip", "norm.hip", "common.h"),
-                  "splitk_pool_norm_kernel": ("norm.hip", "mx.h", "common.h"),
+                  "splitk_pool_norm_kernel": ("norm.hip", "mx.h", "route.h", "common.h"),
                   "splitk_reduce_kernel": ("stream.hip", "common.h"),
                   "stream_mx_kernel": ("stream_mx.hip", "mx.h", "common.h"),
                   "gemm_grouped_kernel": ("gemm_grouped.hip", "common.h"),
@@ -479,8 +479,8 @@ def main():
     packed = w.expert_w == synth.BF16 and not args.row_major_experts
     pack = None
     if packed:
-        # load-time re-layout of the expert weights into 64 x 64 blocks (not
-        # part of a step); the row-major copy is released
+        # load-time re-layout of the expert weights into 64 x 64 blocks, in
+        # place (not part of a step)
         tw, pack = pack_experts(lmoe, torch, tw)
         print(f"[bench] expert weights packed in {pack['ms']:.1f} ms ({pack['GB/s']} GB/s)", file=sys.stderr,
               flush=True)
